@@ -1,0 +1,330 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+* values printed on "DeepSeek Sparse Attention: Learned Token Selection from
+  Scratch" (worked example of sections 2.3-2.5 and 3.2, counts of section 7.3);
+* closed forms (section 7.2 count, exact integer arithmetic);
+* special cases that reduce to a textbook routine or a library routine
+  (dense causal attention == torch scaled_dot_product_attention in float64,
+  lexicographic sort == numpy.lexsort);
+* invariants of the method (full budget == dense, |S_t| = 1 returns v, ...);
+* brute force on tiny inputs (rank-count characterisation of the top-k).
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from golden_io import counts, worked_example
+
+from learned_sparse_attention_lightning_amd import configs, synth
+
+
+def _example_inputs(k10):
+    """Indexer inputs of the worked example as a 1-query block at t = 10,
+    S = 11 (positions 0..10); position 10's key is supplied by the caller."""
+    ex = worked_example()
+    q = np.array([[ex["q"][1], ex["q"][2]]], dtype=np.float64).reshape(1, 1, 2, 2)
+    w = np.array([[ex["w"][1], ex["w"][2]]], dtype=np.float64).reshape(1, 1, 2)
+    keys = [ex["k"][s] for s in range(10)] + [k10]
+    k = np.array(keys, dtype=np.float64).reshape(1, 11, 2)
+    return ex, q, k, w, np.array([[10]], dtype=np.int64)
+
+
+# ---------------------------------------------------------------- indexer ---
+
+def test_worked_example_scores(oracle):
+    ex, q, k, w, pos = _example_inputs([-1.0, 0.0])
+    sc = oracle.indexer_scores(q, k, w, q_pos=pos)[0, 0]
+    for s in range(10):
+        assert abs(sc[s] - ex["I"][s]) <= 1e-12, (s, sc[s], ex["I"][s])
+    assert sc[10] == 0.0  # k_10 = [-1, 0] is anti-aligned with both heads
+
+
+@pytest.mark.parametrize("head", [1, 2])
+def test_worked_example_per_head_tables(oracle, head):
+    ex, q, k, w, pos = _example_inputs([-1.0, 0.0])
+    j = head - 1
+    sc = oracle.indexer_scores(q[:, :, j:j + 1], k, w[:, :, j:j + 1], q_pos=pos)[0, 0]
+    for s in range(10):
+        assert abs(sc[s] - ex["h"][s][j]) <= 1e-12, (head, s)
+
+
+def test_worked_example_selection(oracle):
+    ex, q, k, w, pos = _example_inputs([-1.0, 0.0])
+    sc = oracle.indexer_scores(q, k, w, q_pos=pos)
+    sel = oracle.topk(sc, 3, q_pos=pos)[0, 0]
+    assert list(sel) == ex["select"] == [3, 9, 8]
+
+
+def test_worked_example_tie_lower_index_wins(oracle):
+    # k_10 = k_8 = [0, 2] gives I_{10,10} = I_{10,8} = 2.0: position 8 must win.
+    ex, q, k, w, pos = _example_inputs([0.0, 2.0])
+    sc = oracle.indexer_scores(q, k, w, q_pos=pos)
+    assert sc[0, 0, 10] == sc[0, 0, 8] == 2.0
+    assert list(oracle.topk(sc, 3, q_pos=pos)[0, 0]) == [3, 9, 8]
+    # with k = 4 both tied positions are kept, lower first in rank order
+    assert list(oracle.topk(sc, 4, q_pos=pos)[0, 0]) == [3, 9, 8, 10]
+
+
+def test_causal_mask_and_positions(oracle):
+    w = configs.get("c0")
+    q, k, wt = synth.indexer_inputs(w)
+    sc = oracle.indexer_scores(q, k, wt)
+    n = w.S
+    for t in range(n):
+        assert np.all(np.isneginf(sc[0, t, t + 1:]))
+        assert np.all(np.isfinite(sc[0, t, :t + 1]))
+    # explicit positions select the same rows
+    pos = np.array([[3, 15, 0]], dtype=np.int64)
+    sub = oracle.indexer_scores(q[:, [3, 15, 0]], k, wt[:, [3, 15, 0]], q_pos=pos)
+    assert np.array_equal(sub[0], sc[0, [3, 15, 0]])
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 16, 2, 2, 8), (2, 24, 40, 4, 8, 16),
+                                   (1, 33, 33, 64, 128, 16)])
+def test_exact_integer_twin(oracle, shape):
+    B, T, S, H, D, den = shape
+    rng = np.random.default_rng(7)
+    q = rng.integers(-4, 4, size=(B, T, H, D), endpoint=True).astype(np.float64)
+    k = rng.integers(-4, 4, size=(B, S, D), endpoint=True).astype(np.float64)
+    w = rng.integers(0, den, size=(B, T, H), endpoint=True) / den
+    sc = oracle.indexer_scores(q, k, w)
+    ex = oracle.indexer_scores_exact(q, k, w, den)
+    finite = ex != np.iinfo(np.int64).min
+    assert np.array_equal(np.isneginf(sc), ~finite)
+    assert np.array_equal(sc[finite] * den, ex[finite].astype(np.float64))
+
+
+def test_zero_weights_and_linearity(oracle):
+    w = configs.get("c0")
+    q, k, wt = synth.indexer_inputs(w)
+    zero = oracle.indexer_scores(q, k, torch.zeros_like(wt))
+    fin = np.isfinite(zero)
+    assert np.all(zero[fin] == 0.0)
+    one = oracle.indexer_scores(q, k, wt)
+    two = oracle.indexer_scores(q, k, 2 * wt)
+    assert np.array_equal(two[fin], 2 * one[fin])
+    # ReLU: negating q zeroes exactly the heads that were positive
+    neg = oracle.indexer_scores(-q, k, wt)
+    qq = oracle.as_f64(q)[0]
+    kk = oracle.as_f64(k)[0]
+    ww = oracle.as_f64(wt)[0]
+    dots = np.einsum("thd,sd->ths", qq, kk)
+    low = np.tri(16, dtype=bool)
+    diff = one[0][low] - neg[0][low]
+    lin = np.einsum("th,ths->ts", ww, dots)[low]
+    assert np.array_equal(diff, lin)  # ReLU(x) - ReLU(-x) = x, exact for integers
+
+
+# ------------------------------------------------------------------ top-k ---
+
+def test_counts_running_example(oracle):
+    (n, k, dsa, dense), = counts()
+    w = configs.get("c0")
+    assert (n, k) == (w.S, w.index_topk)
+    q, kk, wt = synth.indexer_inputs(w)
+    sel = oracle.topk(oracle.indexer_scores(q, kk, wt), k)
+    assert int((sel >= 0).sum()) == dsa == 45
+    assert n * (n + 1) // 2 == dense == 136
+
+
+@pytest.mark.parametrize("n,k", [(16, 3), (40, 7), (64, 64), (50, 80), (129, 32)])
+def test_count_closed_form(oracle, n, k):
+    rng = np.random.default_rng(n * 1000 + k)
+    sc = rng.standard_normal((1, n, n))
+    sel = oracle.topk(sc, k)
+    closed = k * (k + 1) // 2 + (n - k) * k if n >= k else n * (n + 1) // 2
+    assert int((sel >= 0).sum()) == closed
+    for t in range(n):
+        row = sel[0, t]
+        nsel = min(t + 1, k)
+        assert np.all(row[:nsel] >= 0) and np.all(row[:nsel] <= t)
+        assert np.all(row[nsel:] == -1)
+        assert len(set(row[:nsel].tolist())) == nsel
+
+
+@pytest.mark.parametrize("levels", [None, 2, 3, 5])
+def test_topk_rank_count_bruteforce(oracle, levels):
+    """s in S_t  <=>  #{s' <= t : I[s'] > I[s] or (I[s'] == I[s] and s' < s)} < k."""
+    n, k = 12, 4
+    sc = synth.random_scores((2, n, n), seed=11, levels=levels).double().numpy()
+    sel = oracle.topk(sc, k)
+    for b, t in itertools.product(range(2), range(n)):
+        row = sc[b, t]
+        chosen = set(sel[b, t][sel[b, t] >= 0].tolist())
+        for s in range(t + 1):
+            beaten_by = sum(1 for s2 in range(t + 1)
+                            if row[s2] > row[s] or (row[s2] == row[s] and s2 < s))
+            assert (s in chosen) == (beaten_by < k), (b, t, s)
+
+
+def test_topk_matches_lexsort(oracle):
+    sc = synth.random_scores((3, 50, 50), seed=5, levels=6).double().numpy()
+    k = 9
+    sel = oracle.topk(sc, k)
+    for b, t in itertools.product(range(3), range(50)):
+        cand = np.arange(t + 1)
+        order = np.lexsort((cand, -sc[b, t, :t + 1]))  # last key is primary
+        want = order[:min(k, t + 1)]
+        assert np.array_equal(sel[b, t, :len(want)], want)
+
+
+def test_all_equal_scores_take_lowest_positions(oracle):
+    sc = np.zeros((1, 20, 20))
+    sel = oracle.topk(sc, 5)
+    for t in range(20):
+        assert list(sel[0, t, :min(5, t + 1)]) == list(range(min(5, t + 1)))
+
+
+def test_signed_zero_is_a_tie(oracle):
+    sc = np.array([[[0.0, -0.0, 0.0, -0.0]]])
+    sel = oracle.topk(sc, 2, q_pos=np.array([[3]]))
+    assert list(sel[0, 0]) == [0, 1]
+
+
+# -------------------------------------------------------------- attention ---
+
+def _mha(B=1, T=10, H=3, d=8, dv=6, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, T, H, d, generator=g, dtype=torch.float64)
+    K = torch.randn(B, T, H, d, generator=g, dtype=torch.float64)
+    V = torch.randn(B, T, H, dv, generator=g, dtype=torch.float64)
+    return q, K, V
+
+
+def test_dense_causal_matches_torch_sdpa(oracle):
+    q, K, V = _mha(B=2, T=17, H=3, d=8, dv=8)
+    scale = 1 / math.sqrt(8)
+    got = oracle.dense_causal_attention("mha", q, K, V, scale)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.transpose(1, 2), K.transpose(1, 2), V.transpose(1, 2), is_causal=True, scale=scale)
+    assert np.allclose(got, ref.transpose(1, 2).numpy(), atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("form", ["mha", "mla"])
+def test_full_budget_equals_dense(oracle, form):
+    """k >= t+1 keeps every candidate, so the sparse form is dense causal
+    attention ("collapses to full attention", section 7.6)."""
+    T, H = 12, 4
+    g = torch.Generator().manual_seed(3)
+    if form == "mha":
+        q, kv, v = _mha(T=T, H=H, d=8, dv=5, seed=3)
+        dv = 5
+    else:
+        q = torch.randn(1, T, H, 12, generator=g, dtype=torch.float64)
+        kv = torch.randn(1, T, 12, generator=g, dtype=torch.float64)
+        v, dv = None, 9
+    sc = np.random.default_rng(0).standard_normal((1, T, T))
+    for k in (T, T + 5):
+        sel = oracle.topk(sc, k)
+        sp = oracle.sparse_attention(form, q, kv, v, sel, 0.3, d_v=dv)
+        dn = oracle.dense_causal_attention(form, q, kv, v, 0.3, d_v=dv)
+        assert np.allclose(sp, dn, atol=1e-13, rtol=0)
+
+
+def test_single_selection_returns_value_row(oracle):
+    q, K, V = _mha(T=9, H=2, d=4, dv=4, seed=9)
+    sel = oracle.topk(np.random.default_rng(1).standard_normal((1, 9, 9)), 1)
+    out = oracle.sparse_attention("mha", q, K, V, sel, 0.5)
+    for t in range(9):
+        s = sel[0, t, 0]
+        assert np.array_equal(out[0, t], V[0, s].numpy())
+    assert sel[0, 0, 0] == 0  # row t=0 only has itself: u_0 = v_0
+
+
+def test_masked_dense_equals_gather(oracle):
+    q, K, V = _mha(B=2, T=14, H=3, d=6, dv=7, seed=4)
+    sc = synth.random_scores((2, 14, 14), seed=2, levels=4).double().numpy()
+    for t in range(14):
+        sc[:, t, t + 1:] = -np.inf
+    sel = oracle.topk(sc, 5)
+    a = oracle.sparse_attention("mha", q, K, V, sel, 0.7)
+    b = oracle.masked_dense_attention("mha", q, K, V, sel, 0.7)
+    assert np.allclose(a, b, atol=1e-13, rtol=0)
+
+
+def test_mla_equals_mha_with_shared_latent(oracle):
+    B, T, H, dqk, dv = 1, 10, 5, 12, 8
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn(B, T, H, dqk, generator=g, dtype=torch.float64)
+    c = torch.randn(B, T, dqk, generator=g, dtype=torch.float64)
+    sel = oracle.topk(np.random.default_rng(2).standard_normal((B, T, T)), 4)
+    mla = oracle.sparse_attention("mla", q, c, None, sel, 0.25, d_v=dv)
+    K = c[:, :, None, :].expand(B, T, H, dqk).contiguous()
+    V = c[:, :, None, :dv].expand(B, T, H, dv).contiguous()
+    mha = oracle.sparse_attention("mha", q, K, V, sel, 0.25)
+    assert np.array_equal(mla, mha)
+
+
+def test_permuting_selection_is_invariant(oracle):
+    q, K, V = _mha(T=16, H=2, d=8, dv=8, seed=6)
+    sel = oracle.topk(np.random.default_rng(3).standard_normal((1, 16, 16)), 6)
+    perm = sel[..., ::-1].copy()
+    a = oracle.sparse_attention("mha", q, K, V, sel, 0.4)
+    b = oracle.sparse_attention("mha", q, K, V, perm, 0.4)
+    assert np.allclose(a, b, atol=1e-14, rtol=0)
+
+
+def test_zero_query_gives_mean_of_selected_values(oracle):
+    q, K, V = _mha(T=11, H=2, d=4, dv=3, seed=8)
+    sel = oracle.topk(np.random.default_rng(4).standard_normal((1, 11, 11)), 3)
+    out = oracle.sparse_attention("mha", torch.zeros_like(q), K, V, sel, 1.0)
+    for t in range(11):
+        rows = sel[0, t][sel[0, t] >= 0]
+        assert np.allclose(out[0, t], V[0, rows].mean(0).numpy(), atol=1e-15, rtol=0)
+
+
+def test_lse_matches_library_logsumexp(oracle):
+    from scipy.special import logsumexp
+    q, K, V = _mha(T=8, H=2, d=4, dv=4, seed=12)
+    sel = oracle.topk(np.random.default_rng(5).standard_normal((1, 8, 8)), 3)
+    _, lse = oracle.sparse_attention("mha", q, K, V, sel, 0.5, with_lse=True)
+    for t, h in itertools.product(range(8), range(2)):
+        rows = sel[0, t][sel[0, t] >= 0]
+        logits = 0.5 * (K[0, rows, h] @ q[0, t, h]).numpy()
+        assert abs(lse[0, t, h] - logsumexp(logits)) < 1e-13
+
+
+# ------------------------------------------------- distillation objective ---
+
+def test_warmup_target_is_head_mean_of_dense_weights(oracle):
+    q, K, V = _mha(T=9, H=3, d=4, dv=4, seed=13)
+    p = oracle.warmup_target(q, K, 0.5)
+    assert np.allclose(p.sum(-1), 1.0, atol=1e-14)
+    for t in range(9):
+        assert np.all(p[0, t, t + 1:] == 0)
+    # per-head dense weights from torch softmax (library) averaged over heads
+    s = torch.einsum("thd,shd->hts", q[0], K[0]) * 0.5
+    s = s.masked_fill(~torch.tril(torch.ones(9, 9, dtype=torch.bool)), float("-inf"))
+    want = torch.softmax(s, -1).mean(0).numpy()
+    assert np.allclose(p[0], want, atol=1e-14, rtol=0)
+
+
+def test_head_mean_worked_number():
+    # section 5.3: eight head weights at (t=10, s=3) sum to 0.91 and average to 0.11375
+    a = [0.15, 0.02, 0.30, 0.05, 0.10, 0.01, 0.20, 0.08]
+    assert abs(sum(a) - 0.91) < 1e-15 and abs(sum(a) / 8 - 0.11375) < 1e-15
+
+
+def test_indexer_kl_against_library(oracle):
+    from scipy.special import rel_entr, softmax
+    rng = np.random.default_rng(6)
+    S = 10
+    p = rng.random((3, S))
+    p /= p.sum(-1, keepdims=True)
+    sc = rng.standard_normal((3, S))
+    mask = np.ones((3, S), dtype=np.int8)
+    want = sum(rel_entr(p[r], softmax(sc[r])).sum() for r in range(3))
+    assert abs(oracle.indexer_kl(p, sc, mask) - want) < 1e-12
+    # identical distributions: zero divergence
+    assert abs(oracle.indexer_kl(softmax(sc, axis=-1), sc, mask)) < 1e-12
+    # restricted to a subset: both sides renormalised over the subset
+    sub = np.zeros((3, S), dtype=np.int8)
+    sub[:, [1, 4, 7]] = 1
+    want_sub = 0.0
+    for r in range(3):
+        pr = p[r, [1, 4, 7]] / p[r, [1, 4, 7]].sum()
+        want_sub += rel_entr(pr, softmax(sc[r, [1, 4, 7]])).sum()
+    assert abs(oracle.indexer_kl(p, sc, sub) - want_sub) < 1e-12
