@@ -1,0 +1,173 @@
+/*
+ * dsa.h -- C ABI of the DeepSeek Sparse Attention (DSA) forward path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The path has three steps, each one entry point, plus one call that runs
+ * them back to back:
+ *   1. lightning-indexer scores      dsa_indexer_scores
+ *   2. per-query top-k selection     dsa_topk
+ *   3. attention over the selection  dsa_sparse_attention (MHA or MLA latent)
+ *   1+2+3                            dsa_forward
+ *
+ * Page references (titles as published):
+ *   [P1] "DeepSeek Sparse Attention: Learned Token Selection from Scratch"
+ *   [P4] "DeepSeek NSA and DSA: From Native Sparse Attention to Fine-Grained
+ *        Token Selection"
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Memory.  Every tensor argument is caller-owned DEVICE memory (for instance a
+ *   torch tensor's data pointer), dense row-major in the layout given, and
+ *   16-byte aligned.  The library allocates nothing, keeps no pointer after a
+ *   call returns and holds no mutable global state.  Buffers must stay alive
+ *   until the work queued on `stream` has finished.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  Every call only enqueues work; none synchronises the host.
+ * Positions.  q_pos [B,T] int32 gives the absolute position t of each query
+ *   row; NULL means t = S - T + i for row i (prefill: T == S, t = i; decode:
+ *   T == 1, t = S - 1, the new token being the last cache entry).  The
+ *   candidates of row t are the cache positions s = 0..t ([P1] sections 2.1,
+ *   7.1).  A position t >= S is treated as S-1; a negative position has no
+ *   candidates (all-masked scores, an all -1 selection, zero output).
+ * Errors.  Argument checks run on the host before anything is enqueued; on
+ *   failure the call returns a status != DSA_OK and writes nothing.  A failed
+ *   kernel launch returns DSA_ERR_HIP.  Faults inside kernels surface at the
+ *   caller's next synchronisation.  Nothing throws or aborts across the ABI.
+ *   Calls are safe from several host threads on distinct streams.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+    DSA_F32 = 0,      /* IEEE binary32 */
+    DSA_BF16 = 1,     /* bfloat16 */
+    DSA_FP8_E4M3 = 2  /* OCP fp8 e4m3fn (no infinities; the format of gfx950) */
+} dsa_dtype_t;
+
+typedef enum {
+    DSA_MHA = 0,  /* per-head keys and values ([P1] section 3.3) */
+    DSA_MLA = 1   /* one latent row per token shared by all heads, MQA mode
+                     of MLA ([P1] section 4.1, [P4] section 3.1) */
+} dsa_form_t;
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_NULL = 1,         /* a required pointer is NULL */
+    DSA_ERR_SHAPE = 2,        /* a size is out of range or sizes disagree */
+    DSA_ERR_DTYPE = 3,        /* unknown dtype code */
+    DSA_ERR_UNSUPPORTED = 4,  /* valid but not implemented combination */
+    DSA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required */
+    DSA_ERR_ALIGN = 6,        /* a tensor pointer is not 16-byte aligned */
+    DSA_ERR_HIP = 7           /* a kernel launch failed */
+} dsa_status_t;
+
+/* Attention description.  Fields are plain ints for a stable ABI. */
+typedef struct {
+    int form;       /* dsa_form_t */
+    int num_heads;  /* attention heads H */
+    int d_qk;       /* query/key width: MHA 64 or 128; MLA 576 */
+    int d_v;        /* value width: MHA == d_qk; MLA 512 (first d_v entries
+                       of the latent row) */
+    float scale;    /* softmax scale, 1/sqrt(d_k) on [P1] section 3.3 */
+    int dtype;      /* dtype of q, K/V or latent: DSA_F32 or DSA_BF16
+                       (MLA: DSA_BF16 only) */
+    int out_dtype;  /* dtype of out: DSA_F32 or DSA_BF16 */
+} dsa_attn_desc_t;
+
+/* Version of this ABI (DSA_ABI_VERSION of the built library). */
+int dsa_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *dsa_status_string(int status);
+
+/*
+ * Lightning-indexer scores, [P1] section 2.1 and [P4] section 3.2:
+ *   scores[b,i,s] = sum_j w[b,i,j] * ReLU( q_idx[b,i,j,:] . k_idx[b,s,:] )
+ * for 0 <= s <= t, and -inf for s > t.  One key per position is shared by
+ * all index heads ([P1] section 2.3).  Products and sums are fp32 (exact
+ * whenever inputs are small integers, as in the shipped workloads).
+ *   q_idx   [B,T,H_I,d_I]  idx_dtype (DSA_F32, DSA_BF16 or DSA_FP8_E4M3)
+ *   k_idx   [B,S,d_I]      idx_dtype
+ *   w       [B,T,H_I]      fp32 head weights (any sign)
+ *   q_pos   [B,T] int32 or NULL
+ *   scores  [B,T,S]        fp32 output, written in full
+ * index_n_heads (H_I) in 1..128, index_head_dim (d_I) in 1..256.
+ */
+dsa_status_t dsa_indexer_scores(const void *q_idx, const void *k_idx, int idx_dtype,
+                                const float *w, const int32_t *q_pos, int B, int T, int S,
+                                int index_n_heads, int index_head_dim, float *scores,
+                                void *stream);
+
+/*
+ * Top-k selection, [P1] section 3.1: row i keeps the n_sel = min(k, t+1)
+ * candidates s in 0..t with the highest scores, ties broken by the lower
+ * position s (the one exactly-defined selection).  -0.0 equals +0.0; NaN
+ * scores are outside the contract.
+ *   scores  [B,T,S] fp32 (entries s > t are never read)
+ *   idx     [B,T,k] int32 output: the n_sel selected positions in ASCENDING
+ *           order, then -1 in the remaining k - n_sel slots.
+ * index_topk (k) in 1..S.  Needs dsa_workspace_bytes(DSA_OP_TOPK, ...) bytes
+ * of workspace (may be 0; then workspace may be NULL).
+ */
+dsa_status_t dsa_topk(const float *scores, const int32_t *q_pos, int B, int T, int S,
+                      int index_topk, int32_t *idx, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/*
+ * Softmax attention restricted to the selected rows, [P1] sections 3.3 and
+ * 10.1, with one selected set per query shared by every head ([P1] section
+ * 4.1):
+ *   out[b,i,h,:] = sum_{s in S} softmax_s( scale * q[b,i,h,:] . key(s,h) ) * value(s,h)
+ * where S = the entries of idx[b,i,:] that are >= 0 (distinct, each < S).
+ *   MHA: kv = K [B,S,H,d_qk], v = V [B,S,H,d_v]; key(s,h) = K[b,s,h],
+ *        value(s,h) = V[b,s,h].
+ *   MLA: kv = latent [B,S,d_qk], v = NULL; key(s,h) = latent[b,s,:] (all
+ *        576 entries), value(s,h) = latent[b,s,0:d_v].
+ *   q    [B,T,H,d_qk]  desc->dtype
+ *   out  [B,T,H,d_v]   desc->out_dtype; a row with an empty set gets zeros
+ *   lse  [B,T,H] fp32 natural-log sum of exp of the scaled logits, or NULL
+ * Logits, softmax and accumulation are fp32.  Needs
+ * dsa_workspace_bytes(DSA_OP_ATTENTION, ...) bytes of workspace.
+ */
+dsa_status_t dsa_sparse_attention(const dsa_attn_desc_t *desc, const void *q, const void *kv,
+                                  const void *v, const int32_t *idx, int B, int T, int S,
+                                  int index_topk, void *out, float *lse, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
+ * The whole forward path ([P4] section 3.2, three steps): indexer scores,
+ * top-k, then attention over the selection, on one stream.  Query rows are
+ * processed in chunks so the fp32 score block stays bounded.  Arguments are
+ * those of the three calls above.  idx_out [B,T,k] receives the selection
+ * when non-NULL.  Needs dsa_workspace_bytes(DSA_OP_FORWARD, ...) bytes.
+ */
+dsa_status_t dsa_forward(const dsa_attn_desc_t *desc, const void *q_idx, const void *k_idx,
+                         int idx_dtype, const float *w, const void *q, const void *kv,
+                         const void *v, const int32_t *q_pos, int B, int T, int S,
+                         int index_n_heads, int index_head_dim, int index_topk, void *out,
+                         int32_t *idx_out, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+enum { DSA_OP_TOPK = 0, DSA_OP_ATTENTION = 1, DSA_OP_FORWARD = 2 };
+
+/*
+ * Workspace bytes needed by one call of `op` with these sizes (desc may be
+ * NULL for DSA_OP_TOPK).  Returns (size_t)-1 when the sizes are invalid.
+ */
+size_t dsa_workspace_bytes(int op, const dsa_attn_desc_t *desc, int B, int T, int S,
+                           int index_n_heads, int index_head_dim, int index_topk);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

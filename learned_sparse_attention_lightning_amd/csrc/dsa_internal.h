@@ -1,0 +1,97 @@
+// dsa_internal.h -- device helpers and kernel launchers shared by the HIP
+// translation units of the DSA library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa {
+
+// ----------------------------------------------------------- vector types --
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxGridY = 65535;  // launch limit of gridDim.y / gridDim.z
+
+// ------------------------------------------------------ scalar conversions --
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// OCP fp8 e4m3fn -> fp32, exact (bias 7, no infinities, S.1111.111 = NaN).
+__device__ __forceinline__ float fp8e4m3_to_f32(uint32_t v) {
+    const uint32_t sign = (v & 0x80u) << 24;
+    const uint32_t e = (v >> 3) & 0xfu;
+    const uint32_t m = v & 0x7u;
+    if (e == 0xfu && m == 0x7u) return __uint_as_float(0x7fc00000u | sign);
+    if (e == 0) {  // subnormal: m * 2^-9
+        const float mag = (float)m * 0.001953125f;
+        return sign ? -mag : mag;
+    }
+    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+}
+
+// Load element i of an index-tensor of dtype `dt` as fp32.
+__device__ __forceinline__ float load_as_f32(const void *p, size_t i, int dt) {
+    if (dt == DSA_F32) return static_cast<const float *>(p)[i];
+    if (dt == DSA_BF16) return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
+    return fp8e4m3_to_f32(static_cast<const uint8_t *>(p)[i]);
+}
+
+// Order-preserving map fp32 -> uint32 (a < b  <=>  key(a) < key(b)), with
+// -0.0 folded onto +0.0 so that signed zeros tie.
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Absolute position of query row i (see dsa.h), clamped to S-1.
+__device__ __forceinline__ int query_pos(const int32_t *q_pos, int b, int i, int T, int S) {
+    int t = q_pos ? q_pos[(size_t)b * T + i] : (S - T + i);
+    return t >= S ? S - 1 : t;
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------ launchers --
+// Every launcher enqueues on `stream` and returns the launch status.
+
+// Indexer scores for rows [row0, row0+rows) of every batch.  `scores` points
+// at row row0 of batch 0 with row stride S and batch stride `batch_stride`
+// (in floats).  write_masked: also write -inf for s in (t, S).
+hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, const float *w,
+                          const int32_t *q_pos, int B, int T, int S, int H, int D, int row0,
+                          int rows, float *scores, size_t batch_stride, bool write_masked,
+                          hipStream_t stream);
+
+bool indexer_shape_supported(int H, int D);
+
+size_t topk_workspace_bytes(int B, int T, int S, int k);
+hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *q_pos, int B,
+                       int T, int S, int row0, int rows, int k, int32_t *idx, void *workspace,
+                       hipStream_t stream);
+
+size_t attention_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int S, int k);
+hipError_t launch_attention(const dsa_attn_desc_t &d, const void *q, const void *kv,
+                            const void *v, const int32_t *idx, int B, int T, int S, int row0,
+                            int rows, int k, void *out, float *lse, void *workspace,
+                            hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,239 @@
+// indexer.hip -- lightning-indexer scores on gfx950.
+//
+//   I[t,s] = sum_j w[t,j] * ReLU( q_I[t,j] . k_I[s] ),  0 <= s <= t
+// ("DeepSeek Sparse Attention: Learned Token Selection from Scratch", section
+// 2.1; "DeepSeek NSA and DSA", section 3.2).  One key per position serves all
+// index heads, so for one query the H_I head vectors form the rows of an
+// M = H_I matrix and the keys the columns: a dense contraction over d_I that
+// maps onto MFMA, followed by an elementwise ReLU and a w-weighted reduction
+// over the rows (the heads) kept in fp32.
+//
+// Two kernels:
+//  * indexer_mfma_kernel<Fp8>: H_I = 64, d_I = 128 in bf16 (v_mfma 32x32x16)
+//    or OCP fp8 e4m3 (v_mfma 32x32x64 f8f6f4).  One wave owns one query row
+//    and a chunk of key positions; its 64x128 query block stays in registers
+//    as the A operand, each 32-key tile of keys is the B operand.
+//  * indexer_generic_kernel: any H_I*d_I <= 16384 and any index dtype, plain
+//    fp32 FMA (small shapes such as the n=16 running example).
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kIdxHeads = 64;
+constexpr int kIdxDim = 128;
+constexpr int kKeyTile = 32;
+
+// ---------------------------------------------------------------- MFMA ----
+// Register layouts (32x32 MFMA, wave of 64 lanes, h = lane / 32):
+//   A (query heads x dims): lane holds head (lane % 32) of a 32-head tile and
+//     the dims of k-step ks given by dim_base(ks, h) -- the same dims that the
+//     B operand of the same lane half holds for its key, so the k-sum covers
+//     every dim exactly once.
+//   B (dims x keys): lane holds key (lane % 32) of the tile.
+//   D (heads x keys): register r holds head 8*(r/4) + 4*h + r%4 of the tile,
+//     key lane % 32.
+// bf16: 8 dims per lane per k-step, 8 k-steps; half h reads dims
+//   [64h + 8ks, 64h + 8ks + 8), i.e. one contiguous 128-byte half row.
+// fp8:  32 dims per lane per k-step, 2 k-steps; half h reads dims
+//   [64h + 32ks, 64h + 32ks + 32), one contiguous 64-byte half row.
+template <bool Fp8>
+struct IdxTraits;
+
+template <>
+struct IdxTraits<false> {
+    typedef bf16x8 operand;
+    static constexpr int ksteps = 8;
+    static constexpr int elem_bytes = 2;
+    static constexpr int dims_per_step = 8;
+    __device__ static operand load(const uint8_t *p) {
+        return *reinterpret_cast<const operand *>(p);
+    }
+    __device__ static operand zero() { return operand{}; }
+    __device__ static f32x16 mma(operand a, operand b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct IdxTraits<true> {
+    typedef i32x8 operand;
+    static constexpr int ksteps = 2;
+    static constexpr int elem_bytes = 1;
+    static constexpr int dims_per_step = 32;
+    __device__ static operand load(const uint8_t *p) {
+        return *reinterpret_cast<const operand *>(p);
+    }
+    __device__ static operand zero() { return operand{}; }
+    __device__ static f32x16 mma(operand a, operand b, f32x16 c) {
+        // format 0 = fp8 e4m3 for both operands; E8M0 scale 127 = 1.0
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    }
+};
+
+template <bool Fp8>
+__global__ __launch_bounds__(256) void indexer_mfma_kernel(
+    const uint8_t *__restrict__ q_idx, const uint8_t *__restrict__ k_idx,
+    const float *__restrict__ w, const int32_t *__restrict__ q_pos, int B, int T, int S,
+    int row0, int rows, int chunk, int nchunks, float *__restrict__ scores,
+    size_t batch_stride, int write_masked) {
+    typedef IdxTraits<Fp8> Tr;
+    typedef typename Tr::operand Op;
+    constexpr int EB = Tr::elem_bytes;
+    constexpr int KS = Tr::ksteps;
+    constexpr int DPS = Tr::dims_per_step;
+
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
+    const int col = lane & 31;
+    const long long wave_id = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const long long total = (long long)B * rows * nchunks;
+    if (wave_id >= total) return;
+    // longest rows first: the causal row length grows with the row index
+    const int c = (int)(wave_id % nchunks);
+    const int rr = (int)((wave_id / nchunks) % rows);
+    const int b = (int)(wave_id / ((long long)nchunks * rows));
+    const int r = rows - 1 - rr;
+    const int i = row0 + r;
+    const int t = query_pos(q_pos, b, i, T, S);
+
+    const int s_begin = c * chunk;
+    const int s_end = min(s_begin + chunk, S);
+    const int s_hi = min(s_end, t + 1);  // causal end of this chunk
+    float *out = scores + (size_t)b * batch_stride + (size_t)r * S;
+
+    if (write_masked) {
+        for (int s = max(s_begin, s_hi) + lane; s < s_end; s += 64) out[s] = -INFINITY;
+    }
+    if (s_begin >= s_hi) return;
+
+    // query block (A operand) and head weights
+    const size_t qrow = ((size_t)b * T + i) * kIdxHeads;
+    Op qa[2][KS];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+        const uint8_t *qp = q_idx + ((qrow + tile * 32 + col) * kIdxDim + 64 * half) * EB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa[tile][ks] = Tr::load(qp + ks * DPS * EB);
+    }
+    float wr[2][16];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg)
+            wr[tile][rg] = w[qrow + tile * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
+
+    const uint8_t *kbase = k_idx + ((size_t)b * S * kIdxDim + 64 * half) * EB;
+    Op kb[KS], kn[KS];
+    {
+        const int key = s_begin + col;
+        const uint8_t *kp = kbase + (size_t)key * kIdxDim * EB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kb[ks] = key < s_hi ? Tr::load(kp + ks * DPS * EB) : Tr::zero();
+    }
+    for (int s0 = s_begin; s0 < s_hi; s0 += kKeyTile) {
+        // prefetch the next tile while this one is multiplied
+        const int nkey = s0 + kKeyTile + col;
+        const uint8_t *np = kbase + (size_t)nkey * kIdxDim * EB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kn[ks] = nkey < s_hi ? Tr::load(np + ks * DPS * EB) : Tr::zero();
+
+        f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            acc0 = Tr::mma(qa[0][ks], kb[ks], acc0);
+            acc1 = Tr::mma(qa[1][ks], kb[ks], acc1);
+        }
+        float part = 0.0f;
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) {
+            part = fmaf(wr[0][rg], fmaxf(acc0[rg], 0.0f), part);
+            part = fmaf(wr[1][rg], fmaxf(acc1[rg], 0.0f), part);
+        }
+        const float other = __shfl_xor(part, 32, 64);
+        const int key = s0 + col;
+        if (half == 0 && key < s_hi) out[key] = part + other;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kb[ks] = kn[ks];
+    }
+}
+
+// ------------------------------------------------------------- generic ----
+constexpr int kGenericThreads = 256;
+constexpr int kGenericMaxQ = 16384;
+
+__global__ __launch_bounds__(kGenericThreads) void indexer_generic_kernel(
+    const void *__restrict__ q_idx, const void *__restrict__ k_idx, int dt,
+    const float *__restrict__ w, const int32_t *__restrict__ q_pos, int B, int T, int S, int H,
+    int D, int row0, float *__restrict__ scores, size_t batch_stride, int write_masked) {
+    __shared__ float qs[kGenericMaxQ];
+    __shared__ float ws[128];
+    const int r = blockIdx.y;
+    const int b = blockIdx.z;
+    const int i = row0 + r;
+    const int t = query_pos(q_pos, b, i, T, S);
+    const int s = blockIdx.x * kGenericThreads + threadIdx.x;
+    const int tile_first = blockIdx.x * kGenericThreads;
+    if (tile_first > t && !write_masked) return;
+
+    const size_t qrow = ((size_t)b * T + i) * H;
+    for (int e = threadIdx.x; e < H * D; e += kGenericThreads)
+        qs[e] = load_as_f32(q_idx, qrow * D + e, dt);
+    for (int e = threadIdx.x; e < H; e += kGenericThreads) ws[e] = w[qrow + e];
+    __syncthreads();
+    if (s >= S) return;
+    float *out = scores + (size_t)b * batch_stride + (size_t)r * S;
+    if (s > t) {
+        out[s] = -INFINITY;
+        return;
+    }
+    const size_t krow = ((size_t)b * S + s) * D;
+    float total = 0.0f;
+    for (int j = 0; j < H; ++j) {
+        float dot = 0.0f;
+        for (int d = 0; d < D; ++d) dot = fmaf(qs[j * D + d], load_as_f32(k_idx, krow + d, dt), dot);
+        total = fmaf(ws[j], fmaxf(dot, 0.0f), total);
+    }
+    out[s] = total;
+}
+
+}  // namespace
+
+bool indexer_shape_supported(int H, int D) { return H >= 1 && D >= 1 && H <= 128 && H * D <= kGenericMaxQ; }
+
+hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, const float *w,
+                          const int32_t *q_pos, int B, int T, int S, int H, int D, int row0,
+                          int rows, float *scores, size_t batch_stride, bool write_masked,
+                          hipStream_t stream) {
+    if (H == kIdxHeads && D == kIdxDim && idx_dtype != DSA_F32) {
+        // key chunk per wave: long enough to amortise the query-block load,
+        // short enough to spread one decode row over many CUs
+        const int chunk = (T == 1) ? 1024 : 2048;
+        const int nchunks = ceil_div(S, chunk);
+        const long long waves = (long long)B * rows * nchunks;
+        const int blocks = (int)((waves + 3) / 4);
+        if (idx_dtype == DSA_BF16)
+            hipLaunchKernelGGL((indexer_mfma_kernel<false>), dim3(blocks), dim3(256), 0, stream,
+                               static_cast<const uint8_t *>(q_idx),
+                               static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
+                               rows, chunk, nchunks, scores, batch_stride, (int)write_masked);
+        else
+            hipLaunchKernelGGL((indexer_mfma_kernel<true>), dim3(blocks), dim3(256), 0, stream,
+                               static_cast<const uint8_t *>(q_idx),
+                               static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
+                               rows, chunk, nchunks, scores, batch_stride, (int)write_masked);
+        return hipGetLastError();
+    }
+    for (int r0 = 0; r0 < rows; r0 += kMaxGridY) {
+        const int n = min(kMaxGridY, rows - r0);
+        dim3 grid(ceil_div(S, kGenericThreads), n, B);
+        hipLaunchKernelGGL(indexer_generic_kernel, grid, dim3(kGenericThreads), 0, stream, q_idx,
+                           k_idx, idx_dtype, w, q_pos, B, T, S, H, D, row0 + r0,
+                           scores + (size_t)r0 * S, batch_stride, (int)write_masked);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace dsa

@@ -1,0 +1,273 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar: index sets bit-exact; scores bit-exact (the indexer inputs are small
+integers or dyadic values, so every fp32 partial sum is exact); attention
+outputs within max-abs 1e-5 (fp32) or 2e-2 (bf16)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import TOL, assert_selection_equal, max_abs_err
+
+from learned_sparse_attention_lightning_amd import configs, dsa, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsa.load()
+    oracle.build()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _int_indexer(B, T, S, H, D, dtype, seed, lo=-4, hi=4, den=16, signed_w=False):
+    g = np.random.default_rng(seed)
+    q = torch.from_numpy(g.integers(lo, hi, (B, T, H, D), endpoint=True).astype(np.float32))
+    k = torch.from_numpy(g.integers(lo, hi, (B, S, D), endpoint=True).astype(np.float32))
+    num = g.integers(0, den, (B, T, H), endpoint=True).astype(np.float32)
+    if signed_w:
+        num -= den // 2
+    w = torch.from_numpy(num / den)
+    tdt = synth.TORCH_DTYPES[dtype]
+    return q.to(tdt).to(DEV), k.to(tdt).to(DEV), w.to(DEV)
+
+
+def _assert_scores_equal(gpu_rows, ref_rows, where):
+    g = gpu_rows.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(g), np.isneginf(ref_rows)), f"{where}: mask differs"
+    fin = np.isfinite(ref_rows)
+    bad = np.argwhere(g[fin] != ref_rows[fin])
+    assert bad.size == 0, f"{where}: {bad.size} scores differ"
+
+
+# ------------------------------------------------------------------ indexer --
+
+def test_indexer_running_example_values():
+    """Section 2.3-2.5 inputs through the GPU: the ten printed scores."""
+    from golden_io import worked_example
+    ex = worked_example()
+    q = torch.tensor([[ex["q"][1], ex["q"][2]]], dtype=torch.float32).reshape(1, 1, 2, 2)
+    w = torch.tensor([[ex["w"][1], ex["w"][2]]], dtype=torch.float32).reshape(1, 1, 2)
+    k = torch.tensor([ex["k"][s] for s in range(10)] + [[-1.0, 0.0]]).reshape(1, 11, 2)
+    pos = torch.tensor([[10]], dtype=torch.int32)
+    sc = dsa.dsa_indexer_scores(q.to(DEV), k.to(DEV), w.to(DEV), q_pos=pos.to(DEV))
+    got = sc[0, 0].cpu().double().numpy()
+    for s in range(10):
+        assert abs(got[s] - ex["I"][s]) < 1e-6  # 0.3 is not a binary fraction
+    idx = dsa.dsa_topk(sc, 3, q_pos=pos.to(DEV))
+    assert idx[0, 0].tolist() == sorted(ex["select"])
+
+
+def test_indexer_generic_c0_exact():
+    w = configs.get("c0")
+    q, k, wt = synth.indexer_inputs(w, device=DEV)
+    sc = dsa.dsa_indexer_scores(q, k, wt)
+    _assert_scores_equal(sc, oracle.indexer_scores(q, k, wt), "c0")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_indexer_mfma_ragged_rows(dtype):
+    B, S, H, D = 2, 2600, 64, 128
+    pos = torch.tensor([[0, 1, 31, 32, 33, 63, 64, 2047, 2048, 2049, 2599, 1000, 17, 2500],
+                        [2599, 0, 5, 2048, 2047, 96, 1, 127, 128, 1999, 2560, 2561, 33, 300]],
+                       dtype=torch.int32)
+    T = pos.shape[1]
+    q, k, wt = _int_indexer(B, T, S, H, D, dtype, seed=21)
+    sc = dsa.dsa_indexer_scores(q, k, wt, q_pos=pos.to(DEV))
+    _assert_scores_equal(sc, oracle.indexer_scores(q, k, wt, q_pos=pos), f"{dtype} rows")
+
+
+def test_indexer_signed_weights_and_max_magnitude():
+    B, T, S, H, D = 1, 70, 70, 64, 128
+    q, k, wt = _int_indexer(B, T, S, H, D, "bf16", seed=5, signed_w=True)
+    sc = dsa.dsa_indexer_scores(q, k, wt)
+    _assert_scores_equal(sc, oracle.indexer_scores(q, k, wt), "signed w")
+    # all q = k = 4 and w = 1: every candidate scores 64 * 16 * 128 = 131072
+    q4 = torch.full_like(q, 4.0)
+    k4 = torch.full_like(k, 4.0)
+    w1 = torch.ones_like(wt)
+    sc = dsa.dsa_indexer_scores(q4, k4, w1).cpu()
+    low = torch.tril(torch.ones(T, S, dtype=torch.bool))
+    assert torch.all(sc[0][low] == 131072.0)
+    assert torch.all(torch.isneginf(sc[0][~low]))
+
+
+def test_indexer_c1_sampled_rows():
+    w = configs.get("c1")
+    q, k, wt = synth.indexer_inputs(w, device=DEV)
+    sc = dsa.dsa_indexer_scores(q, k, wt)
+    rows = [0, 1, 31, 32, 33, 1023, 2047, 2048, 2049, 3000, 4094, 4095]
+    _say(f"c1 indexer: comparing rows {rows}")
+    ref = oracle.indexer_scores(q[:, rows], k, wt[:, rows],
+                                q_pos=np.array([rows], dtype=np.int64))
+    _assert_scores_equal(sc[:, rows], ref, "c1")
+
+
+# -------------------------------------------------------------------- top-k --
+
+@pytest.mark.parametrize("levels", [None, 3, 40])
+@pytest.mark.parametrize("k", [1, 7, 64, 300])
+def test_topk_against_oracle(levels, k):
+    B, T, S = 2, 300, 300
+    sc = synth.random_scores((B, T, S), seed=k * 7 + (levels or 0), levels=levels)
+    idx = dsa.dsa_topk(sc.to(DEV), k)
+    assert_selection_equal(idx, oracle.topk(sc, k), f"levels={levels} k={k}")
+
+
+@pytest.mark.parametrize("S", [32768, 131072])
+def test_topk_wide_rows(S):
+    B, k = 3, 2048
+    pos = torch.tensor([[S - 1], [S // 2], [2048]], dtype=torch.int32)
+    sc = synth.random_scores((B, 1, S), seed=S, levels=None)
+    sc[1, 0, : S // 4] = 0.5  # a block of ties
+    idx = dsa.dsa_topk(sc.to(DEV), k, q_pos=pos.to(DEV))
+    assert_selection_equal(idx, oracle.topk(sc, k, q_pos=pos), f"S={S}")
+
+
+def test_topk_ties_signed_zero_and_short_rows():
+    sc = torch.zeros(1, 50, 50)
+    sc[0, :, 1::2] = -0.0
+    idx = dsa.dsa_topk(sc.to(DEV), 5).cpu()
+    for t in range(50):
+        n = min(5, t + 1)
+        assert idx[0, t, :n].tolist() == list(range(n))
+        assert idx[0, t, n:].tolist() == [-1] * (5 - n)
+    # heavy ties from all-zero head weights through the indexer
+    q, k, wt = _int_indexer(1, 100, 100, 64, 128, "bf16", seed=2)
+    scz = dsa.dsa_indexer_scores(q, k, torch.zeros_like(wt))
+    idx = dsa.dsa_topk(scz, 8).cpu()
+    assert idx[0, 99].tolist() == list(range(8))
+
+
+def test_topk_deterministic():
+    sc = synth.random_scores((1, 512, 512), seed=3, levels=7).to(DEV)
+    a = dsa.dsa_topk(sc, 100)
+    b = dsa.dsa_topk(sc, 100)
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- attention --
+
+def _oracle_idx(w, x):
+    return oracle.topk(oracle.indexer_scores(x["q_idx"], x["k_idx"], x["w"]), w.index_topk)
+
+
+def test_attention_mha_fp32_c0():
+    w = configs.get("c0")
+    x = synth.make_inputs(w, device=DEV)
+    ref_idx = _oracle_idx(w, x)
+    idx = torch.from_numpy(ref_idx).to(DEV)
+    lse = torch.empty((w.B, w.T, w.num_heads), dtype=torch.float32, device=DEV)
+    out = dsa.dsa_sparse_attention(dsa.desc_for(w), x["q"], x["kv"], x["v"], idx, lse=lse)
+    ref, ref_lse = oracle.sparse_attention("mha", x["q"], x["kv"], x["v"], ref_idx, w.scale,
+                                           with_lse=True)
+    assert max_abs_err(out, ref) <= TOL["f32"]
+    assert max_abs_err(lse, ref_lse) <= 1e-5
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_attention_mha_bf16(out_dtype):
+    w = configs.get("c1").with_(name="mha-small", B=2, T=300, S=300, index_topk=64,
+                                num_heads=4, out_dtype=out_dtype)
+    x = synth.make_inputs(w, device=DEV, seed=77)
+    sc = synth.random_scores((w.B, w.T, w.S), seed=8)
+    ref_idx = oracle.topk(sc, w.index_topk)
+    idx = dsa.dsa_topk(sc.to(DEV), w.index_topk)
+    assert_selection_equal(idx, ref_idx)
+    out = dsa.dsa_sparse_attention(dsa.desc_for(w), x["q"], x["kv"], x["v"], idx)
+    ref = oracle.sparse_attention("mha", x["q"], x["kv"], x["v"], ref_idx, w.scale)
+    err = max_abs_err(out, ref)
+    assert err <= (TOL["bf16"] if out_dtype == "bf16" else 1e-4), err
+
+
+def test_attention_mla_small_and_edges():
+    w = configs.get("c2").with_(name="mla-small", B=2, T=600, S=600, index_topk=64,
+                                num_heads=16)
+    x = synth.make_inputs(w, device=DEV, seed=78)
+    sc = synth.random_scores((w.B, w.T, w.S), seed=9)
+    ref_idx = oracle.topk(sc, w.index_topk)
+    ref_idx[1, 599, :] = -1            # an empty selection: zero output
+    ref_idx[0, 300, 1:] = -1           # a single selection: the value row itself
+    idx = torch.from_numpy(ref_idx).to(DEV)
+    lse = torch.empty((w.B, w.T, w.num_heads), dtype=torch.float32, device=DEV)
+    out = dsa.dsa_sparse_attention(dsa.desc_for(w), x["q"], x["kv"], None, idx, lse=lse)
+    ref, ref_lse = oracle.sparse_attention("mla", x["q"], x["kv"], None, ref_idx, w.scale,
+                                           d_v=w.d_v, with_lse=True)
+    assert max_abs_err(out[:, :599], ref[:, :599]) <= TOL["bf16"]
+    assert max_abs_err(out[0], ref[0]) <= TOL["bf16"]
+    assert torch.all(out[1, 599] == 0)
+    assert torch.all(torch.isneginf(lse[1, 599]))
+    s = int(ref_idx[0, 300, 0])
+    assert torch.equal(out[0, 300, 0], x["kv"][0, s, : w.d_v])
+    fin = np.isfinite(ref_lse)
+    assert np.abs(lse.cpu().numpy()[fin] - ref_lse[fin]).max() < 1e-3
+
+
+# ------------------------------------------------------------------ forward --
+
+def _forward(w, seed=None):
+    x = synth.make_inputs(w, device=DEV, seed=seed)
+    idx = torch.empty((w.B, w.T, w.index_topk), dtype=torch.int32, device=DEV)
+    out = dsa.dsa_forward(dsa.desc_for(w), x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"],
+                          x["v"], w.index_topk, idx_out=idx)
+    torch.cuda.synchronize()
+    return x, idx, out
+
+
+def test_forward_c0_all_rows():
+    w = configs.get("c0")
+    x, idx, out = _forward(w)
+    ref_idx = _oracle_idx(w, x)
+    assert_selection_equal(idx, ref_idx, "c0")
+    assert int((idx >= 0).sum()) == 45
+    ref = oracle.sparse_attention("mha", x["q"], x["kv"], x["v"], ref_idx, w.scale)
+    assert max_abs_err(out, ref) <= TOL["f32"]
+
+
+def test_forward_c1_sets_all_rows_outputs_sampled():
+    w = configs.get("c1")
+    x, idx, out = _forward(w)
+    sc = dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"])
+    rows = [0, 5, 2046, 2047, 2048, 4095]
+    ref_rows = oracle.indexer_scores(x["q_idx"][:, rows], x["k_idx"], x["w"][:, rows],
+                                     q_pos=np.array([rows]))
+    _assert_scores_equal(sc[:, rows], ref_rows, "c1 forward scores")
+    _say("c1: oracle top-k over every row")
+    ref_idx = oracle.topk(sc, w.index_topk)
+    assert_selection_equal(idx, ref_idx, "c1")
+    sample = [0, 1, 100, 2047, 2048, 3333, 4095]
+    ref = oracle.sparse_attention("mha", x["q"][:, sample], x["kv"], x["v"],
+                                  ref_idx[:, sample], w.scale)
+    assert max_abs_err(out[:, sample], ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_forward_decode_full(name):
+    w = configs.get(name)
+    x, idx, out = _forward(w)
+    _say(f"{name}: oracle indexer over {w.B} rows of {w.S}")
+    ref_idx = _oracle_idx(w, x)
+    assert_selection_equal(idx, ref_idx, name)
+    ref = oracle.sparse_attention("mla", x["q"], x["kv"], None, ref_idx, w.scale, d_v=w.d_v)
+    err = max_abs_err(out, ref)
+    _say(f"{name}: max-abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_forward_repeatable_bitwise():
+    w = configs.get("c1").with_(name="rep", T=1024, S=1024, index_topk=256)
+    x, idx1, out1 = _forward(w, seed=4)
+    out2 = dsa.dsa_forward(dsa.desc_for(w), x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"],
+                           x["v"], w.index_topk, idx_out=(idx2 := torch.empty_like(idx1)))
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2) and torch.equal(out1, out2)
