@@ -1,0 +1,263 @@
+"""Throughput of the DSA forward path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
+
+A step is one dsa_forward call (indexer scores -> top-k -> sparse attention)
+over one batch of synthetic inputs already resident in HBM.  The default
+workload is the 128K-context decode: 8 sequences of 131072 cached tokens, one
+new query each, k = 2048, fp8 e4m3 indexer keys, MLA latent 576/512 bf16.
+Decode inputs are rotated over several replicas so that consecutive steps do
+not find the key cache in the last-level cache.
+
+Prints one JSON line.  Besides the step throughput it carries:
+  * roofline: the dominant kernel's algorithmic bytes (or flops) per launch
+    over its average duration, timed with HIP events on the library's stream;
+  * cpu_baseline: the CPU oracle timed on a bounded sample of the same
+    workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer+sparse-attn tokens/s (prefill) & decode steps/s at 128K ctx, k=2048"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense MFMA
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4"])
+    ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = auto)")
+    ap.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
+    ap.add_argument("--cpu-baseline", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def algorithmic(w):
+    """Algorithmic work of one step and of each stage (what the method must
+    read, write or compute; dense work a masked kernel might add is not
+    counted)."""
+    from learned_sparse_attention_lightning_amd.configs import causal_pairs, selected_entries
+    eb = {"f32": 4, "bf16": 2, "fp8": 1}
+    B, T, S, H, D, k = w.B, w.T, w.S, w.index_n_heads, w.index_head_dim, w.index_topk
+    pairs = B * causal_pairs(T, S)
+    entries = B * selected_entries(T, S, k)
+    ib = eb[w.idx_dtype]
+    idx_bytes = B * S * D * ib + B * T * H * D * ib + B * T * H * 4
+    idx_flops = pairs * 2 * H * D
+    if w.form == "mla":
+        attn_flops = entries * 2 * w.num_heads * (w.d_qk + w.d_v)
+        attn_bytes = entries * w.d_qk * 2 + B * T * w.num_heads * (w.d_qk * 2 + w.d_v * 2)
+    else:
+        attn_flops = entries * 2 * w.num_heads * (w.d_qk + w.d_v)
+        attn_bytes = entries * w.num_heads * (w.d_qk + w.d_v) * 2 + B * T * w.num_heads * (
+            w.d_qk * 2 + w.d_v * 2)
+    sel_bytes = B * T * k * 4
+    return {"indexer_bytes": idx_bytes, "indexer_flops": idx_flops, "attn_bytes": attn_bytes,
+            "attn_flops": attn_flops, "step_bytes": idx_bytes + attn_bytes + sel_bytes,
+            "pairs": pairs, "entries": entries}
+
+
+def kernel_source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "learned_sparse_attention_lightning_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_record(workload: str, kernel_file: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the summary is missing or the kernel source changed since."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("source_sha256_16") != kernel_source_hash(kernel_file):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, budget_s: float):
+    """The oracle, untuned, on a bounded sample: whole sequences (decode) or
+    whole query rows (prefill), as many as fit in the time budget."""
+    import numpy as np
+
+    import oracle
+    oracle.build()
+    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    t0 = time.perf_counter()
+    done = 0
+    if w.decode:
+        for b in range(w.B):
+            sc = oracle.indexer_scores(x["q_idx"][b:b + 1], x["k_idx"][b:b + 1], x["w"][b:b + 1])
+            sel = oracle.topk(sc, w.index_topk)
+            oracle.sparse_attention(w.form, x["q"][b:b + 1], x["kv"][b:b + 1],
+                                    None if x["v"] is None else x["v"][b:b + 1], sel, w.scale,
+                                    d_v=w.d_v)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        el = time.perf_counter() - t0
+        return {"value": done / w.B / el, "unit": "steps/s", "cores": cores, "kind": "oracle",
+                "sample": f"{done} of {w.B} sequences of one step (indexer over {w.S} keys, "
+                          f"top-{w.index_topk}, {w.num_heads}-head attention), {el:.1f} s"}
+    rows = []
+    rng = np.random.default_rng(0)
+    cand = rng.permutation(w.T)
+    for r in cand:
+        rows.append(int(r))
+        pos = np.array([[r]])
+        sc = oracle.indexer_scores(x["q_idx"][:, [r]], x["k_idx"], x["w"][:, [r]], q_pos=pos)
+        sel = oracle.topk(sc, w.index_topk, q_pos=pos)
+        oracle.sparse_attention(w.form, x["q"][:, [r]], x["kv"], x["v"], sel, w.scale,
+                                d_v=w.d_v)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    # scale the sampled rows to whole-sequence work by their causal length
+    frac = sum(r + 1 for r in rows) / sum(t + 1 for t in range(w.T))
+    return {"value": w.T * w.B / (el / frac), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "sample": f"{len(rows)} random query rows of {w.T}, "
+                                        f"{el:.1f} s, scaled by causal length"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path shards by "
+              "sequence or query rows and is not built for several GPUs here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from learned_sparse_attention_lightning_amd import configs, dsa, synth
+
+    w = configs.get(args.workload)
+    dev = torch.device("cuda:0")
+    R = args.replicas or (4 if w.decode else 1)
+    reps = [synth.make_inputs(w, device=dev, seed=synth.default_seed(w) + r) for r in range(R)]
+    desc = dsa.desc_for(w)
+    out = torch.empty((w.B, w.T, w.num_heads, w.d_v),
+                      dtype=synth.TORCH_DTYPES[w.out_dtype], device=dev)
+    idx = torch.empty((w.B, w.T, w.index_topk), dtype=torch.int32, device=dev)
+    nws = dsa.workspace_bytes(dsa.DSA_OP_FORWARD, desc, w.B, w.T, w.S, w.index_n_heads,
+                              w.index_head_dim, w.index_topk)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+    def step(r):
+        x = reps[r]
+        dsa.dsa_forward(desc, x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"], x["v"],
+                        w.index_topk, out=out, idx_out=idx, workspace=ws)
+
+    for s in range(args.warmup):
+        step(s % R)
+    torch.cuda.synchronize()
+
+    graphs = None
+    if args.graph:
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        for r in range(R):
+            graphs[r].replay()
+        torch.cuda.synchronize()
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for s in range(args.steps):
+        if graphs:
+            graphs[s % R].replay()
+        else:
+            step(s % R)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # ---- per-stage kernel durations (same kernels and launch shapes as the
+    # step: for decode the three entry points issue exactly dsa_forward's launches)
+    alg = algorithmic(w)
+    stage_ms = None
+    if w.decode:
+        sc = torch.empty((w.B, w.T, w.S), dtype=torch.float32, device=dev)
+        nst = max(10, args.steps)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nst)]
+        for s in range(nst):
+            x = reps[s % R]
+            ev[s][0].record()
+            dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"], scores=sc)
+            ev[s][1].record()
+            dsa.dsa_topk(sc, w.index_topk, idx=idx)
+            ev[s][2].record()
+            dsa.dsa_sparse_attention(desc, x["q"], x["kv"], x["v"], idx, out=out)
+            ev[s][3].record()
+        torch.cuda.synchronize()
+        stage_ms = [sum(ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(nst)) / nst
+                    for j in range(3)]
+
+    if w.decode:
+        kern_ms = stage_ms[0]
+        achieved = alg["indexer_bytes"] / (kern_ms * 1e-3) / 1e9
+        tr = traffic_record(w.name, "indexer.hip")
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr,
+                "kernel": f"indexer_mfma_kernel<{w.idx_dtype}>",
+                "algorithmic_bytes_per_launch": alg["indexer_bytes"],
+                "avg_launch_ms": round(kern_ms, 5)}
+        value = 1e3 / ms
+        unit = "steps/s"
+    else:
+        value = w.B * w.T / (ms * 1e-3)
+        unit = "tokens/s"
+        peak = BF16_PEAK_TFLOPS
+        achieved = (alg["indexer_flops"] + alg["attn_flops"]) / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": "whole step", "avg_launch_ms": round(ms, 4)}
+
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8+bf16" if w.idx_dtype == "fp8" else w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}", "batch": w.B, "ctx": w.S,
+                   "query_rows": w.T, "index_n_heads": w.index_n_heads,
+                   "index_head_dim": w.index_head_dim, "index_topk": w.index_topk,
+                   "form": w.form, "heads": w.num_heads, "d_qk": w.d_qk, "d_v": w.d_v,
+                   "input_replicas": R, "launch": "hip-graph" if graphs else "eager",
+                   "parallelism": "single-gpu"},
+        "roofline": roof,
+        "host_ms_per_step": round(wall_ms, 5),
+        "step_algorithmic_bytes": alg["step_bytes"],
+        "step_hbm_frac": round(alg["step_bytes"] / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+    }
+    if w.decode:
+        res["tokens_per_s"] = round(value * w.B, 1)
+        res["stage_ms"] = {"indexer": round(stage_ms[0], 5), "topk": round(stage_ms[1], 5),
+                           "attention": round(stage_ms[2], 5)}
+    if args.cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, reps[0], args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
