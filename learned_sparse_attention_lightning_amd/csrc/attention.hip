@@ -129,12 +129,17 @@ hipError_t launch_gather(const dsa_attn_desc_t &d, const void *q, const void *kv
 
 }  // namespace
 
-size_t attention_workspace_bytes(const dsa_attn_desc_t &, int, int, int, int) { return 0; }
+size_t attention_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int, int k) {
+    if (mla_fast_path(d)) return mla_workspace_bytes(d, B, T, k);
+    return 0;
+}
 
 hipError_t launch_attention(const dsa_attn_desc_t &d, const void *q, const void *kv,
                             const void *v, const int32_t *idx, int B, int T, int S, int row0,
-                            int rows, int k, void *out, float *lse, void *,
+                            int rows, int k, void *out, float *lse, void *workspace,
                             hipStream_t stream) {
+    if (mla_fast_path(d))
+        return launch_mla(d, q, kv, idx, B, T, S, row0, rows, k, out, lse, workspace, stream);
     const bool in_bf16 = d.dtype == DSA_BF16;
     const bool out_bf16 = d.out_dtype == DSA_BF16;
     if (in_bf16 && out_bf16)

@@ -1,0 +1,354 @@
+// attention_mla.hip -- MLA-latent sparse attention on gfx950 matrix cores.
+//
+// Attention over the selected latent rows in the MQA mode of MLA: one latent
+// row c_s (576 = 512 latent + 64 rope dims, bf16) per position is both the key
+// (all 576 dims) and the value (first 512 dims) of every head, and one
+// selected set per query serves all heads ("DeepSeek Sparse Attention:
+// Learned Token Selection from Scratch", sections 3.3 and 4.1-4.2; "DeepSeek
+// NSA and DSA", section 3.1).  Because every gathered row is shared by all
+// heads, the heads form the M dimension of dense MFMA tiles.
+//
+// Workgroup = 4 waves = one query row x 64 heads x one range of selected
+// entries, walked 64 entries at a time:
+//   gather  the 64 selected rows into LDS (row pitch padded against bank
+//           conflicts; masked entries are zero rows);
+//   S phase wave w computes S^T = C(32 keys) . Q^T(32 heads) over 576 dims for
+//           key tile w/2 and head tile w%2 (v_mfma_f32_32x32x16_bf16), with
+//           its 32x576 query block held in registers as the B operand;
+//   softmax online, fp32: tile max exchanged through LDS, probabilities
+//           written to LDS as bf16 [head][key];
+//   PV phase wave w accumulates O[64 heads, dims 128w..128w+127] += P . V,
+//           V read straight from the row-major tile with the LDS transpose
+//           read (ds_read_b64_tr_b16) as the B operand.
+// Decode rows split their entries over several workgroups; each writes a
+// normalised partial output and its log-sum-exp, merged by a second kernel.
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kHg = 64;            // heads per workgroup
+constexpr int kKt = 64;            // selected entries per step
+constexpr int kKsteps = kDqk / 16; // 36
+constexpr int kRowPitch = kDqk * 2 + 16;   // bytes: 1168 (bank shift of 36 dwords)
+constexpr int kPPitch = kKt * 2 + 16;      // bytes: 144
+constexpr int kChunksPerRow = kDqk * 2 / 16;  // 72 chunks of 16 bytes
+constexpr int kThreads = 256;
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+struct __align__(16) MlaSmem {
+    uint8_t kv[kKt * kRowPitch];       // 74752
+    uint8_t p[kHg * kPPitch];          // 9216
+    float tile_max[2][kHg];            // per key tile, per head
+    float corr[kHg];
+    float lsum[2][kHg];
+    int32_t sel[kKt];
+};
+
+__device__ __forceinline__ bf16x8 lds_b128(const uint8_t *p) {
+    return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element i%4 of the 4-element vectors addressed by lanes
+// 4e + i/4 (e = 0..3): pointing lane j at row r0 + j/4, column c0 + 4*(j%4)
+// of a row-major bf16 tile hands lane i the column c0 + i of rows r0..r0+3.
+__device__ __forceinline__ bf16x4 lds_tr16(const uint8_t *p) {
+    typedef __attribute__((address_space(3))) bf16x4 *lds_v4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4)(p));
+}
+
+// Load 16 bytes of the latent row into LDS (zeros for a masked entry).
+__device__ __forceinline__ void gather_tile(MlaSmem &sm, const uint8_t *__restrict__ lat_b,
+                                            int tid) {
+    for (int c = tid; c < kKt * kChunksPerRow; c += kThreads) {
+        const int row = c / kChunksPerRow;
+        const int ch = c - row * kChunksPerRow;
+        const int s = sm.sel[row];
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (s >= 0) v = *reinterpret_cast<const u32x4 *>(lat_b + (size_t)s * (kDqk * 2) + ch * 16);
+        *reinterpret_cast<u32x4 *>(sm.kv + row * kRowPitch + ch * 16) = v;
+    }
+}
+
+template <typename Tout>
+__device__ __forceinline__ void store_out(Tout *p, float v);
+template <>
+__device__ __forceinline__ void store_out<float>(float *p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float v) {
+    *p = (uint16_t)f32_to_bf16_bits(v);
+}
+
+// grid: x = head group, y = split * rows + row, z = batch
+template <typename Tout>
+__global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ lat,
+    const int32_t *__restrict__ idx, int T, int S, int H, int k, float scale, int row0,
+    int rows, int splits, int per_split, Tout *__restrict__ out, float *__restrict__ lse,
+    float *__restrict__ o_part, float *__restrict__ lse_part) {
+    __shared__ MlaSmem sm;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const int hg = blockIdx.x;
+    const int split = blockIdx.y / rows;
+    const int r = blockIdx.y - split * rows;
+    const int b = blockIdx.z;
+    const int i = row0 + r;
+    const int head0 = hg * kHg;
+
+    const int e_begin = split * per_split;
+    const int e_end = min(k, e_begin + per_split);
+    const int32_t *sel_row = idx + ((size_t)b * T + i) * k;
+    const uint8_t *lat_b = reinterpret_cast<const uint8_t *>(lat) + (size_t)b * S * (kDqk * 2);
+
+    // ---- S-phase role and its query block (B operand: 32 heads x 576 dims)
+    const int kt = wave >> 1;  // key tile of the S phase
+    const int ht = wave & 1;   // head tile of the S phase
+    bf16x8 qb[kKsteps];
+    {
+        const uint16_t *qp = q + (((size_t)b * T + i) * H + head0 + ht * 32 + l32) * kDqk + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < kKsteps; ++ks)
+            qb[ks] = *reinterpret_cast<const bf16x8 *>(qp + ks * 16);
+    }
+
+    // ---- PV-phase accumulators: 2 head tiles x 4 dim tiles of 32x32
+    f32x16 o[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[a][c] = f32x16{};
+
+    float m_run = -INFINITY;  // running max of head (head0 + 32*ht + l32), S-phase view
+    float l_run = 0.0f;       // this wave's share of the running sum
+    const float sl2 = scale * 1.4426950408889634f;  // logits in base-2 units
+
+    for (int e0 = e_begin; e0 < e_end; e0 += kKt) {
+        __syncthreads();  // previous step's readers are done with kv / p / sel
+        if (tid < kKt) sm.sel[tid] = (e0 + tid < e_end) ? sel_row[e0 + tid] : -1;
+        __syncthreads();
+        gather_tile(sm, lat_b, tid);
+        __syncthreads();
+
+        // ---- S^T = C . Q^T for (key tile kt, head tile ht)
+        f32x16 sacc = {};
+        const uint8_t *arow = sm.kv + (kt * 32 + l32) * kRowPitch + 16 * half;
+#pragma unroll
+        for (int ks = 0; ks < kKsteps; ++ks)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(arow + ks * 32), qb[ks], sacc,
+                                                           0, 0, 0);
+        // register rg holds key kt*32 + 8*(rg/4) + 4*half + rg%4, head ht*32 + l32
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) {
+            const int key = kt * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3);
+            const float x = sm.sel[key] >= 0 ? sacc[rg] * sl2 : -INFINITY;
+            sacc[rg] = x;
+            tmax = fmaxf(tmax, x);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        if (half == 0) sm.tile_max[kt][ht * 32 + l32] = tmax;
+        __syncthreads();
+        const float m_tile = fmaxf(sm.tile_max[0][ht * 32 + l32], sm.tile_max[1][ht * 32 + l32]);
+        const float m_new = fmaxf(m_run, m_tile);
+        const float corr = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
+        m_run = m_new;
+        float psum = 0.0f;
+        uint8_t *prow = sm.p + (ht * 32 + l32) * kPPitch;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            uint32_t packed[2];
+#pragma unroll
+            for (int j = 0; j < 4; j += 2) {
+                const float p0 = m_new == -INFINITY ? 0.0f : exp2f(sacc[4 * g + j] - m_new);
+                const float p1 = m_new == -INFINITY ? 0.0f : exp2f(sacc[4 * g + j + 1] - m_new);
+                psum += p0 + p1;
+                packed[j >> 1] = f32_to_bf16_bits(p0) | (f32_to_bf16_bits(p1) << 16);
+            }
+            const int key = kt * 32 + 8 * g + 4 * half;
+            *reinterpret_cast<uint2 *>(prow + key * 2) = make_uint2(packed[0], packed[1]);
+        }
+        l_run = l_run * corr + psum;
+        if (kt == 0 && half == 0) sm.corr[ht * 32 + l32] = corr;
+        __syncthreads();
+
+        // ---- O[64 heads, 128 dims of this wave] = O * corr + P . V
+        const int dv0 = wave * 128;
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            float cr[16];
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) cr[rg] = sm.corr[a * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int rg = 0; rg < 16; ++rg) o[a][c][rg] *= cr[rg];
+        }
+#pragma unroll
+        for (int ks = 0; ks < kKt / 16; ++ks) {
+            bf16x8 pa[2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+                pa[a] = lds_b128(sm.p + (a * 32 + l32) * kPPitch + (16 * ks + 8 * half) * 2);
+            // transpose-read lane address: row key0 + j/4, column col0 + 4*(j%4)
+            const int j = lane & 15;
+            const int grp = lane >> 4;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int col0 = dv0 + 32 * c + 16 * (grp & 1) + 4 * (j & 3);
+                const int key0 = 16 * ks + 8 * (grp >> 1) + (j >> 2);
+                const uint8_t *vp = sm.kv + key0 * kRowPitch + col0 * 2;
+                const bf16x4 lo = lds_tr16(vp);
+                const bf16x4 hi = lds_tr16(vp + 4 * kRowPitch);
+                const bf16x8 vb = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+                    o[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[a], vb, o[a][c], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- final normalisation: l per head = sum of both key-tile waves' shares
+    const float l_wave = l_run + __shfl_xor(l_run, 32, 64);
+    __syncthreads();
+    if (half == 0) sm.lsum[kt][ht * 32 + l32] = l_wave;
+    if (kt == 0 && half == 0) sm.tile_max[0][ht * 32 + l32] = m_run;  // reuse as final max
+    __syncthreads();
+    const int dv0 = wave * 128;
+    const size_t rowq = ((size_t)b * T + i);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) {
+            const int hl = a * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3);
+            const float l = sm.lsum[0][hl] + sm.lsum[1][hl];
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int d = dv0 + 32 * c + l32;
+                const float v = o[a][c][rg] * inv;
+                if (splits == 1)
+                    store_out(out + (rowq * H + head0 + hl) * kDv + d, v);
+                else
+                    o_part[((rowq * splits + split) * H + head0 + hl) * kDv + d] = v;
+            }
+        }
+    }
+    if (tid < kHg) {
+        const float l = sm.lsum[0][tid] + sm.lsum[1][tid];
+        const float m2 = sm.tile_max[0][tid];  // base-2 units
+        const float ls = l > 0.0f ? (m2 + log2f(l)) * 0.6931471805599453f : -INFINITY;
+        if (splits == 1) {
+            if (lse) lse[rowq * H + head0 + tid] = ls;
+        } else {
+            lse_part[(rowq * splits + split) * H + head0 + tid] = ls;
+        }
+    }
+}
+
+// Merge split partials: out = sum_s exp(lse_s - lse) o_s, lse = log sum exp lse_s.
+template <typename Tout>
+__global__ __launch_bounds__(256) void mla_combine_kernel(
+    const float *__restrict__ o_part, const float *__restrict__ lse_part, int T, int H,
+    int row0, int rows, int splits, Tout *__restrict__ out, float *__restrict__ lse) {
+    const int h = blockIdx.x;
+    const int r = blockIdx.y;
+    const int b = blockIdx.z;
+    const size_t rowq = (size_t)b * T + row0 + r;
+    float mx = -INFINITY;
+    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, lse_part[(rowq * splits + s) * H + h]);
+    float wsum = 0.0f;
+    float acc0 = 0.0f, acc1 = 0.0f;
+    const int d = threadIdx.x;
+    for (int s = 0; s < splits; ++s) {
+        const float ls = lse_part[(rowq * splits + s) * H + h];
+        const float wgt = mx == -INFINITY ? 0.0f : __expf(ls - mx);
+        wsum += wgt;
+        const float *op = o_part + ((rowq * splits + s) * H + h) * kDv;
+        acc0 = fmaf(wgt, op[d], acc0);
+        acc1 = fmaf(wgt, op[d + 256], acc1);
+    }
+    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    store_out(out + (rowq * H + h) * kDv + d, acc0 * inv);
+    store_out(out + (rowq * H + h) * kDv + d + 256, acc1 * inv);
+    if (lse && d == 0) lse[rowq * H + h] = wsum > 0.0f ? mx + __logf(wsum) : -INFINITY;
+}
+
+int mla_splits(int B, int rows, int H, int k) {
+    const long long wgs = (long long)B * rows * (H / kHg);
+    const int max_splits = ceil_div(k, kKt);
+    long long s = (512 + wgs - 1) / wgs;
+    if (s < 1) s = 1;
+    if (s > max_splits) s = max_splits;
+    return (int)s;
+}
+
+}  // namespace
+
+bool mla_fast_path(const dsa_attn_desc_t &d) {
+    return d.form == DSA_MLA && d.dtype == DSA_BF16 && d.d_qk == kDqk && d.d_v == kDv &&
+           d.num_heads % kHg == 0;
+}
+
+size_t mla_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int k) {
+    size_t total = 0;
+    for (int r0 = 0; r0 < T; r0 += kMaxGridY) {
+        const int rows = min(kMaxGridY, T - r0);
+        const int splits = mla_splits(B, rows, d.num_heads, k);
+        if (splits > 1) {
+            const size_t need = (size_t)B * rows * splits * d.num_heads * (kDv + 1) * 4 + 256;
+            total = need > total ? need : total;
+        }
+    }
+    return total;
+}
+
+hipError_t launch_mla(const dsa_attn_desc_t &d, const void *q, const void *kv,
+                      const int32_t *idx, int B, int T, int S, int row0, int rows, int k,
+                      void *out, float *lse, void *workspace, hipStream_t stream) {
+    const int H = d.num_heads;
+    for (int r0 = 0; r0 < rows; r0 += kMaxGridY) {
+        const int n = min(kMaxGridY, rows - r0);
+        const int splits = mla_splits(B, n, H, k);
+        const int per_split = ceil_div(ceil_div(k, splits), kKt) * kKt;
+        const int used_splits = ceil_div(k, per_split);
+        float *o_part = static_cast<float *>(workspace);
+        float *lse_part = o_part + (size_t)B * n * used_splits * H * kDv;
+        dim3 grid(H / kHg, used_splits * n, B);
+        if (d.out_dtype == DSA_BF16)
+            hipLaunchKernelGGL(mla_attention_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
+                               static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),
+                               idx, T, S, H, k, d.scale, row0 + r0, n, used_splits, per_split,
+                               static_cast<uint16_t *>(out), lse, o_part, lse_part);
+        else
+            hipLaunchKernelGGL(mla_attention_kernel<float>, grid, dim3(kThreads), 0, stream,
+                               static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),
+                               idx, T, S, H, k, d.scale, row0 + r0, n, used_splits, per_split,
+                               static_cast<float *>(out), lse, o_part, lse_part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (used_splits > 1) {
+            dim3 cg(H, n, B);
+            if (d.out_dtype == DSA_BF16)
+                hipLaunchKernelGGL(mla_combine_kernel<uint16_t>, cg, dim3(256), 0, stream, o_part,
+                                   lse_part, T, H, row0 + r0, n, used_splits,
+                                   static_cast<uint16_t *>(out), lse);
+            else
+                hipLaunchKernelGGL(mla_combine_kernel<float>, cg, dim3(256), 0, stream, o_part,
+                                   lse_part, T, H, row0 + r0, n, used_splits,
+                                   static_cast<float *>(out), lse);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+}  // namespace dsa

@@ -271,3 +271,65 @@ def test_forward_repeatable_bitwise():
                            x["v"], w.index_topk, idx_out=(idx2 := torch.empty_like(idx1)))
     torch.cuda.synchronize()
     assert torch.equal(idx1, idx2) and torch.equal(out1, out2)
+
+
+# --------------------------------------------------- MLA matrix-core kernel --
+
+@pytest.mark.parametrize("B,T,S,k,out_dtype", [
+    (1, 40, 3000, 2048, "bf16"),   # prefill rows, full budget
+    (2, 1, 5000, 2048, "f32"),     # decode, split entries + merge
+    (3, 7, 700, 100, "bf16"),      # ragged budget (not a multiple of 64)
+    (1, 1, 64, 64, "f32"),         # one step, every entry valid
+])
+def test_mla_mfma_against_oracle(B, T, S, k, out_dtype):
+    w = configs.get("c2").with_(name="mla-mfma", B=B, T=T, S=S, index_topk=k,
+                                out_dtype=out_dtype)
+    x = synth.make_inputs(w, device=DEV, seed=S + k)
+    pos = torch.from_numpy(np.random.default_rng(S).integers(0, S, (B, T)).astype(np.int32))
+    pos[0, 0] = S - 1
+    sc = synth.random_scores((B, T, S), seed=S + 1)
+    ref_idx = oracle.topk(sc, k, q_pos=pos)
+    # selections in arbitrary order with holes are part of the contract
+    ref_idx = np.ascontiguousarray(ref_idx[..., ::-1])
+    idx = torch.from_numpy(ref_idx).to(DEV)
+    lse = torch.empty((B, T, w.num_heads), dtype=torch.float32, device=DEV)
+    out = dsa.dsa_sparse_attention(dsa.desc_for(w), x["q"], x["kv"], None, idx, lse=lse)
+    ref, ref_lse = oracle.sparse_attention("mla", x["q"], x["kv"], None, ref_idx, w.scale,
+                                           d_v=w.d_v, with_lse=True)
+    err = max_abs_err(out, ref)
+    _say(f"mla mfma B={B} T={T} S={S} k={k}: max-abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() < 1e-3
+
+
+def test_mla_mfma_empty_and_single_rows():
+    w = configs.get("c2").with_(name="mla-edge", B=1, T=3, S=256, index_topk=128)
+    x = synth.make_inputs(w, device=DEV, seed=5)
+    sel = -np.ones((1, 3, 128), dtype=np.int32)
+    sel[0, 1, 77] = 200           # one entry, in the middle of the row
+    sel[0, 2, :] = np.arange(128)  # all valid
+    lse = torch.empty((1, 3, w.num_heads), dtype=torch.float32, device=DEV)
+    out = dsa.dsa_sparse_attention(dsa.desc_for(w), x["q"], x["kv"], None,
+                                   torch.from_numpy(sel).to(DEV), lse=lse)
+    assert torch.all(out[0, 0] == 0) and torch.all(torch.isneginf(lse[0, 0]))
+    for h in range(w.num_heads):
+        assert torch.equal(out[0, 1, h], x["kv"][0, 200, : w.d_v])
+    ref = oracle.sparse_attention("mla", x["q"][:, 2:], x["kv"], None, sel[:, 2:], w.scale,
+                                  d_v=w.d_v)
+    assert max_abs_err(out[:, 2:], ref) <= TOL["bf16"]
+
+
+def test_forward_c2_sampled_rows():
+    w = configs.get("c2")
+    x, idx, out = _forward(w)
+    rows = [0, 1, 2047, 2048, 2049, 4095, 4096, 16383, 30000, 32767]
+    _say(f"c2: oracle over rows {rows}")
+    pos = np.array([rows])
+    sc = oracle.indexer_scores(x["q_idx"][:, rows], x["k_idx"], x["w"][:, rows], q_pos=pos)
+    ref_idx = oracle.topk(sc, w.index_topk, q_pos=pos)
+    assert_selection_equal(idx[:, rows], ref_idx, "c2")
+    ref = oracle.sparse_attention("mla", x["q"][:, rows], x["kv"], None, ref_idx, w.scale,
+                                  d_v=w.d_v)
+    err = max_abs_err(out[:, rows], ref)
+    _say(f"c2: max-abs err {err:.3e}")
+    assert err <= TOL["bf16"]
