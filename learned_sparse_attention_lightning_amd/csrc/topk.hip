@@ -5,18 +5,24 @@
 // by the lower position; rows with t+1 <= k keep every candidate (section
 // 7.2).  Output: the selected positions in ascending order, -1 padded.
 //
-// Method (one workgroup of 1024 threads per row):
-//  1. map each score to an order-preserving 32-bit key (-0 folded onto +0);
-//  2. threshold search on the key range: a block-wide min/max, then at most
-//     three passes of a <=2048-bin LDS histogram over the current key range
-//     [lo, hi] (bins are key >> shift, so binning is exact integer work);
-//     each pass keeps only the bin holding the k-th largest key, until the
-//     range is one key value tau.  `need` counts how many keys equal to tau
-//     are still to be taken;
-//  3. one ordered compaction sweep: tiles of 1024 consecutive positions, a
-//     ballot/prefix count gives each tied position its rank among ties (lower
-//     positions first) and each selected position its output slot, so the
-//     output is ascending and identical run to run.
+// All comparisons are on an order-preserving 32-bit key of the fp32 score
+// (-0 folded onto +0), so every decision below is exact integer work.
+//
+// Two paths:
+//  * many rows (prefill): one 1024-thread workgroup per row.  The row is
+//    cached in LDS when it fits (<= 32768 scores), a threshold search narrows
+//    the key range [lo, hi] with <= 2048-bin LDS histograms until it is the
+//    single key value tau of the k-th largest score, then one ordered sweep
+//    takes every key > tau plus the first `need` keys == tau in position order.
+//  * few wide rows (decode): the row is split over many workgroups.
+//      hist     per slice, an LDS histogram of the top 12 key bits, merged into
+//               a per-row histogram in global memory;
+//      scan     every slice finds the digit d1 holding the k-th largest key,
+//               writes a bitmap word of "digit > d1" per 32 positions and
+//               appends the positions with digit == d1 to a candidate list;
+//      resolve  one workgroup per row selects the remaining `need` candidates
+//               exactly (ties by lower position), ORs them into the bitmap and
+//               compacts the bitmap in position order.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -25,41 +31,171 @@ namespace {
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kTkBins = 2048;
+constexpr int kRowCache = 32768;  // scores cached in LDS by the per-row kernel
+
+// wide-row path
+constexpr int kWideThreads = 256;
+constexpr int kWideSlice = kWideThreads * 32;  // positions per slice workgroup
+constexpr int kDigitBits = 12;
+constexpr int kDigits = 1 << kDigitBits;
+constexpr int kWideMinS = 16384;
+constexpr int kWideMaxS = 262144;      // bitmap of one row fits 32 KB of LDS
+constexpr int kWideMaxRows = 512;
+constexpr int kMetaWords = 16;         // per row: [0] candidate count, [1] count above d1
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
     const uint32_t lo = __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u);
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), lo);
 }
 
-// Exclusive prefix count of `flag` over the workgroup in thread order, and
-// the workgroup total.  `scratch` holds kTkWaves entries; two barriers.
-__device__ __forceinline__ uint32_t block_flag_scan(bool flag, uint32_t *scratch,
+// Exclusive prefix sum of v over the workgroup in thread order, and the
+// total.  `scratch` holds one word per wave; two barriers.
+template <int Waves>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *scratch,
                                                     uint32_t &total) {
+    const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const uint64_t m = __ballot(flag);
-    const uint32_t in_wave = lanes_below(m);
-    if ((threadIdx.x & 63) == 0) scratch[wave] = (uint32_t)__popcll(m);
+    uint32_t incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_up((int)incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) scratch[wave] = incl;
     __syncthreads();
     uint32_t before = 0, sum = 0;
 #pragma unroll
-    for (int v = 0; v < kTkWaves; ++v) {
-        const uint32_t c = scratch[v];
-        before += v < wave ? c : 0u;
+    for (int w = 0; w < Waves; ++w) {
+        const uint32_t c = scratch[w];
+        before += w < wave ? c : 0u;
         sum += c;
     }
     __syncthreads();
     total = sum;
-    return before + in_wave;
+    return before + incl - v;
 }
+
+// Exclusive prefix count of a flag (ballot based), same contract.
+template <int Waves>
+__device__ __forceinline__ uint32_t block_flag_scan(bool flag, uint32_t *scratch,
+                                                    uint32_t &total) {
+    const int wave = threadIdx.x >> 6;
+    const uint64_t m = __ballot(flag);
+    if ((threadIdx.x & 63) == 0) scratch[wave] = (uint32_t)__popcll(m);
+    __syncthreads();
+    uint32_t before = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < Waves; ++w) {
+        const uint32_t c = scratch[w];
+        before += w < wave ? c : 0u;
+        sum += c;
+    }
+    __syncthreads();
+    total = sum;
+    return before + lanes_below(m);
+}
+
+struct SelectSmem {
+    uint32_t hist[kTkBins];
+    uint32_t red_lo[kTkWaves], red_hi[kTkWaves];
+    uint32_t found_bin, found_above;
+};
+
+// Key value tau of the need-th largest of n keys key_at(0..n-1), and how many
+// keys equal to tau belong to the top `need` (need_out).  1 <= need <= n.
+// Called by all kTkThreads threads; the result is uniform.
+template <typename KeyAt>
+__device__ void block_select(KeyAt key_at, int n, uint32_t need, SelectSmem &sm,
+                             uint32_t &tau_out, uint32_t &need_out) {
+    const int tid = threadIdx.x;
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    for (int p = tid; p < n; p += kTkThreads) {
+        const uint32_t u = key_at(p);
+        lo = min(lo, u);
+        hi = max(hi, u);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
+    }
+    if ((tid & 63) == 0) {
+        sm.red_lo[tid >> 6] = lo;
+        sm.red_hi[tid >> 6] = hi;
+    }
+    __syncthreads();
+    lo = sm.red_lo[0];
+    hi = sm.red_hi[0];
+#pragma unroll
+    for (int v = 1; v < kTkWaves; ++v) {
+        lo = min(lo, sm.red_lo[v]);
+        hi = max(hi, sm.red_hi[v]);
+    }
+    __syncthreads();
+
+    while (lo != hi) {  // invariant: keys > hi are taken; need more lie in [lo, hi]
+        const uint32_t range = hi - lo;
+        int shift = 0;
+        while ((range >> shift) >= (uint32_t)kTkBins) ++shift;
+        const int nb = (int)(range >> shift) + 1;
+        for (int j = tid; j < nb; j += kTkThreads) sm.hist[j] = 0u;
+        __syncthreads();
+        for (int p = tid; p < n; p += kTkThreads) {
+            const uint32_t u = key_at(p);
+            if (u >= lo && u <= hi) atomicAdd(&sm.hist[(u - lo) >> shift], 1u);
+        }
+        __syncthreads();
+        if (tid < 64) {  // one wave walks the bins down from the top
+            uint32_t above = 0u;
+            int top = nb - 1;
+            bool done = false;
+            while (!done && top >= 0) {
+                const int j = top - tid;
+                uint32_t c = j >= 0 ? sm.hist[j] : 0u;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t o = (uint32_t)__shfl_up((int)c, off, 64);
+                    if (tid >= off) c += o;
+                }
+                const uint32_t incl = above + c;
+                const uint64_t hit = __ballot(j >= 0 && incl >= need);
+                if (hit) {
+                    const int first = __builtin_ctzll(hit);
+                    if (tid == first) {
+                        sm.found_bin = (uint32_t)j;
+                        sm.found_above = incl - sm.hist[j];
+                    }
+                    done = true;
+                } else {
+                    above += (uint32_t)__shfl((int)c, 63, 64);
+                    top -= 64;
+                }
+            }
+        }
+        __syncthreads();
+        const uint32_t bin = sm.found_bin;
+        need -= sm.found_above;
+        const uint32_t new_lo = lo + (bin << shift);
+        const uint32_t width_m1 = (1u << shift) - 1u;
+        hi = (hi - new_lo > width_m1) ? new_lo + width_m1 : hi;
+        lo = new_lo;
+        __syncthreads();
+    }
+    tau_out = lo;
+    need_out = need;
+}
+
+// ------------------------------------------------------- per-row kernel ----
+struct RowSmem {
+    SelectSmem sel;
+    uint32_t scan[kTkWaves];
+    uint32_t keys[kRowCache];
+};
 
 __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
     const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
     int T, int S, int row0, int k, int32_t *__restrict__ idx) {
-    __shared__ uint32_t hist[kTkBins];
-    __shared__ uint32_t red_lo[kTkWaves], red_hi[kTkWaves];
-    __shared__ uint32_t scan_scratch[kTkWaves];
-    __shared__ uint32_t found_bin, found_above;
-
+    __shared__ RowSmem sm;
     const int r = blockIdx.x;
     const int b = blockIdx.y;
     const int i = row0 + r;
@@ -73,111 +209,264 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
         for (int p = tid; p < k; p += kTkThreads) out[p] = p < n ? p : -1;
         return;
     }
+    const bool cached = n <= kRowCache;
+    if (cached) {
+        for (int p = tid; p < n; p += kTkThreads) sm.keys[p] = ordered_key(row[p]);
+        __syncthreads();
+    }
+    auto key_at = [&](int p) -> uint32_t { return cached ? sm.keys[p] : ordered_key(row[p]); };
 
-    // ---- 1. key range of the row
-    uint32_t lo = 0xffffffffu, hi = 0u;
-    for (int p = tid; p < n; p += kTkThreads) {
-        const uint32_t u = ordered_key(row[p]);
-        lo = min(lo, u);
-        hi = max(hi, u);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
-        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
-    }
-    if ((tid & 63) == 0) {
-        red_lo[tid >> 6] = lo;
-        red_hi[tid >> 6] = hi;
-    }
-    __syncthreads();
-    lo = red_lo[0];
-    hi = red_hi[0];
-#pragma unroll
-    for (int v = 1; v < kTkWaves; ++v) {
-        lo = min(lo, red_lo[v]);
-        hi = max(hi, red_hi[v]);
-    }
+    uint32_t tau, need;
+    block_select(key_at, n, (uint32_t)k, sm.sel, tau, need);
 
-    // ---- 2. narrow [lo, hi] to the single key value of the k-th largest
-    uint32_t need = (uint32_t)k;  // still to take from keys inside [lo, hi]
-    while (lo != hi) {
-        const uint32_t range = hi - lo;
-        int shift = 0;
-        while ((range >> shift) >= (uint32_t)kTkBins) ++shift;
-        const int nb = (int)(range >> shift) + 1;
-        for (int j = tid; j < nb; j += kTkThreads) hist[j] = 0u;
-        __syncthreads();
-        for (int p = tid; p < n; p += kTkThreads) {
-            const uint32_t u = ordered_key(row[p]);
-            if (u >= lo && u <= hi) atomicAdd(&hist[(u - lo) >> shift], 1u);
-        }
-        __syncthreads();
-        if (tid < 64) {  // one wave scans the bins from the top
-            uint32_t above = 0u;
-            int top = nb - 1;
-            bool done = false;
-            while (!done && top >= 0) {
-                const int j = top - tid;
-                uint32_t c = j >= 0 ? hist[j] : 0u;
-                // inclusive scan over lanes (lane 0 = highest bin)
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t o = (uint32_t)__shfl_up((int)c, off, 64);
-                    if (tid >= off) c += o;
-                }
-                const uint32_t incl = above + c;
-                const uint64_t hit = __ballot(j >= 0 && incl >= need);
-                if (hit) {
-                    const int first = __builtin_ctzll(hit);
-                    if (tid == first) {
-                        found_bin = (uint32_t)j;
-                        found_above = incl - hist[j];
-                    }
-                    done = true;
-                } else {
-                    above += (uint32_t)__shfl((int)c, 63, 64);
-                    top -= 64;
-                }
-            }
-        }
-        __syncthreads();
-        const uint32_t bin = found_bin;
-        need -= found_above;
-        const uint32_t new_lo = lo + (bin << shift);
-        const uint32_t width_m1 = (shift >= 32) ? 0xffffffffu : ((1u << shift) - 1u);
-        const uint32_t new_hi = (hi - new_lo > width_m1) ? new_lo + width_m1 : hi;
-        lo = new_lo;
-        hi = new_hi;
-        __syncthreads();
-    }
-    const uint32_t tau = lo;
-
-    // ---- 3. ordered compaction: all keys > tau, plus the first `need` ties
+    // ordered compaction: all keys > tau, plus the first `need` ties
     uint32_t written = 0u, ties_seen = 0u;
     for (int base = 0; base < n; base += kTkThreads) {
         const int p = base + tid;
-        const uint32_t u = p < n ? ordered_key(row[p]) : 0u;
+        const uint32_t u = p < n ? key_at(p) : 0u;
         const bool gt = p < n && u > tau;
         const bool eq = p < n && u == tau;
         uint32_t eq_total;
-        const uint32_t eq_rank = block_flag_scan(eq, scan_scratch, eq_total);
+        const uint32_t eq_rank = block_flag_scan<kTkWaves>(eq, sm.scan, eq_total);
         const bool take = gt || (eq && ties_seen + eq_rank < need);
         uint32_t take_total;
-        const uint32_t slot = block_flag_scan(take, scan_scratch, take_total);
+        const uint32_t slot = block_flag_scan<kTkWaves>(take, sm.scan, take_total);
         if (take) out[written + slot] = p;
         written += take_total;
         ties_seen += eq_total;
     }
 }
 
+// ------------------------------------------------------- wide-row path -----
+struct WideLayout {
+    uint32_t *hist;     // [rows][kDigits]
+    uint32_t *meta;     // [rows][kMetaWords]
+    uint32_t *bitmap;   // [rows][words]
+    uint2 *cand;        // [rows][S] (key, position)
+    int words;
+};
+
+__host__ __device__ inline size_t wide_row_bytes(int S) {
+    const size_t words = (size_t)(S + 31) / 32;
+    return (size_t)kDigits * 4 + kMetaWords * 4 + words * 4 + (size_t)S * 8;
+}
+
+__host__ __device__ inline WideLayout wide_layout(void *ws, int nrows, int S) {
+    WideLayout L;
+    char *p = static_cast<char *>(ws);
+    L.words = (S + 31) / 32;
+    L.hist = reinterpret_cast<uint32_t *>(p);
+    p += (size_t)nrows * kDigits * 4;
+    L.meta = reinterpret_cast<uint32_t *>(p);
+    p += (size_t)nrows * kMetaWords * 4;
+    L.bitmap = reinterpret_cast<uint32_t *>(p);
+    p += (size_t)nrows * L.words * 4;
+    p = reinterpret_cast<char *>(((uintptr_t)p + 15) & ~(uintptr_t)15);
+    L.cand = reinterpret_cast<uint2 *>(p);
+    return L;
+}
+
+__global__ __launch_bounds__(256) void topk_wide_clear_kernel(uint32_t *hist, uint32_t *meta,
+                                                              int nrows) {
+    const size_t n1 = (size_t)nrows * kDigits;
+    const size_t n2 = (size_t)nrows * kMetaWords;
+    for (size_t j = blockIdx.x * 256ull + threadIdx.x; j < n1 + n2; j += (size_t)gridDim.x * 256)
+        if (j < n1) hist[j] = 0u;
+        else meta[j - n1] = 0u;
+}
+
+// grid: x = slice, y = row in chunk, z = batch
+__global__ __launch_bounds__(kWideThreads) void topk_wide_hist_kernel(
+    const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
+    int T, int S, int row0, int rows, int k, WideLayout L) {
+    __shared__ uint32_t hist[kDigits];
+    const int r = blockIdx.y, b = blockIdx.z;
+    const int t = query_pos(q_pos, b, row0 + r, T, S);
+    const int n = t < 0 ? 0 : t + 1;
+    const int base = blockIdx.x * kWideSlice;
+    if (n <= k || base >= n) return;
+    const float *row = scores + (size_t)b * batch_stride + (size_t)r * S;
+    for (int j = threadIdx.x; j < kDigits; j += kWideThreads) hist[j] = 0u;
+    __syncthreads();
+    const int end = min(n, base + kWideSlice);
+    for (int p = base + threadIdx.x; p < end; p += kWideThreads)
+        atomicAdd(&hist[ordered_key(row[p]) >> (32 - kDigitBits)], 1u);
+    __syncthreads();
+    uint32_t *gh = L.hist + ((size_t)b * rows + r) * kDigits;
+    for (int j = threadIdx.x; j < kDigits; j += kWideThreads)
+        if (hist[j]) atomicAdd(&gh[j], hist[j]);
+}
+
+// grid: x = slice, y = row in chunk, z = batch
+__global__ __launch_bounds__(kWideThreads) void topk_wide_scan_kernel(
+    const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
+    int T, int S, int row0, int rows, int k, WideLayout L) {
+    __shared__ uint32_t scratch[kWideThreads / 64];
+    __shared__ uint32_t d1_s, above_s;
+    const int r = blockIdx.y, b = blockIdx.z;
+    const int t = query_pos(q_pos, b, row0 + r, T, S);
+    const int n = t < 0 ? 0 : t + 1;
+    const int base = blockIdx.x * kWideSlice;
+    if (n <= k || base >= n) return;
+    const size_t rr = (size_t)b * rows + r;
+    const uint32_t *gh = L.hist + rr * kDigits;
+    const int tid = threadIdx.x;
+
+    // digit d1 holding the k-th largest key: walk the histogram from the top
+    constexpr int per = kDigits / kWideThreads;  // 16 bins per thread
+    uint32_t h[per], csum = 0u;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+        h[j] = gh[tid * per + j];
+        csum += h[j];
+    }
+    // suffix sum over threads above this one: scan in reversed thread order
+    uint32_t total;
+    const uint32_t prefix = block_excl_scan<kWideThreads / 64>(csum, scratch, total);
+    uint32_t running = total - prefix - csum;  // keys in bins of higher threads
+#pragma unroll
+    for (int j = per - 1; j >= 0; --j) {
+        const uint32_t before = running;
+        running += h[j];
+        if (before < (uint32_t)k && running >= (uint32_t)k) {
+            d1_s = (uint32_t)(tid * per + j);
+            above_s = before;
+        }
+    }
+    __syncthreads();
+    const uint32_t d1 = d1_s;
+    if (blockIdx.x == 0 && tid == 0) L.meta[rr * kMetaWords + 1] = above_s;
+
+    // this thread's 32 consecutive positions -> one bitmap word
+    const float *row = scores + (size_t)b * batch_stride + (size_t)r * S;
+    const int p0 = base + tid * 32;
+    uint32_t word = 0u;
+    uint32_t *cnt = &L.meta[rr * kMetaWords + 0];
+    uint2 *cand = L.cand + rr * (size_t)S;
+    const int lane = tid & 63;
+#pragma unroll 4
+    for (int j = 0; j < 32; ++j) {
+        const int p = p0 + j;
+        bool c = false;
+        uint32_t u = 0u;
+        if (p < n) {
+            u = ordered_key(row[p]);
+            const uint32_t d = u >> (32 - kDigitBits);
+            if (d > d1) word |= 1u << j;
+            c = d == d1;
+        }
+        const uint64_t m = __ballot(c);
+        if (m) {  // append this wave's candidates of step j
+            const int leader = __builtin_ctzll(m);
+            uint32_t slot0 = 0u;
+            if (lane == leader) slot0 = atomicAdd(cnt, (uint32_t)__popcll(m));
+            slot0 = (uint32_t)__shfl((int)slot0, leader, 64);
+            if (c) cand[slot0 + lanes_below(m)] = make_uint2(u, (uint32_t)p);
+        }
+    }
+    if (p0 < n) L.bitmap[rr * L.words + (p0 >> 5)] = word;
+}
+
+struct ResolveSmem {
+    SelectSmem sel;
+    uint32_t scan[kTkWaves];
+    uint32_t bits[kWideMaxS / 32];
+};
+
+// grid: x = row in chunk, y = batch
+__global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
+    const int32_t *__restrict__ q_pos, int T, int S, int row0, int rows, int k,
+    int32_t *__restrict__ idx, WideLayout L) {
+    __shared__ ResolveSmem sm;
+    const int r = blockIdx.x, b = blockIdx.y;
+    const int i = row0 + r;
+    const int t = query_pos(q_pos, b, i, T, S);
+    const int n = t < 0 ? 0 : t + 1;
+    int32_t *out = idx + ((size_t)b * T + i) * k;
+    const int tid = threadIdx.x;
+    if (n <= k) {
+        for (int p = tid; p < k; p += kTkThreads) out[p] = p < n ? p : -1;
+        return;
+    }
+    const size_t rr = (size_t)b * rows + r;
+    const int m = (int)L.meta[rr * kMetaWords + 0];
+    const uint32_t need = (uint32_t)k - L.meta[rr * kMetaWords + 1];
+    const uint2 *cand = L.cand + rr * (size_t)S;
+
+    // exact threshold among the candidates of digit d1
+    uint32_t tau, need_tau;
+    block_select([&](int j) -> uint32_t { return cand[j].x; }, m, need, sm.sel, tau, need_tau);
+    // ties at tau: the need_tau lowest positions (select the largest ~position)
+    uint32_t ties = 0u;
+    for (int j = tid; j < m; j += kTkThreads) ties += cand[j].x == tau ? 1u : 0u;
+    uint32_t ties_total;
+    block_excl_scan<kTkWaves>(ties, sm.scan, ties_total);
+    uint32_t pos_cut = 0xffffffffu;
+    if (need_tau < ties_total) {
+        uint32_t tau2, need2;
+        block_select([&](int j) -> uint32_t { return cand[j].x == tau ? ~cand[j].y : 0u; }, m,
+                     need_tau, sm.sel, tau2, need2);
+        pos_cut = ~tau2;  // ties with position <= pos_cut are taken
+    }
+
+    const int words = L.words;
+    const int nw = (n + 31) / 32;
+    for (int w = tid; w < nw; w += kTkThreads) sm.bits[w] = L.bitmap[rr * words + w];
+    __syncthreads();
+    for (int j = tid; j < m; j += kTkThreads) {
+        const uint2 c = cand[j];
+        if (c.x > tau || (c.x == tau && c.y <= pos_cut))
+            atomicOr(&sm.bits[c.y >> 5], 1u << (c.y & 31));
+    }
+    __syncthreads();
+
+    // ordered compaction: contiguous words per thread, prefix of popcounts
+    const int per = (nw + kTkThreads - 1) / kTkThreads;
+    const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
+    uint32_t cntw = 0u;
+    for (int w = w0; w < w1; ++w) cntw += (uint32_t)__popc(sm.bits[w]);
+    uint32_t total;
+    uint32_t slot = block_excl_scan<kTkWaves>(cntw, sm.scan, total);
+    for (int w = w0; w < w1; ++w) {
+        uint32_t x = sm.bits[w];
+        while (x) {
+            const int bit = __builtin_ctz(x);
+            x &= x - 1u;
+            out[slot++] = w * 32 + bit;
+        }
+    }
+}
+
+bool use_wide(int B, int rows, int S) {
+    return S >= kWideMinS && S <= kWideMaxS && (long long)B * rows <= kWideMaxRows;
+}
+
 }  // namespace
 
-size_t topk_workspace_bytes(int, int, int, int) { return 0; }
+size_t topk_workspace_bytes(int B, int T, int S, int) {
+    if (S < kWideMinS || S > kWideMaxS) return 0;
+    const long long bt = (long long)B * T;
+    const long long nrows = bt < kWideMaxRows ? bt : kWideMaxRows;
+    return (size_t)nrows * wide_row_bytes(S) + 64;
+}
 
 hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *q_pos, int B,
-                       int T, int S, int row0, int rows, int k, int32_t *idx, void *,
+                       int T, int S, int row0, int rows, int k, int32_t *idx, void *workspace,
                        hipStream_t stream) {
+    if (use_wide(B, rows, S) && workspace) {
+        const WideLayout L = wide_layout(workspace, B * rows, S);
+        const int nrows = B * rows;
+        hipLaunchKernelGGL(topk_wide_clear_kernel, dim3(min(1024, ceil_div(nrows * (kDigits + kMetaWords), 256))),
+                           dim3(256), 0, stream, L.hist, L.meta, nrows);
+        const dim3 g(ceil_div(S, kWideSlice), rows, B);
+        hipLaunchKernelGGL(topk_wide_hist_kernel, g, dim3(kWideThreads), 0, stream, scores,
+                           batch_stride, q_pos, T, S, row0, rows, k, L);
+        hipLaunchKernelGGL(topk_wide_scan_kernel, g, dim3(kWideThreads), 0, stream, scores,
+                           batch_stride, q_pos, T, S, row0, rows, k, L);
+        hipLaunchKernelGGL(topk_wide_resolve_kernel, dim3(rows, B), dim3(kTkThreads), 0, stream,
+                           q_pos, T, S, row0, rows, k, idx, L);
+        return hipGetLastError();
+    }
     dim3 grid(rows, B);
     hipLaunchKernelGGL(topk_row_kernel, grid, dim3(kTkThreads), 0, stream, scores, batch_stride,
                        q_pos, T, S, row0, k, idx);

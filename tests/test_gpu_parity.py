@@ -333,3 +333,21 @@ def test_forward_c2_sampled_rows():
     err = max_abs_err(out[:, rows], ref)
     _say(f"c2: max-abs err {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("case", ["levels3", "all_equal", "k1", "kS", "short_rows", "neg"])
+def test_topk_wide_path_edges(case):
+    """Few wide rows take the split-row path: ties, degenerate budgets,
+    rows shorter than the budget and negative scores."""
+    B, S = 4, 40000
+    k = {"k1": 1, "kS": S}.get(case, 2048)
+    levels = {"levels3": 3, "all_equal": 1}.get(case)
+    sc = synth.random_scores((B, 1, S), seed=hash(case) % 1000, levels=levels)
+    if case == "neg":
+        sc = -sc.abs() - 1.0
+        sc[0, 0, 5] = -0.0
+    pos = torch.tensor([[S - 1], [S - 1], [20000], [S - 7]], dtype=torch.int32)
+    if case == "short_rows":
+        pos = torch.tensor([[10], [2047], [2048], [2049]], dtype=torch.int32)
+    idx = dsa.dsa_topk(sc.to(DEV), k, q_pos=pos.to(DEV))
+    assert_selection_equal(idx, oracle.topk(sc, k, q_pos=pos), case)
