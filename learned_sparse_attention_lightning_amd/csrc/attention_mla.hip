@@ -10,8 +10,11 @@
 //
 // Workgroup = 4 waves = one query row x 64 heads x one range of selected
 // entries, walked 64 entries at a time:
-//   gather  the 64 selected rows into LDS (row pitch padded against bank
-//           conflicts; masked entries are zero rows);
+//   gather  the 64 selected rows go straight from memory into one of two LDS
+//           tile buffers (global_load_lds, 16 bytes a lane), so the next tile
+//           is in flight while the current one is multiplied; the row pitch
+//           carries one spare 16-byte slot against bank conflicts, and masked
+//           entries load a valid row whose probability is then forced to 0;
 //   S phase wave w computes S^T = C(32 keys) . Q^T(32 heads) over 576 dims for
 //           key tile w/2 and head tile w%2 (v_mfma_f32_32x32x16_bf16), with
 //           its 32x576 query block held in registers as the B operand;
@@ -36,16 +39,21 @@ constexpr int kRowPitch = kDqk * 2 + 16;   // bytes: 1168 (bank shift of 36 dwor
 constexpr int kPPitch = kKt * 2 + 16;      // bytes: 144
 constexpr int kChunksPerRow = kDqk * 2 / 16;  // 72 chunks of 16 bytes
 constexpr int kThreads = 256;
+constexpr float kRescaleLog2 = 8.0f;  // reference-max slack, base-2 units
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
+constexpr int kPitchChunks = kRowPitch / 16;            // 73 slots of 16 bytes a row
+constexpr int kTileLoads = kKt * kPitchChunks / 64;      // 73 wave loads of 1 KB a tile
+static_assert(kKt * kPitchChunks % 64 == 0, "a tile is a whole number of wave loads");
+
 struct __align__(16) MlaSmem {
-    uint8_t kv[kKt * kRowPitch];       // 74752
+    uint8_t kv[2][kKt * kRowPitch];    // 2 x 74752, double-buffered tiles
     uint8_t p[kHg * kPPitch];          // 9216
+    int32_t sel[2][kKt];
     float tile_max[2][kHg];            // per key tile, per head
     float corr[kHg];
     float lsum[2][kHg];
-    int32_t sel[kKt];
 };
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint8_t *p) {
@@ -61,16 +69,29 @@ __device__ __forceinline__ bf16x4 lds_tr16(const uint8_t *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4)(p));
 }
 
-// Load 16 bytes of the latent row into LDS (zeros for a masked entry).
-__device__ __forceinline__ void gather_tile(MlaSmem &sm, const uint8_t *__restrict__ lat_b,
-                                            int tid) {
-    for (int c = tid; c < kKt * kChunksPerRow; c += kThreads) {
-        const int row = c / kChunksPerRow;
-        const int ch = c - row * kChunksPerRow;
-        const int s = sm.sel[row];
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (s >= 0) v = *reinterpret_cast<const u32x4 *>(lat_b + (size_t)s * (kDqk * 2) + ch * 16);
-        *reinterpret_cast<u32x4 *>(sm.kv + row * kRowPitch + ch * 16) = v;
+// Issue the loads of one tile: wave load j fills LDS bytes [1024j, 1024j+1024)
+// of the tile, lane l the 16-byte slot q = 64j + l, i.e. row q / 73, slot
+// q % 73.  Slot 72 is the pitch padding (loaded with chunk 0, never read).  A
+// masked entry (-1) loads row 0; its probability is forced to 0.  Completion
+// is awaited later with s_waitcnt.
+__device__ __forceinline__ void issue_tile(uint8_t *tile, const int32_t *sel,
+                                           const uint8_t *__restrict__ lat_b, int wave,
+                                           int lane) {
+    typedef __attribute__((address_space(3))) void *lds_ptr;
+    constexpr int kStep = 64 * (kThreads / 64);  // slots between a wave's loads
+    int q = 64 * wave + lane;
+    int row = q / kPitchChunks;
+    int c = q - row * kPitchChunks;
+    for (int j = wave; j < kTileLoads; j += kThreads / 64) {
+        const uint32_t s = (uint32_t)max(sel[row], 0);
+        const uint8_t *src = lat_b + s * (uint64_t)(kDqk * 2) + (c < kChunksPerRow ? c * 16 : 0);
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(tile + 1024 * j), 16, 0, 0);
+        row += kStep / kPitchChunks;
+        c += kStep % kPitchChunks;
+        if (c >= kPitchChunks) {
+            c -= kPitchChunks;
+            row += 1;
+        }
     }
 }
 
@@ -83,12 +104,15 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float v) {
     *p = (uint16_t)f32_to_bf16_bits(v);
 }
 
-// grid: x = head group, y = split * rows + row, z = batch
+// grid: 1-D.  Work item = (head group, split, row, batch); with splits == 1
+// and a row count that is a multiple of 8, the head groups of one query row
+// get workgroup ids that are 8 apart, so they run on the same XCD (ids are
+// dealt round-robin over the 8 XCDs) and the second gather hits its L2.
 template <typename Tout>
 __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ lat,
     const int32_t *__restrict__ idx, int T, int S, int H, int k, float scale, int row0,
-    int rows, int splits, int per_split, Tout *__restrict__ out, float *__restrict__ lse,
+    int rows, int B, int splits, int per_split, Tout *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ o_part, float *__restrict__ lse_part) {
     __shared__ MlaSmem sm;
     const int tid = threadIdx.x;
@@ -96,17 +120,38 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     const int lane = tid & 63;
     const int half = lane >> 5;
     const int l32 = lane & 31;
-    const int hg = blockIdx.x;
-    const int split = blockIdx.y / rows;
-    const int r = blockIdx.y - split * rows;
-    const int b = blockIdx.z;
+    const int hgs = H / kHg;
+    const int id = blockIdx.x;
+    int hg, split, qidx;
+    if (splits == 1 && (rows * B) % 8 == 0) {
+        const int slot = id >> 3;
+        hg = slot % hgs;
+        qidx = (slot / hgs) * 8 + (id & 7);
+        split = 0;
+    } else {
+        hg = id % hgs;
+        split = (id / hgs) % splits;
+        qidx = id / (hgs * splits);
+    }
+    const int r = qidx % rows;
+    const int b = qidx / rows;
     const int i = row0 + r;
     const int head0 = hg * kHg;
 
     const int e_begin = split * per_split;
     const int e_end = min(k, e_begin + per_split);
+    const int ntiles = (e_end - e_begin + kKt - 1) / kKt;
     const int32_t *sel_row = idx + ((size_t)b * T + i) * k;
     const uint8_t *lat_b = reinterpret_cast<const uint8_t *>(lat) + (size_t)b * S * (kDqk * 2);
+
+    // ---- prologue: indices of tiles 0 and 1, loads of tile 0 in flight
+    if (tid < kKt) {
+        const int e = e_begin + tid;
+        sm.sel[0][tid] = e < e_end ? sel_row[e] : -1;
+        sm.sel[1][tid] = e + kKt < e_end ? sel_row[e + kKt] : -1;
+    }
+    __syncthreads();
+    issue_tile(sm.kv[0], sm.sel[0], lat_b, wave, lane);
 
     // ---- S-phase role and its query block (B operand: 32 heads x 576 dims)
     const int kt = wave >> 1;  // key tile of the S phase
@@ -129,17 +174,24 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     float m_run = -INFINITY;  // running max of head (head0 + 32*ht + l32), S-phase view
     float l_run = 0.0f;       // this wave's share of the running sum
     const float sl2 = scale * 1.4426950408889634f;  // logits in base-2 units
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
-    for (int e0 = e_begin; e0 < e_end; e0 += kKt) {
-        __syncthreads();  // previous step's readers are done with kv / p / sel
-        if (tid < kKt) sm.sel[tid] = (e0 + tid < e_end) ? sel_row[e0 + tid] : -1;
-        __syncthreads();
-        gather_tile(sm, lat_b, tid);
-        __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        const int buf = it & 1;
+        // loads of the next tile overlap this tile's arithmetic
+        if (it + 1 < ntiles) issue_tile(sm.kv[buf ^ 1], sm.sel[buf ^ 1], lat_b, wave, lane);
+        int next_sel = -1;
+        if (tid < kKt) {
+            const int e = e_begin + (it + 2) * kKt + tid;
+            next_sel = e < e_end ? sel_row[e] : -1;
+        }
+        const uint8_t *kvt = sm.kv[buf];
+        const int32_t *selt = sm.sel[buf];
 
         // ---- S^T = C . Q^T for (key tile kt, head tile ht)
         f32x16 sacc = {};
-        const uint8_t *arow = sm.kv + (kt * 32 + l32) * kRowPitch + 16 * half;
+        const uint8_t *arow = kvt + (kt * 32 + l32) * kRowPitch + 16 * half;
 #pragma unroll
         for (int ks = 0; ks < kKsteps; ++ks)
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(arow + ks * 32), qb[ks], sacc,
@@ -149,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
 #pragma unroll
         for (int rg = 0; rg < 16; ++rg) {
             const int key = kt * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3);
-            const float x = sm.sel[key] >= 0 ? sacc[rg] * sl2 : -INFINITY;
+            const float x = selt[key] >= 0 ? sacc[rg] * sl2 : -INFINITY;
             sacc[rg] = x;
             tmax = fmaxf(tmax, x);
         }
@@ -157,23 +209,29 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         if (half == 0) sm.tile_max[kt][ht * 32 + l32] = tmax;
         __syncthreads();
         const float m_tile = fmaxf(sm.tile_max[0][ht * 32 + l32], sm.tile_max[1][ht * 32 + l32]);
-        const float m_new = fmaxf(m_run, m_tile);
-        const float corr = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
-        m_run = m_new;
+        // Lazy rescaling: the reference max m_run only moves when the tile max
+        // exceeds it by more than 2^8, so probabilities stay <= 256 and the
+        // accumulators are rescaled only on those (rare) steps.  The softmax is
+        // unchanged: numerator and denominator share the reference.
+        float corr = 1.0f;
+        if (m_tile > m_run + kRescaleLog2) {
+            corr = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_tile);
+            m_run = m_tile;
+        }
+        const float m_ref = m_run;
         float psum = 0.0f;
         uint8_t *prow = sm.p + (ht * 32 + l32) * kPPitch;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            uint32_t packed[2];
+            float pv[4];
 #pragma unroll
-            for (int j = 0; j < 4; j += 2) {
-                const float p0 = m_new == -INFINITY ? 0.0f : exp2f(sacc[4 * g + j] - m_new);
-                const float p1 = m_new == -INFINITY ? 0.0f : exp2f(sacc[4 * g + j + 1] - m_new);
-                psum += p0 + p1;
-                packed[j >> 1] = f32_to_bf16_bits(p0) | (f32_to_bf16_bits(p1) << 16);
+            for (int j = 0; j < 4; ++j) {
+                pv[j] = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sacc[4 * g + j] - m_ref);
+                psum += pv[j];
             }
+            const bf16x4 pk = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
             const int key = kt * 32 + 8 * g + 4 * half;
-            *reinterpret_cast<uint2 *>(prow + key * 2) = make_uint2(packed[0], packed[1]);
+            *reinterpret_cast<bf16x4 *>(prow + key * 2) = pk;
         }
         l_run = l_run * corr + psum;
         if (kt == 0 && half == 0) sm.corr[ht * 32 + l32] = corr;
@@ -184,35 +242,48 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
             float cr[16];
+            bool any = false;
 #pragma unroll
-            for (int rg = 0; rg < 16; ++rg) cr[rg] = sm.corr[a * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
+            for (int rg = 0; rg < 16; ++rg) {
+                cr[rg] = sm.corr[a * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
+                any |= cr[rg] != 1.0f;
+            }
+            if (__ballot(any)) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+                for (int c = 0; c < 4; ++c)
 #pragma unroll
-                for (int rg = 0; rg < 16; ++rg) o[a][c][rg] *= cr[rg];
+                    for (int rg = 0; rg < 16; ++rg) o[a][c][rg] *= cr[rg];
+            }
         }
+        // transpose-read lane address: row key0 + j/4, column col0 + 4*(j%4)
+        const int trj = lane & 15;
+        const int trg = lane >> 4;
+        const uint8_t *vbase = kvt + (8 * (trg >> 1) + (trj >> 2)) * kRowPitch +
+                               (dv0 + 16 * (trg & 1) + 4 * (trj & 3)) * 2;
 #pragma unroll
         for (int ks = 0; ks < kKt / 16; ++ks) {
-            bf16x8 pa[2];
+            bf16x8 pa[2], vb[4];
 #pragma unroll
             for (int a = 0; a < 2; ++a)
                 pa[a] = lds_b128(sm.p + (a * 32 + l32) * kPPitch + (16 * ks + 8 * half) * 2);
-            // transpose-read lane address: row key0 + j/4, column col0 + 4*(j%4)
-            const int j = lane & 15;
-            const int grp = lane >> 4;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const int col0 = dv0 + 32 * c + 16 * (grp & 1) + 4 * (j & 3);
-                const int key0 = 16 * ks + 8 * (grp >> 1) + (j >> 2);
-                const uint8_t *vp = sm.kv + key0 * kRowPitch + col0 * 2;
+                const uint8_t *vp = vbase + 16 * ks * kRowPitch + 32 * c * 2;
                 const bf16x4 lo = lds_tr16(vp);
                 const bf16x4 hi = lds_tr16(vp + 4 * kRowPitch);
-                const bf16x8 vb = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                vb[c] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
                 for (int a = 0; a < 2; ++a)
-                    o[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[a], vb, o[a][c], 0, 0, 0);
-            }
+                    o[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[a], vb[c], o[a][c], 0, 0,
+                                                                      0);
         }
+        __syncthreads();  // every wave is done with kv[buf], sel[buf], p
+        if (tid < kKt) sm.sel[buf][tid] = next_sel;  // indices of tile it + 2
+        __builtin_amdgcn_s_waitcnt(0);               // tile it + 1 has landed
+        __syncthreads();
     }
 
     // ---- final normalisation: l per head = sum of both key-tile waves' shares
@@ -281,10 +352,12 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(
     if (lse && d == 0) lse[rowq * H + h] = wsum > 0.0f ? mx + __logf(wsum) : -INFINITY;
 }
 
+// Entry splits per query row: enough workgroups to cover the CUs, but at least
+// four tiles per split so the two-stage gather pipeline has work to overlap.
 int mla_splits(int B, int rows, int H, int k) {
     const long long wgs = (long long)B * rows * (H / kHg);
-    const int max_splits = ceil_div(k, kKt);
-    long long s = (512 + wgs - 1) / wgs;
+    const int max_splits = ceil_div(k, 4 * kKt);
+    long long s = (256 + wgs - 1) / wgs;
     if (s < 1) s = 1;
     if (s > max_splits) s = max_splits;
     return (int)s;
@@ -321,16 +394,17 @@ hipError_t launch_mla(const dsa_attn_desc_t &d, const void *q, const void *kv,
         const int used_splits = ceil_div(k, per_split);
         float *o_part = static_cast<float *>(workspace);
         float *lse_part = o_part + (size_t)B * n * used_splits * H * kDv;
-        dim3 grid(H / kHg, used_splits * n, B);
+        const long long nwg = (long long)(H / kHg) * used_splits * n * B;
+        dim3 grid((unsigned)nwg);
         if (d.out_dtype == DSA_BF16)
             hipLaunchKernelGGL(mla_attention_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
                                static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),
-                               idx, T, S, H, k, d.scale, row0 + r0, n, used_splits, per_split,
+                               idx, T, S, H, k, d.scale, row0 + r0, n, B, used_splits, per_split,
                                static_cast<uint16_t *>(out), lse, o_part, lse_part);
         else
             hipLaunchKernelGGL(mla_attention_kernel<float>, grid, dim3(kThreads), 0, stream,
                                static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),
-                               idx, T, S, H, k, d.scale, row0 + r0, n, used_splits, per_split,
+                               idx, T, S, H, k, d.scale, row0 + r0, n, B, used_splits, per_split,
                                static_cast<float *>(out), lse, o_part, lse_part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -26,12 +26,9 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
     return __uint_as_float(b << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 bits (NaN kept quiet).
+// Round-to-nearest-even fp32 -> bf16 bits (the hardware conversion).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // OCP fp8 e4m3fn -> fp32, exact (bias 7, no infinities, S.1111.111 = NaN).
