@@ -353,10 +353,10 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(
 }
 
 // Entry splits per query row: enough workgroups to cover the CUs, but at least
-// four tiles per split so the two-stage gather pipeline has work to overlap.
+// two tiles per split so the two-stage gather pipeline has work to overlap.
 int mla_splits(int B, int rows, int H, int k) {
     const long long wgs = (long long)B * rows * (H / kHg);
-    const int max_splits = ceil_div(k, 4 * kKt);
+    const int max_splits = ceil_div(k, 2 * kKt);
     long long s = (256 + wgs - 1) / wgs;
     if (s < 1) s = 1;
     if (s > max_splits) s = max_splits;

@@ -126,8 +126,8 @@ DSA_EXPORT dsa_status_t dsa_indexer_scores(const void *q_idx, const void *k_idx,
     if (st != DSA_OK) return st;
     if (!aligned16(scores)) return DSA_ERR_ALIGN;
     return hip_status(launch_indexer(q_idx, k_idx, idx_dtype, w, q_pos, B, T, S, index_n_heads,
-                                     index_head_dim, 0, T, scores, (size_t)T * S, true,
-                                     (hipStream_t)stream));
+                                     index_head_dim, 0, T, scores, (size_t)T * S, true, nullptr,
+                                     0, (hipStream_t)stream));
 }
 
 DSA_EXPORT dsa_status_t dsa_topk(const float *scores, const int32_t *q_pos, int B, int T, int S,
@@ -141,7 +141,7 @@ DSA_EXPORT dsa_status_t dsa_topk(const float *scores, const int32_t *q_pos, int 
     const size_t need = topk_workspace_bytes(B, T, S, index_topk);
     if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
     return hip_status(launch_topk(scores, (size_t)T * S, q_pos, B, T, S, 0, T, index_topk, idx,
-                                  workspace, (hipStream_t)stream));
+                                  workspace, false, (hipStream_t)stream));
 }
 
 DSA_EXPORT dsa_status_t dsa_sparse_attention(const dsa_attn_desc_t *desc, const void *q,
@@ -196,12 +196,14 @@ DSA_EXPORT dsa_status_t dsa_forward(const dsa_attn_desc_t *desc, const void *q_i
     const size_t batch_stride = (size_t)rows * S;
     for (int row0 = 0; row0 < T; row0 += rows) {
         const int n = T - row0 < rows ? T - row0 : rows;
+        // the indexer launch also clears the top-k counters
+        const size_t clear_words = topk_clear_words(B, n, S);
         hipError_t e = launch_indexer(q_idx, k_idx, idx_dtype, w, q_pos, B, T, S, index_n_heads,
                                       index_head_dim, row0, n, score_block, batch_stride, false,
-                                      s);
+                                      static_cast<uint32_t *>(topk_ws), clear_words, s);
         if (e != hipSuccess) return DSA_ERR_HIP;
         e = launch_topk(score_block, batch_stride, q_pos, B, T, S, row0, n, index_topk, sel,
-                        topk_ws, s);
+                        topk_ws, clear_words > 0, s);
         if (e != hipSuccess) return DSA_ERR_HIP;
         e = launch_attention(*desc, q, kv, v, sel, B, T, S, row0, n, index_topk, out, nullptr,
                              attn_ws, s);

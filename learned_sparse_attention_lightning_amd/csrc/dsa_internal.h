@@ -73,17 +73,20 @@ __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b -
 // Indexer scores for rows [row0, row0+rows) of every batch.  `scores` points
 // at row row0 of batch 0 with row stride S and batch stride `batch_stride`
 // (in floats).  write_masked: also write -inf for s in (t, S).
+// clear_words > 0: the launch also zeroes clear[0..clear_words) (the counters
+// of the top-k that follows), so no separate clearing kernel is needed.
 hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, const float *w,
                           const int32_t *q_pos, int B, int T, int S, int H, int D, int row0,
                           int rows, float *scores, size_t batch_stride, bool write_masked,
-                          hipStream_t stream);
+                          uint32_t *clear, size_t clear_words, hipStream_t stream);
 
 bool indexer_shape_supported(int H, int D);
 
 size_t topk_workspace_bytes(int B, int T, int S, int k);
+size_t topk_clear_words(int B, int rows, int S);
 hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *q_pos, int B,
                        int T, int S, int row0, int rows, int k, int32_t *idx, void *workspace,
-                       hipStream_t stream);
+                       bool workspace_cleared, hipStream_t stream);
 
 bool mla_fast_path(const dsa_attn_desc_t &d);
 size_t mla_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int k);

@@ -76,8 +76,13 @@ __global__ __launch_bounds__(256) void indexer_mfma_kernel(
     const uint8_t *__restrict__ q_idx, const uint8_t *__restrict__ k_idx,
     const float *__restrict__ w, const int32_t *__restrict__ q_pos, int B, int T, int S,
     int row0, int rows, int chunk, int nchunks, float *__restrict__ scores,
-    size_t batch_stride, int write_masked) {
+    size_t batch_stride, int write_masked, uint32_t *__restrict__ clear, size_t clear_words) {
     typedef IdxTraits<Fp8> Tr;
+    if (clear_words) {  // zero the next kernel's counters, spread over the grid
+        const size_t nthreads = (size_t)gridDim.x * blockDim.x;
+        for (size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x; j < clear_words; j += nthreads)
+            clear[j] = 0u;
+    }
     typedef typename Tr::operand Op;
     constexpr int EB = Tr::elem_bytes;
     constexpr int KS = Tr::ksteps;
@@ -197,6 +202,11 @@ __global__ __launch_bounds__(kGenericThreads) void indexer_generic_kernel(
     out[s] = total;
 }
 
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t *p, size_t n) {
+    for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < n; j += (size_t)gridDim.x * 256)
+        p[j] = 0u;
+}
+
 }  // namespace
 
 bool indexer_shape_supported(int H, int D) { return H >= 1 && D >= 1 && H <= 128 && H * D <= kGenericMaxQ; }
@@ -204,11 +214,13 @@ bool indexer_shape_supported(int H, int D) { return H >= 1 && D >= 1 && H <= 128
 hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, const float *w,
                           const int32_t *q_pos, int B, int T, int S, int H, int D, int row0,
                           int rows, float *scores, size_t batch_stride, bool write_masked,
-                          hipStream_t stream) {
+                          uint32_t *clear, size_t clear_words, hipStream_t stream) {
     if (H == kIdxHeads && D == kIdxDim && idx_dtype != DSA_F32) {
         // key chunk per wave: long enough to amortise the query-block load,
-        // short enough to spread one decode row over many CUs
-        const int chunk = (T == 1) ? 1024 : 2048;
+        // short enough that a few query rows still give ~16 waves per CU (a
+        // streaming kernel needs that many loads in flight)
+        int chunk = 2048;
+        while (chunk > 128 && (long long)B * rows * ceil_div(S, chunk) < 4096) chunk >>= 1;
         const int nchunks = ceil_div(S, chunk);
         const long long waves = (long long)B * rows * nchunks;
         const int blocks = (int)((waves + 3) / 4);
@@ -216,13 +228,21 @@ hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, c
             hipLaunchKernelGGL((indexer_mfma_kernel<false>), dim3(blocks), dim3(256), 0, stream,
                                static_cast<const uint8_t *>(q_idx),
                                static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
-                               rows, chunk, nchunks, scores, batch_stride, (int)write_masked);
+                               rows, chunk, nchunks, scores, batch_stride, (int)write_masked,
+                               clear, clear_words);
         else
             hipLaunchKernelGGL((indexer_mfma_kernel<true>), dim3(blocks), dim3(256), 0, stream,
                                static_cast<const uint8_t *>(q_idx),
                                static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
-                               rows, chunk, nchunks, scores, batch_stride, (int)write_masked);
+                               rows, chunk, nchunks, scores, batch_stride, (int)write_masked,
+                               clear, clear_words);
         return hipGetLastError();
+    }
+    if (clear_words) {
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(min((size_t)1024, (clear_words + 255) / 256)),
+                           dim3(256), 0, stream, clear, clear_words);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     for (int r0 = 0; r0 < rows; r0 += kMaxGridY) {
         const int n = min(kMaxGridY, rows - r0);

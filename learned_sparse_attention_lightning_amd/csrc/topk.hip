@@ -35,13 +35,16 @@ constexpr int kRowCache = 32768;  // scores cached in LDS by the per-row kernel
 
 // wide-row path
 constexpr int kWideThreads = 256;
-constexpr int kWideSlice = kWideThreads * 32;  // positions per slice workgroup
+constexpr int kWidePer = 8;                         // consecutive positions per thread
+constexpr int kWideSlice = kWideThreads * kWidePer;  // positions per slice workgroup
+constexpr int kCandCache = 8192;                     // candidates the resolve keeps in LDS
 constexpr int kDigitBits = 12;
 constexpr int kDigits = 1 << kDigitBits;
 constexpr int kWideMinS = 16384;
 constexpr int kWideMaxS = 262144;      // bitmap of one row fits 32 KB of LDS
 constexpr int kWideMaxRows = 512;
-constexpr int kMetaWords = 16;         // per row: [0] candidate count, [1] count above d1
+constexpr int kMetaWords = 16;         // per row: [1] count of keys above digit d1
+constexpr int kMaxSlices = kWideMaxS / kWideSlice;  // candidate counts per row (one per slice)
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
     const uint32_t lo = __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u);
@@ -98,6 +101,7 @@ __device__ __forceinline__ uint32_t block_flag_scan(bool flag, uint32_t *scratch
 struct SelectSmem {
     uint32_t hist[kTkBins];
     uint32_t red_lo[kTkWaves], red_hi[kTkWaves];
+    uint32_t scan[kTkWaves];
     uint32_t found_bin, found_above;
 };
 
@@ -145,30 +149,25 @@ __device__ void block_select(KeyAt key_at, int n, uint32_t need, SelectSmem &sm,
             if (u >= lo && u <= hi) atomicAdd(&sm.hist[(u - lo) >> shift], 1u);
         }
         __syncthreads();
-        if (tid < 64) {  // one wave walks the bins down from the top
-            uint32_t above = 0u;
-            int top = nb - 1;
-            bool done = false;
-            while (!done && top >= 0) {
-                const int j = top - tid;
-                uint32_t c = j >= 0 ? sm.hist[j] : 0u;
+        {  // bin holding the need-th largest: suffix counts over thread-owned bin pairs
+            constexpr int kPer = kTkBins / kTkThreads;  // 2 bins per thread
+            uint32_t hb[kPer], c = 0u;
 #pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t o = (uint32_t)__shfl_up((int)c, off, 64);
-                    if (tid >= off) c += o;
-                }
-                const uint32_t incl = above + c;
-                const uint64_t hit = __ballot(j >= 0 && incl >= need);
-                if (hit) {
-                    const int first = __builtin_ctzll(hit);
-                    if (tid == first) {
-                        sm.found_bin = (uint32_t)j;
-                        sm.found_above = incl - sm.hist[j];
-                    }
-                    done = true;
-                } else {
-                    above += (uint32_t)__shfl((int)c, 63, 64);
-                    top -= 64;
+            for (int j = 0; j < kPer; ++j) {
+                const int bj = tid * kPer + j;
+                hb[j] = bj < nb ? sm.hist[bj] : 0u;
+                c += hb[j];
+            }
+            uint32_t tot;
+            const uint32_t pre = block_excl_scan<kTkWaves>(c, sm.scan, tot);
+            uint32_t run = tot - pre - c;  // keys in bins above this thread's pair
+#pragma unroll
+            for (int j = kPer - 1; j >= 0; --j) {
+                const uint32_t before = run;
+                run += hb[j];
+                if (before < need && run >= need) {
+                    sm.found_bin = (uint32_t)(tid * kPer + j);
+                    sm.found_above = before;
                 }
             }
         }
@@ -241,14 +240,16 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
 struct WideLayout {
     uint32_t *hist;     // [rows][kDigits]
     uint32_t *meta;     // [rows][kMetaWords]
+    uint32_t *counts;   // [rows][kMaxSlices] candidates found by each slice
     uint32_t *bitmap;   // [rows][words]
-    uint2 *cand;        // [rows][S] (key, position)
+    uint2 *cand;        // [rows][S] (key, position); slice i owns [i*slice, (i+1)*slice)
     int words;
 };
 
 __host__ __device__ inline size_t wide_row_bytes(int S) {
     const size_t words = (size_t)(S + 31) / 32;
-    return (size_t)kDigits * 4 + kMetaWords * 4 + words * 4 + (size_t)S * 8;
+    return (size_t)kDigits * 4 + kMetaWords * 4 + kMaxSlices * 4 + words * 4 + (size_t)S * 8 +
+           16;
 }
 
 __host__ __device__ inline WideLayout wide_layout(void *ws, int nrows, int S) {
@@ -259,6 +260,8 @@ __host__ __device__ inline WideLayout wide_layout(void *ws, int nrows, int S) {
     p += (size_t)nrows * kDigits * 4;
     L.meta = reinterpret_cast<uint32_t *>(p);
     p += (size_t)nrows * kMetaWords * 4;
+    L.counts = reinterpret_cast<uint32_t *>(p);
+    p += (size_t)nrows * kMaxSlices * 4;
     L.bitmap = reinterpret_cast<uint32_t *>(p);
     p += (size_t)nrows * L.words * 4;
     p = reinterpret_cast<char *>(((uintptr_t)p + 15) & ~(uintptr_t)15);
@@ -275,6 +278,23 @@ __global__ __launch_bounds__(256) void topk_wide_clear_kernel(uint32_t *hist, ui
         else meta[j - n1] = 0u;
 }
 
+// Scores of 8 consecutive positions p0..p0+7 of a row as order-preserving
+// keys (positions >= n read as 0 and are ignored by the callers).
+__device__ __forceinline__ void load8_keys(const float *row, int p0, int n, uint32_t (&u)[8]) {
+    if (p0 + 8 <= n && ((uintptr_t)(row + p0) & 15) == 0) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(row + p0);
+        const f32x4 c = *reinterpret_cast<const f32x4 *>(row + p0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            u[e] = ordered_key(a[e]);
+            u[4 + e] = ordered_key(c[e]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = p0 + e < n ? ordered_key(row[p0 + e]) : 0u;
+    }
+}
+
 // grid: x = slice, y = row in chunk, z = batch
 __global__ __launch_bounds__(kWideThreads) void topk_wide_hist_kernel(
     const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
@@ -288,9 +308,12 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_hist_kernel(
     const float *row = scores + (size_t)b * batch_stride + (size_t)r * S;
     for (int j = threadIdx.x; j < kDigits; j += kWideThreads) hist[j] = 0u;
     __syncthreads();
-    const int end = min(n, base + kWideSlice);
-    for (int p = base + threadIdx.x; p < end; p += kWideThreads)
-        atomicAdd(&hist[ordered_key(row[p]) >> (32 - kDigitBits)], 1u);
+    const int p0 = base + threadIdx.x * kWidePer;
+    uint32_t u[8];
+    load8_keys(row, p0, n, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (p0 + e < n) atomicAdd(&hist[u[e] >> (32 - kDigitBits)], 1u);
     __syncthreads();
     uint32_t *gh = L.hist + ((size_t)b * rows + r) * kDigits;
     for (int j = threadIdx.x; j < kDigits; j += kWideThreads)
@@ -311,6 +334,10 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_scan_kernel(
     const size_t rr = (size_t)b * rows + r;
     const uint32_t *gh = L.hist + rr * kDigits;
     const int tid = threadIdx.x;
+    const float *row = scores + (size_t)b * batch_stride + (size_t)r * S;
+    const int p0 = base + tid * kWidePer;
+    uint32_t u[8];
+    load8_keys(row, p0, n, u);  // issued early; used after the digit search
 
     // digit d1 holding the k-th largest key: walk the histogram from the top
     constexpr int per = kDigits / kWideThreads;  // 16 bins per thread
@@ -320,7 +347,6 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_scan_kernel(
         h[j] = gh[tid * per + j];
         csum += h[j];
     }
-    // suffix sum over threads above this one: scan in reversed thread order
     uint32_t total;
     const uint32_t prefix = block_excl_scan<kWideThreads / 64>(csum, scratch, total);
     uint32_t running = total - prefix - csum;  // keys in bins of higher threads
@@ -337,40 +363,36 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_scan_kernel(
     const uint32_t d1 = d1_s;
     if (blockIdx.x == 0 && tid == 0) L.meta[rr * kMetaWords + 1] = above_s;
 
-    // this thread's 32 consecutive positions -> one bitmap word
-    const float *row = scores + (size_t)b * batch_stride + (size_t)r * S;
-    const int p0 = base + tid * 32;
-    uint32_t word = 0u;
-    uint32_t *cnt = &L.meta[rr * kMetaWords + 0];
-    uint2 *cand = L.cand + rr * (size_t)S;
+    // 8 bits of "digit > d1" per thread; 4 neighbouring lanes form one word.
+    // Candidates (digit == d1) go to this slice's own region in position order.
     const int lane = tid & 63;
-#pragma unroll 4
-    for (int j = 0; j < 32; ++j) {
-        const int p = p0 + j;
-        bool c = false;
-        uint32_t u = 0u;
-        if (p < n) {
-            u = ordered_key(row[p]);
-            const uint32_t d = u >> (32 - kDigitBits);
-            if (d > d1) word |= 1u << j;
-            c = d == d1;
-        }
-        const uint64_t m = __ballot(c);
-        if (m) {  // append this wave's candidates of step j
-            const int leader = __builtin_ctzll(m);
-            uint32_t slot0 = 0u;
-            if (lane == leader) slot0 = atomicAdd(cnt, (uint32_t)__popcll(m));
-            slot0 = (uint32_t)__shfl((int)slot0, leader, 64);
-            if (c) cand[slot0 + lanes_below(m)] = make_uint2(u, (uint32_t)p);
-        }
+    uint32_t byte = 0u, cmask = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bool valid = p0 + e < n;
+        const uint32_t d = u[e] >> (32 - kDigitBits);
+        if (valid && d > d1) byte |= 1u << e;
+        if (valid && d == d1) cmask |= 1u << e;
     }
-    if (p0 < n) L.bitmap[rr * L.words + (p0 >> 5)] = word;
+    uint32_t ncand;
+    uint32_t slot = block_excl_scan<kWideThreads / 64>((uint32_t)__popc(cmask), scratch, ncand);
+    uint2 *cand = L.cand + rr * (size_t)S + base;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (cmask & (1u << e)) cand[slot++] = make_uint2(u[e], (uint32_t)(p0 + e));
+    if (tid == 0) L.counts[rr * kMaxSlices + blockIdx.x] = ncand;
+    uint32_t word = byte << (8 * (lane & 3));
+    word |= (uint32_t)__shfl_xor((int)word, 1, 64);
+    word |= (uint32_t)__shfl_xor((int)word, 2, 64);
+    if ((lane & 3) == 0 && p0 < n) L.bitmap[rr * L.words + (p0 >> 5)] = word;
 }
 
 struct ResolveSmem {
     SelectSmem sel;
     uint32_t scan[kTkWaves];
+    uint32_t offs[kMaxSlices + 1];
     uint32_t bits[kWideMaxS / 32];
+    uint2 cand[kCandCache];
 };
 
 // grid: x = row in chunk, y = batch
@@ -389,23 +411,64 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
         return;
     }
     const size_t rr = (size_t)b * rows + r;
-    const int m = (int)L.meta[rr * kMetaWords + 0];
     const uint32_t need = (uint32_t)k - L.meta[rr * kMetaWords + 1];
-    const uint2 *cand = L.cand + rr * (size_t)S;
+    const uint2 *gcand = L.cand + rr * (size_t)S;
+    const int nslices = (n + kWideSlice - 1) / kWideSlice;
+    if (tid < 64) {  // offsets of the slices' candidate runs
+        uint32_t run = 0u;
+        for (int s0 = 0; s0 < nslices; s0 += 64) {
+            const int sl = s0 + tid;
+            uint32_t c = sl < nslices ? L.counts[rr * kMaxSlices + sl] : 0u;
+            uint32_t incl = c;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t o = (uint32_t)__shfl_up((int)incl, off, 64);
+                if (tid >= off) incl += o;
+            }
+            if (sl < nslices) sm.offs[sl] = run + incl - c;
+            run += (uint32_t)__shfl((int)incl, 63, 64);
+        }
+        if (tid == 0) sm.offs[nslices] = run;
+    }
+    __syncthreads();
+    const int m = (int)sm.offs[nslices];
+    const bool cached = m <= kCandCache;
+    if (cached) {  // one wave per slice run
+        for (int sl = tid >> 6; sl < nslices; sl += kTkWaves) {
+            const uint32_t o = sm.offs[sl], c = sm.offs[sl + 1] - o;
+            for (uint32_t j = tid & 63; j < c; j += 64) sm.cand[o + j] = gcand[sl * kWideSlice + j];
+        }
+        __syncthreads();
+    }
+    // candidate j: from LDS, or found by binary search over the slice offsets
+    auto cand_at = [&](int j) -> uint2 {
+        if (cached) return sm.cand[j];
+        int lo = 0, hi = nslices - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sm.offs[mid] <= (uint32_t)j) lo = mid;
+            else hi = mid - 1;
+        }
+        return gcand[lo * kWideSlice + (j - (int)sm.offs[lo])];
+    };
 
     // exact threshold among the candidates of digit d1
     uint32_t tau, need_tau;
-    block_select([&](int j) -> uint32_t { return cand[j].x; }, m, need, sm.sel, tau, need_tau);
+    block_select([&](int j) -> uint32_t { return cand_at(j).x; }, m, need, sm.sel, tau, need_tau);
     // ties at tau: the need_tau lowest positions (select the largest ~position)
     uint32_t ties = 0u;
-    for (int j = tid; j < m; j += kTkThreads) ties += cand[j].x == tau ? 1u : 0u;
+    for (int j = tid; j < m; j += kTkThreads) ties += cand_at(j).x == tau ? 1u : 0u;
     uint32_t ties_total;
     block_excl_scan<kTkWaves>(ties, sm.scan, ties_total);
     uint32_t pos_cut = 0xffffffffu;
     if (need_tau < ties_total) {
         uint32_t tau2, need2;
-        block_select([&](int j) -> uint32_t { return cand[j].x == tau ? ~cand[j].y : 0u; }, m,
-                     need_tau, sm.sel, tau2, need2);
+        block_select(
+            [&](int j) -> uint32_t {
+                const uint2 c = cand_at(j);
+                return c.x == tau ? ~c.y : 0u;
+            },
+            m, need_tau, sm.sel, tau2, need2);
         pos_cut = ~tau2;  // ties with position <= pos_cut are taken
     }
 
@@ -414,7 +477,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
     for (int w = tid; w < nw; w += kTkThreads) sm.bits[w] = L.bitmap[rr * words + w];
     __syncthreads();
     for (int j = tid; j < m; j += kTkThreads) {
-        const uint2 c = cand[j];
+        const uint2 c = cand_at(j);
         if (c.x > tau || (c.x == tau && c.y <= pos_cut))
             atomicOr(&sm.bits[c.y >> 5], 1u << (c.y & 31));
     }
@@ -450,14 +513,23 @@ size_t topk_workspace_bytes(int B, int T, int S, int) {
     return (size_t)nrows * wide_row_bytes(S) + 64;
 }
 
+// Counters of the wide path that must be zero when its first kernel starts
+// (the histograms and per-row words at the head of the workspace).
+size_t topk_clear_words(int B, int rows, int S) {
+    if (!use_wide(B, rows, S)) return 0;
+    return (size_t)B * rows * (kDigits + kMetaWords);
+}
+
 hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *q_pos, int B,
                        int T, int S, int row0, int rows, int k, int32_t *idx, void *workspace,
-                       hipStream_t stream) {
+                       bool workspace_cleared, hipStream_t stream) {
     if (use_wide(B, rows, S) && workspace) {
         const WideLayout L = wide_layout(workspace, B * rows, S);
         const int nrows = B * rows;
-        hipLaunchKernelGGL(topk_wide_clear_kernel, dim3(min(1024, ceil_div(nrows * (kDigits + kMetaWords), 256))),
-                           dim3(256), 0, stream, L.hist, L.meta, nrows);
+        if (!workspace_cleared)
+            hipLaunchKernelGGL(topk_wide_clear_kernel,
+                               dim3(min(1024, ceil_div(nrows * (kDigits + kMetaWords), 256))),
+                               dim3(256), 0, stream, L.hist, L.meta, nrows);
         const dim3 g(ceil_div(S, kWideSlice), rows, B);
         hipLaunchKernelGGL(topk_wide_hist_kernel, g, dim3(kWideThreads), 0, stream, scores,
                            batch_stride, q_pos, T, S, row0, rows, k, L);
