@@ -43,7 +43,21 @@ def parse():
     ap.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES between two device buffers (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes: int):
+    """A plain device copy of a known size: reads and writes exactly nbytes, so
+    the FETCH_SIZE / WRITE_SIZE counters it produces calibrate their units."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "dispatches": 3}))
 
 
 def algorithmic(w):
@@ -85,7 +99,8 @@ def traffic_record(workload: str, kernel_file: str):
     rec = json.load(open(p))
     if rec.get("source_sha256_16") != kernel_source_hash(kernel_file):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    v = rec.get("hbm_bytes_per_launch")
+    return None if v is None else int(round(v))
 
 
 def cpu_baseline(w, x, budget_s: float):
@@ -134,6 +149,9 @@ def cpu_baseline(w, x, budget_s: float):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path shards by "
               "sequence or query rows and is not built for several GPUs here.",
