@@ -163,6 +163,137 @@ __global__ __launch_bounds__(256) void indexer_mfma_kernel(
     }
 }
 
+// --------------------------------------------------------- key stream ----
+// Decode variant: every key is read by exactly one query row, so the cache is
+// streamed.  Each wave pulls its 32-key tile with fully coalesced nontemporal
+// 16-byte loads (lane l takes bytes 16(l + 64j) of the tile), parks it in a
+// wave-private LDS tile with a padded row pitch (conflict-free operand reads),
+// and reads the B operands of the same MFMA layout as above from there.  The
+// next tile's loads are in flight while the current tile is multiplied.
+template <bool Fp8>
+struct StreamTile {
+    static constexpr int row_bytes = kIdxDim * IdxTraits<Fp8>::elem_bytes;  // 128 / 256
+    static constexpr int pitch = row_bytes + 16;                             // 144 / 272
+    static constexpr int pieces = row_bytes / 16;                            // 8 / 16
+    static constexpr int loads = kKeyTile * row_bytes / 1024;                // 4 / 8
+    static constexpr int bytes = kKeyTile * pitch;
+};
+
+template <bool Fp8>
+__global__ __launch_bounds__(256) void indexer_stream_kernel(
+    const uint8_t *__restrict__ q_idx, const uint8_t *__restrict__ k_idx,
+    const float *__restrict__ w, const int32_t *__restrict__ q_pos, int B, int T, int S,
+    int row0, int rows, int chunk, int nchunks, float *__restrict__ scores,
+    size_t batch_stride, int write_masked, uint32_t *__restrict__ clear, size_t clear_words) {
+    typedef IdxTraits<Fp8> Tr;
+    typedef StreamTile<Fp8> St;
+    __shared__ __align__(16) uint8_t tiles[4][St::bytes];
+    if (clear_words) {  // zero the next kernel's counters, spread over the grid
+        const size_t nthreads = (size_t)gridDim.x * blockDim.x;
+        for (size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x; j < clear_words; j += nthreads)
+            clear[j] = 0u;
+    }
+    typedef typename Tr::operand Op;
+    constexpr int EB = Tr::elem_bytes;
+    constexpr int KS = Tr::ksteps;
+    constexpr int DPS = Tr::dims_per_step;
+
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
+    const int col = lane & 31;
+    uint8_t *tile = tiles[threadIdx.x >> 6];
+    const long long wave_id = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const long long total = (long long)B * rows * nchunks;
+    if (wave_id >= total) return;
+    const int c = (int)(wave_id % nchunks);
+    const int r = (int)((wave_id / nchunks) % rows);
+    const int b = (int)(wave_id / ((long long)nchunks * rows));
+    const int i = row0 + r;
+    const int t = query_pos(q_pos, b, i, T, S);
+
+    const int s_begin = c * chunk;
+    const int s_end = min(s_begin + chunk, S);
+    const int s_hi = min(s_end, t + 1);
+    float *out = scores + (size_t)b * batch_stride + (size_t)r * S;
+    if (write_masked) {
+        for (int s = max(s_begin, s_hi) + lane; s < s_end; s += 64) out[s] = -INFINITY;
+    }
+    if (s_begin >= s_hi) return;
+
+    const size_t qrow = ((size_t)b * T + i) * kIdxHeads;
+    Op qa[2][KS];
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl) {
+        const uint8_t *qp = q_idx + ((qrow + tl * 32 + col) * kIdxDim + 64 * half) * EB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa[tl][ks] = Tr::load(qp + ks * DPS * EB);
+    }
+    float wr[2][16];
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg)
+            wr[tl][rg] = w[qrow + tl * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
+
+    const uint8_t *kb_base = k_idx + (size_t)b * S * St::row_bytes;
+    // Depth tiles in flight per wave (fp8 tiles are small and registers are
+    // free, so two; bf16 keeps one to stay at two waves per SIMD).
+    constexpr int Depth = Fp8 ? 2 : 1;
+    u32x4 g[Depth][St::loads];
+    auto load_tile = [&](u32x4 (&dst)[St::loads], int s0) {
+#pragma unroll
+        for (int j = 0; j < St::loads; ++j) {
+            const int q = lane + 64 * j;
+            const int key = s0 + q / St::pieces;
+            dst[j] = key < S ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                                   kb_base + (size_t)s0 * St::row_bytes + 16 * q))
+                             : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < Depth; ++d)
+        if (s_begin + d * kKeyTile < s_hi) load_tile(g[d], s_begin + d * kKeyTile);
+    for (int s0 = s_begin; s0 < s_hi; s0 += kKeyTile) {
+#pragma unroll
+        for (int j = 0; j < St::loads; ++j) {
+            const int q = lane + 64 * j;
+            *reinterpret_cast<u32x4 *>(tile + (q / St::pieces) * St::pitch + (q % St::pieces) * 16) =
+                g[0][j];
+        }
+#pragma unroll
+        for (int d = 0; d + 1 < Depth; ++d)
+#pragma unroll
+            for (int j = 0; j < St::loads; ++j) g[d][j] = g[d + 1][j];
+        if (s0 + Depth * kKeyTile < s_hi) load_tile(g[Depth - 1], s0 + Depth * kKeyTile);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        Op kb[KS];
+        const uint8_t *brow = tile + col * St::pitch + 64 * half * EB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kb[ks] = Tr::load(brow + ks * DPS * EB);
+
+        f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            acc0 = Tr::mma(qa[0][ks], kb[ks], acc0);
+            acc1 = Tr::mma(qa[1][ks], kb[ks], acc1);
+        }
+        float part = 0.0f;
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) {
+            part = fmaf(wr[0][rg], fmaxf(acc0[rg], 0.0f), part);
+            part = fmaf(wr[1][rg], fmaxf(acc1[rg], 0.0f), part);
+        }
+        const float other = __shfl_xor(part, 32, 64);
+        const int key = s0 + col;
+        if (half == 0 && key < s_hi) out[key] = part + other;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
 // ------------------------------------------------------------- generic ----
 constexpr int kGenericThreads = 256;
 constexpr int kGenericMaxQ = 16384;
@@ -220,10 +351,25 @@ hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, c
         // short enough that a few query rows still give ~16 waves per CU (a
         // streaming kernel needs that many loads in flight)
         int chunk = 2048;
-        while (chunk > 128 && (long long)B * rows * ceil_div(S, chunk) < 4096) chunk >>= 1;
+        while (chunk > 128 && (long long)B * rows * ceil_div(S, chunk) < 2048) chunk >>= 1;
         const int nchunks = ceil_div(S, chunk);
         const long long waves = (long long)B * rows * nchunks;
         const int blocks = (int)((waves + 3) / 4);
+        if (rows == 1) {  // each key is read by one query row: stream the cache
+            if (idx_dtype == DSA_BF16)
+                hipLaunchKernelGGL((indexer_stream_kernel<false>), dim3(blocks), dim3(256), 0,
+                                   stream, static_cast<const uint8_t *>(q_idx),
+                                   static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
+                                   rows, chunk, nchunks, scores, batch_stride, (int)write_masked,
+                                   clear, clear_words);
+            else
+                hipLaunchKernelGGL((indexer_stream_kernel<true>), dim3(blocks), dim3(256), 0,
+                                   stream, static_cast<const uint8_t *>(q_idx),
+                                   static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
+                                   rows, chunk, nchunks, scores, batch_stride, (int)write_masked,
+                                   clear, clear_words);
+            return hipGetLastError();
+        }
         if (idx_dtype == DSA_BF16)
             hipLaunchKernelGGL((indexer_mfma_kernel<false>), dim3(blocks), dim3(256), 0, stream,
                                static_cast<const uint8_t *>(q_idx),

@@ -387,10 +387,13 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_scan_kernel(
     if ((lane & 3) == 0 && p0 < n) L.bitmap[rr * L.words + (p0 >> 5)] = word;
 }
 
+constexpr int kMaxTies = 2048;  // ties at the threshold resolved by rank counting
+
 struct ResolveSmem {
     SelectSmem sel;
     uint32_t scan[kTkWaves];
     uint32_t offs[kMaxSlices + 1];
+    uint32_t ties[kMaxTies];
     uint32_t bits[kWideMaxS / 32];
     uint2 cand[kCandCache];
 };
@@ -411,6 +414,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
         return;
     }
     const size_t rr = (size_t)b * rows + r;
+    const int nw = (n + 31) / 32;
+    uint32_t bitmap_pre[kWideMaxS / 32 / kTkThreads];  // issued now, used after the select
+#pragma unroll
+    for (int u = 0; u < kWideMaxS / 32 / kTkThreads; ++u) {
+        const int w = tid + u * kTkThreads;
+        bitmap_pre[u] = w < nw ? L.bitmap[rr * L.words + w] : 0u;
+    }
     const uint32_t need = (uint32_t)k - L.meta[rr * kMetaWords + 1];
     const uint2 *gcand = L.cand + rr * (size_t)S;
     const int nslices = (n + kWideSlice - 1) / kWideSlice;
@@ -455,13 +465,20 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
     // exact threshold among the candidates of digit d1
     uint32_t tau, need_tau;
     block_select([&](int j) -> uint32_t { return cand_at(j).x; }, m, need, sm.sel, tau, need_tau);
-    // ties at tau: the need_tau lowest positions (select the largest ~position)
-    uint32_t ties = 0u;
-    for (int j = tid; j < m; j += kTkThreads) ties += cand_at(j).x == tau ? 1u : 0u;
-    uint32_t ties_total;
-    block_excl_scan<kTkWaves>(ties, sm.scan, ties_total);
+    // Every candidate above tau is taken.  Of the candidates equal to tau the
+    // need_tau lowest positions are taken: the ties are compacted into LDS
+    // and each one counts how many ties sit at lower positions.  (A row with
+    // more ties than fit falls back to a second select on ~position.)
+    for (int w = tid; w < nw; w += kTkThreads) sm.bits[w] = bitmap_pre[w / kTkThreads];
+    uint32_t tie_count;
+    {
+        uint32_t mine = 0u;
+        for (int j = tid; j < m; j += kTkThreads) mine += cand_at(j).x == tau ? 1u : 0u;
+        block_excl_scan<kTkWaves>(mine, sm.scan, tie_count);
+    }
+    const bool few_ties = tie_count <= kMaxTies;
     uint32_t pos_cut = 0xffffffffu;
-    if (need_tau < ties_total) {
+    if (need_tau < tie_count && !few_ties) {
         uint32_t tau2, need2;
         block_select(
             [&](int j) -> uint32_t {
@@ -471,15 +488,31 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
             m, need_tau, sm.sel, tau2, need2);
         pos_cut = ~tau2;  // ties with position <= pos_cut are taken
     }
-
-    const int words = L.words;
-    const int nw = (n + 31) / 32;
-    for (int w = tid; w < nw; w += kTkThreads) sm.bits[w] = L.bitmap[rr * words + w];
+    if (few_ties && need_tau < tie_count) {
+        uint32_t written = 0u;
+        for (int base = 0; base < m; base += kTkThreads) {  // compact the tie positions
+            const int j = base + tid;
+            const uint2 c = j < m ? cand_at(j) : make_uint2(0u, 0u);
+            const bool tie = j < m && c.x == tau;
+            uint32_t tot;
+            const uint32_t slot = block_flag_scan<kTkWaves>(tie, sm.scan, tot);
+            if (tie) sm.ties[written + slot] = c.y;
+            written += tot;
+        }
+        __syncthreads();
+        for (uint32_t a = tid; a < tie_count; a += kTkThreads) {
+            const uint32_t pa = sm.ties[a];
+            uint32_t below = 0u;
+            for (uint32_t b2 = 0; b2 < tie_count; ++b2) below += sm.ties[b2] < pa ? 1u : 0u;
+            if (below < need_tau) atomicOr(&sm.bits[pa >> 5], 1u << (pa & 31));
+        }
+    }
     __syncthreads();
     for (int j = tid; j < m; j += kTkThreads) {
         const uint2 c = cand_at(j);
-        if (c.x > tau || (c.x == tau && c.y <= pos_cut))
-            atomicOr(&sm.bits[c.y >> 5], 1u << (c.y & 31));
+        const bool take = c.x > tau || (c.x == tau && (need_tau >= tie_count ||
+                                                       (!few_ties && c.y <= pos_cut)));
+        if (take) atomicOr(&sm.bits[c.y >> 5], 1u << (c.y & 31));
     }
     __syncthreads();
 
