@@ -294,6 +294,140 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
     }
 }
 
+// ---------------------------------------------------------- prefill tile --
+// Prefill variant: consecutive query rows read (almost) the same keys, so a
+// workgroup of 8 waves owns 8 consecutive rows and a range of keys; each
+// 64-key tile is brought into LDS once for all 8 rows (direct-to-LDS loads,
+// two buffers so the next tile lands while this one is multiplied) and every
+// wave reads its B operands from there.  Row pitch = row + 16 bytes, so the
+// operand reads are free of bank conflicts.
+constexpr int kPfRows = 8;     // query rows (waves) per workgroup
+constexpr int kPfKeys = 64;    // keys per LDS tile
+
+template <bool Fp8>
+struct PrefillTile {
+    static constexpr int row_bytes = kIdxDim * IdxTraits<Fp8>::elem_bytes;
+    static constexpr int pitch = row_bytes + 16;
+    static constexpr int slots = pitch / 16;                           // 16-byte slots a row
+    static constexpr int loads = (kPfKeys * slots + 63) / 64;          // wave loads a tile
+    static constexpr int bytes = loads * 1024;                         // tile buffer size
+};
+
+template <bool Fp8>
+__device__ __forceinline__ void prefill_issue_tile(uint8_t *buf, const uint8_t *kb_base, int s0,
+                                                   int S, int wave, int lane) {
+    typedef PrefillTile<Fp8> Pt;
+    typedef __attribute__((address_space(3))) void *lds_ptr;
+    for (int j = wave; j < Pt::loads; j += kPfRows) {
+        const int q = 64 * j + lane;
+        const int row = q / Pt::slots;
+        const int piece = q - row * Pt::slots;
+        int key = s0 + row;
+        key = key < S ? key : 0;  // rows past the cache load row 0; never used
+        const uint8_t *src =
+            kb_base + (size_t)key * Pt::row_bytes + (piece * 16 < Pt::row_bytes ? piece * 16 : 0);
+        if (q < kPfKeys * Pt::slots)
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(buf + 1024 * j), 16, 0, 0);
+    }
+}
+
+// grid: 1-D over (batch, row block, key chunk), heaviest row blocks first
+template <bool Fp8>
+__global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
+    const uint8_t *__restrict__ q_idx, const uint8_t *__restrict__ k_idx,
+    const float *__restrict__ w, const int32_t *__restrict__ q_pos, int B, int T, int S,
+    int row0, int rows, int kchunk, int nkc, float *__restrict__ scores, size_t batch_stride,
+    int write_masked) {
+    typedef IdxTraits<Fp8> Tr;
+    typedef PrefillTile<Fp8> Pt;
+    typedef typename Tr::operand Op;
+    constexpr int EB = Tr::elem_bytes;
+    constexpr int KS = Tr::ksteps;
+    constexpr int DPS = Tr::dims_per_step;
+    __shared__ __align__(16) uint8_t tiles[2][Pt::bytes];
+    __shared__ int tmax_s[kPfRows];
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
+    const int col = lane & 31;
+    const int nrb = (rows + kPfRows - 1) / kPfRows;
+    const int id = blockIdx.x;
+    const int kc = id % nkc;
+    const int rb = nrb - 1 - (id / nkc) % nrb;  // last (longest) rows first
+    const int b = id / (nkc * nrb);
+    const int r = rb * kPfRows + wave;
+    const bool live = r < rows;
+    const int i = row0 + (live ? r : rows - 1);
+    const int t = live ? query_pos(q_pos, b, i, T, S) : -1;
+    if (lane == 0) tmax_s[wave] = t;
+    __syncthreads();
+    int tmax = tmax_s[0];
+#pragma unroll
+    for (int v = 1; v < kPfRows; ++v) tmax = max(tmax, tmax_s[v]);
+
+    const int k_begin = kc * kchunk;
+    const int k_end = min(S, k_begin + kchunk);
+    float *out = scores + (size_t)b * batch_stride + (size_t)r * S;
+    if (live && write_masked) {
+        for (int s = max(k_begin, t + 1) + lane; s < k_end; s += 64) out[s] = -INFINITY;
+    }
+    const int k_hi = min(k_end, tmax + 1);  // keys any row of the block needs
+    if (k_begin >= k_hi) return;             // uniform over the workgroup
+
+    const uint8_t *kb_base = k_idx + (size_t)b * S * Pt::row_bytes;
+    prefill_issue_tile<Fp8>(tiles[0], kb_base, k_begin, S, wave, lane);
+
+    const size_t qrow = ((size_t)b * T + i) * kIdxHeads;
+    Op qa[2][KS];
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl) {
+        const uint8_t *qp = q_idx + ((qrow + tl * 32 + col) * kIdxDim + 64 * half) * EB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa[tl][ks] = Tr::load(qp + ks * DPS * EB);
+    }
+    float wr[2][16];
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg)
+            wr[tl][rg] = w[qrow + tl * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
+    const int t_hi = min(k_end, t + 1);  // this row's causal end inside the chunk
+
+    int it = 0;
+    for (int s0 = k_begin; s0 < k_hi; s0 += kPfKeys, ++it) {
+        const int buf = it & 1;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed
+        __syncthreads();                // ... and every other wave's; buf^1 is free
+        if (s0 + kPfKeys < k_hi)
+            prefill_issue_tile<Fp8>(tiles[buf ^ 1], kb_base, s0 + kPfKeys, S, wave, lane);
+        if (s0 < t_hi) {
+#pragma unroll
+            for (int st = 0; st < kPfKeys / 32; ++st) {
+                const uint8_t *brow = tiles[buf] + (st * 32 + col) * Pt::pitch + 64 * half * EB;
+                Op kb[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) kb[ks] = Tr::load(brow + ks * DPS * EB);
+                f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    acc0 = Tr::mma(qa[0][ks], kb[ks], acc0);
+                    acc1 = Tr::mma(qa[1][ks], kb[ks], acc1);
+                }
+                float part = 0.0f;
+#pragma unroll
+                for (int rg = 0; rg < 16; ++rg) {
+                    part = fmaf(wr[0][rg], fmaxf(acc0[rg], 0.0f), part);
+                    part = fmaf(wr[1][rg], fmaxf(acc1[rg], 0.0f), part);
+                }
+                const float other = __shfl_xor(part, 32, 64);
+                const int key = s0 + st * 32 + col;
+                if (half == 0 && key < t_hi) out[key] = part + other;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------- generic ----
 constexpr int kGenericThreads = 256;
 constexpr int kGenericMaxQ = 16384;
@@ -368,6 +502,28 @@ hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, c
                                    static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
                                    rows, chunk, nchunks, scores, batch_stride, (int)write_masked,
                                    clear, clear_words);
+            return hipGetLastError();
+        }
+        if (rows >= kPfRows) {  // rows share key tiles: 8 rows a workgroup
+            const int kchunk = 4096;
+            const int nkc = ceil_div(S, kchunk);
+            const long long wgs = (long long)B * ceil_div(rows, kPfRows) * nkc;
+            if (idx_dtype == DSA_BF16)
+                hipLaunchKernelGGL((indexer_prefill_kernel<false>), dim3((unsigned)wgs),
+                                   dim3(kPfRows * 64), 0, stream,
+                                   static_cast<const uint8_t *>(q_idx),
+                                   static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
+                                   rows, kchunk, nkc, scores, batch_stride, (int)write_masked);
+            else
+                hipLaunchKernelGGL((indexer_prefill_kernel<true>), dim3((unsigned)wgs),
+                                   dim3(kPfRows * 64), 0, stream,
+                                   static_cast<const uint8_t *>(q_idx),
+                                   static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
+                                   rows, kchunk, nkc, scores, batch_stride, (int)write_masked);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess || !clear_words) return e;
+            hipLaunchKernelGGL(fill_zero_kernel, dim3(min((size_t)1024, (clear_words + 255) / 256)),
+                               dim3(256), 0, stream, clear, clear_words);
             return hipGetLastError();
         }
         if (idx_dtype == DSA_BF16)
