@@ -210,25 +210,33 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
 
     # ---- per-stage kernel durations (same kernels and launch shapes as the
-    # step: for decode the three entry points issue exactly dsa_forward's launches)
+    # step: for decode the three entry points issue exactly dsa_forward's
+    # launches).  Each stage runs `nst` times back to back between one pair of
+    # HIP events on the launch stream, so the average is the kernels' own
+    # duration (plus the launch gaps), not the cost of an event pair.
     alg = algorithmic(w)
     stage_ms = None
     if w.decode:
         sc = torch.empty((w.B, w.T, w.S), dtype=torch.float32, device=dev)
-        nst = max(10, args.steps)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nst)]
-        for s in range(nst):
-            x = reps[s % R]
-            ev[s][0].record()
-            dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"], scores=sc)
-            ev[s][1].record()
-            dsa.dsa_topk(sc, w.index_topk, idx=idx)
-            ev[s][2].record()
-            dsa.dsa_sparse_attention(desc, x["q"], x["kv"], x["v"], idx, out=out)
-            ev[s][3].record()
+        nst = max(20, args.steps)
+        stages = [
+            lambda x: dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"], scores=sc),
+            lambda x: dsa.dsa_topk(sc, w.index_topk, idx=idx),
+            lambda x: dsa.dsa_sparse_attention(desc, x["q"], x["kv"], x["v"], idx, out=out),
+        ]
+        for f in stages:  # inputs for the later stages, and warm launches
+            for r in range(R):
+                f(reps[r])
         torch.cuda.synchronize()
-        stage_ms = [sum(ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(nst)) / nst
-                    for j in range(3)]
+        stage_ms = []
+        for f in stages:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for s in range(nst):
+                f(reps[s % R])
+            b.record()
+            torch.cuda.synchronize()
+            stage_ms.append(a.elapsed_time(b) / nst)
 
     if w.decode:
         kern_ms = stage_ms[0]

@@ -104,10 +104,11 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float v) {
     *p = (uint16_t)f32_to_bf16_bits(v);
 }
 
-// grid: 1-D.  Work item = (head group, split, row, batch); with splits == 1
-// and a row count that is a multiple of 8, the head groups of one query row
-// get workgroup ids that are 8 apart, so they run on the same XCD (ids are
-// dealt round-robin over the 8 XCDs) and the second gather hits its L2.
+// grid: 1-D.  Work item = (head group, split, row, batch).  When the number
+// of (row, split) units is a multiple of 8, the head groups of one unit get
+// workgroup ids that are 8 apart, so they run on the same XCD (ids are dealt
+// round-robin over the 8 XCDs) and the second gather of the same rows hits
+// that XCD's L2.
 template <typename Tout>
 __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ lat,
@@ -123,11 +124,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     const int hgs = H / kHg;
     const int id = blockIdx.x;
     int hg, split, qidx;
-    if (splits == 1 && (rows * B) % 8 == 0) {
+    if ((rows * B * splits) % 8 == 0) {
         const int slot = id >> 3;
         hg = slot % hgs;
-        qidx = (slot / hgs) * 8 + (id & 7);
-        split = 0;
+        const int unit = (slot / hgs) * 8 + (id & 7);
+        qidx = unit / splits;
+        split = unit % splits;
     } else {
         hg = id % hgs;
         split = (id / hgs) % splits;
@@ -294,6 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     __syncthreads();
     const int dv0 = wave * 128;
     const size_t rowq = ((size_t)b * T + i);
+    const size_t prow = (size_t)qidx;  // row of this launch's split partials
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
 #pragma unroll
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
                 if (splits == 1)
                     store_out(out + (rowq * H + head0 + hl) * kDv + d, v);
                 else
-                    o_part[((rowq * splits + split) * H + head0 + hl) * kDv + d] = v;
+                    o_part[((prow * splits + split) * H + head0 + hl) * kDv + d] = v;
             }
         }
     }
@@ -319,36 +322,60 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         if (splits == 1) {
             if (lse) lse[rowq * H + head0 + tid] = ls;
         } else {
-            lse_part[(rowq * splits + split) * H + head0 + tid] = ls;
+            lse_part[(prow * splits + split) * H + head0 + tid] = ls;
         }
     }
 }
 
 // Merge split partials: out = sum_s exp(lse_s - lse) o_s, lse = log sum exp lse_s.
+// Two heads per workgroup, 4 dims per thread; the splits are read in batches
+// of 8 whose loads are all issued before any is used (clamped indices, zero
+// weight past the last split), so a row costs a few memory latencies rather
+// than one per split.
+constexpr int kCombineBatch = 8;
+
 template <typename Tout>
 __global__ __launch_bounds__(256) void mla_combine_kernel(
     const float *__restrict__ o_part, const float *__restrict__ lse_part, int T, int H,
     int row0, int rows, int splits, Tout *__restrict__ out, float *__restrict__ lse) {
-    const int h = blockIdx.x;
+    const int h = blockIdx.x * 2 + (threadIdx.x >> 7);
+    const int d = (threadIdx.x & 127) * 4;
     const int r = blockIdx.y;
     const int b = blockIdx.z;
     const size_t rowq = (size_t)b * T + row0 + r;
+    const size_t prow = (size_t)b * rows + r;  // row of the launch's split partials
+    const float *lp = lse_part + prow * splits * H + h;  // split s at lp[s * H]
     float mx = -INFINITY;
-    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, lse_part[(rowq * splits + s) * H + h]);
+    for (int s0 = 0; s0 < splits; s0 += kCombineBatch) {
+        float ls[kCombineBatch];
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j) ls[j] = lp[(size_t)min(s0 + j, splits - 1) * H];
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j) mx = fmaxf(mx, ls[j]);
+    }
+    const float *op = o_part + (prow * splits * H + h) * kDv + d;  // split s at op[s * H * kDv]
     float wsum = 0.0f;
-    float acc0 = 0.0f, acc1 = 0.0f;
-    const int d = threadIdx.x;
-    for (int s = 0; s < splits; ++s) {
-        const float ls = lse_part[(rowq * splits + s) * H + h];
-        const float wgt = mx == -INFINITY ? 0.0f : __expf(ls - mx);
-        wsum += wgt;
-        const float *op = o_part + ((rowq * splits + s) * H + h) * kDv;
-        acc0 = fmaf(wgt, op[d], acc0);
-        acc1 = fmaf(wgt, op[d + 256], acc1);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < splits; s0 += kCombineBatch) {
+        float ls[kCombineBatch];
+        f32x4 ov[kCombineBatch];
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j) {
+            const size_t sc = (size_t)min(s0 + j, splits - 1);
+            ls[j] = lp[sc * H];
+            ov[j] = *reinterpret_cast<const f32x4 *>(op + sc * H * kDv);
+        }
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j) {
+            const float wgt = (s0 + j < splits && mx != -INFINITY) ? __expf(ls[j] - mx) : 0.0f;
+            wsum += wgt;
+            acc += wgt * ov[j];
+        }
     }
     const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-    store_out(out + (rowq * H + h) * kDv + d, acc0 * inv);
-    store_out(out + (rowq * H + h) * kDv + d + 256, acc1 * inv);
+    Tout *o = out + (rowq * H + h) * kDv + d;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out(o + e, acc[e] * inv);
     if (lse && d == 0) lse[rowq * H + h] = wsum > 0.0f ? mx + __logf(wsum) : -INFINITY;
 }
 
@@ -371,12 +398,17 @@ bool mla_fast_path(const dsa_attn_desc_t &d) {
 }
 
 size_t mla_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int k) {
+    // A launch covers at most kMaxGridY rows; any row count up to that bound
+    // (a short last chunk included) may need split partials, and only counts
+    // with fewer than 256 workgroups split at all.
     size_t total = 0;
-    for (int r0 = 0; r0 < T; r0 += kMaxGridY) {
-        const int rows = min(kMaxGridY, T - r0);
-        const int splits = mla_splits(B, rows, d.num_heads, k);
+    const int hgs = d.num_heads / kHg;
+    const int top = min(T, kMaxGridY);
+    for (int n = 1; n <= top; ++n) {
+        if ((long long)B * n * hgs >= 256) break;
+        const int splits = mla_splits(B, n, d.num_heads, k);
         if (splits > 1) {
-            const size_t need = (size_t)B * rows * splits * d.num_heads * (kDv + 1) * 4 + 256;
+            const size_t need = (size_t)B * n * splits * d.num_heads * (kDv + 1) * 4 + 256;
             total = need > total ? need : total;
         }
     }
@@ -409,7 +441,7 @@ hipError_t launch_mla(const dsa_attn_desc_t &d, const void *q, const void *kv,
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (used_splits > 1) {
-            dim3 cg(H, n, B);
+            dim3 cg(H / 2, n, B);
             if (d.out_dtype == DSA_BF16)
                 hipLaunchKernelGGL(mla_combine_kernel<uint16_t>, cg, dim3(256), 0, stream, o_part,
                                    lse_part, T, H, row0 + r0, n, used_splits,

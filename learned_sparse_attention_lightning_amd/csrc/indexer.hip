@@ -23,6 +23,7 @@ namespace {
 constexpr int kIdxHeads = 64;
 constexpr int kIdxDim = 128;
 constexpr int kKeyTile = 32;
+constexpr int kStreamMaxChunk = 2048;  // keys per wave in the decode key stream
 
 // ---------------------------------------------------------------- MFMA ----
 // Register layouts (32x32 MFMA, wave of 64 lanes, h = lane / 32):
@@ -70,6 +71,29 @@ struct IdxTraits<true> {
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
     }
 };
+
+// ReLU as an integer max on the bit pattern: every negative float (and -0)
+// has its sign bit set, i.e. is a negative int32, so max(bits, 0) maps it to
+// +0 and leaves non-negative values alone -- one VALU op, no NaN quieting.
+__device__ __forceinline__ float relu_bits(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// This lane's share of sum_h w[h] ReLU(S[h, key]) over the 32 heads it holds
+// (16 of each 32-head tile); four independent accumulators keep the FMA
+// chain short.  The other 32 heads of the key sit in the partner lane half.
+__device__ __forceinline__ float weighted_relu_sum(const f32x16 &acc0, const f32x16 &acc1,
+                                                   const float (&wr)[2][16]) {
+    float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
+#pragma unroll
+    for (int rg = 0; rg < 16; rg += 2) {
+        p0 = fmaf(wr[0][rg], relu_bits(acc0[rg]), p0);
+        p1 = fmaf(wr[0][rg + 1], relu_bits(acc0[rg + 1]), p1);
+        p2 = fmaf(wr[1][rg], relu_bits(acc1[rg]), p2);
+        p3 = fmaf(wr[1][rg + 1], relu_bits(acc1[rg + 1]), p3);
+    }
+    return (p0 + p1) + (p2 + p3);
+}
 
 template <bool Fp8>
 __global__ __launch_bounds__(256) void indexer_mfma_kernel(
@@ -149,12 +173,7 @@ __global__ __launch_bounds__(256) void indexer_mfma_kernel(
             acc0 = Tr::mma(qa[0][ks], kb[ks], acc0);
             acc1 = Tr::mma(qa[1][ks], kb[ks], acc1);
         }
-        float part = 0.0f;
-#pragma unroll
-        for (int rg = 0; rg < 16; ++rg) {
-            part = fmaf(wr[0][rg], fmaxf(acc0[rg], 0.0f), part);
-            part = fmaf(wr[1][rg], fmaxf(acc1[rg], 0.0f), part);
-        }
+        const float part = weighted_relu_sum(acc0, acc1, wr);
         const float other = __shfl_xor(part, 32, 64);
         const int key = s0 + col;
         if (half == 0 && key < s_hi) out[key] = part + other;
@@ -165,11 +184,15 @@ __global__ __launch_bounds__(256) void indexer_mfma_kernel(
 
 // --------------------------------------------------------- key stream ----
 // Decode variant: every key is read by exactly one query row, so the cache is
-// streamed.  Each wave pulls its 32-key tile with fully coalesced nontemporal
-// 16-byte loads (lane l takes bytes 16(l + 64j) of the tile), parks it in a
-// wave-private LDS tile with a padded row pitch (conflict-free operand reads),
-// and reads the B operands of the same MFMA layout as above from there.  The
-// next tile's loads are in flight while the current tile is multiplied.
+// streamed.  The `nwaves` waves of one (sequence, row) take the 32-key tiles
+// round-robin (wave c owns tiles c, c + nwaves, ...), so at any moment they
+// sweep one contiguous stretch of the cache together -- a long run of adjacent
+// DRAM pages -- instead of nwaves separate streams.  Each tile is pulled with
+// fully coalesced nontemporal 16-byte loads (lane l takes bytes 16(l + 64j)),
+// parked in a wave-private LDS tile with a padded row pitch (conflict-free
+// operand reads), and multiplied with the B operands of the MFMA layout
+// above.  Depth tiles are in flight per wave.  The scores wait in LDS and
+// leave in one pass at the end, so the loop issues no global store.
 template <bool Fp8>
 struct StreamTile {
     static constexpr int row_bytes = kIdxDim * IdxTraits<Fp8>::elem_bytes;  // 128 / 256
@@ -183,11 +206,12 @@ template <bool Fp8>
 __global__ __launch_bounds__(256) void indexer_stream_kernel(
     const uint8_t *__restrict__ q_idx, const uint8_t *__restrict__ k_idx,
     const float *__restrict__ w, const int32_t *__restrict__ q_pos, int B, int T, int S,
-    int row0, int rows, int chunk, int nchunks, float *__restrict__ scores,
-    size_t batch_stride, int write_masked, uint32_t *__restrict__ clear, size_t clear_words) {
+    int row0, int rows, int nwaves, float *__restrict__ scores, size_t batch_stride,
+    int write_masked, uint32_t *__restrict__ clear, size_t clear_words) {
     typedef IdxTraits<Fp8> Tr;
     typedef StreamTile<Fp8> St;
     __shared__ __align__(16) uint8_t tiles[4][St::bytes];
+    __shared__ float staged[4][kStreamMaxChunk];  // a wave's scores until its last tile
     if (clear_words) {  // zero the next kernel's counters, spread over the grid
         const size_t nthreads = (size_t)gridDim.x * blockDim.x;
         for (size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x; j < clear_words; j += nthreads)
@@ -202,23 +226,29 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
     const int half = lane >> 5;
     const int col = lane & 31;
     uint8_t *tile = tiles[threadIdx.x >> 6];
+    float *stage = staged[threadIdx.x >> 6];
     const long long wave_id = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    const long long total = (long long)B * rows * nchunks;
+    const long long total = (long long)B * rows * nwaves;
     if (wave_id >= total) return;
-    const int c = (int)(wave_id % nchunks);
-    const int r = (int)((wave_id / nchunks) % rows);
-    const int b = (int)(wave_id / ((long long)nchunks * rows));
+    const int c = (int)(wave_id % nwaves);
+    const int r = (int)((wave_id / nwaves) % rows);
+    const int b = (int)(wave_id / ((long long)nwaves * rows));
     const int i = row0 + r;
     const int t = query_pos(q_pos, b, i, T, S);
-
-    const int s_begin = c * chunk;
-    const int s_end = min(s_begin + chunk, S);
-    const int s_hi = min(s_end, t + 1);
+    const int s_hi = min(S, t + 1);  // causal end
+    const int tile_step = nwaves * kKeyTile;
     float *out = scores + (size_t)b * batch_stride + (size_t)r * S;
-    if (write_masked) {
-        for (int s = max(s_begin, s_hi) + lane; s < s_end; s += 64) out[s] = -INFINITY;
+    if (write_masked) {  // -inf past the causal end, over this wave's tiles
+        for (int s0 = c * kKeyTile; s0 < S; s0 += tile_step)
+            if (s0 + kKeyTile > s_hi && lane < kKeyTile && s0 + lane >= s_hi && s0 + lane < S)
+                out[s0 + lane] = -INFINITY;
     }
-    if (s_begin >= s_hi) return;
+    const int s_first = c * kKeyTile;
+    if (s_first >= s_hi) return;
+    const int ntiles = (s_hi - s_first + tile_step - 1) / tile_step;
+    // Let the stores above drain: with only loads outstanding from here on,
+    // each tile waits for its own loads and not for the whole pipeline.
+    __builtin_amdgcn_s_waitcnt(0);
 
     const size_t qrow = ((size_t)b * T + i) * kIdxHeads;
     Op qa[2][KS];
@@ -236,61 +266,69 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
             wr[tl][rg] = w[qrow + tl * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
 
     const uint8_t *kb_base = k_idx + (size_t)b * S * St::row_bytes;
-    // Depth tiles in flight per wave (fp8 tiles are small and registers are
-    // free, so two; bf16 keeps one to stay at two waves per SIMD).
-    constexpr int Depth = Fp8 ? 2 : 1;
+    // The loads are unconditional: a key past the causal end re-reads the last
+    // key row (one cache line per wave load; its column is never stored), so
+    // the loop has no branch around a load.
+    constexpr int Depth = Fp8 ? 4 : 2;
     u32x4 g[Depth][St::loads];
-    auto load_tile = [&](u32x4 (&dst)[St::loads], int s0) {
+    auto load_tile = [&](u32x4 (&dst)[St::loads], int m) {
+        const int s0 = s_first + m * tile_step;
 #pragma unroll
         for (int j = 0; j < St::loads; ++j) {
             const int q = lane + 64 * j;
-            const int key = s0 + q / St::pieces;
-            dst[j] = key < S ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                                   kb_base + (size_t)s0 * St::row_bytes + 16 * q))
-                             : u32x4{0u, 0u, 0u, 0u};
+            const int key = min(s0 + q / St::pieces, s_hi - 1);
+            dst[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                kb_base + (size_t)key * St::row_bytes + 16 * (q % St::pieces)));
         }
     };
+    // issued in tile order (the scheduler may not reorder them), so the wait
+    // for tile d counts only the loads behind it
 #pragma unroll
-    for (int d = 0; d < Depth; ++d)
-        if (s_begin + d * kKeyTile < s_hi) load_tile(g[d], s_begin + d * kKeyTile);
-    for (int s0 = s_begin; s0 < s_hi; s0 += kKeyTile) {
+    for (int d = 0; d < Depth; ++d) {
+        load_tile(g[d], d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Unrolled by Depth so register set d always holds tile d (mod Depth): no
+    // register rotation, hence no wait on loads younger than the tile in use.
+    // Tiles past the wave's last one (at most Depth - 1) are multiplied but
+    // not kept.
+    for (int m0 = 0; m0 < ntiles; m0 += Depth) {
 #pragma unroll
-        for (int j = 0; j < St::loads; ++j) {
-            const int q = lane + 64 * j;
-            *reinterpret_cast<u32x4 *>(tile + (q / St::pieces) * St::pitch + (q % St::pieces) * 16) =
-                g[0][j];
-        }
+        for (int d = 0; d < Depth; ++d) {
+            const int m = m0 + d;
 #pragma unroll
-        for (int d = 0; d + 1 < Depth; ++d)
+            for (int j = 0; j < St::loads; ++j) {
+                const int q = lane + 64 * j;
+                *reinterpret_cast<u32x4 *>(tile + (q / St::pieces) * St::pitch +
+                                           (q % St::pieces) * 16) = g[d][j];
+            }
+            load_tile(g[d], m + Depth);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            Op kb[KS];
+            const uint8_t *brow = tile + col * St::pitch + 64 * half * EB;
 #pragma unroll
-            for (int j = 0; j < St::loads; ++j) g[d][j] = g[d + 1][j];
-        if (s0 + Depth * kKeyTile < s_hi) load_tile(g[Depth - 1], s0 + Depth * kKeyTile);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        Op kb[KS];
-        const uint8_t *brow = tile + col * St::pitch + 64 * half * EB;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kb[ks] = Tr::load(brow + ks * DPS * EB);
+            for (int ks = 0; ks < KS; ++ks) kb[ks] = Tr::load(brow + ks * DPS * EB);
 
-        f32x16 acc0 = {}, acc1 = {};
+            f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            acc0 = Tr::mma(qa[0][ks], kb[ks], acc0);
-            acc1 = Tr::mma(qa[1][ks], kb[ks], acc1);
+            for (int ks = 0; ks < KS; ++ks) {
+                acc0 = Tr::mma(qa[0][ks], kb[ks], acc0);
+                acc1 = Tr::mma(qa[1][ks], kb[ks], acc1);
+            }
+            const float part = weighted_relu_sum(acc0, acc1, wr);
+            const float other = __shfl_xor(part, 32, 64);
+            if (half == 0 && m < ntiles) stage[m * kKeyTile + col] = part + other;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        float part = 0.0f;
-#pragma unroll
-        for (int rg = 0; rg < 16; ++rg) {
-            part = fmaf(wr[0][rg], fmaxf(acc0[rg], 0.0f), part);
-            part = fmaf(wr[1][rg], fmaxf(acc1[rg], 0.0f), part);
-        }
-        const float other = __shfl_xor(part, 32, 64);
-        const int key = s0 + col;
-        if (half == 0 && key < s_hi) out[key] = part + other;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    // the wave's scores, two tiles per store instruction
+    for (int e = lane; e < ntiles * kKeyTile; e += 64) {
+        const int key = s_first + (e / kKeyTile) * tile_step + e % kKeyTile;
+        if (key < s_hi) out[key] = stage[e];
     }
 }
 
@@ -414,12 +452,7 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
                     acc0 = Tr::mma(qa[0][ks], kb[ks], acc0);
                     acc1 = Tr::mma(qa[1][ks], kb[ks], acc1);
                 }
-                float part = 0.0f;
-#pragma unroll
-                for (int rg = 0; rg < 16; ++rg) {
-                    part = fmaf(wr[0][rg], fmaxf(acc0[rg], 0.0f), part);
-                    part = fmaf(wr[1][rg], fmaxf(acc1[rg], 0.0f), part);
-                }
+                const float part = weighted_relu_sum(acc0, acc1, wr);
                 const float other = __shfl_xor(part, 32, 64);
                 const int key = s0 + st * 32 + col;
                 if (half == 0 && key < t_hi) out[key] = part + other;
@@ -484,7 +517,7 @@ hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, c
         // key chunk per wave: long enough to amortise the query-block load,
         // short enough that a few query rows still give ~16 waves per CU (a
         // streaming kernel needs that many loads in flight)
-        int chunk = 2048;
+        int chunk = kStreamMaxChunk;
         while (chunk > 128 && (long long)B * rows * ceil_div(S, chunk) < 2048) chunk >>= 1;
         const int nchunks = ceil_div(S, chunk);
         const long long waves = (long long)B * rows * nchunks;
@@ -494,14 +527,14 @@ hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, c
                 hipLaunchKernelGGL((indexer_stream_kernel<false>), dim3(blocks), dim3(256), 0,
                                    stream, static_cast<const uint8_t *>(q_idx),
                                    static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
-                                   rows, chunk, nchunks, scores, batch_stride, (int)write_masked,
-                                   clear, clear_words);
+                                   rows, nchunks, scores, batch_stride, (int)write_masked, clear,
+                                   clear_words);
             else
                 hipLaunchKernelGGL((indexer_stream_kernel<true>), dim3(blocks), dim3(256), 0,
                                    stream, static_cast<const uint8_t *>(q_idx),
                                    static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
-                                   rows, chunk, nchunks, scores, batch_stride, (int)write_masked,
-                                   clear, clear_words);
+                                   rows, nchunks, scores, batch_stride, (int)write_masked, clear,
+                                   clear_words);
             return hipGetLastError();
         }
         if (rows >= kPfRows) {  // rows share key tiles: 8 rows a workgroup

@@ -87,6 +87,30 @@ def test_indexer_mfma_ragged_rows(dtype):
     _assert_scores_equal(sc, oracle.indexer_scores(q, k, wt, q_pos=pos), f"{dtype} rows")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_indexer_decode_stream_ragged(dtype):
+    """One query row per sequence (the key-stream kernel): causal ends at the
+    last key, mid-chunk, inside the first tile and at key 0."""
+    B, T, S, H, D = 4, 1, 5000, 64, 128
+    pos = torch.tensor([[4999], [2500], [33], [0]], dtype=torch.int32)
+    q, k, wt = _int_indexer(B, T, S, H, D, dtype, seed=31)
+    _say(f"stream indexer {dtype}: B={B} S={S} q_pos={pos.flatten().tolist()}")
+    sc = dsa.dsa_indexer_scores(q, k, wt, q_pos=pos.to(DEV))
+    _assert_scores_equal(sc, oracle.indexer_scores(q, k, wt, q_pos=pos), f"{dtype} stream")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_indexer_few_rows(dtype):
+    """Two to seven query rows per sequence (wave-per-row MFMA kernel)."""
+    B, S, H, D = 2, 3000, 64, 128
+    pos = torch.tensor([[2999, 100, 2047], [5, 2048, 1500]], dtype=torch.int32)
+    T = pos.shape[1]
+    q, k, wt = _int_indexer(B, T, S, H, D, dtype, seed=32)
+    _say(f"few-row indexer {dtype}: q_pos={pos.tolist()}")
+    sc = dsa.dsa_indexer_scores(q, k, wt, q_pos=pos.to(DEV))
+    _assert_scores_equal(sc, oracle.indexer_scores(q, k, wt, q_pos=pos), f"{dtype} few rows")
+
+
 def test_indexer_signed_weights_and_max_magnitude():
     B, T, S, H, D = 1, 70, 70, 64, 128
     q, k, wt = _int_indexer(B, T, S, H, D, "bf16", seed=5, signed_w=True)
@@ -332,6 +356,24 @@ def test_forward_c2_sampled_rows():
                                   d_v=w.d_v)
     err = max_abs_err(out[:, rows], ref)
     _say(f"c2: max-abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_forward_short_last_chunk():
+    """Rows beyond one score block run in chunks; a short last chunk takes the
+    split-entry attention path (partials in the workspace) and the wide top-k."""
+    w = configs.get("c2").with_(name="chunked", T=1027, S=65536)
+    x, idx, out = _forward(w, seed=9)
+    rows = [0, 1023, 1024, 1025, 1026]
+    _say(f"chunked forward T={w.T} S={w.S}: oracle over rows {rows}")
+    pos = np.array([[w.S - w.T + r for r in rows]])
+    sc = oracle.indexer_scores(x["q_idx"][:, rows], x["k_idx"], x["w"][:, rows], q_pos=pos)
+    ref_idx = oracle.topk(sc, w.index_topk, q_pos=pos)
+    assert_selection_equal(idx[:, rows], ref_idx, "chunked")
+    ref = oracle.sparse_attention("mla", x["q"][:, rows], x["kv"], None, ref_idx, w.scale,
+                                  d_v=w.d_v)
+    err = max_abs_err(out[:, rows], ref)
+    _say(f"chunked forward: max-abs err {err:.3e}")
     assert err <= TOL["bf16"]
 
 
