@@ -8,21 +8,20 @@
 // NSA and DSA", section 3.1).  Because every gathered row is shared by all
 // heads, the heads form the M dimension of dense MFMA tiles.
 //
-// Workgroup = 4 waves = one query row x 64 heads x one range of selected
-// entries, walked 64 entries at a time:
-//   gather  the 64 selected rows go straight from memory into one of two LDS
-//           tile buffers (global_load_lds, 16 bytes a lane), so the next tile
-//           is in flight while the current one is multiplied; the row pitch
-//           carries one spare 16-byte slot against bank conflicts, and masked
-//           entries load a valid row whose probability is then forced to 0;
-//   S phase wave w computes S^T = C(32 keys) . Q^T(32 heads) over 576 dims for
-//           key tile w/2 and head tile w%2 (v_mfma_f32_32x32x16_bf16), with
-//           its 32x576 query block held in registers as the B operand;
-//   softmax online, fp32: tile max exchanged through LDS, probabilities
-//           written to LDS as bf16 [head][key];
-//   PV phase wave w accumulates O[64 heads, dims 128w..128w+127] += P . V,
-//           V read straight from the row-major tile with the LDS transpose
-//           read (ds_read_b64_tr_b16) as the B operand.
+// Workgroup = 8 waves = one query row x 64 heads x one range of selected
+// entries, walked 32 entries at a time (details at the kernel):
+//   gather  the selected rows are loaded into registers two tiles ahead and
+//           parked in a three-tile LDS ring; the row pitch carries one spare
+//           16-byte slot against bank conflicts; masked entries load a valid
+//           row whose probability is then forced to 0;
+//   S       4 waves compute S^T = C(32 keys) . Q^T(32 heads), each over half
+//           of the 576 dims (v_mfma_f32_32x32x16_bf16), the query block held
+//           in registers as the B operand; the halves meet in LDS;
+//   softmax online, fp32, on the S waves; probabilities written to LDS as
+//           bf16 [head][key];
+//   PV      4 waves accumulate O[64 heads, 128 dims each] += P . V, V read
+//           straight from the row-major tile with the LDS transpose read
+//           (ds_read_b64_tr_b16) as the B operand.
 // Decode rows split their entries over several workgroups; each writes a
 // normalised partial output and its log-sum-exp, merged by a second kernel.
 #include "dsa_internal.h"
@@ -33,28 +32,11 @@ namespace {
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kHg = 64;            // heads per workgroup
-constexpr int kKt = 64;            // selected entries per step
 constexpr int kKsteps = kDqk / 16; // 36
 constexpr int kRowPitch = kDqk * 2 + 16;   // bytes: 1168 (bank shift of 36 dwords)
-constexpr int kPPitch = kKt * 2 + 16;      // bytes: 144
-constexpr int kChunksPerRow = kDqk * 2 / 16;  // 72 chunks of 16 bytes
-constexpr int kThreads = 256;
 constexpr float kRescaleLog2 = 8.0f;  // reference-max slack, base-2 units
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kPitchChunks = kRowPitch / 16;            // 73 slots of 16 bytes a row
-constexpr int kTileLoads = kKt * kPitchChunks / 64;      // 73 wave loads of 1 KB a tile
-static_assert(kKt * kPitchChunks % 64 == 0, "a tile is a whole number of wave loads");
-
-struct __align__(16) MlaSmem {
-    uint8_t kv[2][kKt * kRowPitch];    // 2 x 74752, double-buffered tiles
-    uint8_t p[kHg * kPPitch];          // 9216
-    int32_t sel[2][kKt];
-    float tile_max[2][kHg];            // per key tile, per head
-    float corr[kHg];
-    float lsum[2][kHg];
-};
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint8_t *p) {
     return *reinterpret_cast<const bf16x8 *>(p);
@@ -69,32 +51,6 @@ __device__ __forceinline__ bf16x4 lds_tr16(const uint8_t *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4)(p));
 }
 
-// Issue the loads of one tile: wave load j fills LDS bytes [1024j, 1024j+1024)
-// of the tile, lane l the 16-byte slot q = 64j + l, i.e. row q / 73, slot
-// q % 73.  Slot 72 is the pitch padding (loaded with chunk 0, never read).  A
-// masked entry (-1) loads row 0; its probability is forced to 0.  Completion
-// is awaited later with s_waitcnt.
-__device__ __forceinline__ void issue_tile(uint8_t *tile, const int32_t *sel,
-                                           const uint8_t *__restrict__ lat_b, int wave,
-                                           int lane) {
-    typedef __attribute__((address_space(3))) void *lds_ptr;
-    constexpr int kStep = 64 * (kThreads / 64);  // slots between a wave's loads
-    int q = 64 * wave + lane;
-    int row = q / kPitchChunks;
-    int c = q - row * kPitchChunks;
-    for (int j = wave; j < kTileLoads; j += kThreads / 64) {
-        const uint32_t s = (uint32_t)max(sel[row], 0);
-        const uint8_t *src = lat_b + s * (uint64_t)(kDqk * 2) + (c < kChunksPerRow ? c * 16 : 0);
-        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(tile + 1024 * j), 16, 0, 0);
-        row += kStep / kPitchChunks;
-        c += kStep % kPitchChunks;
-        if (c >= kPitchChunks) {
-            c -= kPitchChunks;
-            row += 1;
-        }
-    }
-}
-
 template <typename Tout>
 __device__ __forceinline__ void store_out(Tout *p, float v);
 template <>
@@ -104,11 +60,78 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float v) {
     *p = (uint16_t)f32_to_bf16_bits(v);
 }
 
-// grid: 1-D.  Work item = (head group, split, row, batch).  When the number
-// of (row, split) units is a multiple of 8, the head groups of one unit get
-// workgroup ids that are 8 apart, so they run on the same XCD (ids are dealt
-// round-robin over the 8 XCDs) and the second gather of the same rows hits
-// that XCD's L2.
+// ---------------------------------------------------------------------------
+// The kernel: 8 waves = 2 per SIMD, 32-entry tiles.
+//   waves 0-3 ("S" waves): wave (ht = w&1, kh = w>>1) holds the query block of
+//       32 heads over half of the 576 dims (18 k-steps, 72 registers) and
+//       computes that half of S^T for every tile; the kh = 1 half goes through
+//       LDS to its kh = 0 partner, which owns the online softmax of those 32
+//       heads (the 32-entry tile max is in-wave: 16 registers and one
+//       cross-half shuffle) and writes P (bf16) and the rescale factors.
+//   waves 4-7 ("PV" waves): wave 4+d owns O[64 heads, dims 128d..128d+127].
+// Iteration it: the S waves work on tile it+1 while the PV waves multiply
+// tile it; two workgroup barriers per iteration split S (partials | softmax)
+// and PV (first | second 16-entry k-step).  S and PV waves share each SIMD,
+// so one role's latencies are covered by the other's matrix work.
+// Gathers are staged through registers: every wave loads its share of tile
+// it+4 at iteration it and parks it in LDS at iteration it+2, so each gather
+// has two iterations to arrive while only three tiles occupy LDS (it, it+1,
+// it+2).  The selection of the whole split is read into LDS up front.
+constexpr int kKt = 32;                          // entries per tile
+constexpr int kRing = 3;                         // tiles resident in LDS
+constexpr int kSlotsRow = kDqk * 2 / 16;         // 72 data slots of 16 bytes a row
+constexpr int kTileSlots = kKt * kSlotsRow;  // 2304
+constexpr int kTileBytes = kKt * kRowPitch;    // 37376
+constexpr int kPPitch = kKt * 2 + 16;          // 80 bytes per head row of P
+constexpr int kHalfSteps = kKsteps / 2;          // 18
+constexpr int kMaxSplit = 4096;                  // entries of one split (LDS table)
+constexpr int kThreads = 512;
+// staged 16-byte loads per lane per tile: slot q = 512 m + 64 w + lane; the
+// S waves (w < 4) also take m = 4, which covers slots 2048..2303
+constexpr int kLoadsS = 5;
+constexpr int kLoadsPV = 4;
+static_assert(kLoadsPV * kThreads + 4 * 64 == kTileSlots, "staging covers a tile");
+
+struct __align__(16) MlaSmem {
+    uint8_t kv[kRing][kTileBytes];  // 3 x 37376
+    int32_t idx[kMaxSplit];           // this split's selection, -1 past its end
+    uint8_t p[2][kHg * kPPitch];      // 2 x 5120
+    f32x16 part[2][64];                 // kh = 1 halves of S, one per head tile
+    float corr[2][kHg];
+    float fin_l[kHg], fin_m[kHg];
+};
+
+// Issue the global loads of this wave's share of tile `t` (entries
+// 32t..32t+31 of the split).  Entries past the split, and masked ones, read
+// row 0 of the sequence: the loads stay unconditional, their data unused.
+template <int NL>
+__device__ __forceinline__ void stage_load(u32x4 (&r)[NL], const MlaSmem &sm, int len,
+                                              int t, const uint8_t *__restrict__ lat_b,
+                                              int wave, int lane) {
+#pragma unroll
+    for (int m = 0; m < NL; ++m) {
+        const int q = 512 * m + 64 * wave + lane;
+        const int row = q / kSlotsRow;
+        const int c = q - row * kSlotsRow;
+        const int e = t * kKt + row;
+        const int sel = sm.idx[min(e, len - 1)];
+        const uint32_t src_row = (uint32_t)(e < len ? max(sel, 0) : 0);
+        r[m] = *reinterpret_cast<const u32x4 *>(lat_b + src_row * (uint64_t)(kDqk * 2) + c * 16);
+    }
+}
+
+template <int NL>
+__device__ __forceinline__ void stage_store(const u32x4 (&r)[NL], uint8_t *tile, int wave,
+                                               int lane) {
+#pragma unroll
+    for (int m = 0; m < NL; ++m) {
+        const int q = 512 * m + 64 * wave + lane;
+        const int row = q / kSlotsRow;
+        const int c = q - row * kSlotsRow;
+        *reinterpret_cast<u32x4 *>(tile + row * kRowPitch + c * 16) = r[m];
+    }
+}
+
 template <typename Tout>
 __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ lat,
@@ -139,138 +162,177 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     const int b = qidx / rows;
     const int i = row0 + r;
     const int head0 = hg * kHg;
-
     const int e_begin = split * per_split;
-    const int e_end = min(k, e_begin + per_split);
-    const int ntiles = (e_end - e_begin + kKt - 1) / kKt;
-    const int32_t *sel_row = idx + ((size_t)b * T + i) * k;
+    const int len = min(k, e_begin + per_split) - e_begin;  // entries of this split
+    const int ntiles = (len + kKt - 1) / kKt;
+    const int32_t *sel_row = idx + ((size_t)b * T + i) * k + e_begin;
     const uint8_t *lat_b = reinterpret_cast<const uint8_t *>(lat) + (size_t)b * S * (kDqk * 2);
+    const size_t rowq = (size_t)b * T + i;
+    const size_t prow = (size_t)qidx;  // row of this launch's split partials
 
-    // ---- prologue: indices of tiles 0 and 1, loads of tile 0 in flight
-    if (tid < kKt) {
-        const int e = e_begin + tid;
-        sm.sel[0][tid] = e < e_end ? sel_row[e] : -1;
-        sm.sel[1][tid] = e + kKt < e_end ? sel_row[e + kKt] : -1;
-    }
-    __syncthreads();
-    issue_tile(sm.kv[0], sm.sel[0], lat_b, wave, lane);
-
-    // ---- S-phase role and its query block (B operand: 32 heads x 576 dims)
-    const int kt = wave >> 1;  // key tile of the S phase
-    const int ht = wave & 1;   // head tile of the S phase
-    bf16x8 qb[kKsteps];
-    {
-        const uint16_t *qp = q + (((size_t)b * T + i) * H + head0 + ht * 32 + l32) * kDqk + 8 * half;
-#pragma unroll
-        for (int ks = 0; ks < kKsteps; ++ks)
-            qb[ks] = *reinterpret_cast<const bf16x8 *>(qp + ks * 16);
-    }
-
-    // ---- PV-phase accumulators: 2 head tiles x 4 dim tiles of 32x32
-    f32x16 o[2][4];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) o[a][c] = f32x16{};
-
-    float m_run = -INFINITY;  // running max of head (head0 + 32*ht + l32), S-phase view
-    float l_run = 0.0f;       // this wave's share of the running sum
-    const float sl2 = scale * 1.4426950408889634f;  // logits in base-2 units
-    __builtin_amdgcn_s_waitcnt(0);
+    // ---- prologue: the split's selection into LDS
+    for (int e = tid; e < ntiles * kKt; e += kThreads) sm.idx[e] = e < len ? sel_row[e] : -1;
     __syncthreads();
 
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1;
-        // loads of the next tile overlap this tile's arithmetic
-        if (it + 1 < ntiles) issue_tile(sm.kv[buf ^ 1], sm.sel[buf ^ 1], lat_b, wave, lane);
-        int next_sel = -1;
-        if (tid < kKt) {
-            const int e = e_begin + (it + 2) * kKt + tid;
-            next_sel = e < e_end ? sel_row[e] : -1;
+    const float sl2 = scale * 1.4426950408889634f;
+    if (wave < 4) {
+        // ======================= S waves =======================
+        const int ht = wave & 1, kh = wave >> 1;
+        u32x4 stg[2][kLoadsS];
+        stage_load(stg[0], sm, len, 0, lat_b, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_load(stg[1], sm, len, 1, lat_b, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 qb[kHalfSteps];
+        {
+            const uint16_t *qp = q + (rowq * H + head0 + ht * 32 + l32) * kDqk + 8 * half +
+                                 16 * kHalfSteps * kh;
+#pragma unroll
+            for (int ks = 0; ks < kHalfSteps; ++ks)
+                qb[ks] = *reinterpret_cast<const bf16x8 *>(qp + ks * 16);
         }
-        const uint8_t *kvt = sm.kv[buf];
-        const int32_t *selt = sm.sel[buf];
-
-        // ---- S^T = C . Q^T for (key tile kt, head tile ht)
-        f32x16 sacc = {};
-        const uint8_t *arow = kvt + (kt * 32 + l32) * kRowPitch + 16 * half;
+        stage_store(stg[0], sm.kv[0], wave, lane);
+        stage_store(stg[1], sm.kv[1], wave, lane);
+        stage_load(stg[0], sm, len, 2, lat_b, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_load(stg[1], sm, len, 3, lat_b, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < kKsteps; ++ks)
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(arow + ks * 32), qb[ks], sacc,
-                                                           0, 0, 0);
-        // register rg holds key kt*32 + 8*(rg/4) + 4*half + rg%4, head ht*32 + l32
-        float tmax = -INFINITY;
+        for (int ks = 0; ks < kHalfSteps; ++ks) asm volatile("" ::"v"(qb[ks]));
+        lds_barrier();  // tiles 0 and 1 in LDS
+        float m_run = -INFINITY, l_run = 0.0f;
+        auto s_half = [&](const uint8_t *kvt) -> f32x16 {  // this wave's half of S^T
+            const uint8_t *arow = kvt + l32 * kRowPitch + 16 * half + 32 * kHalfSteps * kh;
+            f32x16 acc = {};
 #pragma unroll
-        for (int rg = 0; rg < 16; ++rg) {
-            const int key = kt * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3);
-            const float x = selt[key] >= 0 ? sacc[rg] * sl2 : -INFINITY;
-            sacc[rg] = x;
-            tmax = fmaxf(tmax, x);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        if (half == 0) sm.tile_max[kt][ht * 32 + l32] = tmax;
-        __syncthreads();
-        const float m_tile = fmaxf(sm.tile_max[0][ht * 32 + l32], sm.tile_max[1][ht * 32 + l32]);
-        // Lazy rescaling: the reference max m_run only moves when the tile max
-        // exceeds it by more than 2^8, so probabilities stay <= 256 and the
-        // accumulators are rescaled only on those (rare) steps.  The softmax is
-        // unchanged: numerator and denominator share the reference.
-        float corr = 1.0f;
-        if (m_tile > m_run + kRescaleLog2) {
-            corr = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_tile);
-            m_run = m_tile;
-        }
-        const float m_ref = m_run;
-        float psum = 0.0f;
-        uint8_t *prow = sm.p + (ht * 32 + l32) * kPPitch;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float pv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pv[j] = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sacc[4 * g + j] - m_ref);
-                psum += pv[j];
-            }
-            const bf16x4 pk = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
-            const int key = kt * 32 + 8 * g + 4 * half;
-            *reinterpret_cast<bf16x4 *>(prow + key * 2) = pk;
-        }
-        l_run = l_run * corr + psum;
-        if (kt == 0 && half == 0) sm.corr[ht * 32 + l32] = corr;
-        __syncthreads();
-
-        // ---- O[64 heads, 128 dims of this wave] = O * corr + P . V
-        const int dv0 = wave * 128;
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            float cr[16];
-            bool any = false;
+            for (int ks = 0; ks < kHalfSteps; ++ks)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(arow + ks * 32), qb[ks],
+                                                              acc, 0, 0, 0);
+            return acc;
+        };
+        auto softmax = [&](int tile, f32x16 acc) {  // kh = 0: full S^T in acc
+            const int32_t *selt = sm.idx + tile * kKt;
+            float tmax = -INFINITY;
 #pragma unroll
             for (int rg = 0; rg < 16; ++rg) {
-                cr[rg] = sm.corr[a * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
-                any |= cr[rg] != 1.0f;
+                const int key = 8 * (rg >> 2) + 4 * half + (rg & 3);
+                const float x = selt[key] >= 0 ? acc[rg] * sl2 : -INFINITY;
+                acc[rg] = x;
+                tmax = fmaxf(tmax, x);
             }
-            if (__ballot(any)) {
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            float corr = 1.0f;
+            if (tmax > m_run + kRescaleLog2) {
+                corr = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - tmax);
+                m_run = tmax;
+            }
+            const float m_ref = m_run;
+            float ps0 = 0.0f, ps1 = 0.0f;
+            uint8_t *prow = sm.p[tile & 1] + (ht * 32 + l32) * kPPitch;
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
+            for (int g = 0; g < 4; ++g) {
+                float pv[4];
 #pragma unroll
-                    for (int rg = 0; rg < 16; ++rg) o[a][c][rg] *= cr[rg];
+                for (int j = 0; j < 4; ++j)
+                    pv[j] = m_ref == -INFINITY ? 0.0f
+                                               : __builtin_amdgcn_exp2f(acc[4 * g + j] - m_ref);
+                ps0 += pv[0] + pv[1];
+                ps1 += pv[2] + pv[3];
+                const bf16x4 pk = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
+                *reinterpret_cast<bf16x4 *>(prow + (8 * g + 4 * half) * 2) = pk;
+            }
+            l_run = l_run * corr + (ps0 + ps1);
+            if (half == 0) sm.corr[tile & 1][ht * 32 + l32] = corr;
+        };
+
+        // "iteration -1": S and softmax of tile 0
+        {
+            f32x16 acc = s_half(sm.kv[0]);
+            if (kh == 1) sm.part[ht][lane] = acc;
+            lds_barrier();
+            if (kh == 0) {
+                const f32x16 other = sm.part[ht][lane];
+#pragma unroll
+                for (int rg = 0; rg < 16; ++rg) acc[rg] += other[rg];
+                softmax(0, acc);
+            }
+            lds_barrier();
+        }
+        // iteration it: park tile it+2, load tile it+4, S of tile it+1
+        auto s_step = [&](const int it, u32x4 (&st)[kLoadsS]) {
+            stage_store(st, sm.kv[(it + 2) % kRing], wave, lane);
+            stage_load(st, sm, len, it + 4, lat_b, wave, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            const bool more = it + 1 < ntiles;
+            f32x16 acc = {};
+            if (more) acc = s_half(sm.kv[(it + 1) % kRing]);
+            if (more && kh == 1) sm.part[ht][lane] = acc;
+            lds_barrier();  // ---- barrier 1
+            if (more && kh == 0) {
+                const f32x16 other = sm.part[ht][lane];
+#pragma unroll
+                for (int rg = 0; rg < 16; ++rg) acc[rg] += other[rg];
+                softmax(it + 1, acc);
+            }
+            lds_barrier();  // ---- barrier 2
+        };
+        for (int it = 0; it < ntiles; it += 2) {
+            s_step(it, stg[0]);
+            if (it + 1 < ntiles) s_step(it + 1, stg[1]);
+        }
+        __syncthreads();
+        if (kh == 0) {
+            const float l_all = l_run + __shfl_xor(l_run, 32, 64);  // both key halves
+            if (half == 0) {
+                sm.fin_l[ht * 32 + l32] = l_all;
+                sm.fin_m[ht * 32 + l32] = m_run;
             }
         }
-        // transpose-read lane address: row key0 + j/4, column col0 + 4*(j%4)
-        const int trj = lane & 15;
-        const int trg = lane >> 4;
-        const uint8_t *vbase = kvt + (8 * (trg >> 1) + (trj >> 2)) * kRowPitch +
-                               (dv0 + 16 * (trg & 1) + 4 * (trj & 3)) * 2;
+        __syncthreads();
+        if (kh == 0 && half == 0) {
+            const int hl = ht * 32 + l32;
+            const float l = sm.fin_l[hl];
+            const float ls = l > 0.0f ? (sm.fin_m[hl] + log2f(l)) * 0.6931471805599453f : -INFINITY;
+            if (splits == 1) {
+                if (lse) lse[rowq * H + head0 + hl] = ls;
+            } else {
+                lse_part[(prow * splits + split) * H + head0 + hl] = ls;
+            }
+        }
+    } else {
+        // ======================= PV waves =======================
+        const int d = wave - 4;
+        const int dv0 = d * 128;
+        u32x4 stg[2][kLoadsPV];
+        stage_load(stg[0], sm, len, 0, lat_b, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_load(stg[1], sm, len, 1, lat_b, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 o[2][4];
 #pragma unroll
-        for (int ks = 0; ks < kKt / 16; ++ks) {
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o[a][c] = f32x16{};
+        stage_store(stg[0], sm.kv[0], wave, lane);
+        stage_store(stg[1], sm.kv[1], wave, lane);
+        stage_load(stg[0], sm, len, 2, lat_b, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_load(stg[1], sm, len, 3, lat_b, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();  // tiles 0 and 1 in LDS (matches the S waves')
+        const int trj = lane & 15, trg = lane >> 4;
+        const int vrow = 8 * (trg >> 1) + (trj >> 2);
+        const int vcol = (dv0 + 16 * (trg & 1) + 4 * (trj & 3)) * 2;
+        auto pv_step = [&](int tile, int ks) {
+            const uint8_t *kvt = sm.kv[tile % kRing];
+            const uint8_t *pt = sm.p[tile & 1];
             bf16x8 pa[2], vb[4];
 #pragma unroll
             for (int a = 0; a < 2; ++a)
-                pa[a] = lds_b128(sm.p + (a * 32 + l32) * kPPitch + (16 * ks + 8 * half) * 2);
+                pa[a] = lds_b128(pt + (a * 32 + l32) * kPPitch + (16 * ks + 8 * half) * 2);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const uint8_t *vp = vbase + 16 * ks * kRowPitch + 32 * c * 2;
+                const uint8_t *vp = kvt + (16 * ks + vrow) * kRowPitch + vcol + 64 * c;
                 const bf16x4 lo = lds_tr16(vp);
                 const bf16x4 hi = lds_tr16(vp + 4 * kRowPitch);
                 vb[c] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -279,50 +341,59 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             for (int c = 0; c < 4; ++c)
 #pragma unroll
                 for (int a = 0; a < 2; ++a)
-                    o[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[a], vb[c], o[a][c], 0, 0,
-                                                                      0);
-        }
-        __syncthreads();  // every wave is done with kv[buf], sel[buf], p
-        if (tid < kKt) sm.sel[buf][tid] = next_sel;  // indices of tile it + 2
-        __builtin_amdgcn_s_waitcnt(0);               // tile it + 1 has landed
-        __syncthreads();
-    }
-
-    // ---- final normalisation: l per head = sum of both key-tile waves' shares
-    const float l_wave = l_run + __shfl_xor(l_run, 32, 64);
-    __syncthreads();
-    if (half == 0) sm.lsum[kt][ht * 32 + l32] = l_wave;
-    if (kt == 0 && half == 0) sm.tile_max[0][ht * 32 + l32] = m_run;  // reuse as final max
-    __syncthreads();
-    const int dv0 = wave * 128;
-    const size_t rowq = ((size_t)b * T + i);
-    const size_t prow = (size_t)qidx;  // row of this launch's split partials
+                    o[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[a], vb[c], o[a][c], 0,
+                                                                      0, 0);
+        };
+        lds_barrier();  // matches the S waves' "iteration -1"
+        lds_barrier();
+        auto o_step = [&](const int it, u32x4 (&st)[kLoadsPV]) {
+            stage_store(st, sm.kv[(it + 2) % kRing], wave, lane);
+            stage_load(st, sm, len, it + 4, lat_b, wave, lane);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+            for (int a = 0; a < 2; ++a) {
+                float cr[16];
+                bool any = false;
 #pragma unroll
-        for (int rg = 0; rg < 16; ++rg) {
-            const int hl = a * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3);
-            const float l = sm.lsum[0][hl] + sm.lsum[1][hl];
-            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+                for (int rg = 0; rg < 16; ++rg) {
+                    cr[rg] = sm.corr[it & 1][a * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
+                    any |= cr[rg] != 1.0f;
+                }
+                if (__ballot(any)) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int d = dv0 + 32 * c + l32;
-                const float v = o[a][c][rg] * inv;
-                if (splits == 1)
-                    store_out(out + (rowq * H + head0 + hl) * kDv + d, v);
-                else
-                    o_part[((prow * splits + split) * H + head0 + hl) * kDv + d] = v;
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int rg = 0; rg < 16; ++rg) o[a][c][rg] *= cr[rg];
+                }
             }
+            pv_step(it, 0);
+            lds_barrier();  // ---- barrier 1
+            pv_step(it, 1);
+            lds_barrier();  // ---- barrier 2
+        };
+        for (int it = 0; it < ntiles; it += 2) {
+            o_step(it, stg[0]);
+            if (it + 1 < ntiles) o_step(it + 1, stg[1]);
         }
-    }
-    if (tid < kHg) {
-        const float l = sm.lsum[0][tid] + sm.lsum[1][tid];
-        const float m2 = sm.tile_max[0][tid];  // base-2 units
-        const float ls = l > 0.0f ? (m2 + log2f(l)) * 0.6931471805599453f : -INFINITY;
-        if (splits == 1) {
-            if (lse) lse[rowq * H + head0 + tid] = ls;
-        } else {
-            lse_part[(prow * splits + split) * H + head0 + tid] = ls;
+        __syncthreads();
+        __syncthreads();
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) {
+                const int hl = a * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3);
+                const float l = sm.fin_l[hl];
+                const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int dd = dv0 + 32 * c + l32;
+                    const float v = o[a][c][rg] * inv;
+                    if (splits == 1)
+                        store_out(out + (rowq * H + head0 + hl) * kDv + dd, v);
+                    else
+                        o_part[((prow * splits + split) * H + head0 + hl) * kDv + dd] = v;
+                }
+            }
         }
     }
 }
@@ -383,10 +454,11 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(
 // two tiles per split so the two-stage gather pipeline has work to overlap.
 int mla_splits(int B, int rows, int H, int k) {
     const long long wgs = (long long)B * rows * (H / kHg);
-    const int max_splits = ceil_div(k, 2 * kKt);
+    const int max_splits = ceil_div(k, 4 * kKt);
     long long s = (256 + wgs - 1) / wgs;
-    if (s < 1) s = 1;
     if (s > max_splits) s = max_splits;
+    if (s < ceil_div(k, kMaxSplit)) s = ceil_div(k, kMaxSplit);  // selection table bound
+    if (s < 1) s = 1;
     return (int)s;
 }
 

@@ -21,6 +21,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kMaxGridY = 65535;  // launch limit of gridDim.y / gridDim.z
 
+// ------------------------------------------------------------- barriers --
+// Workgroup barrier for LDS traffic only.  __syncthreads() carries a
+// workgroup release fence, which also waits for this wave's outstanding
+// global loads -- including direct-to-LDS loads meant to stay in flight
+// across the barrier.  Here only the wave's LDS operations are waited for
+// (s_waitcnt lgkmcnt(0), vmcnt and expcnt left at their maxima), and the
+// compiler-only fences keep memory accesses on their side of the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ------------------------------------------------------ scalar conversions --
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
     return __uint_as_float(b << 16);

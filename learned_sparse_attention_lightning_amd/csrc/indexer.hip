@@ -382,7 +382,11 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
     constexpr int EB = Tr::elem_bytes;
     constexpr int KS = Tr::ksteps;
     constexpr int DPS = Tr::dims_per_step;
-    __shared__ __align__(16) uint8_t tiles[2][Pt::bytes];
+    // Two separate LDS objects, named statically in a loop unrolled by two:
+    // the compiler can then tell that the direct-to-LDS loads of the next
+    // tile do not alias the reads of this one, and does not wait for them.
+    __shared__ __align__(16) uint8_t tile0[Pt::bytes];
+    __shared__ __align__(16) uint8_t tile1[Pt::bytes];
     __shared__ int tmax_s[kPfRows];
 
     const int wave = threadIdx.x >> 6;
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
     if (k_begin >= k_hi) return;             // uniform over the workgroup
 
     const uint8_t *kb_base = k_idx + (size_t)b * S * Pt::row_bytes;
-    prefill_issue_tile<Fp8>(tiles[0], kb_base, k_begin, S, wave, lane);
+    prefill_issue_tile<Fp8>(tile0, kb_base, k_begin, S, wave, lane);
 
     const size_t qrow = ((size_t)b * T + i) * kIdxHeads;
     Op qa[2][KS];
@@ -432,17 +436,15 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
             wr[tl][rg] = w[qrow + tl * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
     const int t_hi = min(k_end, t + 1);  // this row's causal end inside the chunk
 
-    int it = 0;
-    for (int s0 = k_begin; s0 < k_hi; s0 += kPfKeys, ++it) {
-        const int buf = it & 1;
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile `it` have landed
-        __syncthreads();                // ... and every other wave's; buf^1 is free
+    auto step = [&](const int s0, const uint8_t *cur, uint8_t *next) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of this tile have landed
+        __syncthreads();                // ... and every other wave's; `next` is free
         if (s0 + kPfKeys < k_hi)
-            prefill_issue_tile<Fp8>(tiles[buf ^ 1], kb_base, s0 + kPfKeys, S, wave, lane);
+            prefill_issue_tile<Fp8>(next, kb_base, s0 + kPfKeys, S, wave, lane);
         if (s0 < t_hi) {
 #pragma unroll
             for (int st = 0; st < kPfKeys / 32; ++st) {
-                const uint8_t *brow = tiles[buf] + (st * 32 + col) * Pt::pitch + 64 * half * EB;
+                const uint8_t *brow = cur + (st * 32 + col) * Pt::pitch + 64 * half * EB;
                 Op kb[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) kb[ks] = Tr::load(brow + ks * DPS * EB);
@@ -458,6 +460,10 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
                 if (half == 0 && key < t_hi) out[key] = part + other;
             }
         }
+    };
+    for (int s0 = k_begin; s0 < k_hi; s0 += 2 * kPfKeys) {
+        step(s0, tile0, tile1);
+        if (s0 + kPfKeys < k_hi) step(s0 + kPfKeys, tile1, tile0);
     }
 }
 
