@@ -96,7 +96,8 @@ struct __align__(16) MlaSmem {
     uint8_t kv[kRing][kTileBytes];  // 3 x 37376
     int32_t idx[kMaxSplit];           // this split's selection, -1 past its end
     uint8_t p[2][kHg * kPPitch];      // 2 x 5120
-    f32x16 part[2][64];                 // kh = 1 halves of S, one per head tile
+    f32x4 part[2][4][64];               // kh = 1 halves of S, one per head tile,
+                                        // registers 4j..4j+3 of lane l at [j][l]
     float corr[2][kHg];
     float fin_l[kHg], fin_m[kHg];
 };
@@ -201,14 +202,34 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         for (int ks = 0; ks < kHalfSteps; ++ks) asm volatile("" ::"v"(qb[ks]));
         lds_barrier();  // tiles 0 and 1 in LDS
         float m_run = -INFINITY, l_run = 0.0f;
-        auto s_half = [&](const uint8_t *kvt) -> f32x16 {  // this wave's half of S^T
+        // This wave's half of S^T.  All 18 A fragments are read before the
+        // first product, so the LDS latency is paid once per tile rather than
+        // once per pair of products.
+        auto s_half = [&](const uint8_t *kvt) -> f32x16 {
             const uint8_t *arow = kvt + l32 * kRowPitch + 16 * half + 32 * kHalfSteps * kh;
+            bf16x8 af[kHalfSteps];
+#pragma unroll
+            for (int ks = 0; ks < kHalfSteps; ++ks) af[ks] = lds_b128(arow + ks * 32);
+            __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
             f32x16 acc = {};
 #pragma unroll
             for (int ks = 0; ks < kHalfSteps; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(arow + ks * 32), qb[ks],
-                                                              acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qb[ks], acc, 0, 0, 0);
             return acc;
+        };
+        auto put_part = [&](const f32x16 &acc) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sm.part[ht][j][lane] = f32x4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2],
+                                             acc[4 * j + 3]};
+        };
+        auto add_part = [&](f32x16 &acc) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 o = sm.part[ht][j][lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[4 * j + e] += o[e];
+            }
         };
         auto softmax = [&](int tile, f32x16 acc) {  // kh = 0: full S^T in acc
             const int32_t *selt = sm.idx + tile * kKt;
@@ -248,12 +269,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         // "iteration -1": S and softmax of tile 0
         {
             f32x16 acc = s_half(sm.kv[0]);
-            if (kh == 1) sm.part[ht][lane] = acc;
+            if (kh == 1) put_part(acc);
             lds_barrier();
             if (kh == 0) {
-                const f32x16 other = sm.part[ht][lane];
-#pragma unroll
-                for (int rg = 0; rg < 16; ++rg) acc[rg] += other[rg];
+                add_part(acc);
                 softmax(0, acc);
             }
             lds_barrier();
@@ -266,12 +285,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             const bool more = it + 1 < ntiles;
             f32x16 acc = {};
             if (more) acc = s_half(sm.kv[(it + 1) % kRing]);
-            if (more && kh == 1) sm.part[ht][lane] = acc;
+            if (more && kh == 1) put_part(acc);
             lds_barrier();  // ---- barrier 1
             if (more && kh == 0) {
-                const f32x16 other = sm.part[ht][lane];
-#pragma unroll
-                for (int rg = 0; rg < 16; ++rg) acc[rg] += other[rg];
+                add_part(acc);
                 softmax(it + 1, acc);
             }
             lds_barrier();  // ---- barrier 2
