@@ -45,6 +45,7 @@ constexpr int kWideMaxS = 262144;      // bitmap of one row fits 32 KB of LDS
 constexpr int kWideMaxRows = 512;
 constexpr int kMetaWords = 16;         // per row: [1] count of keys above digit d1
 constexpr int kMaxSlices = kWideMaxS / kWideSlice;  // candidate counts per row (one per slice)
+constexpr int kHist2Direct = 256;      // candidates a slice adds to hist2 without LDS staging
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
     const uint32_t lo = __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u);
@@ -238,7 +239,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
 
 // ------------------------------------------------------- wide-row path -----
 struct WideLayout {
-    uint32_t *hist;     // [rows][kDigits]
+    uint32_t *hist;     // [rows][kDigits]   top 12 key bits, every key
+    uint32_t *hist2;    // [rows][kDigits]   key bits 19..8 of the keys whose top 12 bits are d1
     uint32_t *meta;     // [rows][kMetaWords]
     uint32_t *counts;   // [rows][kMaxSlices] candidates found by each slice
     uint32_t *bitmap;   // [rows][words]
@@ -248,8 +250,8 @@ struct WideLayout {
 
 __host__ __device__ inline size_t wide_row_bytes(int S) {
     const size_t words = (size_t)(S + 31) / 32;
-    return (size_t)kDigits * 4 + kMetaWords * 4 + kMaxSlices * 4 + words * 4 + (size_t)S * 8 +
-           16;
+    return (size_t)2 * kDigits * 4 + kMetaWords * 4 + kMaxSlices * 4 + words * 4 +
+           (size_t)S * 8 + 16;
 }
 
 __host__ __device__ inline WideLayout wide_layout(void *ws, int nrows, int S) {
@@ -257,6 +259,8 @@ __host__ __device__ inline WideLayout wide_layout(void *ws, int nrows, int S) {
     char *p = static_cast<char *>(ws);
     L.words = (S + 31) / 32;
     L.hist = reinterpret_cast<uint32_t *>(p);
+    p += (size_t)nrows * kDigits * 4;
+    L.hist2 = reinterpret_cast<uint32_t *>(p);
     p += (size_t)nrows * kDigits * 4;
     L.meta = reinterpret_cast<uint32_t *>(p);
     p += (size_t)nrows * kMetaWords * 4;
@@ -269,9 +273,10 @@ __host__ __device__ inline WideLayout wide_layout(void *ws, int nrows, int S) {
     return L;
 }
 
+// hist, hist2 and meta are contiguous: one sweep clears them
 __global__ __launch_bounds__(256) void topk_wide_clear_kernel(uint32_t *hist, uint32_t *meta,
                                                               int nrows) {
-    const size_t n1 = (size_t)nrows * kDigits;
+    const size_t n1 = (size_t)nrows * kDigits * 2;
     const size_t n2 = (size_t)nrows * kMetaWords;
     for (size_t j = blockIdx.x * 256ull + threadIdx.x; j < n1 + n2; j += (size_t)gridDim.x * 256)
         if (j < n1) hist[j] = 0u;
@@ -326,6 +331,7 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_scan_kernel(
     int T, int S, int row0, int rows, int k, WideLayout L) {
     __shared__ uint32_t scratch[kWideThreads / 64];
     __shared__ uint32_t d1_s, above_s;
+    __shared__ uint32_t h2[kDigits];  // second-digit counts when a slice has many candidates
     const int r = blockIdx.y, b = blockIdx.z;
     const int t = query_pos(q_pos, b, row0 + r, T, S);
     const int n = t < 0 ? 0 : t + 1;
@@ -381,24 +387,49 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_scan_kernel(
     for (int e = 0; e < 8; ++e)
         if (cmask & (1u << e)) cand[slot++] = make_uint2(u[e], (uint32_t)(p0 + e));
     if (tid == 0) L.counts[rr * kMaxSlices + blockIdx.x] = ncand;
+    // second digit (key bits 19..8) of the candidates; a slice with many of
+    // them (ties) aggregates in LDS first so no global counter gets hammered
+    uint32_t *gh2 = L.hist2 + rr * kDigits;
+    if (ncand <= kHist2Direct) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (cmask & (1u << e)) atomicAdd(&gh2[(u[e] >> 8) & (kDigits - 1)], 1u);
+    } else {
+        for (int j = tid; j < kDigits; j += kWideThreads) h2[j] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (cmask & (1u << e)) atomicAdd(&h2[(u[e] >> 8) & (kDigits - 1)], 1u);
+        __syncthreads();
+        for (int j = tid; j < kDigits; j += kWideThreads)
+            if (h2[j]) atomicAdd(&gh2[j], h2[j]);
+    }
     uint32_t word = byte << (8 * (lane & 3));
     word |= (uint32_t)__shfl_xor((int)word, 1, 64);
     word |= (uint32_t)__shfl_xor((int)word, 2, 64);
     if ((lane & 3) == 0 && p0 < n) L.bitmap[rr * L.words + (p0 >> 5)] = word;
 }
 
-constexpr int kMaxTies = 2048;  // ties at the threshold resolved by rank counting
+constexpr int kMaxTies = 2048;  // members of the final group resolved by rank counting
 
 struct ResolveSmem {
     SelectSmem sel;
     uint32_t scan[kTkWaves];
     uint32_t offs[kMaxSlices + 1];
-    uint32_t ties[kMaxTies];
+    uint32_t d2, above2;
+    uint2 group[kMaxTies];          // (key, position) of the keys in bin (d1, d2)
     uint32_t bits[kWideMaxS / 32];
     uint2 cand[kCandCache];
 };
 
 // grid: x = row in chunk, y = batch
+//
+// The candidates (keys whose top 12 bits are d1) are split once more by key
+// bits 19..8 with the histogram the scan built: d2 is the bin holding the
+// need1-th largest candidate, so every candidate above d2 is taken and only
+// the few in bin d2 need ordering -- each of them counts the group members
+// ahead of it (larger key, or equal key at a lower position).  A group too
+// large for that (massive ties) goes through the general threshold search.
 __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
     const int32_t *__restrict__ q_pos, int T, int S, int row0, int rows, int k,
     int32_t *__restrict__ idx, WideLayout L) {
@@ -415,13 +446,20 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
     }
     const size_t rr = (size_t)b * rows + r;
     const int nw = (n + 31) / 32;
-    uint32_t bitmap_pre[kWideMaxS / 32 / kTkThreads];  // issued now, used after the select
+    uint32_t bitmap_pre[kWideMaxS / 32 / kTkThreads];  // issued now, used later
 #pragma unroll
     for (int u = 0; u < kWideMaxS / 32 / kTkThreads; ++u) {
         const int w = tid + u * kTkThreads;
         bitmap_pre[u] = w < nw ? L.bitmap[rr * L.words + w] : 0u;
     }
-    const uint32_t need = (uint32_t)k - L.meta[rr * kMetaWords + 1];
+    constexpr int kPer2 = kDigits / kTkThreads;  // 4 second-digit bins per thread
+    uint32_t h2[kPer2], c2 = 0u;
+#pragma unroll
+    for (int j = 0; j < kPer2; ++j) {
+        h2[j] = L.hist2[rr * kDigits + tid * kPer2 + j];
+        c2 += h2[j];
+    }
+    const uint32_t need1 = (uint32_t)k - L.meta[rr * kMetaWords + 1];
     const uint2 *gcand = L.cand + rr * (size_t)S;
     const int nslices = (n + kWideSlice - 1) / kWideSlice;
     if (tid < 64) {  // offsets of the slices' candidate runs
@@ -440,19 +478,24 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
         }
         if (tid == 0) sm.offs[nslices] = run;
     }
-    __syncthreads();
+    {  // bin d2 of the need1-th largest candidate (histogram walked from the top)
+        uint32_t tot;
+        const uint32_t pre = block_excl_scan<kTkWaves>(c2, sm.scan, tot);  // also syncs offs
+        uint32_t running = tot - pre - c2;
+#pragma unroll
+        for (int j = kPer2 - 1; j >= 0; --j) {
+            const uint32_t before = running;
+            running += h2[j];
+            if (before < need1 && running >= need1) {
+                sm.d2 = (uint32_t)(tid * kPer2 + j);
+                sm.above2 = before;
+            }
+        }
+    }
     const int m = (int)sm.offs[nslices];
     const bool cached = m <= kCandCache;
-    if (cached) {  // one wave per slice run
-        for (int sl = tid >> 6; sl < nslices; sl += kTkWaves) {
-            const uint32_t o = sm.offs[sl], c = sm.offs[sl + 1] - o;
-            for (uint32_t j = tid & 63; j < c; j += 64) sm.cand[o + j] = gcand[sl * kWideSlice + j];
-        }
-        __syncthreads();
-    }
-    // candidate j: from LDS, or found by binary search over the slice offsets
-    auto cand_at = [&](int j) -> uint2 {
-        if (cached) return sm.cand[j];
+    // candidate j: slice found by binary search over the run offsets
+    auto cand_global = [&](int j) -> uint2 {
         int lo = 0, hi = nslices - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -461,58 +504,70 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
         }
         return gcand[lo * kWideSlice + (j - (int)sm.offs[lo])];
     };
-
-    // exact threshold among the candidates of digit d1
-    uint32_t tau, need_tau;
-    block_select([&](int j) -> uint32_t { return cand_at(j).x; }, m, need, sm.sel, tau, need_tau);
-    // Every candidate above tau is taken.  Of the candidates equal to tau the
-    // need_tau lowest positions are taken: the ties are compacted into LDS
-    // and each one counts how many ties sit at lower positions.  (A row with
-    // more ties than fit falls back to a second select on ~position.)
+    if (cached)  // every thread loads its candidates at once
+        for (int j = tid; j < m; j += kTkThreads) sm.cand[j] = cand_global(j);
     for (int w = tid; w < nw; w += kTkThreads) sm.bits[w] = bitmap_pre[w / kTkThreads];
-    uint32_t tie_count;
-    {
+    __syncthreads();
+    auto cand_at = [&](int j) -> uint2 { return cached ? sm.cand[j] : cand_global(j); };
+    const uint32_t d2 = sm.d2;
+    const uint32_t need2 = need1 - sm.above2;  // to take from bin d2
+    const uint32_t gsize = L.hist2[rr * kDigits + d2];
+
+    if (gsize <= (uint32_t)kMaxTies) {
+        // contiguous candidate segments per thread: take bins above d2, and
+        // gather bin d2 (in position order) for ranking
+        const int per = (m + kTkThreads - 1) / kTkThreads;
+        const int j0 = min(m, tid * per), j1 = min(m, j0 + per);
         uint32_t mine = 0u;
-        for (int j = tid; j < m; j += kTkThreads) mine += cand_at(j).x == tau ? 1u : 0u;
-        block_excl_scan<kTkWaves>(mine, sm.scan, tie_count);
-    }
-    const bool few_ties = tie_count <= kMaxTies;
-    uint32_t pos_cut = 0xffffffffu;
-    if (need_tau < tie_count && !few_ties) {
-        uint32_t tau2, need2;
-        block_select(
-            [&](int j) -> uint32_t {
-                const uint2 c = cand_at(j);
-                return c.x == tau ? ~c.y : 0u;
-            },
-            m, need_tau, sm.sel, tau2, need2);
-        pos_cut = ~tau2;  // ties with position <= pos_cut are taken
-    }
-    if (few_ties && need_tau < tie_count) {
-        uint32_t written = 0u;
-        for (int base = 0; base < m; base += kTkThreads) {  // compact the tie positions
-            const int j = base + tid;
-            const uint2 c = j < m ? cand_at(j) : make_uint2(0u, 0u);
-            const bool tie = j < m && c.x == tau;
-            uint32_t tot;
-            const uint32_t slot = block_flag_scan<kTkWaves>(tie, sm.scan, tot);
-            if (tie) sm.ties[written + slot] = c.y;
-            written += tot;
+        for (int j = j0; j < j1; ++j) {
+            const uint2 c = cand_at(j);
+            const uint32_t dg = (c.x >> 8) & (kDigits - 1);
+            if (dg > d2) atomicOr(&sm.bits[c.y >> 5], 1u << (c.y & 31));
+            mine += dg == d2 ? 1u : 0u;
+        }
+        uint32_t total;
+        uint32_t slot = block_excl_scan<kTkWaves>(mine, sm.scan, total);
+        for (int j = j0; j < j1; ++j) {
+            const uint2 c = cand_at(j);
+            if (((c.x >> 8) & (kDigits - 1)) == d2) sm.group[slot++] = c;
         }
         __syncthreads();
-        for (uint32_t a = tid; a < tie_count; a += kTkThreads) {
-            const uint32_t pa = sm.ties[a];
-            uint32_t below = 0u;
-            for (uint32_t b2 = 0; b2 < tie_count; ++b2) below += sm.ties[b2] < pa ? 1u : 0u;
-            if (below < need_tau) atomicOr(&sm.bits[pa >> 5], 1u << (pa & 31));
+        for (uint32_t a = tid; a < total; a += kTkThreads) {
+            const uint2 ca = sm.group[a];
+            uint32_t ahead = 0u;
+            for (uint32_t g = 0; g < total; ++g) {
+                const uint2 cg = sm.group[g];
+                ahead += (cg.x > ca.x || (cg.x == ca.x && cg.y < ca.y)) ? 1u : 0u;
+            }
+            if (ahead < need2) atomicOr(&sm.bits[ca.y >> 5], 1u << (ca.y & 31));
         }
-    }
-    __syncthreads();
-    for (int j = tid; j < m; j += kTkThreads) {
-        const uint2 c = cand_at(j);
-        const bool take = c.x > tau || (c.x == tau && (need_tau >= tie_count ||
-                                                       (!few_ties && c.y <= pos_cut)));
-        if (take) atomicOr(&sm.bits[c.y >> 5], 1u << (c.y & 31));
+    } else {
+        // general path: exact threshold among all candidates, ties by position
+        uint32_t tau, need_tau;
+        block_select([&](int j) -> uint32_t { return cand_at(j).x; }, m, need1, sm.sel, tau,
+                     need_tau);
+        uint32_t tie_count;
+        {
+            uint32_t mine = 0u;
+            for (int j = tid; j < m; j += kTkThreads) mine += cand_at(j).x == tau ? 1u : 0u;
+            block_excl_scan<kTkWaves>(mine, sm.scan, tie_count);
+        }
+        uint32_t pos_cut = 0xffffffffu;  // ties at positions <= pos_cut are taken
+        if (need_tau < tie_count) {
+            uint32_t tau2, need2b;
+            block_select(
+                [&](int j) -> uint32_t {
+                    const uint2 c = cand_at(j);
+                    return c.x == tau ? ~c.y : 0u;
+                },
+                m, need_tau, sm.sel, tau2, need2b);
+            pos_cut = ~tau2;
+        }
+        for (int j = tid; j < m; j += kTkThreads) {
+            const uint2 c = cand_at(j);
+            if (c.x > tau || (c.x == tau && c.y <= pos_cut))
+                atomicOr(&sm.bits[c.y >> 5], 1u << (c.y & 31));
+        }
     }
     __syncthreads();
 
@@ -550,7 +605,7 @@ size_t topk_workspace_bytes(int B, int T, int S, int) {
 // (the histograms and per-row words at the head of the workspace).
 size_t topk_clear_words(int B, int rows, int S) {
     if (!use_wide(B, rows, S)) return 0;
-    return (size_t)B * rows * (kDigits + kMetaWords);
+    return (size_t)B * rows * (2 * kDigits + kMetaWords);
 }
 
 hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *q_pos, int B,
@@ -561,7 +616,7 @@ hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *
         const int nrows = B * rows;
         if (!workspace_cleared)
             hipLaunchKernelGGL(topk_wide_clear_kernel,
-                               dim3(min(1024, ceil_div(nrows * (kDigits + kMetaWords), 256))),
+                               dim3(min(1024, ceil_div(nrows * (2 * kDigits + kMetaWords), 256))),
                                dim3(256), 0, stream, L.hist, L.meta, nrows);
         const dim3 g(ceil_div(S, kWideSlice), rows, B);
         hipLaunchKernelGGL(topk_wide_hist_kernel, g, dim3(kWideThreads), 0, stream, scores,

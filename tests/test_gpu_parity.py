@@ -377,17 +377,29 @@ def test_forward_short_last_chunk():
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("case", ["levels3", "all_equal", "k1", "kS", "short_rows", "neg"])
+@pytest.mark.parametrize("case", ["levels3", "all_equal", "k1", "kS", "short_rows", "neg",
+                                  "planted_ties", "wide_tie_group"])
 def test_topk_wide_path_edges(case):
     """Few wide rows take the split-row path: ties, degenerate budgets,
-    rows shorter than the budget and negative scores."""
+    rows shorter than the budget and negative scores.  planted_ties puts a
+    handful of copies of the k-th largest value across the row (a small tie
+    group straddling the threshold, ranked by position); wide_tie_group puts
+    thousands (the group exceeds the ranking buffer and takes the general
+    threshold search)."""
     B, S = 4, 40000
     k = {"k1": 1, "kS": S}.get(case, 2048)
     levels = {"levels3": 3, "all_equal": 1}.get(case)
-    sc = synth.random_scores((B, 1, S), seed=hash(case) % 1000, levels=levels)
+    sc = synth.random_scores((B, 1, S), seed=sum(map(ord, case)), levels=levels)
     if case == "neg":
         sc = -sc.abs() - 1.0
         sc[0, 0, 5] = -0.0
+    if case in ("planted_ties", "wide_tie_group"):
+        copies = 9 if case == "planted_ties" else 3000
+        g = np.random.default_rng(7)
+        for bb in range(B):
+            kth = torch.sort(sc[bb, 0], descending=True).values[k - 1]
+            where = torch.from_numpy(g.choice(S, copies, replace=False))
+            sc[bb, 0, where] = kth
     pos = torch.tensor([[S - 1], [S - 1], [20000], [S - 7]], dtype=torch.int32)
     if case == "short_rows":
         pos = torch.tensor([[10], [2047], [2048], [2049]], dtype=torch.int32)
