@@ -416,11 +416,18 @@ struct ResolveSmem {
     SelectSmem sel;
     uint32_t scan[kTkWaves];
     uint32_t offs[kMaxSlices + 1];
-    uint32_t d2, above2;
-    uint2 group[kMaxTies];          // (key, position) of the keys in bin (d1, d2)
+    uint32_t d2, above2, gsize, gcount;
+    uint2 group[kMaxTies];          // (key, position) of the candidates in bin d2
     uint32_t bits[kWideMaxS / 32];
     uint2 cand[kCandCache];
 };
+
+// Candidates a thread fetches before the second digit is known: kResolveSub
+// threads per slice, kResolveFetch each, so runs of up to 64 candidates a
+// slice arrive in a single round of loads.
+constexpr int kResolveSub = 16;
+constexpr int kResolveFetch = 4;
+constexpr int kResolvePairs = kMaxSlices * kResolveSub / kTkThreads;  // (slice, sub) pairs a thread
 
 // grid: x = row in chunk, y = batch
 //
@@ -446,7 +453,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
     }
     const size_t rr = (size_t)b * rows + r;
     const int nw = (n + 31) / 32;
-    uint32_t bitmap_pre[kWideMaxS / 32 / kTkThreads];  // issued now, used later
+    const int nslices = (n + kWideSlice - 1) / kWideSlice;
+    const uint2 *gcand = L.cand + rr * (size_t)S;
+
+    // ---- everything this thread needs from memory, issued up front
+    uint32_t bitmap_pre[kWideMaxS / 32 / kTkThreads];
 #pragma unroll
     for (int u = 0; u < kWideMaxS / 32 / kTkThreads; ++u) {
         const int w = tid + u * kTkThreads;
@@ -460,28 +471,26 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
         c2 += h2[j];
     }
     const uint32_t need1 = (uint32_t)k - L.meta[rr * kMetaWords + 1];
-    const uint2 *gcand = L.cand + rr * (size_t)S;
-    const int nslices = (n + kWideSlice - 1) / kWideSlice;
-    if (tid < 64) {  // offsets of the slices' candidate runs
-        uint32_t run = 0u;
-        for (int s0 = 0; s0 < nslices; s0 += 64) {
-            const int sl = s0 + tid;
-            uint32_t c = sl < nslices ? L.counts[rr * kMaxSlices + sl] : 0u;
-            uint32_t incl = c;
+    uint32_t cnt[kResolvePairs];
+    uint2 pre[kResolvePairs][kResolveFetch];
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t o = (uint32_t)__shfl_up((int)incl, off, 64);
-                if (tid >= off) incl += o;
-            }
-            if (sl < nslices) sm.offs[sl] = run + incl - c;
-            run += (uint32_t)__shfl((int)incl, 63, 64);
+    for (int v = 0; v < kResolvePairs; ++v) {
+        const int u = tid + v * kTkThreads;
+        const int sl = u / kResolveSub, sub = u % kResolveSub;
+        cnt[v] = sl < nslices ? L.counts[rr * kMaxSlices + sl] : 0u;
+#pragma unroll
+        for (int f = 0; f < kResolveFetch; ++f) {
+            const uint32_t j = (uint32_t)(sub + kResolveSub * f);
+            pre[v][f] = j < cnt[v] ? gcand[(size_t)sl * kWideSlice + j] : make_uint2(0u, 0u);
         }
-        if (tid == 0) sm.offs[nslices] = run;
     }
-    {  // bin d2 of the need1-th largest candidate (histogram walked from the top)
+
+    // ---- bin d2 of the need1-th largest candidate (histogram walked from the top)
+    if (tid == 0) sm.gcount = 0u;
+    {
         uint32_t tot;
-        const uint32_t pre = block_excl_scan<kTkWaves>(c2, sm.scan, tot);  // also syncs offs
-        uint32_t running = tot - pre - c2;
+        const uint32_t before_me = block_excl_scan<kTkWaves>(c2, sm.scan, tot);
+        uint32_t running = tot - before_me - c2;
 #pragma unroll
         for (int j = kPer2 - 1; j >= 0; --j) {
             const uint32_t before = running;
@@ -489,53 +498,43 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
             if (before < need1 && running >= need1) {
                 sm.d2 = (uint32_t)(tid * kPer2 + j);
                 sm.above2 = before;
+                sm.gsize = h2[j];
             }
         }
     }
-    const int m = (int)sm.offs[nslices];
-    const bool cached = m <= kCandCache;
-    // candidate j: slice found by binary search over the run offsets
-    auto cand_global = [&](int j) -> uint2 {
-        int lo = 0, hi = nslices - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (sm.offs[mid] <= (uint32_t)j) lo = mid;
-            else hi = mid - 1;
-        }
-        return gcand[lo * kWideSlice + (j - (int)sm.offs[lo])];
-    };
-    if (cached)  // every thread loads its candidates at once
-        for (int j = tid; j < m; j += kTkThreads) sm.cand[j] = cand_global(j);
     for (int w = tid; w < nw; w += kTkThreads) sm.bits[w] = bitmap_pre[w / kTkThreads];
     __syncthreads();
-    auto cand_at = [&](int j) -> uint2 { return cached ? sm.cand[j] : cand_global(j); };
     const uint32_t d2 = sm.d2;
     const uint32_t need2 = need1 - sm.above2;  // to take from bin d2
-    const uint32_t gsize = L.hist2[rr * kDigits + d2];
+    const uint32_t gsize = sm.gsize;
 
     if (gsize <= (uint32_t)kMaxTies) {
-        // contiguous candidate segments per thread: take bins above d2, and
-        // gather bin d2 (in position order) for ranking
-        const int per = (m + kTkThreads - 1) / kTkThreads;
-        const int j0 = min(m, tid * per), j1 = min(m, j0 + per);
-        uint32_t mine = 0u;
-        for (int j = j0; j < j1; ++j) {
-            const uint2 c = cand_at(j);
+        auto visit = [&](const uint2 c) {
             const uint32_t dg = (c.x >> 8) & (kDigits - 1);
             if (dg > d2) atomicOr(&sm.bits[c.y >> 5], 1u << (c.y & 31));
-            mine += dg == d2 ? 1u : 0u;
-        }
-        uint32_t total;
-        uint32_t slot = block_excl_scan<kTkWaves>(mine, sm.scan, total);
-        for (int j = j0; j < j1; ++j) {
-            const uint2 c = cand_at(j);
-            if (((c.x >> 8) & (kDigits - 1)) == d2) sm.group[slot++] = c;
+            else if (dg == d2) {
+                const uint32_t slot = atomicAdd(&sm.gcount, 1u);
+                if (slot < (uint32_t)kMaxTies) sm.group[slot] = c;
+            }
+        };
+#pragma unroll
+        for (int v = 0; v < kResolvePairs; ++v) {
+            const int u = tid + v * kTkThreads;
+            const int sl = u / kResolveSub, sub = u % kResolveSub;
+#pragma unroll
+            for (int f = 0; f < kResolveFetch; ++f)
+                if ((uint32_t)(sub + kResolveSub * f) < cnt[v]) visit(pre[v][f]);
+            // long runs (many candidates in one slice): the rest, one by one
+            for (uint32_t j = (uint32_t)(sub + kResolveSub * kResolveFetch); j < cnt[v];
+                 j += kResolveSub)
+                visit(gcand[(size_t)sl * kWideSlice + j]);
         }
         __syncthreads();
-        for (uint32_t a = tid; a < total; a += kTkThreads) {
+        // rank inside the group: larger key first, then lower position
+        for (uint32_t a = tid; a < gsize; a += kTkThreads) {
             const uint2 ca = sm.group[a];
             uint32_t ahead = 0u;
-            for (uint32_t g = 0; g < total; ++g) {
+            for (uint32_t g = 0; g < gsize; ++g) {
                 const uint2 cg = sm.group[g];
                 ahead += (cg.x > ca.x || (cg.x == ca.x && cg.y < ca.y)) ? 1u : 0u;
             }
@@ -543,6 +542,39 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
         }
     } else {
         // general path: exact threshold among all candidates, ties by position
+        if (tid < 64) {  // offsets of the slices' candidate runs
+            uint32_t run = 0u;
+            for (int s0 = 0; s0 < nslices; s0 += 64) {
+                const int sl = s0 + tid;
+                uint32_t c = sl < nslices ? L.counts[rr * kMaxSlices + sl] : 0u;
+                uint32_t incl = c;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t o = (uint32_t)__shfl_up((int)incl, off, 64);
+                    if (tid >= off) incl += o;
+                }
+                if (sl < nslices) sm.offs[sl] = run + incl - c;
+                run += (uint32_t)__shfl((int)incl, 63, 64);
+            }
+            if (tid == 0) sm.offs[nslices] = run;
+        }
+        __syncthreads();
+        const int m = (int)sm.offs[nslices];
+        const bool cached = m <= kCandCache;
+        auto cand_global = [&](int j) -> uint2 {  // slice by binary search over the runs
+            int lo = 0, hi = nslices - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (sm.offs[mid] <= (uint32_t)j) lo = mid;
+                else hi = mid - 1;
+            }
+            return gcand[lo * kWideSlice + (j - (int)sm.offs[lo])];
+        };
+        if (cached) {
+            for (int j = tid; j < m; j += kTkThreads) sm.cand[j] = cand_global(j);
+            __syncthreads();
+        }
+        auto cand_at = [&](int j) -> uint2 { return cached ? sm.cand[j] : cand_global(j); };
         uint32_t tau, need_tau;
         block_select([&](int j) -> uint32_t { return cand_at(j).x; }, m, need1, sm.sel, tau,
                      need_tau);
