@@ -15,6 +15,8 @@
 //    as the A operand, each 32-key tile of keys is the B operand.
 //  * indexer_generic_kernel: any H_I*d_I <= 16384 and any index dtype, plain
 //    fp32 FMA (small shapes such as the n=16 running example).
+#include <type_traits>
+
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -341,6 +343,11 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
 // operand reads are free of bank conflicts.
 constexpr int kPfRows = 8;     // query rows (waves) per workgroup
 constexpr int kPfKeys = 64;    // keys per LDS tile
+// Waves 0..6 issue the tile loads; wave 7 writes every row's scores to
+// memory.  A wave's s_waitcnt counts its loads and stores together, so the
+// loaders must never have stores outstanding (waiting for this tile's loads
+// would also wait for the stores), and the storing wave never waits.
+constexpr int kPfLoaders = kPfRows - 1;
 
 template <bool Fp8>
 struct PrefillTile {
@@ -348,24 +355,30 @@ struct PrefillTile {
     static constexpr int pitch = row_bytes + 16;
     static constexpr int slots = pitch / 16;                           // 16-byte slots a row
     static constexpr int loads = (kPfKeys * slots + 63) / 64;          // wave loads a tile
-    static constexpr int bytes = loads * 1024;                         // tile buffer size
+    static constexpr int per_loader = (loads + kPfLoaders - 1) / kPfLoaders;
+    // every loader issues per_loader loads a tile (the surplus ones land in
+    // the padding at the end of the buffer), so wait counts are static
+    static constexpr int bytes = per_loader * kPfLoaders * 1024;
 };
+constexpr int kPfRing = 4;   // tile buffers; loads run three tiles ahead
 
 template <bool Fp8>
 __device__ __forceinline__ void prefill_issue_tile(uint8_t *buf, const uint8_t *kb_base, int s0,
                                                    int S, int wave, int lane) {
     typedef PrefillTile<Fp8> Pt;
     typedef __attribute__((address_space(3))) void *lds_ptr;
-    for (int j = wave; j < Pt::loads; j += kPfRows) {
+#pragma unroll
+    for (int m = 0; m < Pt::per_loader; ++m) {
+        const int j = wave + kPfLoaders * m;
         const int q = 64 * j + lane;
         const int row = q / Pt::slots;
         const int piece = q - row * Pt::slots;
         int key = s0 + row;
         key = key < S ? key : 0;  // rows past the cache load row 0; never used
-        const uint8_t *src =
-            kb_base + (size_t)key * Pt::row_bytes + (piece * 16 < Pt::row_bytes ? piece * 16 : 0);
-        if (q < kPfKeys * Pt::slots)
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr)(buf + 1024 * j), 16, 0, 0);
+        const bool real = q < kPfKeys * Pt::slots && piece * 16 < Pt::row_bytes;
+        const uint8_t *src = kb_base + (size_t)(real ? key : s0) * Pt::row_bytes +
+                             (real ? piece * 16 : 0);
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(buf + 1024 * j), 16, 0, 0);
     }
 }
 
@@ -382,12 +395,15 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
     constexpr int EB = Tr::elem_bytes;
     constexpr int KS = Tr::ksteps;
     constexpr int DPS = Tr::dims_per_step;
-    // Two separate LDS objects, named statically in a loop unrolled by two:
-    // the compiler can then tell that the direct-to-LDS loads of the next
-    // tile do not alias the reads of this one, and does not wait for them.
+    // Four separate LDS objects, named statically in a loop unrolled by four:
+    // the compiler can then tell that the direct-to-LDS loads of later tiles
+    // do not alias the reads of this one, and does not wait for them.
     __shared__ __align__(16) uint8_t tile0[Pt::bytes];
     __shared__ __align__(16) uint8_t tile1[Pt::bytes];
+    __shared__ __align__(16) uint8_t tile2[Pt::bytes];
+    __shared__ __align__(16) uint8_t tile3[Pt::bytes];
     __shared__ int tmax_s[kPfRows];
+    __shared__ float staged[2][kPfRows][kPfKeys];  // one tile's scores of all rows
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -418,7 +434,15 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
     if (k_begin >= k_hi) return;             // uniform over the workgroup
 
     const uint8_t *kb_base = k_idx + (size_t)b * S * Pt::row_bytes;
-    prefill_issue_tile<Fp8>(tile0, kb_base, k_begin, S, wave, lane);
+    const int last_tile = k_begin + (k_hi - 1 - k_begin) / kPfKeys * kPfKeys;
+    auto issue = [&](uint8_t *buf, int s_tile) {  // past the last tile: reload the last
+        prefill_issue_tile<Fp8>(buf, kb_base, min(s_tile, last_tile), S, wave, lane);
+    };
+    if (wave < kPfLoaders) {
+        issue(tile0, k_begin);
+        issue(tile1, k_begin + kPfKeys);
+        issue(tile2, k_begin + 2 * kPfKeys);
+    }
 
     const size_t qrow = ((size_t)b * T + i) * kIdxHeads;
     Op qa[2][KS];
@@ -436,35 +460,85 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
             wr[tl][rg] = w[qrow + tl * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
     const int t_hi = min(k_end, t + 1);  // this row's causal end inside the chunk
 
-    auto step = [&](const int s0, const uint8_t *cur, uint8_t *next) {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of this tile have landed
-        __syncthreads();                // ... and every other wave's; `next` is free
-        if (s0 + kPfKeys < k_hi)
-            prefill_issue_tile<Fp8>(next, kb_base, s0 + kPfKeys, S, wave, lane);
+    // wave 7: scores of the tile starting at s_prev (staging buffer sb) to memory
+    auto flush = [&](const int s_prev, const int sb) {
+        const int key = s_prev + lane;
+#pragma unroll
+        for (int v = 0; v < kPfRows; ++v) {
+            const int tv = tmax_s[v];  // -1 for rows past the block's end
+            if (key < min(k_end, tv + 1))
+                scores[(size_t)b * batch_stride + (size_t)(rb * kPfRows + v) * S + key] =
+                    staged[sb][v][lane];
+        }
+    };
+    // loads of this tile landed once at most two tiles' loads are outstanding
+    constexpr int kAhead = 2 * Pt::per_loader;
+    constexpr int kWaitThis = (kAhead & 15) | ((kAhead >> 4) << 14) | 0x70 | 0xF00;
+    // The storing wave and the loaders run separate copies of the loop, so the
+    // compiler's wait counts on the loaders never see a store.
+    auto step = [&](auto storer, const int s0, const uint8_t *cur, uint8_t *ahead3,
+                    const int sb) {
+        if (!storer) __builtin_amdgcn_s_waitcnt(kWaitThis);
+        lds_barrier();  // ... every loader's; ahead3 (tile s0 - 64) and staged[sb] are free
+        if (storer) {
+            if (s0 > k_begin) flush(s0 - kPfKeys, sb ^ 1);
+        } else {
+            issue(ahead3, s0 + 3 * kPfKeys);
+        }
         if (s0 < t_hi) {
+            // both 32-key halves of the tile: the products of the second half
+            // are interleaved with the ReLU-weighted reduction of the first,
+            // so the matrix pipe stays busy while the VALU works
+            Op kb[2][KS];
 #pragma unroll
-            for (int st = 0; st < kPfKeys / 32; ++st) {
-                const uint8_t *brow = cur + (st * 32 + col) * Pt::pitch + 64 * half * EB;
-                Op kb[KS];
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) kb[ks] = Tr::load(brow + ks * DPS * EB);
-                f32x16 acc0 = {}, acc1 = {};
+                for (int ks = 0; ks < KS; ++ks)
+                    kb[st][ks] = Tr::load(cur + (st * 32 + col) * Pt::pitch + 64 * half * EB +
+                                          ks * DPS * EB);
+            f32x16 acc[2][2];
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                acc[st][0] = f32x16{};
+                acc[st][1] = f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    acc0 = Tr::mma(qa[0][ks], kb[ks], acc0);
-                    acc1 = Tr::mma(qa[1][ks], kb[ks], acc1);
+                    acc[st][0] = Tr::mma(qa[0][ks], kb[st][ks], acc[st][0]);
+                    acc[st][1] = Tr::mma(qa[1][ks], kb[st][ks], acc[st][1]);
                 }
-                const float part = weighted_relu_sum(acc0, acc1, wr);
-                const float other = __shfl_xor(part, 32, 64);
-                const int key = s0 + st * 32 + col;
-                if (half == 0 && key < t_hi) out[key] = part + other;
+            }
+            const float part0 = weighted_relu_sum(acc[0][0], acc[0][1], wr);
+            const float part1 = weighted_relu_sum(acc[1][0], acc[1][1], wr);
+            constexpr int kMm = 2 * KS;                 // products per half tile
+            constexpr int kVa = (72 + kMm - 1) / kMm;   // reduction ops between them
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);  // operand reads
+            __builtin_amdgcn_sched_group_barrier(0x008, kMm, 0);     // first half
+#pragma unroll
+            for (int g = 0; g < kMm; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);
+            }
+            const float other0 = __shfl_xor(part0, 32, 64);
+            const float other1 = __shfl_xor(part1, 32, 64);
+            if (half == 0) {
+                staged[sb][wave][col] = part0 + other0;
+                staged[sb][wave][col + 32] = part1 + other1;
             }
         }
     };
-    for (int s0 = k_begin; s0 < k_hi; s0 += 2 * kPfKeys) {
-        step(s0, tile0, tile1);
-        if (s0 + kPfKeys < k_hi) step(s0 + kPfKeys, tile1, tile0);
-    }
+    auto walk = [&](auto storer) {
+        for (int s0 = k_begin; s0 < k_hi; s0 += kPfRing * kPfKeys) {
+            step(storer, s0, tile0, tile3, 0);
+            if (s0 + kPfKeys < k_hi) step(storer, s0 + kPfKeys, tile1, tile0, 1);
+            if (s0 + 2 * kPfKeys < k_hi) step(storer, s0 + 2 * kPfKeys, tile2, tile1, 0);
+            if (s0 + 3 * kPfKeys < k_hi) step(storer, s0 + 3 * kPfKeys, tile3, tile2, 1);
+        }
+    };
+    if (wave == kPfRows - 1) walk(std::true_type{});
+    else walk(std::false_type{});
+    __builtin_amdgcn_s_waitcnt(0);  // the surplus loads of the last steps
+    lds_barrier();
+    if (wave == kPfRows - 1) flush(last_tile, ((last_tile - k_begin) / kPfKeys) & 1);
 }
 
 // ------------------------------------------------------------- generic ----
