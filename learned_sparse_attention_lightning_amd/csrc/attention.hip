@@ -129,8 +129,11 @@ hipError_t launch_gather(const dsa_attn_desc_t &d, const void *q, const void *kv
 
 }  // namespace
 
-size_t attention_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int, int k) {
+size_t attention_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int S, int k) {
     if (mla_fast_path(d)) return mla_workspace_bytes(d, B, T, k);
+    // the masked-dense MHA form keeps a selection bitmap; a launch covers up
+    // to T rows (dsa_forward passes its chunk)
+    if (mha_dense_path(d, T, S, k)) return mha_workspace_bytes(B, T, S);
     return 0;
 }
 
@@ -140,6 +143,9 @@ hipError_t launch_attention(const dsa_attn_desc_t &d, const void *q, const void 
                             hipStream_t stream) {
     if (mla_fast_path(d))
         return launch_mla(d, q, kv, idx, B, T, S, row0, rows, k, out, lse, workspace, stream);
+    if (mha_dense_path(d, rows, S, k) && workspace)
+        return launch_mha_dense(d, q, kv, v, idx, B, T, S, row0, rows, k, out, lse, workspace,
+                                stream);
     const bool in_bf16 = d.dtype == DSA_BF16;
     const bool out_bf16 = d.out_dtype == DSA_BF16;
     if (in_bf16 && out_bf16)

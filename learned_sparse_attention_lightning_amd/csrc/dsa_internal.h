@@ -102,6 +102,12 @@ hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *
                        int T, int S, int row0, int rows, int k, int32_t *idx, void *workspace,
                        bool workspace_cleared, hipStream_t stream);
 
+bool mha_dense_path(const dsa_attn_desc_t &d, int rows, int S, int k);
+size_t mha_workspace_bytes(int B, int rows, int S);
+hipError_t launch_mha_dense(const dsa_attn_desc_t &d, const void *q, const void *kv,
+                            const void *v, const int32_t *idx, int B, int T, int S, int row0,
+                            int rows, int k, void *out, float *lse, void *workspace,
+                            hipStream_t stream);
 bool mla_fast_path(const dsa_attn_desc_t &d);
 size_t mla_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int k);
 hipError_t launch_mla(const dsa_attn_desc_t &d, const void *q, const void *kv,

@@ -214,6 +214,35 @@ def test_attention_mha_bf16(out_dtype):
     assert err <= (TOL["bf16"] if out_dtype == "bf16" else 1e-4), err
 
 
+@pytest.mark.parametrize("B,T,S,k,d,out_dtype", [
+    (1, 70, 70, 64, 128, "bf16"),    # ragged query block, most of the causal prefix selected
+    (2, 200, 256, 96, 64, "f32"),    # d = 64, fp32 output, rows at the end of a longer cache
+    (1, 96, 96, 96, 128, "f32"),     # every causal key selected (dense causal)
+])
+def test_attention_mha_dense(B, T, S, k, d, out_dtype):
+    """Masked-dense MFMA form of the MHA attention (k >= S/4, >= 32 rows):
+    selections in arbitrary order with holes, an empty row, lse."""
+    w = configs.get("c1").with_(name="mha-dense", B=B, T=T, S=S, index_topk=k, num_heads=3,
+                                d_qk=d, d_v=d, out_dtype=out_dtype, scale=1.0 / math.sqrt(d))
+    x = synth.make_inputs(w, device=DEV, seed=T + k)
+    sc = synth.random_scores((B, T, S), seed=T)
+    ref_idx = np.ascontiguousarray(oracle.topk(sc, k)[..., ::-1])
+    ref_idx[0, 5, :7] = -1      # holes
+    ref_idx[0, 3, :] = -1       # nothing selected
+    idx = torch.from_numpy(ref_idx).to(DEV)
+    lse = torch.empty((B, T, w.num_heads), dtype=torch.float32, device=DEV)
+    _say(f"mha dense B={B} T={T} S={S} k={k} d={d} out={out_dtype}")
+    out = dsa.dsa_sparse_attention(dsa.desc_for(w), x["q"], x["kv"], x["v"], idx, lse=lse)
+    assert torch.all(out[0, 3] == 0) and torch.all(torch.isneginf(lse[0, 3]))
+    keep = [r for r in range(T) if r != 3]
+    ref, ref_lse = oracle.sparse_attention("mha", x["q"], x["kv"], x["v"], ref_idx, w.scale,
+                                           with_lse=True)
+    err = max_abs_err(out[:, keep], ref[:, keep])
+    _say(f"mha dense: max-abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.abs(lse[:, keep].cpu().numpy() - ref_lse[:, keep]).max() < 1e-3
+
+
 def test_attention_mla_small_and_edges():
     w = configs.get("c2").with_(name="mla-small", B=2, T=600, S=600, index_topk=64,
                                 num_heads=16)
