@@ -51,6 +51,19 @@ __device__ __forceinline__ bf16x4 lds_tr16(const uint8_t *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4)(p));
 }
 
+// 4 consecutive outputs (16-byte aligned as fp32, 8-byte as bf16)
+template <typename Tout>
+__device__ __forceinline__ void store_out4(Tout *p, f32x4 v);
+template <>
+__device__ __forceinline__ void store_out4<float>(float *p, f32x4 v) {
+    *reinterpret_cast<f32x4 *>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store_out4<uint16_t>(uint16_t *p, f32x4 v) {
+    const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *reinterpret_cast<bf16x4 *>(p) = b;
+}
+
 template <typename Tout>
 __device__ __forceinline__ void store_out(Tout *p, float v);
 template <>
@@ -86,6 +99,7 @@ constexpr int kPPitch = kKt * 2 + 16;          // 80 bytes per head row of P
 constexpr int kHalfSteps = kKsteps / 2;          // 18
 constexpr int kMaxSplit = 4096;                  // entries of one split (LDS table)
 constexpr int kThreads = 512;
+constexpr int kOutPitch = 136;  // floats per head row of the output staging block
 // staged 16-byte loads per lane per tile: slot q = 512 m + 64 w + lane; the
 // S waves (w < 4) also take m = 4, which covers slots 2048..2303
 constexpr int kLoadsS = 5;
@@ -99,12 +113,14 @@ struct __align__(16) MlaSmem {
     f32x4 part[2][4][64];               // kh = 1 halves of S, one per head tile,
                                         // registers 4j..4j+3 of lane l at [j][l]
     float corr[2][kHg];
-    float fin_l[kHg], fin_m[kHg];
+    float fin_l[kHg];                   // 1 / softmax denominator per head
 };
 
 // Issue the global loads of this wave's share of tile `t` (entries
-// 32t..32t+31 of the split).  Entries past the split, and masked ones, read
-// row 0 of the sequence: the loads stay unconditional, their data unused.
+// 32t..32t+31 of the split).  Entries past the split re-read the split's last
+// row (just fetched, so a cache hit rather than a cold memory access that the
+// end of the kernel would wait for) and masked ones read row 0: the loads stay
+// unconditional, their data unused.
 template <int NL>
 __device__ __forceinline__ void stage_load(u32x4 (&r)[NL], const MlaSmem &sm, int len,
                                               int t, const uint8_t *__restrict__ lat_b,
@@ -116,7 +132,7 @@ __device__ __forceinline__ void stage_load(u32x4 (&r)[NL], const MlaSmem &sm, in
         const int c = q - row * kSlotsRow;
         const int e = t * kKt + row;
         const int sel = sm.idx[min(e, len - 1)];
-        const uint32_t src_row = (uint32_t)(e < len ? max(sel, 0) : 0);
+        const uint32_t src_row = (uint32_t)max(sel, 0);
         r[m] = *reinterpret_cast<const u32x4 *>(lat_b + src_row * (uint64_t)(kDqk * 2) + c * 16);
     }
 }
@@ -297,19 +313,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             s_step(it, stg[0]);
             if (it + 1 < ntiles) s_step(it + 1, stg[1]);
         }
-        __syncthreads();
+        lds_barrier();  // loads past the last tile may still be in flight
+        float l_all = 0.0f;
         if (kh == 0) {
-            const float l_all = l_run + __shfl_xor(l_run, 32, 64);  // both key halves
-            if (half == 0) {
-                sm.fin_l[ht * 32 + l32] = l_all;
-                sm.fin_m[ht * 32 + l32] = m_run;
-            }
+            l_all = l_run + __shfl_xor(l_run, 32, 64);  // both key halves
+            if (half == 0) sm.fin_l[ht * 32 + l32] = l_all > 0.0f ? 1.0f / l_all : 0.0f;
         }
-        __syncthreads();
+        lds_barrier();  // loads past the last tile may still be in flight
         if (kh == 0 && half == 0) {
             const int hl = ht * 32 + l32;
-            const float l = sm.fin_l[hl];
-            const float ls = l > 0.0f ? (sm.fin_m[hl] + log2f(l)) * 0.6931471805599453f : -INFINITY;
+            const float ls = l_all > 0.0f ? (m_run + log2f(l_all)) * 0.6931471805599453f : -INFINITY;
             if (splits == 1) {
                 if (lse) lse[rowq * H + head0 + hl] = ls;
             } else {
@@ -392,35 +405,58 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             o_step(it, stg[0]);
             if (it + 1 < ntiles) o_step(it + 1, stg[1]);
         }
-        __syncthreads();
-        __syncthreads();
+        lds_barrier();  // loads past the last tile may still be in flight
+        lds_barrier();  // loads past the last tile may still be in flight
+        // Output through LDS (the tile ring is free now): the accumulator
+        // layout gives a lane one dim of 16 heads, memory wants rows of dims;
+        // each 32-head half goes to a [head][dim] block (pitch 136 floats, so
+        // the two lane halves write disjoint banks) and leaves in 16-byte
+        // pieces, 4 consecutive dims a lane.
+        float *blk = reinterpret_cast<float *>(sm.kv[0]) + d * (32 * kOutPitch);
+        float inv[2][16];  // 1/l per head, all read before any block write
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) {
+                inv[a][rg] = sm.fin_l[a * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
+            }
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
 #pragma unroll
             for (int rg = 0; rg < 16; ++rg) {
-                const int hl = a * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3);
-                const float l = sm.fin_l[hl];
-                const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+                const int hr = 8 * (rg >> 2) + 4 * half + (rg & 3);  // head within the half
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int dd = dv0 + 32 * c + l32;
-                    const float v = o[a][c][rg] * inv;
-                    if (splits == 1)
-                        store_out(out + (rowq * H + head0 + hl) * kDv + dd, v);
-                    else
-                        o_part[((prow * splits + split) * H + head0 + hl) * kDv + dd] = v;
-                }
+                for (int c = 0; c < 4; ++c)
+                    blk[hr * kOutPitch + 32 * c + l32] = o[a][c][rg] * inv[a][rg];
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {  // 32 heads x 128 dims = 16 rounds of 64 x 4
+                const int hr = 2 * m + half;
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(blk + hr * kOutPitch + 4 * l32);
+                const int hl = a * 32 + hr;
+                const int dd = dv0 + 4 * l32;
+                if (splits == 1)
+                    store_out4(out + (rowq * H + head0 + hl) * kDv + dd, v);
+                else
+                    *reinterpret_cast<f32x4 *>(
+                        o_part + ((prow * splits + split) * H + head0 + hl) * kDv + dd) = v;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();  // block reused by the second half
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
 }
 
 // Merge split partials: out = sum_s exp(lse_s - lse) o_s, lse = log sum exp lse_s.
 // Two heads per workgroup, 4 dims per thread; the splits are read in batches
-// of 8 whose loads are all issued before any is used (clamped indices, zero
-// weight past the last split), so a row costs a few memory latencies rather
-// than one per split.
-constexpr int kCombineBatch = 8;
+// of 16 whose loads are all issued before any is used (clamped indices, zero
+// weight past the last split), merged online across batches, so a row costs
+// one memory latency per 16 splits.
+constexpr int kCombineBatch = 16;
 
 template <typename Tout>
 __global__ __launch_bounds__(256) void mla_combine_kernel(
@@ -433,16 +469,8 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(
     const size_t rowq = (size_t)b * T + row0 + r;
     const size_t prow = (size_t)b * rows + r;  // row of the launch's split partials
     const float *lp = lse_part + prow * splits * H + h;  // split s at lp[s * H]
-    float mx = -INFINITY;
-    for (int s0 = 0; s0 < splits; s0 += kCombineBatch) {
-        float ls[kCombineBatch];
-#pragma unroll
-        for (int j = 0; j < kCombineBatch; ++j) ls[j] = lp[(size_t)min(s0 + j, splits - 1) * H];
-#pragma unroll
-        for (int j = 0; j < kCombineBatch; ++j) mx = fmaxf(mx, ls[j]);
-    }
     const float *op = o_part + (prow * splits * H + h) * kDv + d;  // split s at op[s * H * kDv]
-    float wsum = 0.0f;
+    float mx = -INFINITY, wsum = 0.0f;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int s0 = 0; s0 < splits; s0 += kCombineBatch) {
         float ls[kCombineBatch];
@@ -453,9 +481,19 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(
             ls[j] = lp[sc * H];
             ov[j] = *reinterpret_cast<const f32x4 *>(op + sc * H * kDv);
         }
+        float bmx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j)
+            if (s0 + j < splits) bmx = fmaxf(bmx, ls[j]);
+        const float nmx = fmaxf(mx, bmx);
+        if (nmx == -INFINITY) continue;  // nothing selected so far
+        const float rs = mx == -INFINITY ? 0.0f : __expf(mx - nmx);
+        wsum *= rs;
+        acc *= rs;
+        mx = nmx;
 #pragma unroll
         for (int j = 0; j < kCombineBatch; ++j) {
-            const float wgt = (s0 + j < splits && mx != -INFINITY) ? __expf(ls[j] - mx) : 0.0f;
+            const float wgt = s0 + j < splits ? __expf(ls[j] - mx) : 0.0f;
             wsum += wgt;
             acc += wgt * ov[j];
         }
