@@ -100,10 +100,11 @@ constexpr int kHalfSteps = kKsteps / 2;          // 18
 constexpr int kMaxSplit = 4096;                  // entries of one split (LDS table)
 constexpr int kThreads = 512;
 constexpr int kOutPitch = 136;  // floats per head row of the output staging block
-// staged 16-byte loads per lane per tile: slot q = 512 m + 64 w + lane; the
-// S waves (w < 4) also take m = 4, which covers slots 2048..2303
+// Staged 16-byte loads per lane per tile: slot q = 512 m + 64 w + lane; the
+// S waves (w < 4) also take m = 4, which covers slots 2048..2303.
 constexpr int kLoadsS = 5;
 constexpr int kLoadsPV = 4;
+constexpr int kStageStride = 512;
 static_assert(kLoadsPV * kThreads + 4 * 64 == kTileSlots, "staging covers a tile");
 
 struct __align__(16) MlaSmem {
@@ -114,20 +115,23 @@ struct __align__(16) MlaSmem {
                                         // registers 4j..4j+3 of lane l at [j][l]
     float corr[2][kHg];
     float fin_l[kHg];                   // 1 / softmax denominator per head
+    int32_t resc[2][2];                 // per tile parity and head tile: any corr != 1
 };
+static_assert(offsetof(MlaSmem, corr) % 16 == 0, "corr is read in 16-byte pieces");
 
 // Issue the global loads of this wave's share of tile `t` (entries
 // 32t..32t+31 of the split).  Entries past the split re-read the split's last
 // row (just fetched, so a cache hit rather than a cold memory access that the
 // end of the kernel would wait for) and masked ones read row 0: the loads stay
 // unconditional, their data unused.
+// Slot of load m: q0 + stride * m.
 template <int NL>
 __device__ __forceinline__ void stage_load(u32x4 (&r)[NL], const MlaSmem &sm, int len,
                                               int t, const uint8_t *__restrict__ lat_b,
-                                              int wave, int lane) {
+                                              int q0, int stride) {
 #pragma unroll
     for (int m = 0; m < NL; ++m) {
-        const int q = 512 * m + 64 * wave + lane;
+        const int q = q0 + stride * m;
         const int row = q / kSlotsRow;
         const int c = q - row * kSlotsRow;
         const int e = t * kKt + row;
@@ -138,11 +142,11 @@ __device__ __forceinline__ void stage_load(u32x4 (&r)[NL], const MlaSmem &sm, in
 }
 
 template <int NL>
-__device__ __forceinline__ void stage_store(const u32x4 (&r)[NL], uint8_t *tile, int wave,
-                                               int lane) {
+__device__ __forceinline__ void stage_store(const u32x4 (&r)[NL], uint8_t *tile, int q0,
+                                               int stride) {
 #pragma unroll
     for (int m = 0; m < NL; ++m) {
-        const int q = 512 * m + 64 * wave + lane;
+        const int q = q0 + stride * m;
         const int row = q / kSlotsRow;
         const int c = q - row * kSlotsRow;
         *reinterpret_cast<u32x4 *>(tile + row * kRowPitch + c * 16) = r[m];
@@ -195,10 +199,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     if (wave < 4) {
         // ======================= S waves =======================
         const int ht = wave & 1, kh = wave >> 1;
+        const int q0 = 64 * wave + lane;  // staging slots
+        constexpr int qs = kStageStride;
         u32x4 stg[2][kLoadsS];
-        stage_load(stg[0], sm, len, 0, lat_b, wave, lane);
+        stage_load(stg[0], sm, len, 0, lat_b, q0, qs);
         __builtin_amdgcn_sched_barrier(0);
-        stage_load(stg[1], sm, len, 1, lat_b, wave, lane);
+        stage_load(stg[1], sm, len, 1, lat_b, q0, qs);
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 qb[kHalfSteps];
         {
@@ -208,11 +214,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             for (int ks = 0; ks < kHalfSteps; ++ks)
                 qb[ks] = *reinterpret_cast<const bf16x8 *>(qp + ks * 16);
         }
-        stage_store(stg[0], sm.kv[0], wave, lane);
-        stage_store(stg[1], sm.kv[1], wave, lane);
-        stage_load(stg[0], sm, len, 2, lat_b, wave, lane);
+        stage_store(stg[0], sm.kv[0], q0, qs);
+        stage_store(stg[1], sm.kv[1], q0, qs);
+        stage_load(stg[0], sm, len, 2, lat_b, q0, qs);
         __builtin_amdgcn_sched_barrier(0);
-        stage_load(stg[1], sm, len, 3, lat_b, wave, lane);
+        stage_load(stg[1], sm, len, 3, lat_b, q0, qs);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < kHalfSteps; ++ks) asm volatile("" ::"v"(qb[ks]));
@@ -221,17 +227,23 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         // This wave's half of S^T.  All 18 A fragments are read before the
         // first product, so the LDS latency is paid once per tile rather than
         // once per pair of products.
-        auto s_half = [&](const uint8_t *kvt) -> f32x16 {
+        auto s_read = [&](const uint8_t *kvt, bf16x8 (&af)[kHalfSteps]) {
             const uint8_t *arow = kvt + l32 * kRowPitch + 16 * half + 32 * kHalfSteps * kh;
-            bf16x8 af[kHalfSteps];
 #pragma unroll
             for (int ks = 0; ks < kHalfSteps; ++ks) af[ks] = lds_b128(arow + ks * 32);
-            __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
+        };
+        auto s_mfma = [&](const bf16x8 (&af)[kHalfSteps]) -> f32x16 {
             f32x16 acc = {};
 #pragma unroll
             for (int ks = 0; ks < kHalfSteps; ++ks)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qb[ks], acc, 0, 0, 0);
             return acc;
+        };
+        auto s_half = [&](const uint8_t *kvt) -> f32x16 {
+            bf16x8 af[kHalfSteps];
+            s_read(kvt, af);
+            __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
+            return s_mfma(af);
         };
         auto put_part = [&](const f32x16 &acc) {
 #pragma unroll
@@ -247,17 +259,29 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
                 for (int e = 0; e < 4; ++e) acc[4 * j + e] += o[e];
             }
         };
-        auto softmax = [&](int tile, f32x16 acc) {  // kh = 0: full S^T in acc
-            const int32_t *selt = sm.idx + tile * kKt;
+        // Bit j of the result: entry j of the tile is a selected row.
+        auto tile_mask = [&](int tile) -> uint32_t {
+            return (uint32_t)__ballot(sm.idx[tile * kKt + l32] >= 0);
+        };
+        auto softmax = [&](int tile, f32x16 acc, uint32_t vmask) {  // kh = 0: full S^T
             float tmax = -INFINITY;
+            if (vmask == 0xffffffffu) {
 #pragma unroll
-            for (int rg = 0; rg < 16; ++rg) {
-                const int key = 8 * (rg >> 2) + 4 * half + (rg & 3);
-                const float x = selt[key] >= 0 ? acc[rg] * sl2 : -INFINITY;
-                acc[rg] = x;
-                tmax = fmaxf(tmax, x);
+                for (int rg = 0; rg < 16; ++rg) {
+                    acc[rg] *= sl2;
+                    tmax = fmaxf(tmax, acc[rg]);
+                }
+            } else {
+                const uint32_t mh = vmask >> (4 * half);
+#pragma unroll
+                for (int rg = 0; rg < 16; ++rg) {
+                    const float x =
+                        (mh >> (8 * (rg >> 2) + (rg & 3))) & 1u ? acc[rg] * sl2 : -INFINITY;
+                    acc[rg] = x;
+                    tmax = fmaxf(tmax, x);
+                }
             }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            tmax = max_halves(tmax);
             float corr = 1.0f;
             if (tmax > m_run + kRescaleLog2) {
                 corr = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - tmax);
@@ -280,6 +304,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             }
             l_run = l_run * corr + (ps0 + ps1);
             if (half == 0) sm.corr[tile & 1][ht * 32 + l32] = corr;
+            const bool resc = __ballot(corr != 1.0f) != 0;
+            if (lane == 0) sm.resc[tile & 1][ht] = resc;
         };
 
         // "iteration -1": S and softmax of tile 0
@@ -288,35 +314,47 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             if (kh == 1) put_part(acc);
             lds_barrier();
             if (kh == 0) {
+                const uint32_t vm = tile_mask(0);
                 add_part(acc);
-                softmax(0, acc);
+                softmax(0, acc, vm);
             }
             lds_barrier();
         }
-        // iteration it: park tile it+2, load tile it+4, S of tile it+1
+        // iteration it: S of tile it+1, park this wave's share of tile it+2
+        // and load its share of tile it+4; the K fragments are requested
+        // first, so their LDS latency overlaps the parking and the gathers
         auto s_step = [&](const int it, u32x4 (&st)[kLoadsS]) {
-            stage_store(st, sm.kv[(it + 2) % kRing], wave, lane);
-            stage_load(st, sm, len, it + 4, lat_b, wave, lane);
-            __builtin_amdgcn_sched_barrier(0);
             const bool more = it + 1 < ntiles;
+            stage_store(st, sm.kv[(it + 2) % kRing], q0, qs);
+            stage_load(st, sm, len, it + 4, lat_b, q0, qs);
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 af[kHalfSteps];
+            if (more) s_read(sm.kv[(it + 1) % kRing], af);
+            __builtin_amdgcn_sched_barrier(0);
             f32x16 acc = {};
-            if (more) acc = s_half(sm.kv[(it + 1) % kRing]);
+            if (more) acc = s_mfma(af);
             if (more && kh == 1) put_part(acc);
+            uint32_t vm = 0;
+            if (more && kh == 0) vm = tile_mask(it + 1);
             lds_barrier();  // ---- barrier 1
             if (more && kh == 0) {
                 add_part(acc);
-                softmax(it + 1, acc);
+                softmax(it + 1, acc, vm);
             }
             lds_barrier();  // ---- barrier 2
         };
-        for (int it = 0; it < ntiles; it += 2) {
+        // Pairs of steps, so that at the top of the loop the stg[1] loads are
+        // always the newer ones and parking stg[0] waits for its own loads only.
+        int it = 0;
+        for (; it + 1 < ntiles; it += 2) {
             s_step(it, stg[0]);
-            if (it + 1 < ntiles) s_step(it + 1, stg[1]);
+            s_step(it + 1, stg[1]);
         }
+        if (it < ntiles) s_step(it, stg[0]);
         lds_barrier();  // loads past the last tile may still be in flight
         float l_all = 0.0f;
         if (kh == 0) {
-            l_all = l_run + __shfl_xor(l_run, 32, 64);  // both key halves
+            l_all = sum_halves(l_run);  // both key halves
             if (half == 0) sm.fin_l[ht * 32 + l32] = l_all > 0.0f ? 1.0f / l_all : 0.0f;
         }
         lds_barrier();  // loads past the last tile may still be in flight
@@ -333,30 +371,33 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         // ======================= PV waves =======================
         const int d = wave - 4;
         const int dv0 = d * 128;
+        const int q0 = 64 * wave + lane;  // staging slots
+        constexpr int qs = kStageStride;
         u32x4 stg[2][kLoadsPV];
-        stage_load(stg[0], sm, len, 0, lat_b, wave, lane);
+        stage_load(stg[0], sm, len, 0, lat_b, q0, qs);
         __builtin_amdgcn_sched_barrier(0);
-        stage_load(stg[1], sm, len, 1, lat_b, wave, lane);
+        stage_load(stg[1], sm, len, 1, lat_b, q0, qs);
         __builtin_amdgcn_sched_barrier(0);
         f32x16 o[2][4];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int c = 0; c < 4; ++c) o[a][c] = f32x16{};
-        stage_store(stg[0], sm.kv[0], wave, lane);
-        stage_store(stg[1], sm.kv[1], wave, lane);
-        stage_load(stg[0], sm, len, 2, lat_b, wave, lane);
+        stage_store(stg[0], sm.kv[0], q0, qs);
+        stage_store(stg[1], sm.kv[1], q0, qs);
+        stage_load(stg[0], sm, len, 2, lat_b, q0, qs);
         __builtin_amdgcn_sched_barrier(0);
-        stage_load(stg[1], sm, len, 3, lat_b, wave, lane);
+        stage_load(stg[1], sm, len, 3, lat_b, q0, qs);
         __builtin_amdgcn_sched_barrier(0);
         lds_barrier();  // tiles 0 and 1 in LDS (matches the S waves')
         const int trj = lane & 15, trg = lane >> 4;
         const int vrow = 8 * (trg >> 1) + (trj >> 2);
         const int vcol = (dv0 + 16 * (trg & 1) + 4 * (trj & 3)) * 2;
-        auto pv_step = [&](int tile, int ks) {
+        // Operands of one 16-entry k-step of tile `tile`: P (A, 32 heads x 16
+        // entries per head tile) and V (B, 16 entries x 32 dims per column tile).
+        auto pv_read = [&](int tile, int ks, bf16x8 (&pa)[2], bf16x8 (&vb)[4]) {
             const uint8_t *kvt = sm.kv[tile % kRing];
             const uint8_t *pt = sm.p[tile & 1];
-            bf16x8 pa[2], vb[4];
 #pragma unroll
             for (int a = 0; a < 2; ++a)
                 pa[a] = lds_b128(pt + (a * 32 + l32) * kPPitch + (16 * ks + 8 * half) * 2);
@@ -367,6 +408,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
                 const bf16x4 hi = lds_tr16(vp + 4 * kRowPitch);
                 vb[c] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
+        };
+        auto pv_mfma = [&](const bf16x8 (&pa)[2], const bf16x8 (&vb)[4]) {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -376,35 +419,46 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         };
         lds_barrier();  // matches the S waves' "iteration -1"
         lds_barrier();
+        // The first k-step's LDS reads (and the rescale flags) are issued
+        // before the tile parking, so their latency overlaps it; the next
+        // gathers and the second k-step's reads follow the first k-step's
+        // products and complete under them.
         auto o_step = [&](const int it, u32x4 (&st)[kLoadsPV]) {
-            stage_store(st, sm.kv[(it + 2) % kRing], wave, lane);
-            stage_load(st, sm, len, it + 4, lat_b, wave, lane);
+            const int32_t f0 = sm.resc[it & 1][0], f1 = sm.resc[it & 1][1];
+            bf16x8 pa[2], vb[4];
+            pv_read(it, 0, pa, vb);
+            __builtin_amdgcn_sched_barrier(0);
+            stage_store(st, sm.kv[(it + 2) % kRing], q0, qs);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
-                float cr[16];
-                bool any = false;
+                if (__builtin_amdgcn_readfirstlane(a == 0 ? f0 : f1)) {
+                    f32x4 cr[4];
 #pragma unroll
-                for (int rg = 0; rg < 16; ++rg) {
-                    cr[rg] = sm.corr[it & 1][a * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
-                    any |= cr[rg] != 1.0f;
-                }
-                if (__ballot(any)) {
+                    for (int j = 0; j < 4; ++j)
+                        cr[j] = *reinterpret_cast<const f32x4 *>(
+                            &sm.corr[it & 1][a * 32 + 8 * j + 4 * half]);
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
 #pragma unroll
-                        for (int rg = 0; rg < 16; ++rg) o[a][c][rg] *= cr[rg];
+                        for (int rg = 0; rg < 16; ++rg) o[a][c][rg] *= cr[rg >> 2][rg & 3];
                 }
             }
-            pv_step(it, 0);
+            pv_mfma(pa, vb);
+            __builtin_amdgcn_sched_barrier(0);
+            stage_load(st, sm, len, it + 4, lat_b, q0, qs);
+            __builtin_amdgcn_sched_barrier(0);
+            pv_read(it, 1, pa, vb);
             lds_barrier();  // ---- barrier 1
-            pv_step(it, 1);
+            pv_mfma(pa, vb);
             lds_barrier();  // ---- barrier 2
         };
-        for (int it = 0; it < ntiles; it += 2) {
+        int it = 0;
+        for (; it + 1 < ntiles; it += 2) {
             o_step(it, stg[0]);
-            if (it + 1 < ntiles) o_step(it + 1, stg[1]);
+            o_step(it + 1, stg[1]);
         }
+        if (it < ntiles) o_step(it, stg[0]);
         lds_barrier();  // loads past the last tile may still be in flight
         lds_barrier();  // loads past the last tile may still be in flight
         // Output through LDS (the tile ring is free now): the accumulator
@@ -432,17 +486,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            f32x4 v[16];  // 32 heads x 128 dims = 16 rounds of 64 x 4, all read first
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {  // 32 heads x 128 dims = 16 rounds of 64 x 4
-                const int hr = 2 * m + half;
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(blk + hr * kOutPitch + 4 * l32);
-                const int hl = a * 32 + hr;
-                const int dd = dv0 + 4 * l32;
-                if (splits == 1)
-                    store_out4(out + (rowq * H + head0 + hl) * kDv + dd, v);
-                else
+            for (int m = 0; m < 16; ++m)
+                v[m] = *reinterpret_cast<const f32x4 *>(blk + (2 * m + half) * kOutPitch + 4 * l32);
+            const int dd = dv0 + 4 * l32;
+            if (splits == 1) {
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    store_out4(out + (rowq * H + head0 + a * 32 + 2 * m + half) * kDv + dd, v[m]);
+            } else {
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
                     *reinterpret_cast<f32x4 *>(
-                        o_part + ((prow * splits + split) * H + head0 + hl) * kDv + dd) = v;
+                        o_part + ((prow * splits + split) * H + head0 + a * 32 + 2 * m + half) * kDv +
+                        dd) = v[m];
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();  // block reused by the second half

@@ -35,6 +35,20 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Reductions across the two 32-lane halves of a wave: v_permlane32_swap
+// exchanges the halves in registers (no trip through the LDS crossbar that
+// a generic shuffle takes), then both halves hold the combined value.
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ------------------------------------------------------ scalar conversions --
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
     return __uint_as_float(b << 16);
