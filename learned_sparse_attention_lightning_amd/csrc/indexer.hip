@@ -338,16 +338,22 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
 // Prefill variant: consecutive query rows read (almost) the same keys, so a
 // workgroup of 8 waves owns 8 consecutive rows and a range of keys; each
 // 64-key tile is brought into LDS once for all 8 rows (direct-to-LDS loads,
-// two buffers so the next tile lands while this one is multiplied) and every
-// wave reads its B operands from there.  Row pitch = row + 16 bytes, so the
-// operand reads are free of bank conflicts.
+// issued three tiles ahead into a ring of four buffers) and every wave reads
+// its B operands from there.  Row pitch = row + 16 bytes, so the operand
+// reads are free of bank conflicts.
+//
+// Software pipeline inside a wave: the products of a half tile (32 keys) run
+// while the VALU reduces the previous half tile (ReLU, head weights), so the
+// matrix pipe always has independent work next to the reduction; the second
+// half of a tile is reduced during the first half of the next one.
+//
+// Every wave issues, per tile, the same number of tile loads and exactly one
+// score store (a bounds-checked buffer store: keys outside the row's causal
+// range fall outside the buffer and are dropped), so the wait for a tile's
+// loads is one static vmcnt.
 constexpr int kPfRows = 8;     // query rows (waves) per workgroup
 constexpr int kPfKeys = 64;    // keys per LDS tile
-// Waves 0..6 issue the tile loads; wave 7 writes every row's scores to
-// memory.  A wave's s_waitcnt counts its loads and stores together, so the
-// loaders must never have stores outstanding (waiting for this tile's loads
-// would also wait for the stores), and the storing wave never waits.
-constexpr int kPfLoaders = kPfRows - 1;
+constexpr int kPfLoaders = kPfRows;
 
 template <bool Fp8>
 struct PrefillTile {
@@ -382,6 +388,14 @@ __device__ __forceinline__ void prefill_issue_tile(uint8_t *buf, const uint8_t *
     }
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (dword 3: the usual
+// untyped-buffer configuration on gfx9); accesses at offsets >= bytes are
+// dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kDropOffset = 0x7ffffff0;  // beyond every buffer here: the store is dropped
+
 // grid: 1-D over (batch, row block, key chunk), heaviest row blocks first
 template <bool Fp8>
 __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
@@ -403,9 +417,10 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
     __shared__ __align__(16) uint8_t tile2[Pt::bytes];
     __shared__ __align__(16) uint8_t tile3[Pt::bytes];
     __shared__ int tmax_s[kPfRows];
-    __shared__ float staged[2][kPfRows][kPfKeys];  // one tile's scores of all rows
 
-    const int wave = threadIdx.x >> 6;
+    // wave-uniform as far as the compiler can tell: the row, its buffer
+    // resource and its causal bounds then live in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
     const int col = lane & 31;
@@ -426,23 +441,32 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
 
     const int k_begin = kc * kchunk;
     const int k_end = min(S, k_begin + kchunk);
-    float *out = scores + (size_t)b * batch_stride + (size_t)r * S;
+    float *out = scores + (size_t)b * batch_stride + (size_t)(live ? r : 0) * S;
     if (live && write_masked) {
         for (int s = max(k_begin, t + 1) + lane; s < k_end; s += 64) out[s] = -INFINITY;
     }
     const int k_hi = min(k_end, tmax + 1);  // keys any row of the block needs
     if (k_begin >= k_hi) return;             // uniform over the workgroup
 
+    const int t_hi = min(k_end, t + 1);  // this row's causal end inside the chunk (0 if none)
+    // this row's scores: keys [0, t_hi) of the row are inside the buffer
+    const __amdgpu_buffer_rsrc_t orow = raw_buffer(out, live ? (uint32_t)t_hi * 4u : 0u);
+
     const uint8_t *kb_base = k_idx + (size_t)b * S * Pt::row_bytes;
     const int last_tile = k_begin + (k_hi - 1 - k_begin) / kPfKeys * kPfKeys;
     auto issue = [&](uint8_t *buf, int s_tile) {  // past the last tile: reload the last
         prefill_issue_tile<Fp8>(buf, kb_base, min(s_tile, last_tile), S, wave, lane);
     };
-    if (wave < kPfLoaders) {
-        issue(tile0, k_begin);
-        issue(tile1, k_begin + kPfKeys);
-        issue(tile2, k_begin + 2 * kPfKeys);
-    }
+    auto store = [&](float v, int key) {  // one instruction a call, whatever the key
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orow, key * 4, 0, 0);
+    };
+    // prologue: three tiles, each followed by a (dropped) store as in a step
+    issue(tile0, k_begin);
+    store(0.0f, kDropOffset / 4);
+    issue(tile1, k_begin + kPfKeys);
+    store(0.0f, kDropOffset / 4);
+    issue(tile2, k_begin + 2 * kPfKeys);
+    store(0.0f, kDropOffset / 4);
 
     const size_t qrow = ((size_t)b * T + i) * kIdxHeads;
     Op qa[2][KS];
@@ -458,87 +482,97 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
 #pragma unroll
         for (int rg = 0; rg < 16; ++rg)
             wr[tl][rg] = w[qrow + tl * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
-    const int t_hi = min(k_end, t + 1);  // this row's causal end inside the chunk
 
-    // wave 7: scores of the tile starting at s_prev (staging buffer sb) to memory
-    auto flush = [&](const int s_prev, const int sb) {
-        const int key = s_prev + lane;
+    // loads of tile t were issued at step t-3; after them: that step's store
+    // and two more steps of (per_loader loads + one store)
+    constexpr int kAfter = 2 * (Pt::per_loader + 1) + 1;
+    constexpr int kWaitThis = (kAfter & 15) | ((kAfter >> 4) << 14) | 0x70 | 0xF00;
+    f32x16 pacc[2] = {f32x16{}, f32x16{}};  // second half of the previous tile
+    int pkey = kDropOffset / 4 - 32;         // its first key (none before the first tile)
+    auto step = [&](const int s0, const uint8_t *cur, uint8_t *ahead3) {
+        __builtin_amdgcn_s_waitcnt(kWaitThis);
+        lds_barrier();  // ... every wave's; ahead3 (tile s0 - 64) is free
+        issue(ahead3, s0 + 3 * kPfKeys);
+        // One straight block (no per-row branch: a row past its causal end
+        // multiplies a few tiles for nothing, its stores are dropped), so the
+        // scheduler can put the reduction between the products.
+        // The first half's operands now; the second half's are requested
+        // one by one between the first half's products, so the LDS serves
+        // the eight waves' reads spread over the tile rather than in a burst.
+        Op kb[2][KS];
+        auto kb_read = [&](int st, int ks) {
+            kb[st][ks] = Tr::load(cur + (st * 32 + col) * Pt::pitch + 64 * half * EB +
+                                  ks * DPS * EB);
+        };
 #pragma unroll
-        for (int v = 0; v < kPfRows; ++v) {
-            const int tv = tmax_s[v];  // -1 for rows past the block's end
-            if (key < min(k_end, tv + 1))
-                scores[(size_t)b * batch_stride + (size_t)(rb * kPfRows + v) * S + key] =
-                    staged[sb][v][lane];
-        }
-    };
-    // loads of this tile landed once at most two tiles' loads are outstanding
-    constexpr int kAhead = 2 * Pt::per_loader;
-    constexpr int kWaitThis = (kAhead & 15) | ((kAhead >> 4) << 14) | 0x70 | 0xF00;
-    // The storing wave and the loaders run separate copies of the loop, so the
-    // compiler's wait counts on the loaders never see a store.
-    auto step = [&](auto storer, const int s0, const uint8_t *cur, uint8_t *ahead3,
-                    const int sb) {
-        if (!storer) __builtin_amdgcn_s_waitcnt(kWaitThis);
-        lds_barrier();  // ... every loader's; ahead3 (tile s0 - 64) and staged[sb] are free
-        if (storer) {
-            if (s0 > k_begin) flush(s0 - kPfKeys, sb ^ 1);
-        } else {
-            issue(ahead3, s0 + 3 * kPfKeys);
-        }
-        if (s0 < t_hi) {
-            // both 32-key halves of the tile: the products of the second half
-            // are interleaved with the ReLU-weighted reduction of the first,
-            // so the matrix pipe stays busy while the VALU works
-            Op kb[2][KS];
+        for (int ks = 0; ks < KS; ++ks) kb_read(0, ks);
+        // Explicit interleave: product g of a half tile, then two elements of
+        // the reduction of the previous half tile (ReLU + head weight), with a
+        // scheduling fence after each group so the order holds.
+        f32x16 acc[2] = {f32x16{}, f32x16{}}, nacc[2] = {f32x16{}, f32x16{}};
+        float r0 = 0.0f, r1 = 0.0f, r2 = 0.0f, r3 = 0.0f;  // previous half (pacc)
+        float u0 = 0.0f, u1 = 0.0f, u2 = 0.0f, u3 = 0.0f;  // this tile's first half
+        static_assert(16 % (2 * KS) == 0, "reduction split over the products");
+        constexpr int kPer = 16 / (2 * KS);  // register pairs reduced after each product
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+        for (int g = 0; g < 2 * KS; ++g) {
+            const int ks = g >> 1, tl = g & 1;
+            acc[tl] = Tr::mma(qa[tl][ks], kb[0][ks], acc[tl]);
+            if (tl == 1) kb_read(1, ks);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    kb[st][ks] = Tr::load(cur + (st * 32 + col) * Pt::pitch + 64 * half * EB +
-                                          ks * DPS * EB);
-            f32x16 acc[2][2];
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                acc[st][0] = f32x16{};
-                acc[st][1] = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    acc[st][0] = Tr::mma(qa[0][ks], kb[st][ks], acc[st][0]);
-                    acc[st][1] = Tr::mma(qa[1][ks], kb[st][ks], acc[st][1]);
+            for (int e = 0; e < kPer; ++e) {
+                const int idx = g * kPer + e;  // pair 0..15: registers 2idx, 2idx+1 of 32
+                const int rg = (2 * idx) & 15, th = (2 * idx) >> 4;
+                if (th == 0) {
+                    r0 = fmaf(wr[0][rg], relu_bits(pacc[0][rg]), r0);
+                    r1 = fmaf(wr[0][rg + 1], relu_bits(pacc[0][rg + 1]), r1);
+                } else {
+                    r2 = fmaf(wr[1][rg], relu_bits(pacc[1][rg]), r2);
+                    r3 = fmaf(wr[1][rg + 1], relu_bits(pacc[1][rg + 1]), r3);
                 }
             }
-            const float part0 = weighted_relu_sum(acc[0][0], acc[0][1], wr);
-            const float part1 = weighted_relu_sum(acc[1][0], acc[1][1], wr);
-            constexpr int kMm = 2 * KS;                 // products per half tile
-            constexpr int kVa = (72 + kMm - 1) / kMm;   // reduction ops between them
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);  // operand reads
-            __builtin_amdgcn_sched_group_barrier(0x008, kMm, 0);     // first half
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-            for (int g = 0; g < kMm; ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);
+        for (int g = 0; g < 2 * KS; ++g) {
+            const int ks = g >> 1, tl = g & 1;
+            nacc[tl] = Tr::mma(qa[tl][ks], kb[1][ks], nacc[tl]);
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) {
+                const int idx = g * kPer + e;
+                const int rg = (2 * idx) & 15, th = (2 * idx) >> 4;
+                if (th == 0) {
+                    u0 = fmaf(wr[0][rg], relu_bits(acc[0][rg]), u0);
+                    u1 = fmaf(wr[0][rg + 1], relu_bits(acc[0][rg + 1]), u1);
+                } else {
+                    u2 = fmaf(wr[1][rg], relu_bits(acc[1][rg]), u2);
+                    u3 = fmaf(wr[1][rg + 1], relu_bits(acc[1][rg + 1]), u3);
+                }
             }
-            const float other0 = __shfl_xor(part0, 32, 64);
-            const float other1 = __shfl_xor(part1, 32, 64);
-            if (half == 0) {
-                staged[sb][wave][col] = part0 + other0;
-                staged[sb][wave][col + 32] = part1 + other1;
-            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+        const float prev = (r0 + r1) + (r2 + r3);
+        const float part0 = (u0 + u1) + (u2 + u3);
+        pacc[0] = nacc[0];
+        pacc[1] = nacc[1];
+        // lanes 0..31: the previous tile's keys 32..63; lanes 32..63: this
+        // tile's keys 0..31 (each sum needs the partner half's 32 heads)
+        const float prev_all = sum_halves(prev);
+        const float part_all = sum_halves(part0);
+        store(half ? part_all : prev_all, half ? s0 + col : pkey + col);
+        pkey = s0 + 32;
     };
-    auto walk = [&](auto storer) {
-        for (int s0 = k_begin; s0 < k_hi; s0 += kPfRing * kPfKeys) {
-            step(storer, s0, tile0, tile3, 0);
-            if (s0 + kPfKeys < k_hi) step(storer, s0 + kPfKeys, tile1, tile0, 1);
-            if (s0 + 2 * kPfKeys < k_hi) step(storer, s0 + 2 * kPfKeys, tile2, tile1, 0);
-            if (s0 + 3 * kPfKeys < k_hi) step(storer, s0 + 3 * kPfKeys, tile3, tile2, 1);
-        }
-    };
-    if (wave == kPfRows - 1) walk(std::true_type{});
-    else walk(std::false_type{});
-    __builtin_amdgcn_s_waitcnt(0);  // the surplus loads of the last steps
-    lds_barrier();
-    if (wave == kPfRows - 1) flush(last_tile, ((last_tile - k_begin) / kPfKeys) & 1);
+    for (int s0 = k_begin; s0 < k_hi; s0 += kPfRing * kPfKeys) {
+        step(s0, tile0, tile3);
+        if (s0 + kPfKeys < k_hi) step(s0 + kPfKeys, tile1, tile0);
+        if (s0 + 2 * kPfKeys < k_hi) step(s0 + 2 * kPfKeys, tile2, tile1);
+        if (s0 + 3 * kPfKeys < k_hi) step(s0 + 3 * kPfKeys, tile3, tile2);
+    }
+    {  // the last tile's second half
+        const float prev_all = sum_halves(weighted_relu_sum(pacc[0], pacc[1], wr));
+        store(prev_all, half ? kDropOffset / 4 : pkey + col);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the surplus tile loads of the last steps
 }
 
 // ------------------------------------------------------------- generic ----
