@@ -347,13 +347,16 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
 // matrix pipe always has independent work next to the reduction; the second
 // half of a tile is reduced during the first half of the next one.
 //
-// Every wave issues, per tile, the same number of tile loads and exactly one
-// score store (a bounds-checked buffer store: keys outside the row's causal
-// range fall outside the buffer and are dropped), so the wait for a tile's
-// loads is one static vmcnt.
+// Waves 0..6 issue the tile loads, the same number every tile, and no other
+// memory operation, so the wait for a tile's loads is one static vmcnt
+// (loads complete in order among themselves; a store between them could
+// complete early and satisfy the count).  Every wave parks its scores in LDS;
+// wave 7, which issues no loads, writes all eight rows' scores with
+// bounds-checked buffer stores (keys outside a row's causal range get an
+// offset past the buffer and are dropped).
 constexpr int kPfRows = 8;     // query rows (waves) per workgroup
 constexpr int kPfKeys = 64;    // keys per LDS tile
-constexpr int kPfLoaders = kPfRows;
+constexpr int kPfLoaders = kPfRows - 1;
 
 template <bool Fp8>
 struct PrefillTile {
@@ -417,6 +420,7 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
     __shared__ __align__(16) uint8_t tile2[Pt::bytes];
     __shared__ __align__(16) uint8_t tile3[Pt::bytes];
     __shared__ int tmax_s[kPfRows];
+    __shared__ __align__(16) float staged[2][kPfRows][kPfKeys];  // one step's scores, all rows
 
     // wave-uniform as far as the compiler can tell: the row, its buffer
     // resource and its causal bounds then live in scalar registers
@@ -448,25 +452,40 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
     const int k_hi = min(k_end, tmax + 1);  // keys any row of the block needs
     if (k_begin >= k_hi) return;             // uniform over the workgroup
 
-    const int t_hi = min(k_end, t + 1);  // this row's causal end inside the chunk (0 if none)
-    // this row's scores: keys [0, t_hi) of the row are inside the buffer
-    const __amdgpu_buffer_rsrc_t orow = raw_buffer(out, live ? (uint32_t)t_hi * 4u : 0u);
+    // wave 7's stores: lane l writes 8 consecutive entries (8(l&7)..) of the
+    // staged scores of row l>>3; one buffer over the block's live rows
+    const int srow = lane >> 3, spart = lane & 7;
+    const int s_hi = min(k_end, tmax_s[srow] + 1);  // that row's causal end in the chunk
+    const int live_rows = min(kPfRows, rows - rb * kPfRows);
+    const __amdgpu_buffer_rsrc_t oblk =
+        raw_buffer(scores + (size_t)b * batch_stride + (size_t)rb * kPfRows * S,
+                   (uint32_t)live_rows * (uint32_t)S * 4u);
 
     const uint8_t *kb_base = k_idx + (size_t)b * S * Pt::row_bytes;
     const int last_tile = k_begin + (k_hi - 1 - k_begin) / kPfKeys * kPfKeys;
     auto issue = [&](uint8_t *buf, int s_tile) {  // past the last tile: reload the last
         prefill_issue_tile<Fp8>(buf, kb_base, min(s_tile, last_tile), S, wave, lane);
     };
-    auto store = [&](float v, int key) {  // one instruction a call, whatever the key
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orow, key * 4, 0, 0);
+    // staged[sb] holds, per row, the previous tile's keys 32..63 (entries
+    // 0..31, first key pk) and this tile's keys 0..31 (entries 32..63, first
+    // key sk); wave 7 writes them out after the next barrier
+    auto flush = [&](int sb, int pk, int sk) {
+        const float4 a = *reinterpret_cast<const float4 *>(&staged[sb][srow][8 * spart]);
+        const float4 c = *reinterpret_cast<const float4 *>(&staged[sb][srow][8 * spart + 4]);
+        const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        const int key0 = spart < 4 ? pk + 8 * spart : sk + 8 * spart - 32;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int key = key0 + e;
+            const int off = key >= k_begin && key < s_hi ? (srow * S + key) * 4 : kDropOffset;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), oblk, off, 0, 0);
+        }
     };
-    // prologue: three tiles, each followed by a (dropped) store as in a step
-    issue(tile0, k_begin);
-    store(0.0f, kDropOffset / 4);
-    issue(tile1, k_begin + kPfKeys);
-    store(0.0f, kDropOffset / 4);
-    issue(tile2, k_begin + 2 * kPfKeys);
-    store(0.0f, kDropOffset / 4);
+    if (wave < kPfLoaders) {
+        issue(tile0, k_begin);
+        issue(tile1, k_begin + kPfKeys);
+        issue(tile2, k_begin + 2 * kPfKeys);
+    }
 
     const size_t qrow = ((size_t)b * T + i) * kIdxHeads;
     Op qa[2][KS];
@@ -483,16 +502,22 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
         for (int rg = 0; rg < 16; ++rg)
             wr[tl][rg] = w[qrow + tl * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
 
-    // loads of tile t were issued at step t-3; after them: that step's store
-    // and two more steps of (per_loader loads + one store)
-    constexpr int kAfter = 2 * (Pt::per_loader + 1) + 1;
-    constexpr int kWaitThis = (kAfter & 15) | ((kAfter >> 4) << 14) | 0x70 | 0xF00;
+    // loads of this tile landed once at most two tiles' loads are outstanding
+    constexpr int kAhead = 2 * Pt::per_loader;
+    constexpr int kWaitThis = (kAhead & 15) | ((kAhead >> 4) << 14) | 0x70 | 0xF00;
     f32x16 pacc[2] = {f32x16{}, f32x16{}};  // second half of the previous tile
-    int pkey = kDropOffset / 4 - 32;         // its first key (none before the first tile)
-    auto step = [&](const int s0, const uint8_t *cur, uint8_t *ahead3) {
-        __builtin_amdgcn_s_waitcnt(kWaitThis);
-        lds_barrier();  // ... every wave's; ahead3 (tile s0 - 64) is free
-        issue(ahead3, s0 + 3 * kPfKeys);
+    int pkey = -64;                          // its first key (none before the first tile)
+    int sb = 0;                              // staging buffer of this step
+    // The storing wave and the loaders run separate copies of the loop, so the
+    // compiler's wait counts on the loaders never see a store.
+    auto step = [&](auto storer, const int s0, const uint8_t *cur, uint8_t *ahead3) {
+        if (!storer) __builtin_amdgcn_s_waitcnt(kWaitThis);
+        lds_barrier();  // ... every loader's; ahead3 (tile s0 - 64) and staged[sb] are free
+        if (storer) {
+            if (s0 > k_begin) flush(sb ^ 1, pkey - 64, s0 - kPfKeys);
+        } else {
+            issue(ahead3, s0 + 3 * kPfKeys);
+        }
         // One straight block (no per-row branch: a row past its causal end
         // multiplies a few tiles for nothing, its stores are dropped), so the
         // scheduler can put the reduction between the products.
@@ -555,24 +580,33 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
         const float part0 = (u0 + u1) + (u2 + u3);
         pacc[0] = nacc[0];
         pacc[1] = nacc[1];
-        // lanes 0..31: the previous tile's keys 32..63; lanes 32..63: this
-        // tile's keys 0..31 (each sum needs the partner half's 32 heads)
+        // entries 0..31: the previous tile's keys 32..63; 32..63: this tile's
+        // keys 0..31 (each sum needs the partner half's 32 heads)
         const float prev_all = sum_halves(prev);
         const float part_all = sum_halves(part0);
-        store(half ? part_all : prev_all, half ? s0 + col : pkey + col);
+        staged[sb][wave][lane] = half ? part_all : prev_all;
         pkey = s0 + 32;
+        sb ^= 1;
     };
-    for (int s0 = k_begin; s0 < k_hi; s0 += kPfRing * kPfKeys) {
-        step(s0, tile0, tile3);
-        if (s0 + kPfKeys < k_hi) step(s0 + kPfKeys, tile1, tile0);
-        if (s0 + 2 * kPfKeys < k_hi) step(s0 + 2 * kPfKeys, tile2, tile1);
-        if (s0 + 3 * kPfKeys < k_hi) step(s0 + 3 * kPfKeys, tile3, tile2);
-    }
-    {  // the last tile's second half
-        const float prev_all = sum_halves(weighted_relu_sum(pacc[0], pacc[1], wr));
-        store(prev_all, half ? kDropOffset / 4 : pkey + col);
-    }
+    auto walk = [&](auto storer) {
+        for (int s0 = k_begin; s0 < k_hi; s0 += kPfRing * kPfKeys) {
+            step(storer, s0, tile0, tile3);
+            if (s0 + kPfKeys < k_hi) step(storer, s0 + kPfKeys, tile1, tile0);
+            if (s0 + 2 * kPfKeys < k_hi) step(storer, s0 + 2 * kPfKeys, tile2, tile1);
+            if (s0 + 3 * kPfKeys < k_hi) step(storer, s0 + 3 * kPfKeys, tile3, tile2);
+        }
+    };
+    if (wave == kPfRows - 1) walk(std::true_type{});
+    else walk(std::false_type{});
+    // the last step's scores, then the last tile's second half
     __builtin_amdgcn_s_waitcnt(0);  // the surplus tile loads of the last steps
+    lds_barrier();
+    if (wave == kPfRows - 1) flush(sb ^ 1, pkey - 64, pkey - 32);
+    const float last_all = sum_halves(weighted_relu_sum(pacc[0], pacc[1], wr));
+    lds_barrier();  // staged[sb] is free (its previous contents left two steps ago)
+    staged[sb][wave][lane] = half ? 0.0f : last_all;
+    lds_barrier();
+    if (wave == kPfRows - 1) flush(sb, pkey, kDropOffset / 4);
 }
 
 // ------------------------------------------------------------- generic ----
