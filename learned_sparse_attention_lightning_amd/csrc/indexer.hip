@@ -347,16 +347,16 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
 // matrix pipe always has independent work next to the reduction; the second
 // half of a tile is reduced during the first half of the next one.
 //
-// Waves 0..6 issue the tile loads, the same number every tile, and no other
+// Waves 0..5 issue the tile loads, the same number every tile, and no other
 // memory operation, so the wait for a tile's loads is one static vmcnt
 // (loads complete in order among themselves; a store between them could
 // complete early and satisfy the count).  Every wave parks its scores in LDS;
-// wave 7, which issues no loads, writes all eight rows' scores with
+// waves 6 and 7, which issue no loads, write four rows' scores each with
 // bounds-checked buffer stores (keys outside a row's causal range get an
 // offset past the buffer and are dropped).
 constexpr int kPfRows = 8;     // query rows (waves) per workgroup
 constexpr int kPfKeys = 64;    // keys per LDS tile
-constexpr int kPfLoaders = kPfRows - 1;
+constexpr int kPfLoaders = kPfRows - 2;
 
 template <bool Fp8>
 struct PrefillTile {
@@ -452,9 +452,10 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
     const int k_hi = min(k_end, tmax + 1);  // keys any row of the block needs
     if (k_begin >= k_hi) return;             // uniform over the workgroup
 
-    // wave 7's stores: lane l writes 8 consecutive entries (8(l&7)..) of the
-    // staged scores of row l>>3; one buffer over the block's live rows
-    const int srow = lane >> 3, spart = lane & 7;
+    // the storing waves: lane l of wave 6 + j writes 4 consecutive entries
+    // (4(l&15)..) of the staged scores of row 4j + (l>>4); one buffer over the
+    // block's live rows
+    const int srow = 4 * (wave & 1) + (lane >> 4), spart = lane & 15;
     const int s_hi = min(k_end, tmax_s[srow] + 1);  // that row's causal end in the chunk
     const int live_rows = min(kPfRows, rows - rb * kPfRows);
     const __amdgpu_buffer_rsrc_t oblk =
@@ -470,12 +471,11 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
     // 0..31, first key pk) and this tile's keys 0..31 (entries 32..63, first
     // key sk); wave 7 writes them out after the next barrier
     auto flush = [&](int sb, int pk, int sk) {
-        const float4 a = *reinterpret_cast<const float4 *>(&staged[sb][srow][8 * spart]);
-        const float4 c = *reinterpret_cast<const float4 *>(&staged[sb][srow][8 * spart + 4]);
-        const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-        const int key0 = spart < 4 ? pk + 8 * spart : sk + 8 * spart - 32;
+        const float4 a = *reinterpret_cast<const float4 *>(&staged[sb][srow][4 * spart]);
+        const float v[4] = {a.x, a.y, a.z, a.w};
+        const int key0 = spart < 8 ? pk + 4 * spart : sk + 4 * spart - 32;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
             const int key = key0 + e;
             const int off = key >= k_begin && key < s_hi ? (srow * S + key) * 4 : kDropOffset;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), oblk, off, 0, 0);
@@ -596,17 +596,17 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
             if (s0 + 3 * kPfKeys < k_hi) step(storer, s0 + 3 * kPfKeys, tile3, tile2);
         }
     };
-    if (wave == kPfRows - 1) walk(std::true_type{});
+    if (wave >= kPfLoaders) walk(std::true_type{});
     else walk(std::false_type{});
     // the last step's scores, then the last tile's second half
     __builtin_amdgcn_s_waitcnt(0);  // the surplus tile loads of the last steps
     lds_barrier();
-    if (wave == kPfRows - 1) flush(sb ^ 1, pkey - 64, pkey - 32);
+    if (wave >= kPfLoaders) flush(sb ^ 1, pkey - 64, pkey - 32);
     const float last_all = sum_halves(weighted_relu_sum(pacc[0], pacc[1], wr));
     lds_barrier();  // staged[sb] is free (its previous contents left two steps ago)
     staged[sb][wave][lane] = half ? 0.0f : last_all;
     lds_barrier();
-    if (wave == kPfRows - 1) flush(sb, pkey, kDropOffset / 4);
+    if (wave >= kPfLoaders) flush(sb, pkey, kDropOffset / 4);
 }
 
 // ------------------------------------------------------------- generic ----
