@@ -609,6 +609,213 @@ __global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
     if (wave >= kPfLoaders) flush(sb, pkey, kDropOffset / 4);
 }
 
+// ------------------------------------------------------ prefill, 16 waves --
+// Same tiles and ring as above, but each query row is split over two waves
+// (one 32-head tile each), 16 waves a workgroup = 4 per SIMD: about 120
+// registers a wave instead of 244, so while one wave waits (LDS operands, the
+// barrier, a dependent product) three others can issue.  The two head tiles'
+// partial sums meet in the LDS staging buffer; waves 12..15 (which issue no
+// tile loads) add them and write the scores.
+constexpr int kP16Waves = 16;
+constexpr int kP16Loaders = 12;
+constexpr int kP16Ahead = 4;  // operand fragments read ahead of their product
+
+template <bool Fp8>
+struct Prefill16Tile {
+    static constexpr int row_bytes = kIdxDim * IdxTraits<Fp8>::elem_bytes;
+    static constexpr int pitch = row_bytes + 16;
+    static constexpr int slots = pitch / 16;
+    static constexpr int loads = (kPfKeys * slots + 63) / 64;
+    static constexpr int per_loader = (loads + kP16Loaders - 1) / kP16Loaders;
+    static constexpr int bytes = per_loader * kP16Loaders * 1024;
+};
+
+template <bool Fp8>
+__device__ __forceinline__ void prefill16_issue_tile(uint8_t *buf, const uint8_t *kb_base,
+                                                     int s0, int S, int wave, int lane) {
+    typedef Prefill16Tile<Fp8> Pt;
+    typedef __attribute__((address_space(3))) void *lds_ptr;
+#pragma unroll
+    for (int m = 0; m < Pt::per_loader; ++m) {
+        const int j = wave + kP16Loaders * m;
+        const int q = 64 * j + lane;
+        const int row = q / Pt::slots;
+        const int piece = q - row * Pt::slots;
+        int key = s0 + row;
+        key = key < S ? key : 0;  // rows past the cache load row 0; never used
+        const bool real = q < kPfKeys * Pt::slots && piece * 16 < Pt::row_bytes;
+        const uint8_t *src = kb_base + (size_t)(real ? key : s0) * Pt::row_bytes +
+                             (real ? piece * 16 : 0);
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(buf + 1024 * j), 16, 0, 0);
+    }
+}
+
+template <bool Fp8>
+__global__ __launch_bounds__(kP16Waves * 64) void indexer_prefill16_kernel(
+    const uint8_t *__restrict__ q_idx, const uint8_t *__restrict__ k_idx,
+    const float *__restrict__ w, const int32_t *__restrict__ q_pos, int B, int T, int S,
+    int row0, int rows, int kchunk, int nkc, float *__restrict__ scores, size_t batch_stride,
+    int write_masked) {
+    typedef IdxTraits<Fp8> Tr;
+    typedef Prefill16Tile<Fp8> Pt;
+    typedef typename Tr::operand Op;
+    constexpr int EB = Tr::elem_bytes;
+    constexpr int KS = Tr::ksteps;
+    constexpr int DPS = Tr::dims_per_step;
+    __shared__ __align__(16) uint8_t tile0[Pt::bytes];
+    __shared__ __align__(16) uint8_t tile1[Pt::bytes];
+    __shared__ __align__(16) uint8_t tile2[Pt::bytes];
+    __shared__ __align__(16) uint8_t tile3[Pt::bytes];
+    __shared__ int tmax_s[kPfRows];
+    __shared__ __align__(16) float staged[2][kPfRows][2][kPfKeys];  // [step][row][head tile][entry]
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
+    const int col = lane & 31;
+    const int rw = wave & 7, ht = wave >> 3;  // row in the block, head tile
+    const int nrb = (rows + kPfRows - 1) / kPfRows;
+    const int id = blockIdx.x;
+    const int kc = id % nkc;
+    const int rb = nrb - 1 - (id / nkc) % nrb;  // last (longest) rows first
+    const int b = id / (nkc * nrb);
+    const int r = rb * kPfRows + rw;
+    const bool live = r < rows;
+    const int i = row0 + (live ? r : rows - 1);
+    const int t = live ? query_pos(q_pos, b, i, T, S) : -1;
+    if (lane == 0 && ht == 0) tmax_s[rw] = t;
+    __syncthreads();
+    int tmax = tmax_s[0];
+#pragma unroll
+    for (int v = 1; v < kPfRows; ++v) tmax = max(tmax, tmax_s[v]);
+
+    const int k_begin = kc * kchunk;
+    const int k_end = min(S, k_begin + kchunk);
+    float *out = scores + (size_t)b * batch_stride + (size_t)(live ? r : 0) * S;
+    if (live && write_masked && ht == 0) {
+        for (int s = max(k_begin, t + 1) + lane; s < k_end; s += 64) out[s] = -INFINITY;
+    }
+    const int k_hi = min(k_end, tmax + 1);  // keys any row of the block needs
+    if (k_begin >= k_hi) return;             // uniform over the workgroup
+
+    // storing waves 12 + j: lane l adds and writes entries 2(l&31), 2(l&31)+1
+    // of row 2j + (l>>5)
+    const bool storer = wave >= kP16Loaders;
+    const int srow = 2 * (wave & 3) + half, spart = col;
+    const int s_hi = min(k_end, tmax_s[srow] + 1);
+    const int live_rows = min(kPfRows, rows - rb * kPfRows);
+    const __amdgpu_buffer_rsrc_t oblk =
+        raw_buffer(scores + (size_t)b * batch_stride + (size_t)rb * kPfRows * S,
+                   (uint32_t)live_rows * (uint32_t)S * 4u);
+
+    const uint8_t *kb_base = k_idx + (size_t)b * S * Pt::row_bytes;
+    const int last_tile = k_begin + (k_hi - 1 - k_begin) / kPfKeys * kPfKeys;
+    auto issue = [&](uint8_t *buf, int s_tile) {
+        prefill16_issue_tile<Fp8>(buf, kb_base, min(s_tile, last_tile), S, wave, lane);
+    };
+    auto flush = [&](int sb, int pk, int sk) {
+        const float2 a = *reinterpret_cast<const float2 *>(&staged[sb][srow][0][2 * spart]);
+        const float2 c = *reinterpret_cast<const float2 *>(&staged[sb][srow][1][2 * spart]);
+        const float v[2] = {a.x + c.x, a.y + c.y};
+        const int key0 = spart < 16 ? pk + 2 * spart : sk + 2 * spart - 32;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int key = key0 + e;
+            const int off = key >= k_begin && key < s_hi ? (srow * S + key) * 4 : kDropOffset;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), oblk, off, 0, 0);
+        }
+    };
+    if (!storer) {
+        issue(tile0, k_begin);
+        issue(tile1, k_begin + kPfKeys);
+        issue(tile2, k_begin + 2 * kPfKeys);
+    }
+
+    const size_t qrow = ((size_t)b * T + i) * kIdxHeads + ht * 32;
+    Op qa[KS];
+    {
+        const uint8_t *qp = q_idx + ((qrow + col) * kIdxDim + 64 * half) * EB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa[ks] = Tr::load(qp + ks * DPS * EB);
+    }
+    float wr[16];
+#pragma unroll
+    for (int rg = 0; rg < 16; ++rg) wr[rg] = w[qrow + 8 * (rg >> 2) + 4 * half + (rg & 3)];
+
+    constexpr int kAhead = 2 * Pt::per_loader;
+    constexpr int kWaitThis = (kAhead & 15) | ((kAhead >> 4) << 14) | 0x70 | 0xF00;
+    f32x16 pacc = f32x16{};  // second half of the previous tile
+    int pkey = -64;
+    int sb = 0;
+    // operand fragment f (0..2KS-1: half f/KS, k-step f%KS) of tile cur
+    auto frag = [&](const uint8_t *cur, int f) -> Op {
+        const int st = f / KS, ks = f % KS;
+        return Tr::load(cur + (st * 32 + col) * Pt::pitch + 64 * half * EB + ks * DPS * EB);
+    };
+    auto step = [&](auto is_storer, const int s0, const uint8_t *cur, uint8_t *ahead3) {
+        if (!is_storer) __builtin_amdgcn_s_waitcnt(kWaitThis);
+        lds_barrier();
+        if (is_storer) {
+            if (s0 > k_begin) flush(sb ^ 1, pkey - 64, s0 - kPfKeys);
+        } else {
+            issue(ahead3, s0 + 3 * kPfKeys);
+        }
+        constexpr int NF = 2 * KS;
+        constexpr int DA = kP16Ahead < NF ? kP16Ahead : NF;
+        Op kb[NF];
+#pragma unroll
+        for (int f = 0; f < DA; ++f) kb[f] = frag(cur, f);
+        f32x16 acc = f32x16{}, nacc = f32x16{};
+        float r0 = 0.0f, r1 = 0.0f, r2 = 0.0f, r3 = 0.0f;
+        float u0 = 0.0f, u1 = 0.0f, u2 = 0.0f, u3 = 0.0f;
+        static_assert(16 % KS == 0, "reduction split over the products");
+        constexpr int kPer = 16 / KS;  // elements reduced after each product
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            if (f + DA < NF) kb[f + DA] = frag(cur, f + DA);
+            const int ks = f % KS;
+            if (f < KS) acc = Tr::mma(qa[ks], kb[f], acc);
+            else nacc = Tr::mma(qa[ks], kb[f], nacc);
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) {
+                const int rg = ks * kPer + e;
+                float &rr = (rg & 1) ? ((rg & 2) ? r3 : r1) : ((rg & 2) ? r2 : r0);
+                float &uu = (rg & 1) ? ((rg & 2) ? u3 : u1) : ((rg & 2) ? u2 : u0);
+                if (f < KS) rr = fmaf(wr[rg], relu_bits(pacc[rg]), rr);
+                else uu = fmaf(wr[rg], relu_bits(acc[rg]), uu);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        pacc = nacc;
+        const float prev_all = sum_halves((r0 + r1) + (r2 + r3));
+        const float part_all = sum_halves((u0 + u1) + (u2 + u3));
+        staged[sb][rw][ht][lane] = half ? part_all : prev_all;
+        pkey = s0 + 32;
+        sb ^= 1;
+    };
+    auto walk = [&](auto is_storer) {
+        for (int s0 = k_begin; s0 < k_hi; s0 += kPfRing * kPfKeys) {
+            step(is_storer, s0, tile0, tile3);
+            if (s0 + kPfKeys < k_hi) step(is_storer, s0 + kPfKeys, tile1, tile0);
+            if (s0 + 2 * kPfKeys < k_hi) step(is_storer, s0 + 2 * kPfKeys, tile2, tile1);
+            if (s0 + 3 * kPfKeys < k_hi) step(is_storer, s0 + 3 * kPfKeys, tile3, tile2);
+        }
+    };
+    if (storer) walk(std::true_type{});
+    else walk(std::false_type{});
+    __builtin_amdgcn_s_waitcnt(0);  // the surplus tile loads of the last steps
+    lds_barrier();
+    if (storer) flush(sb ^ 1, pkey - 64, pkey - 32);
+    float last = 0.0f;
+#pragma unroll
+    for (int rg = 0; rg < 16; ++rg) last = fmaf(wr[rg], relu_bits(pacc[rg]), last);
+    const float last_all = sum_halves(last);
+    lds_barrier();  // staged[sb] is free (its previous contents left two steps ago)
+    staged[sb][rw][ht][lane] = half ? 0.0f : last_all;
+    lds_barrier();
+    if (storer) flush(sb, pkey, kDropOffset / 4);
+}
+
 // ------------------------------------------------------------- generic ----
 constexpr int kGenericThreads = 256;
 constexpr int kGenericMaxQ = 16384;
@@ -686,18 +893,25 @@ hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, c
             return hipGetLastError();
         }
         if (rows >= kPfRows) {  // rows share key tiles: 8 rows a workgroup
-            const int kchunk = 4096;
+            // Keys per workgroup: the whole causal row when the row blocks alone
+            // give enough workgroups (each block then loads its query rows once
+            // and its prologue is paid once), halved while there are fewer than
+            // 512 of them.
+            int kchunk = 4096;
+            while (kchunk < S) kchunk <<= 1;
+            while (kchunk > 4096 && (long long)B * ceil_div(rows, kPfRows) * ceil_div(S, kchunk) < 512)
+                kchunk >>= 1;
             const int nkc = ceil_div(S, kchunk);
             const long long wgs = (long long)B * ceil_div(rows, kPfRows) * nkc;
             if (idx_dtype == DSA_BF16)
-                hipLaunchKernelGGL((indexer_prefill_kernel<false>), dim3((unsigned)wgs),
-                                   dim3(kPfRows * 64), 0, stream,
+                hipLaunchKernelGGL((indexer_prefill16_kernel<false>), dim3((unsigned)wgs),
+                                   dim3(kP16Waves * 64), 0, stream,
                                    static_cast<const uint8_t *>(q_idx),
                                    static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
                                    rows, kchunk, nkc, scores, batch_stride, (int)write_masked);
             else
-                hipLaunchKernelGGL((indexer_prefill_kernel<true>), dim3((unsigned)wgs),
-                                   dim3(kPfRows * 64), 0, stream,
+                hipLaunchKernelGGL((indexer_prefill16_kernel<true>), dim3((unsigned)wgs),
+                                   dim3(kP16Waves * 64), 0, stream,
                                    static_cast<const uint8_t *>(q_idx),
                                    static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
                                    rows, kchunk, nkc, scores, batch_stride, (int)write_masked);
