@@ -335,45 +335,55 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
 }
 
 // ---------------------------------------------------------- prefill tile --
-// Prefill variant: consecutive query rows read (almost) the same keys, so a
-// workgroup of 8 waves owns 8 consecutive rows and a range of keys; each
-// 64-key tile is brought into LDS once for all 8 rows (direct-to-LDS loads,
-// issued three tiles ahead into a ring of four buffers) and every wave reads
-// its B operands from there.  Row pitch = row + 16 bytes, so the operand
-// reads are free of bank conflicts.
+// Prefill: consecutive query rows read (almost) the same keys, so a workgroup
+// owns 8 consecutive rows and a range of keys; each 64-key tile is brought
+// into LDS once for all 8 rows (direct-to-LDS loads, issued three tiles ahead
+// into a ring of four buffers) and every wave reads its B operands from
+// there.  Row pitch = row + 16 bytes, so the operand reads are free of bank
+// conflicts.
 //
-// Software pipeline inside a wave: the products of a half tile (32 keys) run
-// while the VALU reduces the previous half tile (ReLU, head weights), so the
-// matrix pipe always has independent work next to the reduction; the second
-// half of a tile is reduced during the first half of the next one.
+// Each query row is split over two waves (one 32-head tile each): 16 waves a
+// workgroup, 4 per SIMD, about 120 registers a wave.  Software pipeline inside
+// a wave: the products of a half tile (32 keys) run while the VALU reduces
+// the previous half tile (ReLU, head weights), so the matrix pipe always has
+// independent work next to the reduction.
 //
-// Waves 0..5 issue the tile loads, the same number every tile, and no other
-// memory operation, so the wait for a tile's loads is one static vmcnt
-// (loads complete in order among themselves; a store between them could
-// complete early and satisfy the count).  Every wave parks its scores in LDS;
-// waves 6 and 7, which issue no loads, write four rows' scores each with
-// bounds-checked buffer stores (keys outside a row's causal range get an
-// offset past the buffer and are dropped).
-constexpr int kPfRows = 8;     // query rows (waves) per workgroup
+// Waves 0..11 issue the tile loads, the same number every tile, and no other
+// memory operation, so the wait for a tile's loads is one static vmcnt (loads
+// complete in order among themselves; a store between them could complete
+// early and satisfy the count).  Every wave parks its partial scores in LDS;
+// waves 12..15, which issue no loads, add the two head tiles' partials and
+// write the scores with bounds-checked buffer stores (keys outside a row's
+// causal range get an offset past the buffer and are dropped).
+constexpr int kPfRows = 8;     // query rows per workgroup
 constexpr int kPfKeys = 64;    // keys per LDS tile
-constexpr int kPfLoaders = kPfRows - 2;
+constexpr int kPfRing = 4;     // tile buffers; loads run three tiles ahead
+
+// Raw buffer resource over `bytes` bytes at `base` (dword 3: the usual
+// untyped-buffer configuration on gfx9); accesses at offsets >= bytes are
+// dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kDropOffset = 0x7ffffff0;  // beyond every buffer here: the store is dropped
+
+constexpr int kPfWaves = 16;
+constexpr int kPfLoaders = 12;
+constexpr int kPfAhead = 4;  // operand fragments read ahead of their product
 
 template <bool Fp8>
 struct PrefillTile {
     static constexpr int row_bytes = kIdxDim * IdxTraits<Fp8>::elem_bytes;
     static constexpr int pitch = row_bytes + 16;
-    static constexpr int slots = pitch / 16;                           // 16-byte slots a row
-    static constexpr int loads = (kPfKeys * slots + 63) / 64;          // wave loads a tile
+    static constexpr int slots = pitch / 16;
+    static constexpr int loads = (kPfKeys * slots + 63) / 64;
     static constexpr int per_loader = (loads + kPfLoaders - 1) / kPfLoaders;
-    // every loader issues per_loader loads a tile (the surplus ones land in
-    // the padding at the end of the buffer), so wait counts are static
     static constexpr int bytes = per_loader * kPfLoaders * 1024;
 };
-constexpr int kPfRing = 4;   // tile buffers; loads run three tiles ahead
 
 template <bool Fp8>
-__device__ __forceinline__ void prefill_issue_tile(uint8_t *buf, const uint8_t *kb_base, int s0,
-                                                   int S, int wave, int lane) {
+__device__ __forceinline__ void prefill_issue_tile(uint8_t *buf, const uint8_t *kb_base,
+                                                     int s0, int S, int wave, int lane) {
     typedef PrefillTile<Fp8> Pt;
     typedef __attribute__((address_space(3))) void *lds_ptr;
 #pragma unroll
@@ -391,273 +401,14 @@ __device__ __forceinline__ void prefill_issue_tile(uint8_t *buf, const uint8_t *
     }
 }
 
-// Raw buffer resource over `bytes` bytes at `base` (dword 3: the usual
-// untyped-buffer configuration on gfx9); accesses at offsets >= bytes are
-// dropped by the hardware.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
-}
-constexpr int kDropOffset = 0x7ffffff0;  // beyond every buffer here: the store is dropped
-
-// grid: 1-D over (batch, row block, key chunk), heaviest row blocks first
 template <bool Fp8>
-__global__ __launch_bounds__(kPfRows * 64) void indexer_prefill_kernel(
+__global__ __launch_bounds__(kPfWaves * 64) void indexer_prefill_kernel(
     const uint8_t *__restrict__ q_idx, const uint8_t *__restrict__ k_idx,
     const float *__restrict__ w, const int32_t *__restrict__ q_pos, int B, int T, int S,
     int row0, int rows, int kchunk, int nkc, float *__restrict__ scores, size_t batch_stride,
     int write_masked) {
     typedef IdxTraits<Fp8> Tr;
     typedef PrefillTile<Fp8> Pt;
-    typedef typename Tr::operand Op;
-    constexpr int EB = Tr::elem_bytes;
-    constexpr int KS = Tr::ksteps;
-    constexpr int DPS = Tr::dims_per_step;
-    // Four separate LDS objects, named statically in a loop unrolled by four:
-    // the compiler can then tell that the direct-to-LDS loads of later tiles
-    // do not alias the reads of this one, and does not wait for them.
-    __shared__ __align__(16) uint8_t tile0[Pt::bytes];
-    __shared__ __align__(16) uint8_t tile1[Pt::bytes];
-    __shared__ __align__(16) uint8_t tile2[Pt::bytes];
-    __shared__ __align__(16) uint8_t tile3[Pt::bytes];
-    __shared__ int tmax_s[kPfRows];
-    __shared__ __align__(16) float staged[2][kPfRows][kPfKeys];  // one step's scores, all rows
-
-    // wave-uniform as far as the compiler can tell: the row, its buffer
-    // resource and its causal bounds then live in scalar registers
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int half = lane >> 5;
-    const int col = lane & 31;
-    const int nrb = (rows + kPfRows - 1) / kPfRows;
-    const int id = blockIdx.x;
-    const int kc = id % nkc;
-    const int rb = nrb - 1 - (id / nkc) % nrb;  // last (longest) rows first
-    const int b = id / (nkc * nrb);
-    const int r = rb * kPfRows + wave;
-    const bool live = r < rows;
-    const int i = row0 + (live ? r : rows - 1);
-    const int t = live ? query_pos(q_pos, b, i, T, S) : -1;
-    if (lane == 0) tmax_s[wave] = t;
-    __syncthreads();
-    int tmax = tmax_s[0];
-#pragma unroll
-    for (int v = 1; v < kPfRows; ++v) tmax = max(tmax, tmax_s[v]);
-
-    const int k_begin = kc * kchunk;
-    const int k_end = min(S, k_begin + kchunk);
-    float *out = scores + (size_t)b * batch_stride + (size_t)(live ? r : 0) * S;
-    if (live && write_masked) {
-        for (int s = max(k_begin, t + 1) + lane; s < k_end; s += 64) out[s] = -INFINITY;
-    }
-    const int k_hi = min(k_end, tmax + 1);  // keys any row of the block needs
-    if (k_begin >= k_hi) return;             // uniform over the workgroup
-
-    // the storing waves: lane l of wave 6 + j writes 4 consecutive entries
-    // (4(l&15)..) of the staged scores of row 4j + (l>>4); one buffer over the
-    // block's live rows
-    const int srow = 4 * (wave & 1) + (lane >> 4), spart = lane & 15;
-    const int s_hi = min(k_end, tmax_s[srow] + 1);  // that row's causal end in the chunk
-    const int live_rows = min(kPfRows, rows - rb * kPfRows);
-    const __amdgpu_buffer_rsrc_t oblk =
-        raw_buffer(scores + (size_t)b * batch_stride + (size_t)rb * kPfRows * S,
-                   (uint32_t)live_rows * (uint32_t)S * 4u);
-
-    const uint8_t *kb_base = k_idx + (size_t)b * S * Pt::row_bytes;
-    const int last_tile = k_begin + (k_hi - 1 - k_begin) / kPfKeys * kPfKeys;
-    auto issue = [&](uint8_t *buf, int s_tile) {  // past the last tile: reload the last
-        prefill_issue_tile<Fp8>(buf, kb_base, min(s_tile, last_tile), S, wave, lane);
-    };
-    // staged[sb] holds, per row, the previous tile's keys 32..63 (entries
-    // 0..31, first key pk) and this tile's keys 0..31 (entries 32..63, first
-    // key sk); wave 7 writes them out after the next barrier
-    auto flush = [&](int sb, int pk, int sk) {
-        const float4 a = *reinterpret_cast<const float4 *>(&staged[sb][srow][4 * spart]);
-        const float v[4] = {a.x, a.y, a.z, a.w};
-        const int key0 = spart < 8 ? pk + 4 * spart : sk + 4 * spart - 32;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int key = key0 + e;
-            const int off = key >= k_begin && key < s_hi ? (srow * S + key) * 4 : kDropOffset;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), oblk, off, 0, 0);
-        }
-    };
-    if (wave < kPfLoaders) {
-        issue(tile0, k_begin);
-        issue(tile1, k_begin + kPfKeys);
-        issue(tile2, k_begin + 2 * kPfKeys);
-    }
-
-    const size_t qrow = ((size_t)b * T + i) * kIdxHeads;
-    Op qa[2][KS];
-#pragma unroll
-    for (int tl = 0; tl < 2; ++tl) {
-        const uint8_t *qp = q_idx + ((qrow + tl * 32 + col) * kIdxDim + 64 * half) * EB;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qa[tl][ks] = Tr::load(qp + ks * DPS * EB);
-    }
-    float wr[2][16];
-#pragma unroll
-    for (int tl = 0; tl < 2; ++tl)
-#pragma unroll
-        for (int rg = 0; rg < 16; ++rg)
-            wr[tl][rg] = w[qrow + tl * 32 + 8 * (rg >> 2) + 4 * half + (rg & 3)];
-
-    // loads of this tile landed once at most two tiles' loads are outstanding
-    constexpr int kAhead = 2 * Pt::per_loader;
-    constexpr int kWaitThis = (kAhead & 15) | ((kAhead >> 4) << 14) | 0x70 | 0xF00;
-    f32x16 pacc[2] = {f32x16{}, f32x16{}};  // second half of the previous tile
-    int pkey = -64;                          // its first key (none before the first tile)
-    int sb = 0;                              // staging buffer of this step
-    // The storing wave and the loaders run separate copies of the loop, so the
-    // compiler's wait counts on the loaders never see a store.
-    auto step = [&](auto storer, const int s0, const uint8_t *cur, uint8_t *ahead3) {
-        if (!storer) __builtin_amdgcn_s_waitcnt(kWaitThis);
-        lds_barrier();  // ... every loader's; ahead3 (tile s0 - 64) and staged[sb] are free
-        if (storer) {
-            if (s0 > k_begin) flush(sb ^ 1, pkey - 64, s0 - kPfKeys);
-        } else {
-            issue(ahead3, s0 + 3 * kPfKeys);
-        }
-        // One straight block (no per-row branch: a row past its causal end
-        // multiplies a few tiles for nothing, its stores are dropped), so the
-        // scheduler can put the reduction between the products.
-        // The first half's operands now; the second half's are requested
-        // one by one between the first half's products, so the LDS serves
-        // the eight waves' reads spread over the tile rather than in a burst.
-        Op kb[2][KS];
-        auto kb_read = [&](int st, int ks) {
-            kb[st][ks] = Tr::load(cur + (st * 32 + col) * Pt::pitch + 64 * half * EB +
-                                  ks * DPS * EB);
-        };
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kb_read(0, ks);
-        // Explicit interleave: product g of a half tile, then two elements of
-        // the reduction of the previous half tile (ReLU + head weight), with a
-        // scheduling fence after each group so the order holds.
-        f32x16 acc[2] = {f32x16{}, f32x16{}}, nacc[2] = {f32x16{}, f32x16{}};
-        float r0 = 0.0f, r1 = 0.0f, r2 = 0.0f, r3 = 0.0f;  // previous half (pacc)
-        float u0 = 0.0f, u1 = 0.0f, u2 = 0.0f, u3 = 0.0f;  // this tile's first half
-        static_assert(16 % (2 * KS) == 0, "reduction split over the products");
-        constexpr int kPer = 16 / (2 * KS);  // register pairs reduced after each product
-#pragma unroll
-        for (int g = 0; g < 2 * KS; ++g) {
-            const int ks = g >> 1, tl = g & 1;
-            acc[tl] = Tr::mma(qa[tl][ks], kb[0][ks], acc[tl]);
-            if (tl == 1) kb_read(1, ks);
-#pragma unroll
-            for (int e = 0; e < kPer; ++e) {
-                const int idx = g * kPer + e;  // pair 0..15: registers 2idx, 2idx+1 of 32
-                const int rg = (2 * idx) & 15, th = (2 * idx) >> 4;
-                if (th == 0) {
-                    r0 = fmaf(wr[0][rg], relu_bits(pacc[0][rg]), r0);
-                    r1 = fmaf(wr[0][rg + 1], relu_bits(pacc[0][rg + 1]), r1);
-                } else {
-                    r2 = fmaf(wr[1][rg], relu_bits(pacc[1][rg]), r2);
-                    r3 = fmaf(wr[1][rg + 1], relu_bits(pacc[1][rg + 1]), r3);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int g = 0; g < 2 * KS; ++g) {
-            const int ks = g >> 1, tl = g & 1;
-            nacc[tl] = Tr::mma(qa[tl][ks], kb[1][ks], nacc[tl]);
-#pragma unroll
-            for (int e = 0; e < kPer; ++e) {
-                const int idx = g * kPer + e;
-                const int rg = (2 * idx) & 15, th = (2 * idx) >> 4;
-                if (th == 0) {
-                    u0 = fmaf(wr[0][rg], relu_bits(acc[0][rg]), u0);
-                    u1 = fmaf(wr[0][rg + 1], relu_bits(acc[0][rg + 1]), u1);
-                } else {
-                    u2 = fmaf(wr[1][rg], relu_bits(acc[1][rg]), u2);
-                    u3 = fmaf(wr[1][rg + 1], relu_bits(acc[1][rg + 1]), u3);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const float prev = (r0 + r1) + (r2 + r3);
-        const float part0 = (u0 + u1) + (u2 + u3);
-        pacc[0] = nacc[0];
-        pacc[1] = nacc[1];
-        // entries 0..31: the previous tile's keys 32..63; 32..63: this tile's
-        // keys 0..31 (each sum needs the partner half's 32 heads)
-        const float prev_all = sum_halves(prev);
-        const float part_all = sum_halves(part0);
-        staged[sb][wave][lane] = half ? part_all : prev_all;
-        pkey = s0 + 32;
-        sb ^= 1;
-    };
-    auto walk = [&](auto storer) {
-        for (int s0 = k_begin; s0 < k_hi; s0 += kPfRing * kPfKeys) {
-            step(storer, s0, tile0, tile3);
-            if (s0 + kPfKeys < k_hi) step(storer, s0 + kPfKeys, tile1, tile0);
-            if (s0 + 2 * kPfKeys < k_hi) step(storer, s0 + 2 * kPfKeys, tile2, tile1);
-            if (s0 + 3 * kPfKeys < k_hi) step(storer, s0 + 3 * kPfKeys, tile3, tile2);
-        }
-    };
-    if (wave >= kPfLoaders) walk(std::true_type{});
-    else walk(std::false_type{});
-    // the last step's scores, then the last tile's second half
-    __builtin_amdgcn_s_waitcnt(0);  // the surplus tile loads of the last steps
-    lds_barrier();
-    if (wave >= kPfLoaders) flush(sb ^ 1, pkey - 64, pkey - 32);
-    const float last_all = sum_halves(weighted_relu_sum(pacc[0], pacc[1], wr));
-    lds_barrier();  // staged[sb] is free (its previous contents left two steps ago)
-    staged[sb][wave][lane] = half ? 0.0f : last_all;
-    lds_barrier();
-    if (wave >= kPfLoaders) flush(sb, pkey, kDropOffset / 4);
-}
-
-// ------------------------------------------------------ prefill, 16 waves --
-// Same tiles and ring as above, but each query row is split over two waves
-// (one 32-head tile each), 16 waves a workgroup = 4 per SIMD: about 120
-// registers a wave instead of 244, so while one wave waits (LDS operands, the
-// barrier, a dependent product) three others can issue.  The two head tiles'
-// partial sums meet in the LDS staging buffer; waves 12..15 (which issue no
-// tile loads) add them and write the scores.
-constexpr int kP16Waves = 16;
-constexpr int kP16Loaders = 12;
-constexpr int kP16Ahead = 4;  // operand fragments read ahead of their product
-
-template <bool Fp8>
-struct Prefill16Tile {
-    static constexpr int row_bytes = kIdxDim * IdxTraits<Fp8>::elem_bytes;
-    static constexpr int pitch = row_bytes + 16;
-    static constexpr int slots = pitch / 16;
-    static constexpr int loads = (kPfKeys * slots + 63) / 64;
-    static constexpr int per_loader = (loads + kP16Loaders - 1) / kP16Loaders;
-    static constexpr int bytes = per_loader * kP16Loaders * 1024;
-};
-
-template <bool Fp8>
-__device__ __forceinline__ void prefill16_issue_tile(uint8_t *buf, const uint8_t *kb_base,
-                                                     int s0, int S, int wave, int lane) {
-    typedef Prefill16Tile<Fp8> Pt;
-    typedef __attribute__((address_space(3))) void *lds_ptr;
-#pragma unroll
-    for (int m = 0; m < Pt::per_loader; ++m) {
-        const int j = wave + kP16Loaders * m;
-        const int q = 64 * j + lane;
-        const int row = q / Pt::slots;
-        const int piece = q - row * Pt::slots;
-        int key = s0 + row;
-        key = key < S ? key : 0;  // rows past the cache load row 0; never used
-        const bool real = q < kPfKeys * Pt::slots && piece * 16 < Pt::row_bytes;
-        const uint8_t *src = kb_base + (size_t)(real ? key : s0) * Pt::row_bytes +
-                             (real ? piece * 16 : 0);
-        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(buf + 1024 * j), 16, 0, 0);
-    }
-}
-
-template <bool Fp8>
-__global__ __launch_bounds__(kP16Waves * 64) void indexer_prefill16_kernel(
-    const uint8_t *__restrict__ q_idx, const uint8_t *__restrict__ k_idx,
-    const float *__restrict__ w, const int32_t *__restrict__ q_pos, int B, int T, int S,
-    int row0, int rows, int kchunk, int nkc, float *__restrict__ scores, size_t batch_stride,
-    int write_masked) {
-    typedef IdxTraits<Fp8> Tr;
-    typedef Prefill16Tile<Fp8> Pt;
     typedef typename Tr::operand Op;
     constexpr int EB = Tr::elem_bytes;
     constexpr int KS = Tr::ksteps;
@@ -700,7 +451,7 @@ __global__ __launch_bounds__(kP16Waves * 64) void indexer_prefill16_kernel(
 
     // storing waves 12 + j: lane l adds and writes entries 2(l&31), 2(l&31)+1
     // of row 2j + (l>>5)
-    const bool storer = wave >= kP16Loaders;
+    const bool storer = wave >= kPfLoaders;
     const int srow = 2 * (wave & 3) + half, spart = col;
     const int s_hi = min(k_end, tmax_s[srow] + 1);
     const int live_rows = min(kPfRows, rows - rb * kPfRows);
@@ -711,7 +462,7 @@ __global__ __launch_bounds__(kP16Waves * 64) void indexer_prefill16_kernel(
     const uint8_t *kb_base = k_idx + (size_t)b * S * Pt::row_bytes;
     const int last_tile = k_begin + (k_hi - 1 - k_begin) / kPfKeys * kPfKeys;
     auto issue = [&](uint8_t *buf, int s_tile) {
-        prefill16_issue_tile<Fp8>(buf, kb_base, min(s_tile, last_tile), S, wave, lane);
+        prefill_issue_tile<Fp8>(buf, kb_base, min(s_tile, last_tile), S, wave, lane);
     };
     auto flush = [&](int sb, int pk, int sk) {
         const float2 a = *reinterpret_cast<const float2 *>(&staged[sb][srow][0][2 * spart]);
@@ -761,7 +512,7 @@ __global__ __launch_bounds__(kP16Waves * 64) void indexer_prefill16_kernel(
             issue(ahead3, s0 + 3 * kPfKeys);
         }
         constexpr int NF = 2 * KS;
-        constexpr int DA = kP16Ahead < NF ? kP16Ahead : NF;
+        constexpr int DA = kPfAhead < NF ? kPfAhead : NF;
         Op kb[NF];
 #pragma unroll
         for (int f = 0; f < DA; ++f) kb[f] = frag(cur, f);
@@ -904,14 +655,14 @@ hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, c
             const int nkc = ceil_div(S, kchunk);
             const long long wgs = (long long)B * ceil_div(rows, kPfRows) * nkc;
             if (idx_dtype == DSA_BF16)
-                hipLaunchKernelGGL((indexer_prefill16_kernel<false>), dim3((unsigned)wgs),
-                                   dim3(kP16Waves * 64), 0, stream,
+                hipLaunchKernelGGL((indexer_prefill_kernel<false>), dim3((unsigned)wgs),
+                                   dim3(kPfWaves * 64), 0, stream,
                                    static_cast<const uint8_t *>(q_idx),
                                    static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
                                    rows, kchunk, nkc, scores, batch_stride, (int)write_masked);
             else
-                hipLaunchKernelGGL((indexer_prefill16_kernel<true>), dim3((unsigned)wgs),
-                                   dim3(kP16Waves * 64), 0, stream,
+                hipLaunchKernelGGL((indexer_prefill_kernel<true>), dim3((unsigned)wgs),
+                                   dim3(kPfWaves * 64), 0, stream,
                                    static_cast<const uint8_t *>(q_idx),
                                    static_cast<const uint8_t *>(k_idx), w, q_pos, B, T, S, row0,
                                    rows, kchunk, nkc, scores, batch_stride, (int)write_masked);
