@@ -175,10 +175,9 @@ __global__ __launch_bounds__(256) void indexer_mfma_kernel(
             acc0 = Tr::mma(qa[0][ks], kb[ks], acc0);
             acc1 = Tr::mma(qa[1][ks], kb[ks], acc1);
         }
-        const float part = weighted_relu_sum(acc0, acc1, wr);
-        const float other = __shfl_xor(part, 32, 64);
+        const float all = sum_halves(weighted_relu_sum(acc0, acc1, wr));
         const int key = s0 + col;
-        if (half == 0 && key < s_hi) out[key] = part + other;
+        if (half == 0 && key < s_hi) out[key] = all;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kb[ks] = kn[ks];
     }
@@ -319,9 +318,8 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
                 acc0 = Tr::mma(qa[0][ks], kb[ks], acc0);
                 acc1 = Tr::mma(qa[1][ks], kb[ks], acc1);
             }
-            const float part = weighted_relu_sum(acc0, acc1, wr);
-            const float other = __shfl_xor(part, 32, 64);
-            if (half == 0 && m < ntiles) stage[m * kKeyTile + col] = part + other;
+            const float all = sum_halves(weighted_relu_sum(acc0, acc1, wr));
+            if (half == 0 && m < ntiles) stage[m * kKeyTile + col] = all;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
