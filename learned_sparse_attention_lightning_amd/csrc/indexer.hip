@@ -334,17 +334,21 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
 
 // ---------------------------------------------------------- prefill tile --
 // Prefill: consecutive query rows read (almost) the same keys, so a workgroup
-// owns 8 consecutive rows and a range of keys; each 64-key tile is brought
-// into LDS once for all 8 rows (direct-to-LDS loads, issued three tiles ahead
-// into a ring of four buffers) and every wave reads its B operands from
+// owns 8 consecutive rows and a range of keys; each 128-key tile is brought
+// into LDS once for all 8 rows (direct-to-LDS loads, issued two tiles ahead
+// into a ring of three buffers) and every wave reads its B operands from
 // there.  Row pitch = row + 16 bytes, so the operand reads are free of bank
-// conflicts.
+// conflicts.  One barrier a tile: the longer the tile, the smaller the share
+// of the per-barrier costs (the drain of the matrix pipe before it, the
+// operand reads after it, the hand-over of the scores).
 //
 // Each query row is split over two waves (one 32-head tile each): 16 waves a
-// workgroup, 4 per SIMD, about 120 registers a wave.  Software pipeline inside
-// a wave: the products of a half tile (32 keys) run while the VALU reduces
-// the previous half tile (ReLU, head weights), so the matrix pipe always has
-// independent work next to the reduction.
+// workgroup, 4 per SIMD, at most 128 registers a wave.  Software pipeline
+// inside a wave: a tile is four quarters of 32 keys; the products of a
+// quarter go to one of two accumulator sets while the VALU reduces the other
+// set (the previous quarter: ReLU, head weights), so the matrix pipe always
+// has independent work next to the reduction, and the two sets alternate
+// without copies.
 //
 // Waves 0..11 issue the tile loads, the same number every tile, and no other
 // memory operation, so the wait for a tile's loads is one static vmcnt (loads
@@ -353,9 +357,10 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(
 // waves 12..15, which issue no loads, add the two head tiles' partials and
 // write the scores with bounds-checked buffer stores (keys outside a row's
 // causal range get an offset past the buffer and are dropped).
-constexpr int kPfRows = 8;     // query rows per workgroup
-constexpr int kPfKeys = 64;    // keys per LDS tile
-constexpr int kPfRing = 4;     // tile buffers; loads run three tiles ahead
+constexpr int kPfRows = 8;                   // query rows per workgroup
+constexpr int kPfKeys = 128;                 // keys per LDS tile
+constexpr int kPfQuarters = kPfKeys / 32;    // 32-key product blocks a tile
+constexpr int kPfRing = 3;                   // tile buffers; loads run two tiles ahead
 
 // Raw buffer resource over `bytes` bytes at `base` (dword 3: the usual
 // untyped-buffer configuration on gfx9); accesses at offsets >= bytes are
@@ -365,8 +370,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(void *base, uint32_
 }
 constexpr int kDropOffset = 0x7ffffff0;  // beyond every buffer here: the store is dropped
 
-constexpr int kPfWaves = 16;
-constexpr int kPfLoaders = 12;
+constexpr int kPfWaves = 2 * kPfRows;           // a wave per (row, 32-head tile)
+constexpr int kPfStorers = kPfRows / 2;         // a storing wave per two rows
+constexpr int kPfLoaders = kPfWaves - kPfStorers;
+static_assert(kPfRows % 2 == 0, "storing waves take rows in pairs");
+static_assert(kPfQuarters % 2 == 0, "the two accumulator sets alternate evenly over a tile");
+constexpr int kPfMinWgs = 2 * 256 * 16 / kPfWaves;  // two rounds of 4 waves a SIMD
 constexpr int kPfAhead = 4;  // operand fragments read ahead of their product
 
 template <bool Fp8>
@@ -379,28 +388,47 @@ struct PrefillTile {
     static constexpr int bytes = per_loader * kPfLoaders * 1024;
 };
 
+// Byte offset, inside a tile's key rows, of the 16 bytes that lane `lane` of
+// loading wave `wave` brings in with its m-th load; slots of the LDS row
+// padding get an offset past every tile and are filled with zeros.
+template <bool Fp8>
+__device__ __forceinline__ uint32_t prefill_load_offset(int wave, int lane, int m) {
+    typedef PrefillTile<Fp8> Pt;
+    const int q = 64 * (wave + kPfLoaders * m) + lane;
+    const int row = q / Pt::slots;
+    const int piece = q - row * Pt::slots;
+    const bool real = q < kPfKeys * Pt::slots && piece * 16 < Pt::row_bytes;
+    return real ? (uint32_t)(row * Pt::row_bytes + piece * 16) : (uint32_t)kDropOffset;
+}
+
+// Buffer loads straight to LDS over the tile's rows: rows past the cache are
+// outside the buffer and read as zeros (their scores are never stored).
 template <bool Fp8>
 __device__ __forceinline__ void prefill_issue_tile(uint8_t *buf, const uint8_t *kb_base,
-                                                     int s0, int S, int wave, int lane) {
+                                                     int s0, int S, int wave,
+                                                     const uint32_t *voff) {
     typedef PrefillTile<Fp8> Pt;
     typedef __attribute__((address_space(3))) void *lds_ptr;
+    const __amdgpu_buffer_rsrc_t rs =
+        raw_buffer(const_cast<uint8_t *>(kb_base) + (size_t)s0 * Pt::row_bytes,
+                   (uint32_t)min(S - s0, kPfKeys) * (uint32_t)Pt::row_bytes);
 #pragma unroll
-    for (int m = 0; m < Pt::per_loader; ++m) {
-        const int j = wave + kPfLoaders * m;
-        const int q = 64 * j + lane;
-        const int row = q / Pt::slots;
-        const int piece = q - row * Pt::slots;
-        int key = s0 + row;
-        key = key < S ? key : 0;  // rows past the cache load row 0; never used
-        const bool real = q < kPfKeys * Pt::slots && piece * 16 < Pt::row_bytes;
-        const uint8_t *src = kb_base + (size_t)(real ? key : s0) * Pt::row_bytes +
-                             (real ? piece * 16 : 0);
-        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(buf + 1024 * j), 16, 0, 0);
-    }
+    for (int m = 0; m < Pt::per_loader; ++m)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(buf + 1024 * (wave + kPfLoaders * m)),
+                                                 16, voff[m], 0, 0, 0);
+}
+
+// Lanes 0..31 get lo summed over the two half-waves, lanes 32..63 get hi
+// summed likewise (one lane swap: lanes 32..63 of the first operand trade
+// places with lanes 0..31 of the second).
+__device__ __forceinline__ float sum_pair_halves(float lo, float hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi),
+                                                     false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <bool Fp8>
-__global__ __launch_bounds__(kPfWaves * 64) void indexer_prefill_kernel(
+__global__ __launch_bounds__(kPfWaves * 64, 4) void indexer_prefill_kernel(
     const uint8_t *__restrict__ q_idx, const uint8_t *__restrict__ k_idx,
     const float *__restrict__ w, const int32_t *__restrict__ q_pos, int B, int T, int S,
     int row0, int rows, int kchunk, int nkc, float *__restrict__ scores, size_t batch_stride,
@@ -414,15 +442,17 @@ __global__ __launch_bounds__(kPfWaves * 64) void indexer_prefill_kernel(
     __shared__ __align__(16) uint8_t tile0[Pt::bytes];
     __shared__ __align__(16) uint8_t tile1[Pt::bytes];
     __shared__ __align__(16) uint8_t tile2[Pt::bytes];
-    __shared__ __align__(16) uint8_t tile3[Pt::bytes];
     __shared__ int tmax_s[kPfRows];
-    __shared__ __align__(16) float staged[2][kPfRows][2][kPfKeys];  // [step][row][head tile][entry]
+    // [buffer][row][head tile][entry]; entry e of a tile's scores is key base + e,
+    // base = the tile's first key - 32 (its first 32 entries hold the previous
+    // tile's last quarter)
+    __shared__ __align__(16) float staged[2][kPfRows][2][kPfKeys];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
     const int col = lane & 31;
-    const int rw = wave & 7, ht = wave >> 3;  // row in the block, head tile
+    const int rw = wave % kPfRows, ht = wave / kPfRows;  // row in the block, head tile
     const int nrb = (rows + kPfRows - 1) / kPfRows;
     const int id = blockIdx.x;
     const int kc = id % nkc;
@@ -447,10 +477,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void indexer_prefill_kernel(
     const int k_hi = min(k_end, tmax + 1);  // keys any row of the block needs
     if (k_begin >= k_hi) return;             // uniform over the workgroup
 
-    // storing waves 12 + j: lane l adds and writes entries 2(l&31), 2(l&31)+1
-    // of row 2j + (l>>5)
+    // storing wave kPfLoaders + j: lane l adds and writes entries 4(l&31) ..
+    // 4(l&31)+3 of row 2j + (l>>5)
     const bool storer = wave >= kPfLoaders;
-    const int srow = 2 * (wave & 3) + half, spart = col;
+    const int srow = storer ? 2 * (wave - kPfLoaders) + half : 0, spart = col;
     const int s_hi = min(k_end, tmax_s[srow] + 1);
     const int live_rows = min(kPfRows, rows - rb * kPfRows);
     const __amdgpu_buffer_rsrc_t oblk =
@@ -459,17 +489,19 @@ __global__ __launch_bounds__(kPfWaves * 64) void indexer_prefill_kernel(
 
     const uint8_t *kb_base = k_idx + (size_t)b * S * Pt::row_bytes;
     const int last_tile = k_begin + (k_hi - 1 - k_begin) / kPfKeys * kPfKeys;
-    auto issue = [&](uint8_t *buf, int s_tile) {
-        prefill_issue_tile<Fp8>(buf, kb_base, min(s_tile, last_tile), S, wave, lane);
-    };
-    auto flush = [&](int sb, int pk, int sk) {
-        const float2 a = *reinterpret_cast<const float2 *>(&staged[sb][srow][0][2 * spart]);
-        const float2 c = *reinterpret_cast<const float2 *>(&staged[sb][srow][1][2 * spart]);
-        const float v[2] = {a.x + c.x, a.y + c.y};
-        const int key0 = spart < 16 ? pk + 2 * spart : sk + 2 * spart - 32;
+    uint32_t voff[Pt::per_loader];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int key = key0 + e;
+    for (int m = 0; m < Pt::per_loader; ++m) voff[m] = prefill_load_offset<Fp8>(wave, lane, m);
+    auto issue = [&](uint8_t *buf, int s_tile) {
+        prefill_issue_tile<Fp8>(buf, kb_base, min(s_tile, last_tile), S, wave, voff);
+    };
+    auto flush = [&](int sb, int base) {
+        const float4 a = *reinterpret_cast<const float4 *>(&staged[sb][srow][0][4 * spart]);
+        const float4 c = *reinterpret_cast<const float4 *>(&staged[sb][srow][1][4 * spart]);
+        const float v[4] = {a.x + c.x, a.y + c.y, a.z + c.z, a.w + c.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int key = base + 4 * spart + e;
             const int off = key >= k_begin && key < s_hi ? (srow * S + key) * 4 : kDropOffset;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), oblk, off, 0, 0);
         }
@@ -477,7 +509,6 @@ __global__ __launch_bounds__(kPfWaves * 64) void indexer_prefill_kernel(
     if (!storer) {
         issue(tile0, k_begin);
         issue(tile1, k_begin + kPfKeys);
-        issue(tile2, k_begin + 2 * kPfKeys);
     }
 
     const size_t qrow = ((size_t)b * T + i) * kIdxHeads + ht * 32;
@@ -491,78 +522,88 @@ __global__ __launch_bounds__(kPfWaves * 64) void indexer_prefill_kernel(
 #pragma unroll
     for (int rg = 0; rg < 16; ++rg) wr[rg] = w[qrow + 8 * (rg >> 2) + 4 * half + (rg & 3)];
 
-    constexpr int kAhead = 2 * Pt::per_loader;
+    constexpr int kAhead = Pt::per_loader;  // loads of the next tile, still in flight
     constexpr int kWaitThis = (kAhead & 15) | ((kAhead >> 4) << 14) | 0x70 | 0xF00;
-    f32x16 pacc = f32x16{};  // second half of the previous tile
-    int pkey = -64;
+    // products of the even quarters go to acc_a, of the odd ones to acc_b; the
+    // last quarter of a tile is reduced during the first quarter of the next
+    f32x16 acc_a = f32x16{}, acc_b = f32x16{};
+    int pbase = k_begin - kPfKeys - 32;
     int sb = 0;
-    // operand fragment f (0..2KS-1: half f/KS, k-step f%KS) of tile cur
+    // operand fragment f (quarter f/KS, k-step f%KS) of tile cur
     auto frag = [&](const uint8_t *cur, int f) -> Op {
         const int st = f / KS, ks = f % KS;
         return Tr::load(cur + (st * 32 + col) * Pt::pitch + 64 * half * EB + ks * DPS * EB);
     };
-    auto step = [&](auto is_storer, const int s0, const uint8_t *cur, uint8_t *ahead3) {
+    static_assert(KS >= 2, "the reduction starts one product into a quarter");
+    // element rg of the previous quarter is reduced after product red(rg) of
+    // the current one: from the second product on, so the last product of the
+    // previous quarter has finished before its accumulators are read
+    auto red = [](int rg) { return 1 + rg * (KS - 1) / 16; };
+    auto step = [&](auto is_storer, const int s0, const uint8_t *cur,
+                    uint8_t *ahead2) __attribute__((always_inline)) {
         if (!is_storer) __builtin_amdgcn_s_waitcnt(kWaitThis);
         lds_barrier();
         if (is_storer) {
-            if (s0 > k_begin) flush(sb ^ 1, pkey - 64, s0 - kPfKeys);
+            if (s0 > k_begin) flush(sb ^ 1, pbase);
         } else {
-            issue(ahead3, s0 + 3 * kPfKeys);
+            issue(ahead2, s0 + 2 * kPfKeys);
         }
-        constexpr int NF = 2 * KS;
+        constexpr int NF = kPfQuarters * KS;
         constexpr int DA = kPfAhead < NF ? kPfAhead : NF;
         Op kb[NF];
 #pragma unroll
         for (int f = 0; f < DA; ++f) kb[f] = frag(cur, f);
-        f32x16 acc = f32x16{}, nacc = f32x16{};
-        float r0 = 0.0f, r1 = 0.0f, r2 = 0.0f, r3 = 0.0f;
-        float u0 = 0.0f, u1 = 0.0f, u2 = 0.0f, u3 = 0.0f;
-        static_assert(16 % KS == 0, "reduction split over the products");
-        constexpr int kPer = 16 / KS;  // elements reduced after each product
+        float sums[kPfQuarters];  // [0]: previous tile's last quarter, [q]: quarter q-1
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            if (f + DA < NF) kb[f + DA] = frag(cur, f + DA);
-            const int ks = f % KS;
-            if (f < KS) acc = Tr::mma(qa[ks], kb[f], acc);
-            else nacc = Tr::mma(qa[ks], kb[f], nacc);
+        for (int qt = 0; qt < kPfQuarters; ++qt) {
+            f32x16 &dst = (qt & 1) ? acc_b : acc_a;
+            const f32x16 &src = (qt & 1) ? acc_a : acc_b;
+            float r0, r1;  // even and odd elements; both start after product red(0) = red(1)
 #pragma unroll
-            for (int e = 0; e < kPer; ++e) {
-                const int rg = ks * kPer + e;
-                float &rr = (rg & 1) ? ((rg & 2) ? r3 : r1) : ((rg & 2) ? r2 : r0);
-                float &uu = (rg & 1) ? ((rg & 2) ? u3 : u1) : ((rg & 2) ? u2 : u0);
-                if (f < KS) rr = fmaf(wr[rg], relu_bits(pacc[rg]), rr);
-                else uu = fmaf(wr[rg], relu_bits(acc[rg]), uu);
+            for (int ks = 0; ks < KS; ++ks) {
+                const int f = qt * KS + ks;
+                if (f + DA < NF) kb[f + DA] = frag(cur, f + DA);
+                dst = Tr::mma(qa[ks], kb[f], ks == 0 ? f32x16{} : dst);
+#pragma unroll
+                for (int rg = 0; rg < 16; ++rg) {
+                    float &rr = (rg & 1) ? r1 : r0;
+                    if (red(rg) != ks) continue;
+                    const float x = wr[rg] * relu_bits(src[rg]);
+                    rr = rg < 2 ? x : rr + x;
+                }
+                // The sums are materialised here, so the compiler cannot sink the
+                // reduction below the remaining products: interleaved, the VALU
+                // work of one wave runs while the matrix unit serves the others.
+                if (ks >= red(1)) asm volatile("" : "+v"(r0), "+v"(r1));
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
+            sums[qt] = r0 + r1;
         }
-        pacc = nacc;
-        const float prev_all = sum_halves((r0 + r1) + (r2 + r3));
-        const float part_all = sum_halves((u0 + u1) + (u2 + u3));
-        staged[sb][rw][ht][lane] = half ? part_all : prev_all;
-        pkey = s0 + 32;
+        staged[sb][rw][ht][lane] = sum_pair_halves(sums[0], sums[1]);
+        staged[sb][rw][ht][64 + lane] = sum_pair_halves(sums[2], sums[3]);
+        pbase = s0 - 32;
         sb ^= 1;
     };
-    auto walk = [&](auto is_storer) {
+    auto walk = [&](auto is_storer) __attribute__((always_inline)) {
         for (int s0 = k_begin; s0 < k_hi; s0 += kPfRing * kPfKeys) {
-            step(is_storer, s0, tile0, tile3);
+            step(is_storer, s0, tile0, tile2);
             if (s0 + kPfKeys < k_hi) step(is_storer, s0 + kPfKeys, tile1, tile0);
             if (s0 + 2 * kPfKeys < k_hi) step(is_storer, s0 + 2 * kPfKeys, tile2, tile1);
-            if (s0 + 3 * kPfKeys < k_hi) step(is_storer, s0 + 3 * kPfKeys, tile3, tile2);
         }
     };
     if (storer) walk(std::true_type{});
     else walk(std::false_type{});
     __builtin_amdgcn_s_waitcnt(0);  // the surplus tile loads of the last steps
     lds_barrier();
-    if (storer) flush(sb ^ 1, pkey - 64, pkey - 32);
+    if (storer) flush(sb ^ 1, pbase);
     float last = 0.0f;
 #pragma unroll
-    for (int rg = 0; rg < 16; ++rg) last = fmaf(wr[rg], relu_bits(pacc[rg]), last);
-    const float last_all = sum_halves(last);
+    for (int rg = 0; rg < 16; ++rg) last = fmaf(wr[rg], relu_bits(acc_b[rg]), last);
+    const float last_all = sum_pair_halves(last, 0.0f);
     lds_barrier();  // staged[sb] is free (its previous contents left two steps ago)
-    staged[sb][rw][ht][lane] = half ? 0.0f : last_all;
+    staged[sb][rw][ht][lane] = last_all;  // keys pbase + kPfKeys + lane; the rest is dropped
     lds_barrier();
-    if (storer) flush(sb, pkey, kDropOffset / 4);
+    if (storer) flush(sb, pbase + kPfKeys);
 }
 
 // ------------------------------------------------------------- generic ----
@@ -648,7 +689,7 @@ hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, c
             // 512 of them.
             int kchunk = 4096;
             while (kchunk < S) kchunk <<= 1;
-            while (kchunk > 4096 && (long long)B * ceil_div(rows, kPfRows) * ceil_div(S, kchunk) < 512)
+            while (kchunk > 4096 && (long long)B * ceil_div(rows, kPfRows) * ceil_div(S, kchunk) < kPfMinWgs)
                 kchunk >>= 1;
             const int nkc = ceil_div(S, kchunk);
             const long long wgs = (long long)B * ceil_div(rows, kPfRows) * nkc;
