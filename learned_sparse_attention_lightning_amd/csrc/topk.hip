@@ -106,19 +106,17 @@ struct SelectSmem {
     uint32_t found_bin, found_above;
 };
 
-// Key value tau of the need-th largest of n keys key_at(0..n-1), and how many
-// keys equal to tau belong to the top `need` (need_out).  1 <= need <= n.
-// Called by all kTkThreads threads; the result is uniform.
-template <typename KeyAt>
-__device__ void block_select(KeyAt key_at, int n, uint32_t need, SelectSmem &sm,
-                             uint32_t &tau_out, uint32_t &need_out) {
+// Smallest and largest of the keys this thread visits, reduced over the
+// workgroup (uniform result).  `each(f)` calls f(key) for every key the
+// calling thread owns.
+template <typename Each>
+__device__ void block_key_range(Each each, SelectSmem &sm, uint32_t &lo_out, uint32_t &hi_out) {
     const int tid = threadIdx.x;
     uint32_t lo = 0xffffffffu, hi = 0u;
-    for (int p = tid; p < n; p += kTkThreads) {
-        const uint32_t u = key_at(p);
+    each([&](uint32_t u) {
         lo = min(lo, u);
         hi = max(hi, u);
-    }
+    });
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
@@ -137,7 +135,18 @@ __device__ void block_select(KeyAt key_at, int n, uint32_t need, SelectSmem &sm,
         hi = max(hi, sm.red_hi[v]);
     }
     __syncthreads();
+    lo_out = lo;
+    hi_out = hi;
+}
 
+// Key value tau of the need-th largest of the keys visited by `each` (every
+// key of the set, over the workgroup), all of which lie in [lo, hi], and how
+// many keys equal to tau belong to the top `need` (need_out).  1 <= need <=
+// number of keys.  Called by all kTkThreads threads; the result is uniform.
+template <typename Each>
+__device__ void block_select_in(Each each, uint32_t lo, uint32_t hi, uint32_t need,
+                                SelectSmem &sm, uint32_t &tau_out, uint32_t &need_out) {
+    const int tid = threadIdx.x;
     while (lo != hi) {  // invariant: keys > hi are taken; need more lie in [lo, hi]
         const uint32_t range = hi - lo;
         int shift = 0;
@@ -145,10 +154,9 @@ __device__ void block_select(KeyAt key_at, int n, uint32_t need, SelectSmem &sm,
         const int nb = (int)(range >> shift) + 1;
         for (int j = tid; j < nb; j += kTkThreads) sm.hist[j] = 0u;
         __syncthreads();
-        for (int p = tid; p < n; p += kTkThreads) {
-            const uint32_t u = key_at(p);
+        each([&](uint32_t u) {
             if (u >= lo && u <= hi) atomicAdd(&sm.hist[(u - lo) >> shift], 1u);
-        }
+        });
         __syncthreads();
         {  // bin holding the need-th largest: suffix counts over thread-owned bin pairs
             constexpr int kPer = kTkBins / kTkThreads;  // 2 bins per thread
@@ -185,13 +193,31 @@ __device__ void block_select(KeyAt key_at, int n, uint32_t need, SelectSmem &sm,
     need_out = need;
 }
 
+// block_select_in over keys key_at(0..n-1), range found first.
+template <typename KeyAt>
+__device__ void block_select(KeyAt key_at, int n, uint32_t need, SelectSmem &sm,
+                             uint32_t &tau_out, uint32_t &need_out) {
+    auto each = [&](auto f) {
+        for (int p = threadIdx.x; p < n; p += kTkThreads) f(key_at(p));
+    };
+    uint32_t lo, hi;
+    block_key_range(each, sm, lo, hi);
+    block_select_in(each, lo, hi, need, sm, tau_out, need_out);
+}
+
 // ------------------------------------------------------- per-row kernel ----
 struct RowSmem {
     SelectSmem sel;
-    uint32_t scan[kTkWaves];
-    uint32_t keys[kRowCache];
+    uint32_t cnt_gt[kTkWaves], cnt_eq[kTkWaves];
+    __align__(16) uint32_t keys[kRowCache];
 };
 
+// One workgroup per row.  A cached row is read with 16-byte loads, four in
+// flight per thread, converted to keys on the way into LDS; the threshold
+// search and the selection then read LDS only.  The selection gives each
+// wave one contiguous segment of positions: a first sweep counts the keys
+// above tau and equal to tau per wave, and after one barrier a second sweep
+// writes the wave's selected positions in order (ballot prefix counts).
 __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
     const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
     int T, int S, int row0, int k, int32_t *__restrict__ idx) {
@@ -204,36 +230,101 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
     int32_t *out = idx + ((size_t)b * T + i) * k;
     const int n = t < 0 ? 0 : t + 1;
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
 
     if (n <= k) {  // every candidate is selected
         for (int p = tid; p < k; p += kTkThreads) out[p] = p < n ? p : -1;
         return;
     }
     const bool cached = n <= kRowCache;
+    const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+    uint32_t lo, hi;
     if (cached) {
-        for (int p = tid; p < n; p += kTkThreads) sm.keys[p] = ordered_key(row[p]);
-        __syncthreads();
+        // 16-byte pieces j = tid + kTkThreads * (4 * it + u), four loads in flight
+        const int n16 = aligned ? n / 4 : 0;  // whole pieces read as vectors
+        uint32_t vlo = 0xffffffffu, vhi = 0u;
+        for (int j0 = tid; j0 < n16; j0 += 4 * kTkThreads) {
+            f32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + u * kTkThreads;
+                if (j < n16) v[u] = reinterpret_cast<const f32x4 *>(row)[j];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + u * kTkThreads;
+                if (j < n16) {
+                    uint32_t kk[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        kk[e] = ordered_key(v[u][e]);
+                        vlo = min(vlo, kk[e]);
+                        vhi = max(vhi, kk[e]);
+                    }
+                    reinterpret_cast<u32x4 *>(sm.keys)[j] = u32x4{kk[0], kk[1], kk[2], kk[3]};
+                }
+            }
+        }
+        for (int p = 4 * n16 + tid; p < n; p += kTkThreads) {
+            const uint32_t u = ordered_key(row[p]);
+            sm.keys[p] = u;
+            vlo = min(vlo, u);
+            vhi = max(vhi, u);
+        }
+        // the range reduction's barriers also publish the keys
+        block_key_range([&](auto f) { f(vlo); f(vhi); }, sm.sel, lo, hi);
     }
     auto key_at = [&](int p) -> uint32_t { return cached ? sm.keys[p] : ordered_key(row[p]); };
+    auto each = [&](auto f) {
+        if (cached) {
+            const int n16 = (n + 3) / 4;
+            for (int j = tid; j < n16; j += kTkThreads) {
+                const u32x4 v = reinterpret_cast<const u32x4 *>(sm.keys)[j];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * j + e < n) f(v[e]);
+            }
+        } else {
+            for (int p = tid; p < n; p += kTkThreads) f(ordered_key(row[p]));
+        }
+    };
+    if (!cached) block_key_range(each, sm.sel, lo, hi);
 
     uint32_t tau, need;
-    block_select(key_at, n, (uint32_t)k, sm.sel, tau, need);
+    block_select_in(each, lo, hi, (uint32_t)k, sm.sel, tau, need);
 
-    // ordered compaction: all keys > tau, plus the first `need` ties
-    uint32_t written = 0u, ties_seen = 0u;
-    for (int base = 0; base < n; base += kTkThreads) {
-        const int p = base + tid;
-        const uint32_t u = p < n ? key_at(p) : 0u;
-        const bool gt = p < n && u > tau;
-        const bool eq = p < n && u == tau;
-        uint32_t eq_total;
-        const uint32_t eq_rank = block_flag_scan<kTkWaves>(eq, sm.scan, eq_total);
-        const bool take = gt || (eq && ties_seen + eq_rank < need);
-        uint32_t take_total;
-        const uint32_t slot = block_flag_scan<kTkWaves>(take, sm.scan, take_total);
-        if (take) out[written + slot] = p;
-        written += take_total;
-        ties_seen += eq_total;
+    // ordered selection: all keys > tau, plus the first `need` keys == tau
+    const int seg = ceil_div(ceil_div(n, kTkWaves), 64) * 64;  // positions per wave
+    const int w0 = wave * seg, w1 = min(n, w0 + seg);
+    uint32_t c_gt = 0u, c_eq = 0u;
+    for (int p0 = w0; p0 < w1; p0 += 64) {
+        const int p = p0 + lane;
+        const uint32_t u = p < w1 ? key_at(p) : 0u;
+        c_gt += (uint32_t)__popcll(__ballot(p < w1 && u > tau));
+        c_eq += (uint32_t)__popcll(__ballot(p < w1 && u == tau));
+    }
+    if (lane == 0) {
+        sm.cnt_gt[wave] = c_gt;
+        sm.cnt_eq[wave] = c_eq;
+    }
+    __syncthreads();
+    uint32_t gt_before = 0u, eq_before = 0u;
+    for (int v = 0; v < wave; ++v) {
+        gt_before += sm.cnt_gt[v];
+        eq_before += sm.cnt_eq[v];
+    }
+    uint32_t written = gt_before + min(eq_before, need), ties = eq_before;
+    for (int p0 = w0; p0 < w1; p0 += 64) {
+        const int p = p0 + lane;
+        const uint32_t u = p < w1 ? key_at(p) : 0u;
+        const bool gt = p < w1 && u > tau;
+        const bool eq = p < w1 && u == tau;
+        const uint64_t eqm = __ballot(eq);
+        const bool take = gt || (eq && ties + lanes_below(eqm) < need);
+        const uint64_t tm = __ballot(take);
+        if (take) out[written + lanes_below(tm)] = p;
+        written += (uint32_t)__popcll(tm);
+        ties += (uint32_t)__popcll(eqm);
     }
 }
 

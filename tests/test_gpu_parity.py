@@ -158,6 +158,20 @@ def test_topk_wide_rows(S):
     assert_selection_equal(idx, oracle.topk(sc, k, q_pos=pos), f"S={S}")
 
 
+def test_topk_many_long_rows():
+    """More rows than the split-row path takes, longer than the per-row LDS
+    cache: the per-row kernel reads the scores from memory on every pass."""
+    B, T, S, k = 1, 520, 40001, 2048
+    pos = torch.tensor([[S - 1 - 37 * j for j in range(T)]], dtype=torch.int32)
+    sc = synth.random_scores((B, T, S), seed=11, levels=None)
+    sc[0, 5, :20000] = 0.25  # a block of ties
+    idx = dsa.dsa_topk(sc.to(DEV), k, q_pos=pos.to(DEV))
+    rows = [0, 1, 5, 100, 257, 518, 519]
+    _say(f"many long rows: comparing rows {rows}")
+    ref = oracle.topk(sc[:, rows], k, q_pos=pos[:, rows])
+    assert_selection_equal(idx[:, rows], ref, "many long rows")
+
+
 def test_topk_ties_signed_zero_and_short_rows():
     sc = torch.zeros(1, 50, 50)
     sc[0, :, 1::2] = -0.0
