@@ -296,13 +296,36 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
     // ordered selection: all keys > tau, plus the first `need` keys == tau
     const int seg = ceil_div(ceil_div(n, kTkWaves), 64) * 64;  // positions per wave
     const int w0 = wave * seg, w1 = min(n, w0 + seg);
+    // sweep 1 counts the wave's keys above and at tau; after the barrier,
+    // sweep 2 writes the wave's selected positions from the same keys (a
+    // cached row's keys stay in registers between the sweeps)
+    const int nit = w1 > w0 ? ceil_div(w1 - w0, 64) : 0;
+    constexpr int kMaxIt = kRowCache / kTkThreads;  // seg <= 64 * kMaxIt when cached
+    uint32_t kv[kMaxIt];
+    if (cached) {
+#pragma unroll
+        for (int it = 0; it < kMaxIt; ++it) {
+            const int p = w0 + 64 * it + lane;
+            kv[it] = it < nit && p < w1 ? sm.keys[p] : 0u;
+        }
+    }
+    auto sweep = [&](auto body) {
+        if (cached) {
+#pragma unroll
+            for (int it = 0; it < kMaxIt; ++it)
+                if (it < nit) body(kv[it], w0 + 64 * it + lane);
+        } else {
+            for (int it = 0; it < nit; ++it) {
+                const int p = w0 + 64 * it + lane;
+                body(p < w1 ? key_at(p) : 0u, p);
+            }
+        }
+    };
     uint32_t c_gt = 0u, c_eq = 0u;
-    for (int p0 = w0; p0 < w1; p0 += 64) {
-        const int p = p0 + lane;
-        const uint32_t u = p < w1 ? key_at(p) : 0u;
+    sweep([&](uint32_t u, int p) {
         c_gt += (uint32_t)__popcll(__ballot(p < w1 && u > tau));
         c_eq += (uint32_t)__popcll(__ballot(p < w1 && u == tau));
-    }
+    });
     if (lane == 0) {
         sm.cnt_gt[wave] = c_gt;
         sm.cnt_eq[wave] = c_eq;
@@ -314,9 +337,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
         eq_before += sm.cnt_eq[v];
     }
     uint32_t written = gt_before + min(eq_before, need), ties = eq_before;
-    for (int p0 = w0; p0 < w1; p0 += 64) {
-        const int p = p0 + lane;
-        const uint32_t u = p < w1 ? key_at(p) : 0u;
+    sweep([&](uint32_t u, int p) {
         const bool gt = p < w1 && u > tau;
         const bool eq = p < w1 && u == tau;
         const uint64_t eqm = __ballot(eq);
@@ -325,7 +346,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
         if (take) out[written + lanes_below(tm)] = p;
         written += (uint32_t)__popcll(tm);
         ties += (uint32_t)__popcll(eqm);
-    }
+    });
 }
 
 // ------------------------------------------------------- wide-row path -----
