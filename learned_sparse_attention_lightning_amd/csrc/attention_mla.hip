@@ -9,19 +9,23 @@
 // heads, the heads form the M dimension of dense MFMA tiles.
 //
 // Workgroup = 8 waves = one query row x 64 heads x one range of selected
-// entries, walked 32 entries at a time (details at the kernel):
-//   gather  the selected rows are loaded into registers two tiles ahead and
-//           parked in a three-tile LDS ring; the row pitch carries one spare
-//           16-byte slot against bank conflicts; masked entries load a valid
-//           row whose probability is then forced to 0;
+// entries, walked 32 entries at a time, one workgroup barrier a tile
+// (details at the kernel):
+//   gather  the latent dims (0..511) of the selected rows are loaded into
+//           registers two tiles ahead and parked in a four-tile LDS ring; the
+//           row pitch carries one spare 16-byte slot against bank conflicts;
+//           masked entries load a valid row whose probability is then forced
+//           to 0; the rope dims (512..575) go from memory straight into the
+//           registers of the waves that multiply them;
 //   S       4 waves compute S^T = C(32 keys) . Q^T(32 heads), each over half
 //           of the 576 dims (v_mfma_f32_32x32x16_bf16), the query block held
 //           in registers as the B operand; the halves meet in LDS;
-//   softmax online, fp32, on the S waves; probabilities written to LDS as
-//           bf16 [head][key];
-//   PV      4 waves accumulate O[64 heads, 128 dims each] += P . V, V read
-//           straight from the row-major tile with the LDS transpose read
-//           (ds_read_b64_tr_b16) as the B operand.
+//   softmax online, fp32, on the S waves, one tile behind their products and
+//           interleaved with them; probabilities written to LDS as bf16
+//           [head][key];
+//   PV      4 waves accumulate O[64 heads, 128 dims each] += P . V one tile
+//           behind the softmax, V read straight from the row-major tile with
+//           the LDS transpose read (ds_read_b64_tr_b16) as the B operand.
 // Decode rows split their entries over several workgroups; each writes a
 // normalised partial output and its log-sum-exp, merged by a second kernel.
 #include "dsa_internal.h"
@@ -33,7 +37,6 @@ constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kHg = 64;            // heads per workgroup
 constexpr int kKsteps = kDqk / 16; // 36
-constexpr int kRowPitch = kDqk * 2 + 16;   // bytes: 1168 (bank shift of 36 dwords)
 constexpr float kRescaleLog2 = 8.0f;  // reference-max slack, base-2 units
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -74,84 +77,51 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float v) {
 }
 
 // ---------------------------------------------------------------------------
-// The kernel: 8 waves = 2 per SIMD, 32-entry tiles.
+// The kernel: 8 waves = 2 per SIMD, 32-entry tiles.  Iteration it:
 //   waves 0-3 ("S" waves): wave (ht = w&1, kh = w>>1) holds the query block of
 //       32 heads over half of the 576 dims (18 k-steps, 72 registers) and
-//       computes that half of S^T for every tile; the kh = 1 half goes through
-//       LDS to its kh = 0 partner, which owns the online softmax of those 32
-//       heads (the 32-entry tile max is in-wave: 16 registers and one
-//       cross-half shuffle) and writes P (bf16) and the rescale factors.
-//   waves 4-7 ("PV" waves): wave 4+d owns O[64 heads, dims 128d..128d+127].
-// Iteration it: the S waves work on tile it+1 while the PV waves multiply
-// tile it; two workgroup barriers per iteration split S (partials | softmax)
-// and PV (first | second 16-entry k-step).  S and PV waves share each SIMD,
-// so one role's latencies are covered by the other's matrix work.
-// Gathers are staged through registers: every wave loads its share of tile
-// it+4 at iteration it and parks it in LDS at iteration it+2, so each gather
-// has two iterations to arrive while only three tiles occupy LDS (it, it+1,
-// it+2).  The selection of the whole split is read into LDS up front.
+//       computes that half of S^T for tile it+1; the kh = 1 half goes through
+//       LDS to its kh = 0 partner.  Between those products the kh = 0 wave
+//       runs the online softmax of tile it: its own half of S(it), kept in
+//       registers since the previous iteration, plus the partner's half; it
+//       writes P(it) (bf16) and the rescale factors.  The 32-entry tile max
+//       is in-wave (16 registers and one cross-half swap).
+//   waves 4-7 ("PV" waves): wave 4+d owns O[64 heads, dims 128d..128d+127]
+//       and adds P(it-1) . V(it-1); it also gathers the latent dims of rows
+//       8d..8d+7 of tile it+4 into registers and parks those of tile it+2.
+// One workgroup barrier ends each iteration.  Tiles it-1 (PV), it (PV next),
+// it+1 (S) and it+2 (parked now) fill the four ring slots; P, the rescale
+// factors and the S halves alternate between two buffers by tile parity.
+// The S and PV waves share each SIMD, so one role's latencies are covered by
+// the other's matrix work.  The kh = 1 waves read the rope dims of tile it+1
+// from registers loaded one iteration earlier.
 constexpr int kKt = 32;                          // entries per tile
-constexpr int kRing = 3;                         // tiles resident in LDS
-constexpr int kSlotsRow = kDqk * 2 / 16;         // 72 data slots of 16 bytes a row
-constexpr int kTileSlots = kKt * kSlotsRow;  // 2304
-constexpr int kTileBytes = kKt * kRowPitch;    // 37376
-constexpr int kPPitch = kKt * 2 + 16;          // 80 bytes per head row of P
+constexpr int kRing = 4;                         // tiles resident in LDS
+constexpr int kVRowBytes = kDv * 2;              // 1024: the latent dims of a row in LDS
+constexpr int kRowPitch = kVRowBytes + 16;       // 1040 (bank shift of 4 dwords a row)
+constexpr int kTileBytes = kKt * kRowPitch;      // 33280
+constexpr int kPPitch = kKt * 2 + 16;            // 80 bytes per head row of P
 constexpr int kHalfSteps = kKsteps / 2;          // 18
-constexpr int kMaxSplit = 4096;                  // entries of one split (LDS table)
+constexpr int kRopeSteps = (kDqk - kDv) / 16;    // 4 k-steps of rope dims (kh = 1)
+constexpr int kLdsSteps1 = kHalfSteps - kRopeSteps;  // 14 k-steps of kh = 1 read from LDS
 constexpr int kThreads = 512;
 constexpr int kOutPitch = 136;  // floats per head row of the output staging block
-// Staged 16-byte loads per lane per tile: slot q = 512 m + 64 w + lane; the
-// S waves (w < 4) also take m = 4, which covers slots 2048..2303.
-constexpr int kLoadsS = 5;
-constexpr int kLoadsPV = 4;
-constexpr int kStageStride = 512;
-static_assert(kLoadsPV * kThreads + 4 * 64 == kTileSlots, "staging covers a tile");
+constexpr int kStageRows = kKt / 4;              // rows of a tile each PV wave gathers
+constexpr int kSelRing = 8;                      // tiles of the selection kept in LDS
+constexpr int kLatRowBytes = kDqk * 2;           // 1152: a latent row in memory
 
 struct __align__(16) MlaSmem {
-    uint8_t kv[kRing][kTileBytes];  // 3 x 37376
-    int32_t idx[kMaxSplit];           // this split's selection, -1 past its end
+    uint8_t kv[kRing][kTileBytes];    // 4 x 33280
     uint8_t p[2][kHg * kPPitch];      // 2 x 5120
-    f32x4 part[2][4][64];               // kh = 1 halves of S, one per head tile,
-                                        // registers 4j..4j+3 of lane l at [j][l]
+    f32x4 part[2][2][4][64];          // kh = 1 halves of S: [tile parity][head tile][j][lane]
+                                      // = registers 4j..4j+3 of lane l
     float corr[2][kHg];
     float fin_l[kHg];                   // 1 / softmax denominator per head
+    int32_t sel[kSelRing][kKt];         // rows of tile t at [t % kSelRing]; -1: none
     int32_t resc[2][2];                 // per tile parity and head tile: any corr != 1
 };
 static_assert(offsetof(MlaSmem, corr) % 16 == 0, "corr is read in 16-byte pieces");
-
-// Issue the global loads of this wave's share of tile `t` (entries
-// 32t..32t+31 of the split).  Entries past the split re-read the split's last
-// row (just fetched, so a cache hit rather than a cold memory access that the
-// end of the kernel would wait for) and masked ones read row 0: the loads stay
-// unconditional, their data unused.
-// Slot of load m: q0 + stride * m.
-template <int NL>
-__device__ __forceinline__ void stage_load(u32x4 (&r)[NL], const MlaSmem &sm, int len,
-                                              int t, const uint8_t *__restrict__ lat_b,
-                                              int q0, int stride) {
-#pragma unroll
-    for (int m = 0; m < NL; ++m) {
-        const int q = q0 + stride * m;
-        const int row = q / kSlotsRow;
-        const int c = q - row * kSlotsRow;
-        const int e = t * kKt + row;
-        const int sel = sm.idx[min(e, len - 1)];
-        const uint32_t src_row = (uint32_t)max(sel, 0);
-        r[m] = *reinterpret_cast<const u32x4 *>(lat_b + src_row * (uint64_t)(kDqk * 2) + c * 16);
-    }
-}
-
-template <int NL>
-__device__ __forceinline__ void stage_store(const u32x4 (&r)[NL], uint8_t *tile, int q0,
-                                               int stride) {
-#pragma unroll
-    for (int m = 0; m < NL; ++m) {
-        const int q = q0 + stride * m;
-        const int row = q / kSlotsRow;
-        const int c = q - row * kSlotsRow;
-        *reinterpret_cast<u32x4 *>(tile + row * kRowPitch + c * 16) = r[m];
-    }
-}
+static_assert(sizeof(MlaSmem) <= 160 * 1024, "fits the LDS of a CU");
 
 template <typename Tout>
 __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
@@ -161,7 +131,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     float *__restrict__ o_part, float *__restrict__ lse_part) {
     __shared__ MlaSmem sm;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int half = lane >> 5;
     const int l32 = lane & 31;
@@ -187,25 +157,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     const int len = min(k, e_begin + per_split) - e_begin;  // entries of this split
     const int ntiles = (len + kKt - 1) / kKt;
     const int32_t *sel_row = idx + ((size_t)b * T + i) * k + e_begin;
-    const uint8_t *lat_b = reinterpret_cast<const uint8_t *>(lat) + (size_t)b * S * (kDqk * 2);
+    const uint8_t *lat_b = reinterpret_cast<const uint8_t *>(lat) + (size_t)b * S * kLatRowBytes;
     const size_t rowq = (size_t)b * T + i;
     const size_t prow = (size_t)qidx;  // row of this launch's split partials
-
-    // ---- prologue: the split's selection into LDS
-    for (int e = tid; e < ntiles * kKt; e += kThreads) sm.idx[e] = e < len ? sel_row[e] : -1;
-    __syncthreads();
+    // selected row of entry e of the split (-1: masked or past the split)
+    auto sel_of = [&](int e) -> int32_t { return e < len ? sel_row[e] : -1; };
 
     const float sl2 = scale * 1.4426950408889634f;
     if (wave < 4) {
         // ======================= S waves =======================
         const int ht = wave & 1, kh = wave >> 1;
-        const int q0 = 64 * wave + lane;  // staging slots
-        constexpr int qs = kStageStride;
-        u32x4 stg[2][kLoadsS];
-        stage_load(stg[0], sm, len, 0, lat_b, q0, qs);
-        __builtin_amdgcn_sched_barrier(0);
-        stage_load(stg[1], sm, len, 1, lat_b, q0, qs);
-        __builtin_amdgcn_sched_barrier(0);
         bf16x8 qb[kHalfSteps];
         {
             const uint16_t *qp = q + (rowq * H + head0 + ht * 32 + l32) * kDqk + 8 * half +
@@ -214,150 +175,156 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             for (int ks = 0; ks < kHalfSteps; ++ks)
                 qb[ks] = *reinterpret_cast<const bf16x8 *>(qp + ks * 16);
         }
-        stage_store(stg[0], sm.kv[0], q0, qs);
-        stage_store(stg[1], sm.kv[1], q0, qs);
-        stage_load(stg[0], sm, len, 2, lat_b, q0, qs);
-        __builtin_amdgcn_sched_barrier(0);
-        stage_load(stg[1], sm, len, 3, lat_b, q0, qs);
-        __builtin_amdgcn_sched_barrier(0);
+        // rope fragments (kh = 1) of tile t: k-steps 14..17 of this half
+        auto rope_load = [&](int t, bf16x8 (&rp)[kRopeSteps]) {
+            const int32_t s = sm.sel[t % kSelRing][l32];
+            const uint8_t *src = lat_b + (uint32_t)max(s, 0) * (uint64_t)kLatRowBytes +
+                                 kVRowBytes + 16 * half;
 #pragma unroll
-        for (int ks = 0; ks < kHalfSteps; ++ks) asm volatile("" ::"v"(qb[ks]));
-        lds_barrier();  // tiles 0 and 1 in LDS
-        float m_run = -INFINITY, l_run = 0.0f;
-        // This wave's half of S^T.  All 18 A fragments are read before the
-        // first product, so the LDS latency is paid once per tile rather than
-        // once per pair of products.
-        auto s_read = [&](const uint8_t *kvt, bf16x8 (&af)[kHalfSteps]) {
-            const uint8_t *arow = kvt + l32 * kRowPitch + 16 * half + 32 * kHalfSteps * kh;
+            for (int j = 0; j < kRopeSteps; ++j)
+                rp[j] = *reinterpret_cast<const bf16x8 *>(src + 32 * j);
+        };
+        // this wave's half of S^T(t): K fragments from the LDS ring (and, for
+        // kh = 1, the rope registers)
+        auto s_read = [&](int t, bf16x8 (&af)[kHalfSteps], const bf16x8 (&rp)[kRopeSteps]) {
+            const uint8_t *arow = sm.kv[t % kRing] + l32 * kRowPitch + 16 * half + 576 * kh;
+            if (kh == 0) {
 #pragma unroll
-            for (int ks = 0; ks < kHalfSteps; ++ks) af[ks] = lds_b128(arow + ks * 32);
-        };
-        auto s_mfma = [&](const bf16x8 (&af)[kHalfSteps]) -> f32x16 {
-            f32x16 acc = {};
+                for (int ks = 0; ks < kHalfSteps; ++ks) af[ks] = lds_b128(arow + ks * 32);
+            } else {
 #pragma unroll
-            for (int ks = 0; ks < kHalfSteps; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qb[ks], acc, 0, 0, 0);
-            return acc;
+                for (int ks = 0; ks < kLdsSteps1; ++ks) af[ks] = lds_b128(arow + ks * 32);
+#pragma unroll
+                for (int j = 0; j < kRopeSteps; ++j) af[kLdsSteps1 + j] = rp[j];
+            }
         };
-        auto s_half = [&](const uint8_t *kvt) -> f32x16 {
-            bf16x8 af[kHalfSteps];
-            s_read(kvt, af);
-            __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
-            return s_mfma(af);
-        };
-        auto put_part = [&](const f32x16 &acc) {
+        auto put_part = [&](int t, const f32x16 &acc) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                sm.part[ht][j][lane] = f32x4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2],
-                                             acc[4 * j + 3]};
+                sm.part[t & 1][ht][j][lane] = f32x4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2],
+                                                    acc[4 * j + 3]};
         };
-        auto add_part = [&](f32x16 &acc) {
+        float m_run = -INFINITY, l_run = 0.0f;
+        // Online softmax of tile t (kh = 0): own half `acc` plus the partner's
+        // half from LDS; branch-free, so it schedules between the products.
+        auto softmax = [&](int t, f32x16 acc) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const f32x4 o = sm.part[ht][j][lane];
+                const f32x4 o = sm.part[t & 1][ht][j][lane];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[4 * j + e] += o[e];
             }
-        };
-        // Bit j of the result: entry j of the tile is a selected row.
-        auto tile_mask = [&](int tile) -> uint32_t {
-            return (uint32_t)__ballot(sm.idx[tile * kKt + l32] >= 0);
-        };
-        auto softmax = [&](int tile, f32x16 acc, uint32_t vmask) {  // kh = 0: full S^T
+            // bit j: entry j of the tile is a selected row
+            const uint32_t vmask = (uint32_t)__ballot(sm.sel[t % kSelRing][l32] >= 0);
+            const uint32_t mh = vmask >> (4 * half);
             float tmax = -INFINITY;
-            if (vmask == 0xffffffffu) {
 #pragma unroll
-                for (int rg = 0; rg < 16; ++rg) {
-                    acc[rg] *= sl2;
-                    tmax = fmaxf(tmax, acc[rg]);
-                }
-            } else {
-                const uint32_t mh = vmask >> (4 * half);
-#pragma unroll
-                for (int rg = 0; rg < 16; ++rg) {
-                    const float x =
-                        (mh >> (8 * (rg >> 2) + (rg & 3))) & 1u ? acc[rg] * sl2 : -INFINITY;
-                    acc[rg] = x;
-                    tmax = fmaxf(tmax, x);
-                }
+            for (int rg = 0; rg < 16; ++rg) {
+                const float x =
+                    (mh >> (8 * (rg >> 2) + (rg & 3))) & 1u ? acc[rg] * sl2 : -INFINITY;
+                acc[rg] = x;
+                tmax = fmaxf(tmax, x);
             }
             tmax = max_halves(tmax);
-            float corr = 1.0f;
-            if (tmax > m_run + kRescaleLog2) {
-                corr = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - tmax);
-                m_run = tmax;
-            }
+            const bool grow = tmax > m_run + kRescaleLog2;
+            const float corr = grow ? (m_run == -INFINITY ? 0.0f
+                                                          : __builtin_amdgcn_exp2f(m_run - tmax))
+                                    : 1.0f;
+            m_run = grow ? tmax : m_run;
             const float m_ref = m_run;
             float ps0 = 0.0f, ps1 = 0.0f;
-            uint8_t *prow = sm.p[tile & 1] + (ht * 32 + l32) * kPPitch;
+            uint8_t *prow = sm.p[t & 1] + (ht * 32 + l32) * kPPitch;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 float pv[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    pv[j] = m_ref == -INFINITY ? 0.0f
-                                               : __builtin_amdgcn_exp2f(acc[4 * g + j] - m_ref);
+                for (int j = 0; j < 4; ++j) {
+                    const float e = __builtin_amdgcn_exp2f(acc[4 * g + j] - m_ref);
+                    pv[j] = m_ref == -INFINITY ? 0.0f : e;
+                }
                 ps0 += pv[0] + pv[1];
                 ps1 += pv[2] + pv[3];
                 const bf16x4 pk = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
                 *reinterpret_cast<bf16x4 *>(prow + (8 * g + 4 * half) * 2) = pk;
             }
             l_run = l_run * corr + (ps0 + ps1);
-            if (half == 0) sm.corr[tile & 1][ht * 32 + l32] = corr;
-            const bool resc = __ballot(corr != 1.0f) != 0;
-            if (lane == 0) sm.resc[tile & 1][ht] = resc;
+            sm.corr[t & 1][ht * 32 + l32] = corr;  // both halves write the same value
+            sm.resc[t & 1][ht] = __ballot(corr != 1.0f) != 0;
+        };
+        // ask the scheduler to put vector work between the products
+        auto interleave = [&]() {
+#pragma unroll
+            for (int j = 0; j < kHalfSteps; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // up to 8 VALU
+            }
         };
 
-        // "iteration -1": S and softmax of tile 0
-        {
-            f32x16 acc = s_half(sm.kv[0]);
-            if (kh == 1) put_part(acc);
-            lds_barrier();
-            if (kh == 0) {
-                const uint32_t vm = tile_mask(0);
-                add_part(acc);
-                softmax(0, acc, vm);
-            }
-            lds_barrier();
+        bf16x8 rp[2][kRopeSteps];  // kh = 1: rope of tiles it+1 (in use) and it+2
+        lds_barrier();             // B0: tiles 0 and 1 and the selection of tiles 0..3
+        if (kh == 1) {
+            rope_load(0, rp[0]);
+            rope_load(1, rp[1]);
         }
-        // iteration it: S of tile it+1, park this wave's share of tile it+2
-        // and load its share of tile it+4; the K fragments are requested
-        // first, so their LDS latency overlaps the parking and the gathers
-        auto s_step = [&](const int it, u32x4 (&st)[kLoadsS]) {
-            const bool more = it + 1 < ntiles;
-            stage_store(st, sm.kv[(it + 2) % kRing], q0, qs);
-            stage_load(st, sm, len, it + 4, lat_b, q0, qs);
-            __builtin_amdgcn_sched_barrier(0);
+        f32x16 s_cur;  // kh = 0: own half of S of the tile the softmax takes next
+        {
             bf16x8 af[kHalfSteps];
-            if (more) s_read(sm.kv[(it + 1) % kRing], af);
-            __builtin_amdgcn_sched_barrier(0);
+            s_read(0, af, rp[0]);
             f32x16 acc = {};
-            if (more) acc = s_mfma(af);
-            if (more && kh == 1) put_part(acc);
-            uint32_t vm = 0;
-            if (more && kh == 0) vm = tile_mask(it + 1);
-            lds_barrier();  // ---- barrier 1
-            if (more && kh == 0) {
-                add_part(acc);
-                softmax(it + 1, acc, vm);
+#pragma unroll
+            for (int ks = 0; ks < kHalfSteps; ++ks)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qb[ks], acc, 0, 0, 0);
+            if (kh == 1) put_part(0, acc);
+            s_cur = acc;
+        }
+        lds_barrier();  // B1: S(0) halves
+        // iteration it: products of tile it+1, softmax of tile it; rope of
+        // tile it+1 in rp[c], loads of tile it+2 into rp[c ^ 1]
+        auto s_step = [&](const int it, bf16x8 (&rcur)[kRopeSteps],
+                          bf16x8 (&rnext)[kRopeSteps]) {
+            const bool more = it + 1 < ntiles;
+            if (kh == 0) {
+                if (more) {
+                    bf16x8 af[kHalfSteps];
+                    s_read(it + 1, af, rcur);
+                    f32x16 nx = {};
+#pragma unroll
+                    for (int ks = 0; ks < kHalfSteps; ++ks)
+                        nx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qb[ks], nx, 0, 0, 0);
+                    softmax(it, s_cur);
+                    interleave();
+                    s_cur = nx;
+                } else {
+                    softmax(it, s_cur);
+                }
+            } else {
+                if (more) {
+                    bf16x8 af[kHalfSteps];
+                    s_read(it + 1, af, rcur);
+                    f32x16 nx = {};
+#pragma unroll
+                    for (int ks = 0; ks < kHalfSteps; ++ks)
+                        nx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qb[ks], nx, 0, 0, 0);
+                    put_part(it + 1, nx);
+                }
+                if (it + 2 < ntiles) rope_load(it + 2, rnext);
             }
-            lds_barrier();  // ---- barrier 2
+            lds_barrier();
         };
-        // Pairs of steps, so that at the top of the loop the stg[1] loads are
-        // always the newer ones and parking stg[0] waits for its own loads only.
+        // Pairs of steps, so that the rope registers alternate statically.
         int it = 0;
         for (; it + 1 < ntiles; it += 2) {
-            s_step(it, stg[0]);
-            s_step(it + 1, stg[1]);
+            s_step(it, rp[1], rp[0]);
+            s_step(it + 1, rp[0], rp[1]);
         }
-        if (it < ntiles) s_step(it, stg[0]);
-        lds_barrier();  // loads past the last tile may still be in flight
+        if (it < ntiles) s_step(it, rp[1], rp[0]);
+        lds_barrier();  // matches the PV waves' last step
         float l_all = 0.0f;
         if (kh == 0) {
             l_all = sum_halves(l_run);  // both key halves
             if (half == 0) sm.fin_l[ht * 32 + l32] = l_all > 0.0f ? 1.0f / l_all : 0.0f;
         }
-        lds_barrier();  // loads past the last tile may still be in flight
+        lds_barrier();  // E1: 1/l for the output
         if (kh == 0 && half == 0) {
             const int hl = ht * 32 + l32;
             const float ls = l_all > 0.0f ? (m_run + log2f(l_all)) * 0.6931471805599453f : -INFINITY;
@@ -371,25 +338,53 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         // ======================= PV waves =======================
         const int d = wave - 4;
         const int dv0 = d * 128;
-        const int q0 = 64 * wave + lane;  // staging slots
-        constexpr int qs = kStageStride;
-        u32x4 stg[2][kLoadsPV];
-        stage_load(stg[0], sm, len, 0, lat_b, q0, qs);
-        __builtin_amdgcn_sched_barrier(0);
-        stage_load(stg[1], sm, len, 1, lat_b, q0, qs);
-        __builtin_amdgcn_sched_barrier(0);
+        // gather: rows 8d..8d+7 of a tile, one row a load (lane = 16-byte piece)
+        auto stage_load = [&](int32_t selv, u32x4 (&st)[kStageRows]) {
+#pragma unroll
+            for (int m = 0; m < kStageRows; ++m) {
+                const int32_t s = __builtin_amdgcn_readlane(selv, m);
+                st[m] = *reinterpret_cast<const u32x4 *>(
+                    lat_b + (uint32_t)max(s, 0) * (uint64_t)kLatRowBytes + 16 * lane);
+            }
+        };
+        auto stage_store = [&](int t, const u32x4 (&st)[kStageRows]) {
+            uint8_t *dst = sm.kv[t % kRing] + (8 * d) * kRowPitch + 16 * lane;
+#pragma unroll
+            for (int m = 0; m < kStageRows; ++m)
+                *reinterpret_cast<u32x4 *>(dst + m * kRowPitch) = st[m];
+        };
+        // selection of rows 8d..8d+7 of tile t, in lanes 0..7
+        auto sel_load = [&](int t) -> int32_t {
+            return sel_of(t * kKt + 8 * d + (lane & 7));
+        };
+        auto sel_put = [&](int t, int32_t selv) {
+            if (lane < 8) sm.sel[t % kSelRing][8 * d + lane] = selv;
+        };
+        u32x4 stg[2][kStageRows];
+        int32_t sel_next;  // tile it+4's rows at the top of iteration it
+        {
+            int32_t sv[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sv[t] = sel_load(t);
+            sel_next = sel_load(4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sel_put(t, sv[t]);
+            stage_load(sv[0], stg[0]);
+            stage_load(sv[1], stg[1]);
+            stage_store(0, stg[0]);
+            stage_store(1, stg[1]);
+            stage_load(sv[2], stg[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            stage_load(sv[3], stg[1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         f32x16 o[2][4];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int c = 0; c < 4; ++c) o[a][c] = f32x16{};
-        stage_store(stg[0], sm.kv[0], q0, qs);
-        stage_store(stg[1], sm.kv[1], q0, qs);
-        stage_load(stg[0], sm, len, 2, lat_b, q0, qs);
-        __builtin_amdgcn_sched_barrier(0);
-        stage_load(stg[1], sm, len, 3, lat_b, q0, qs);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_barrier();  // tiles 0 and 1 in LDS (matches the S waves')
+        lds_barrier();  // B0 (matches the S waves')
+        lds_barrier();  // B1
         const int trj = lane & 15, trg = lane >> 4;
         const int vrow = 8 * (trg >> 1) + (trj >> 2);
         const int vcol = (dv0 + 16 * (trg & 1) + 4 * (trj & 3)) * 2;
@@ -417,50 +412,61 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
                     o[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[a], vb[c], o[a][c], 0,
                                                                       0, 0);
         };
-        lds_barrier();  // matches the S waves' "iteration -1"
-        lds_barrier();
-        // The first k-step's LDS reads (and the rescale flags) are issued
-        // before the tile parking, so their latency overlaps it; the next
-        // gathers and the second k-step's reads follow the first k-step's
-        // products and complete under them.
-        auto o_step = [&](const int it, u32x4 (&st)[kLoadsPV]) {
-            const int32_t f0 = sm.resc[it & 1][0], f1 = sm.resc[it & 1][1];
+        // Iteration it: P(it-1) . V(it-1); park tile it+2 (loaded two
+        // iterations ago) and gather tile it+4.  The first k-step's reads are
+        // issued before the parking, so their latency overlaps it; the gathers
+        // and the second k-step's reads follow the first k-step's products.
+        auto o_step = [&](const int it, u32x4 (&st)[kStageRows]) {
+            const int tp = it - 1;
+            const bool pv = it >= 1;
+            int32_t f0 = 0, f1 = 0;
             bf16x8 pa[2], vb[4];
-            pv_read(it, 0, pa, vb);
-            __builtin_amdgcn_sched_barrier(0);
-            stage_store(st, sm.kv[(it + 2) % kRing], q0, qs);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                if (__builtin_amdgcn_readfirstlane(a == 0 ? f0 : f1)) {
-                    f32x4 cr[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        cr[j] = *reinterpret_cast<const f32x4 *>(
-                            &sm.corr[it & 1][a * 32 + 8 * j + 4 * half]);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-#pragma unroll
-                        for (int rg = 0; rg < 16; ++rg) o[a][c][rg] *= cr[rg >> 2][rg & 3];
-                }
+            if (pv) {
+                f0 = sm.resc[tp & 1][0];
+                f1 = sm.resc[tp & 1][1];
+                pv_read(tp, 0, pa, vb);
             }
-            pv_mfma(pa, vb);
             __builtin_amdgcn_sched_barrier(0);
-            stage_load(st, sm, len, it + 4, lat_b, q0, qs);
+            stage_store(it + 2, st);
             __builtin_amdgcn_sched_barrier(0);
-            pv_read(it, 1, pa, vb);
-            lds_barrier();  // ---- barrier 1
-            pv_mfma(pa, vb);
-            lds_barrier();  // ---- barrier 2
+            if (pv) {
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    if (__builtin_amdgcn_readfirstlane(a == 0 ? f0 : f1)) {
+                        f32x4 cr[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            cr[j] = *reinterpret_cast<const f32x4 *>(
+                                &sm.corr[tp & 1][a * 32 + 8 * j + 4 * half]);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+#pragma unroll
+                            for (int rg = 0; rg < 16; ++rg) o[a][c][rg] *= cr[rg >> 2][rg & 3];
+                    }
+                }
+                pv_mfma(pa, vb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            stage_load(sel_next, st);
+            sel_put(it + 4, sel_next);
+            sel_next = sel_load(it + 5);
+            __builtin_amdgcn_sched_barrier(0);
+            if (pv) {
+                pv_read(tp, 1, pa, vb);
+                pv_mfma(pa, vb);
+            }
+            lds_barrier();
         };
+        // ntiles + 1 steps, in pairs so that at the top of the loop the stg[1]
+        // loads are always the newer ones and parking stg[0] waits for its own
+        // loads only.
         int it = 0;
-        for (; it + 1 < ntiles; it += 2) {
+        for (; it + 1 <= ntiles; it += 2) {
             o_step(it, stg[0]);
             o_step(it + 1, stg[1]);
         }
-        if (it < ntiles) o_step(it, stg[0]);
-        lds_barrier();  // loads past the last tile may still be in flight
-        lds_barrier();  // loads past the last tile may still be in flight
+        if (it <= ntiles) o_step(it, stg[0]);
+        lds_barrier();  // E1: 1/l from the S waves
         // Output through LDS (the tile ring is free now): the accumulator
         // layout gives a lane one dim of 16 heads, memory wants rows of dims;
         // each 32-head half goes to a [head][dim] block (pitch 136 floats, so
@@ -570,7 +576,6 @@ int mla_splits(int B, int rows, int H, int k) {
     const int max_splits = ceil_div(k, 4 * kKt);
     long long s = (256 + wgs - 1) / wgs;
     if (s > max_splits) s = max_splits;
-    if (s < ceil_div(k, kMaxSplit)) s = ceil_div(k, kMaxSplit);  // selection table bound
     if (s < 1) s = 1;
     return (int)s;
 }
