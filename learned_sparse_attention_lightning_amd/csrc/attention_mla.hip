@@ -89,6 +89,8 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float v) {
 //   waves 4-7 ("PV" waves): wave 4+d owns O[64 heads, dims 128d..128d+127]
 //       and adds P(it-1) . V(it-1); it also gathers the latent dims of rows
 //       8d..8d+7 of tile it+4 into registers and parks those of tile it+2.
+// The rows of each tile sit in an LDS ring of selections, kept filled by
+// wave 0 five tiles ahead.
 // One workgroup barrier ends each iteration.  Tiles it-1 (PV), it (PV next),
 // it+1 (S) and it+2 (parked now) fill the four ring slots; P, the rescale
 // factors and the S halves alternate between two buffers by tile parity.
@@ -205,8 +207,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
                                                     acc[4 * j + 3]};
         };
         float m_run = -INFINITY, l_run = 0.0f;
-        // Online softmax of tile t (kh = 0): own half `acc` plus the partner's
-        // half from LDS; branch-free, so it schedules between the products.
+        // Masked entries of tile t (kh = 0): its own half of S set to -inf, so
+        // the sum with the partner's half is -inf too.  Whole tiles are the
+        // rule; the branch is uniform.
+        auto mask_tile = [&](int t, f32x16 &acc) {
+            const uint32_t vmask = (uint32_t)__ballot(sm.sel[t % kSelRing][l32] >= 0);
+            if (vmask != 0xffffffffu) {
+                const uint32_t mh = vmask >> (4 * half);
+#pragma unroll
+                for (int rg = 0; rg < 16; ++rg)
+                    if (!((mh >> (8 * (rg >> 2) + (rg & 3))) & 1u)) acc[rg] = -INFINITY;
+            }
+        };
+        // Online softmax of tile t (kh = 0): own half `acc` (masked entries
+        // -inf) plus the partner's half from LDS.  Branch-free, so it
+        // schedules between the products; the scale is applied to the max and
+        // inside the exponent (fma), since scale > 0 keeps the order.
         auto softmax = [&](int t, f32x16 acc) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -214,34 +230,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[4 * j + e] += o[e];
             }
-            // bit j: entry j of the tile is a selected row
-            const uint32_t vmask = (uint32_t)__ballot(sm.sel[t % kSelRing][l32] >= 0);
-            const uint32_t mh = vmask >> (4 * half);
             float tmax = -INFINITY;
 #pragma unroll
-            for (int rg = 0; rg < 16; ++rg) {
-                const float x =
-                    (mh >> (8 * (rg >> 2) + (rg & 3))) & 1u ? acc[rg] * sl2 : -INFINITY;
-                acc[rg] = x;
-                tmax = fmaxf(tmax, x);
-            }
-            tmax = max_halves(tmax);
+            for (int rg = 0; rg < 16; ++rg) tmax = fmaxf(tmax, acc[rg]);
+            tmax = max_halves(tmax) * sl2;
             const bool grow = tmax > m_run + kRescaleLog2;
             const float corr = grow ? (m_run == -INFINITY ? 0.0f
                                                           : __builtin_amdgcn_exp2f(m_run - tmax))
                                     : 1.0f;
             m_run = grow ? tmax : m_run;
-            const float m_ref = m_run;
+            // no selected entry so far: every entry is -inf and exp2 gives 0
+            const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
             float ps0 = 0.0f, ps1 = 0.0f;
             uint8_t *prow = sm.p[t & 1] + (ht * 32 + l32) * kPPitch;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 float pv[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float e = __builtin_amdgcn_exp2f(acc[4 * g + j] - m_ref);
-                    pv[j] = m_ref == -INFINITY ? 0.0f : e;
-                }
+                for (int j = 0; j < 4; ++j)
+                    pv[j] = __builtin_amdgcn_exp2f(fmaf(acc[4 * g + j], sl2, -m_ref));
                 ps0 += pv[0] + pv[1];
                 ps1 += pv[2] + pv[3];
                 const bf16x4 pk = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
@@ -251,17 +258,40 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             sm.corr[t & 1][ht * 32 + l32] = corr;  // both halves write the same value
             sm.resc[t & 1][ht] = __ballot(corr != 1.0f) != 0;
         };
-        // ask the scheduler to put vector work between the products
-        auto interleave = [&]() {
+        // Ask the scheduler to spread the LDS reads over the products (the
+        // first few ahead of them) and to put vector work between the
+        // products: right after a barrier every wave wants LDS at once, and
+        // reading a whole K half before the first product would hold the
+        // matrix pipe until the slowest read.
+        auto interleave = [&](auto valu_per_product) {
+            constexpr int kValu = decltype(valu_per_product)::value;
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // 6 LDS reads
 #pragma unroll
             for (int j = 0; j < kHalfSteps; ++j) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // up to 8 VALU
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                if constexpr (kValu > 0) __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
             }
         };
 
+        // Wave 0 keeps the selection ring filled: the rows of tile it+5 are
+        // written at iteration it from a load issued one iteration earlier
+        // (the wave has no other memory loads, so that wait is free), ahead of
+        // every reader: the gathering waves (tile it+4), the rope loads (tile
+        // it+2) and the softmax mask (tile it).
+        int32_t sel_next = 0;
+        if (wave == 0) {
+            int32_t sv[5];
+#pragma unroll
+            for (int t = 0; t < 5; ++t) sv[t] = sel_of(t * kKt + l32);
+            sel_next = sel_of(5 * kKt + l32);
+#pragma unroll
+            for (int t = 0; t < 5; ++t)
+                if (half == 0) sm.sel[t][l32] = sv[t];
+        }
+        __syncthreads();  // selection of tiles 0..4
         bf16x8 rp[2][kRopeSteps];  // kh = 1: rope of tiles it+1 (in use) and it+2
-        lds_barrier();             // B0: tiles 0 and 1 and the selection of tiles 0..3
+        lds_barrier();             // B0: tiles 0 and 1
         if (kh == 1) {
             rope_load(0, rp[0]);
             rope_load(1, rp[1]);
@@ -275,6 +305,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             for (int ks = 0; ks < kHalfSteps; ++ks)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qb[ks], acc, 0, 0, 0);
             if (kh == 1) put_part(0, acc);
+            if (kh == 0) mask_tile(0, acc);
             s_cur = acc;
         }
         lds_barrier();  // B1: S(0) halves
@@ -283,6 +314,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         auto s_step = [&](const int it, bf16x8 (&rcur)[kRopeSteps],
                           bf16x8 (&rnext)[kRopeSteps]) {
             const bool more = it + 1 < ntiles;
+            if (wave == 0) {
+                if (half == 0) sm.sel[(it + 5) % kSelRing][l32] = sel_next;
+                sel_next = sel_of((it + 6) * kKt + l32);
+            }
             if (kh == 0) {
                 if (more) {
                     bf16x8 af[kHalfSteps];
@@ -292,7 +327,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
                     for (int ks = 0; ks < kHalfSteps; ++ks)
                         nx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qb[ks], nx, 0, 0, 0);
                     softmax(it, s_cur);
-                    interleave();
+                    interleave(std::integral_constant<int, 5>{});
+                    mask_tile(it + 1, nx);
                     s_cur = nx;
                 } else {
                     softmax(it, s_cur);
@@ -305,6 +341,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
 #pragma unroll
                     for (int ks = 0; ks < kHalfSteps; ++ks)
                         nx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qb[ks], nx, 0, 0, 0);
+                    interleave(std::integral_constant<int, 0>{});
                     put_part(it + 1, nx);
                 }
                 if (it + 2 < ntiles) rope_load(it + 2, rnext);
@@ -338,11 +375,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         // ======================= PV waves =======================
         const int d = wave - 4;
         const int dv0 = d * 128;
-        // gather: rows 8d..8d+7 of a tile, one row a load (lane = 16-byte piece)
-        auto stage_load = [&](int32_t selv, u32x4 (&st)[kStageRows]) {
+        // gather: rows 8d..8d+7 of tile t, one row a load (lane = 16-byte
+        // piece); the rows come from the selection ring
+        auto stage_load = [&](int t, u32x4 (&st)[kStageRows]) {
+            const int32_t *sr = sm.sel[t % kSelRing] + 8 * d;
+            int32_t rowv[kStageRows];
+#pragma unroll
+            for (int m = 0; m < kStageRows; ++m) rowv[m] = sr[m];
 #pragma unroll
             for (int m = 0; m < kStageRows; ++m) {
-                const int32_t s = __builtin_amdgcn_readlane(selv, m);
+                const int32_t s = __builtin_amdgcn_readfirstlane(rowv[m]);
                 st[m] = *reinterpret_cast<const u32x4 *>(
                     lat_b + (uint32_t)max(s, 0) * (uint64_t)kLatRowBytes + 16 * lane);
             }
@@ -353,31 +395,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             for (int m = 0; m < kStageRows; ++m)
                 *reinterpret_cast<u32x4 *>(dst + m * kRowPitch) = st[m];
         };
-        // selection of rows 8d..8d+7 of tile t, in lanes 0..7
-        auto sel_load = [&](int t) -> int32_t {
-            return sel_of(t * kKt + 8 * d + (lane & 7));
-        };
-        auto sel_put = [&](int t, int32_t selv) {
-            if (lane < 8) sm.sel[t % kSelRing][8 * d + lane] = selv;
-        };
         u32x4 stg[2][kStageRows];
-        int32_t sel_next;  // tile it+4's rows at the top of iteration it
-        {
-            int32_t sv[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) sv[t] = sel_load(t);
-            sel_next = sel_load(4);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) sel_put(t, sv[t]);
-            stage_load(sv[0], stg[0]);
-            stage_load(sv[1], stg[1]);
-            stage_store(0, stg[0]);
-            stage_store(1, stg[1]);
-            stage_load(sv[2], stg[0]);
-            __builtin_amdgcn_sched_barrier(0);
-            stage_load(sv[3], stg[1]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        __syncthreads();  // selection of tiles 0..4 (matches the S waves')
+        stage_load(0, stg[0]);
+        stage_load(1, stg[1]);
+        stage_store(0, stg[0]);
+        stage_store(1, stg[1]);
+        stage_load(2, stg[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_load(3, stg[1]);
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 o[2][4];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
@@ -447,9 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
                 pv_mfma(pa, vb);
             }
             __builtin_amdgcn_sched_barrier(0);
-            stage_load(sel_next, st);
-            sel_put(it + 4, sel_next);
-            sel_next = sel_load(it + 5);
+            stage_load(it + 4, st);
             __builtin_amdgcn_sched_barrier(0);
             if (pv) {
                 pv_read(tp, 1, pa, vb);
