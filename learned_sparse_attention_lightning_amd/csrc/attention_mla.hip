@@ -112,6 +112,16 @@ constexpr int kStageRows = kKt / 4;              // rows of a tile each PV wave 
 constexpr int kSelRing = 8;                      // tiles of the selection kept in LDS
 constexpr int kLatRowBytes = kDqk * 2;           // 1152: a latent row in memory
 
+// LDS row of entry m of a tile: within each block of 16 entries, entry
+// 4a + b sits in row 4b + a.  A row is 1040 bytes (16 bytes past a multiple
+// of 256), so rows 16 bytes apart in bank order; the S reads (16 consecutive
+// entries, one 16-byte piece each) still hit 16 distinct bank groups, and the
+// transposed V reads (4 consecutive entries x 64 bytes) now land 64 bytes
+// apart instead of overlapping.
+__device__ __forceinline__ int tile_row(int m) {
+    return (m & ~15) | ((m & 3) << 2) | ((m >> 2) & 3);
+}
+
 struct __align__(16) MlaSmem {
     uint8_t kv[kRing][kTileBytes];    // 4 x 33280
     uint8_t p[2][kHg * kPPitch];      // 2 x 5120
@@ -189,7 +199,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         // this wave's half of S^T(t): K fragments from the LDS ring (and, for
         // kh = 1, the rope registers)
         auto s_read = [&](int t, bf16x8 (&af)[kHalfSteps], const bf16x8 (&rp)[kRopeSteps]) {
-            const uint8_t *arow = sm.kv[t % kRing] + l32 * kRowPitch + 16 * half + 576 * kh;
+            const uint8_t *arow =
+                sm.kv[t % kRing] + tile_row(l32) * kRowPitch + 16 * half + 576 * kh;
             if (kh == 0) {
 #pragma unroll
                 for (int ks = 0; ks < kHalfSteps; ++ks) af[ks] = lds_b128(arow + ks * 32);
@@ -390,10 +401,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             }
         };
         auto stage_store = [&](int t, const u32x4 (&st)[kStageRows]) {
-            uint8_t *dst = sm.kv[t % kRing] + (8 * d) * kRowPitch + 16 * lane;
+            uint8_t *dst = sm.kv[t % kRing] + 16 * lane;
 #pragma unroll
             for (int m = 0; m < kStageRows; ++m)
-                *reinterpret_cast<u32x4 *>(dst + m * kRowPitch) = st[m];
+                *reinterpret_cast<u32x4 *>(dst + tile_row(8 * d + m) * kRowPitch) = st[m];
         };
         u32x4 stg[2][kStageRows];
         __syncthreads();  // selection of tiles 0..4 (matches the S waves')
@@ -414,6 +425,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         lds_barrier();  // B1
         const int trj = lane & 15, trg = lane >> 4;
         const int vrow = 8 * (trg >> 1) + (trj >> 2);
+        const int vrow_lo = tile_row(vrow), vrow_hi = tile_row(vrow + 4);
         const int vcol = (dv0 + 16 * (trg & 1) + 4 * (trj & 3)) * 2;
         // Operands of one 16-entry k-step of tile `tile`: P (A, 32 heads x 16
         // entries per head tile) and V (B, 16 entries x 32 dims per column tile).
@@ -425,9 +437,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
                 pa[a] = lds_b128(pt + (a * 32 + l32) * kPPitch + (16 * ks + 8 * half) * 2);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const uint8_t *vp = kvt + (16 * ks + vrow) * kRowPitch + vcol + 64 * c;
-                const bf16x4 lo = lds_tr16(vp);
-                const bf16x4 hi = lds_tr16(vp + 4 * kRowPitch);
+                const uint8_t *vp = kvt + 16 * ks * kRowPitch + vcol + 64 * c;
+                const bf16x4 lo = lds_tr16(vp + vrow_lo * kRowPitch);
+                const bf16x4 hi = lds_tr16(vp + vrow_hi * kRowPitch);
                 vb[c] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
         };
