@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ lat,
     const int32_t *__restrict__ idx, int T, int S, int H, int k, float scale, int row0,
     int rows, int B, int splits, int per_split, Tout *__restrict__ out, float *__restrict__ lse,
-    float *__restrict__ o_part, float *__restrict__ lse_part) {
+    Tout *__restrict__ o_part, float *__restrict__ lse_part) {
     __shared__ MlaSmem sm;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -541,9 +541,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             } else {
 #pragma unroll
                 for (int m = 0; m < 16; ++m)
-                    *reinterpret_cast<f32x4 *>(
-                        o_part + ((prow * splits + split) * H + head0 + a * 32 + 2 * m + half) * kDv +
-                        dd) = v[m];
+                    store_out4(o_part + ((prow * splits + split) * H + head0 + a * 32 + 2 * m + half) *
+                                            kDv + dd, v[m]);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();  // block reused by the second half
@@ -552,7 +551,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     }
 }
 
+// 4 consecutive partial outputs as fp32
+template <typename Tout>
+__device__ __forceinline__ f32x4 load_out4(const Tout *p);
+template <>
+__device__ __forceinline__ f32x4 load_out4<float>(const float *p) {
+    return *reinterpret_cast<const f32x4 *>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 load_out4<uint16_t>(const uint16_t *p) {
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p);
+    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+}
+
 // Merge split partials: out = sum_s exp(lse_s - lse) o_s, lse = log sum exp lse_s.
+// The partials are normalised outputs kept in the output type (bf16 partials
+// halve the bytes written and read back; their rounding is that of the output).
 // Two heads per workgroup, 4 dims per thread; the splits are read in batches
 // of 16 whose loads are all issued before any is used (clamped indices, zero
 // weight past the last split), merged online across batches, so a row costs
@@ -561,7 +575,7 @@ constexpr int kCombineBatch = 16;
 
 template <typename Tout>
 __global__ __launch_bounds__(256) void mla_combine_kernel(
-    const float *__restrict__ o_part, const float *__restrict__ lse_part, int T, int H,
+    const Tout *__restrict__ o_part, const float *__restrict__ lse_part, int T, int H,
     int row0, int rows, int splits, Tout *__restrict__ out, float *__restrict__ lse) {
     const int h = blockIdx.x * 2 + (threadIdx.x >> 7);
     const int d = (threadIdx.x & 127) * 4;
@@ -570,7 +584,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(
     const size_t rowq = (size_t)b * T + row0 + r;
     const size_t prow = (size_t)b * rows + r;  // row of the launch's split partials
     const float *lp = lse_part + prow * splits * H + h;  // split s at lp[s * H]
-    const float *op = o_part + (prow * splits * H + h) * kDv + d;  // split s at op[s * H * kDv]
+    const Tout *op = o_part + (prow * splits * H + h) * kDv + d;  // split s at op[s * H * kDv]
     float mx = -INFINITY, wsum = 0.0f;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int s0 = 0; s0 < splits; s0 += kCombineBatch) {
@@ -580,7 +594,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(
         for (int j = 0; j < kCombineBatch; ++j) {
             const size_t sc = (size_t)min(s0 + j, splits - 1);
             ls[j] = lp[sc * H];
-            ov[j] = *reinterpret_cast<const f32x4 *>(op + sc * H * kDv);
+            ov[j] = load_out4(op + sc * H * kDv);
         }
         float bmx = -INFINITY;
 #pragma unroll
@@ -651,31 +665,38 @@ hipError_t launch_mla(const dsa_attn_desc_t &d, const void *q, const void *kv,
         const int splits = mla_splits(B, n, H, k);
         const int per_split = ceil_div(ceil_div(k, splits), kKt) * kKt;
         const int used_splits = ceil_div(k, per_split);
-        float *o_part = static_cast<float *>(workspace);
-        float *lse_part = o_part + (size_t)B * n * used_splits * H * kDv;
+        const size_t part_elems = (size_t)B * n * used_splits * H * kDv;
         const long long nwg = (long long)(H / kHg) * used_splits * n * B;
         dim3 grid((unsigned)nwg);
         if (d.out_dtype == DSA_BF16)
             hipLaunchKernelGGL(mla_attention_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
                                static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),
                                idx, T, S, H, k, d.scale, row0 + r0, n, B, used_splits, per_split,
-                               static_cast<uint16_t *>(out), lse, o_part, lse_part);
+                               static_cast<uint16_t *>(out), lse,
+                               static_cast<uint16_t *>(workspace),
+                               reinterpret_cast<float *>(static_cast<uint16_t *>(workspace) + part_elems));
         else
             hipLaunchKernelGGL(mla_attention_kernel<float>, grid, dim3(kThreads), 0, stream,
                                static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),
                                idx, T, S, H, k, d.scale, row0 + r0, n, B, used_splits, per_split,
-                               static_cast<float *>(out), lse, o_part, lse_part);
+                               static_cast<float *>(out), lse, static_cast<float *>(workspace),
+                               static_cast<float *>(workspace) + part_elems);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (used_splits > 1) {
             dim3 cg(H / 2, n, B);
             if (d.out_dtype == DSA_BF16)
-                hipLaunchKernelGGL(mla_combine_kernel<uint16_t>, cg, dim3(256), 0, stream, o_part,
-                                   lse_part, T, H, row0 + r0, n, used_splits,
+                hipLaunchKernelGGL(mla_combine_kernel<uint16_t>, cg, dim3(256), 0, stream,
+                                   static_cast<const uint16_t *>(workspace),
+                                   reinterpret_cast<const float *>(
+                                       static_cast<const uint16_t *>(workspace) + part_elems),
+                                   T, H, row0 + r0, n, used_splits,
                                    static_cast<uint16_t *>(out), lse);
             else
-                hipLaunchKernelGGL(mla_combine_kernel<float>, cg, dim3(256), 0, stream, o_part,
-                                   lse_part, T, H, row0 + r0, n, used_splits,
+                hipLaunchKernelGGL(mla_combine_kernel<float>, cg, dim3(256), 0, stream,
+                                   static_cast<const float *>(workspace),
+                                   static_cast<const float *>(workspace) + part_elems, T, H,
+                                   row0 + r0, n, used_splits,
                                    static_cast<float *>(out), lse);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
