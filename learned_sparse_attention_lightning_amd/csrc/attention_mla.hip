@@ -150,7 +150,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     const int hgs = H / kHg;
     const int id = blockIdx.x;
     int hg, split, qidx;
-    if ((rows * B * splits) % 8 == 0) {
+    if ((rows * B) % 8 == 0) {
+        // XCD x (= id mod 8) takes the query rows qidx = x mod 8, each with all
+        // its head groups and splits: the two head groups share the gathered
+        // rows and the query block in that XCD's L2, and the split partials
+        // are written where the merge reads them.
+        const int x = id & 7, j = id >> 3;
+        const int per = hgs * splits;
+        const int qg = j / per, rem = j - qg * per;
+        hg = rem % hgs;
+        split = rem / hgs;
+        qidx = 8 * qg + x;
+    } else if ((rows * B * splits) % 8 == 0) {
         const int slot = id >> 3;
         hg = slot % hgs;
         const int unit = (slot / hgs) * 8 + (id & 7);
@@ -576,11 +587,24 @@ constexpr int kCombineBatch = 16;
 template <typename Tout>
 __global__ __launch_bounds__(256) void mla_combine_kernel(
     const Tout *__restrict__ o_part, const float *__restrict__ lse_part, int T, int H,
-    int row0, int rows, int splits, Tout *__restrict__ out, float *__restrict__ lse) {
-    const int h = blockIdx.x * 2 + (threadIdx.x >> 7);
+    int row0, int rows, int B, int splits, Tout *__restrict__ out, float *__restrict__ lse) {
+    // workgroup = (query row, head pair); with a multiple of 8 rows the rows
+    // map to XCDs as in the attention kernel, so the partials come from L2
+    const int hps = H / 2;
+    const int id = blockIdx.x;
+    int hp, qidx;
+    if ((rows * B) % 8 == 0) {
+        const int x = id & 7, j = id >> 3;
+        hp = j % hps;
+        qidx = 8 * (j / hps) + x;
+    } else {
+        hp = id % hps;
+        qidx = id / hps;
+    }
+    const int h = hp * 2 + (threadIdx.x >> 7);
     const int d = (threadIdx.x & 127) * 4;
-    const int r = blockIdx.y;
-    const int b = blockIdx.z;
+    const int r = qidx % rows;
+    const int b = qidx / rows;
     const size_t rowq = (size_t)b * T + row0 + r;
     const size_t prow = (size_t)b * rows + r;  // row of the launch's split partials
     const float *lp = lse_part + prow * splits * H + h;  // split s at lp[s * H]
@@ -684,19 +708,19 @@ hipError_t launch_mla(const dsa_attn_desc_t &d, const void *q, const void *kv,
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (used_splits > 1) {
-            dim3 cg(H / 2, n, B);
+            const dim3 cg((unsigned)((long long)(H / 2) * n * B));
             if (d.out_dtype == DSA_BF16)
                 hipLaunchKernelGGL(mla_combine_kernel<uint16_t>, cg, dim3(256), 0, stream,
                                    static_cast<const uint16_t *>(workspace),
                                    reinterpret_cast<const float *>(
                                        static_cast<const uint16_t *>(workspace) + part_elems),
-                                   T, H, row0 + r0, n, used_splits,
+                                   T, H, row0 + r0, n, B, used_splits,
                                    static_cast<uint16_t *>(out), lse);
             else
                 hipLaunchKernelGGL(mla_combine_kernel<float>, cg, dim3(256), 0, stream,
                                    static_cast<const float *>(workspace),
                                    static_cast<const float *>(workspace) + part_elems, T, H,
-                                   row0 + r0, n, used_splits,
+                                   row0 + r0, n, B, used_splits,
                                    static_cast<float *>(out), lse);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
