@@ -311,13 +311,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             for (int t = 0; t < 5; ++t)
                 if (half == 0) sm.sel[t][l32] = sv[t];
         }
-        __syncthreads();  // selection of tiles 0..4
+        lds_barrier();  // selection of tiles 0..4
         bf16x8 rp[2][kRopeSteps];  // kh = 1: rope of tiles it+1 (in use) and it+2
-        lds_barrier();             // B0: tiles 0 and 1
-        if (kh == 1) {
+        if (kh == 1) {  // in flight together with the first gathers
             rope_load(0, rp[0]);
             rope_load(1, rp[1]);
         }
+        lds_barrier();  // B0: tiles 0 and 1
         f32x16 s_cur;  // kh = 0: own half of S of the tile the softmax takes next
         {
             bf16x8 af[kHalfSteps];
@@ -417,10 +417,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             for (int m = 0; m < kStageRows; ++m)
                 *reinterpret_cast<u32x4 *>(dst + tile_row(8 * d + m) * kRowPitch) = st[m];
         };
+        // the first tiles take their rows straight from the selection in memory
+        // (uniform loads), so their gathers start before the ring is filled
+        auto stage_load_first = [&](int t, u32x4 (&st)[kStageRows]) {
+#pragma unroll
+            for (int m = 0; m < kStageRows; ++m) {
+                const int32_t s = __builtin_amdgcn_readfirstlane(sel_of(t * kKt + 8 * d + m));
+                st[m] = *reinterpret_cast<const u32x4 *>(
+                    lat_b + (uint32_t)max(s, 0) * (uint64_t)kLatRowBytes + 16 * lane);
+            }
+        };
         u32x4 stg[2][kStageRows];
-        __syncthreads();  // selection of tiles 0..4 (matches the S waves')
-        stage_load(0, stg[0]);
-        stage_load(1, stg[1]);
+        stage_load_first(0, stg[0]);
+        stage_load_first(1, stg[1]);
+        lds_barrier();  // selection of tiles 0..4 (matches the S waves')
         stage_store(0, stg[0]);
         stage_store(1, stg[1]);
         stage_load(2, stg[0]);
