@@ -375,7 +375,7 @@ constexpr int kPfStorers = kPfRows / 2;         // a storing wave per two rows
 constexpr int kPfLoaders = kPfWaves - kPfStorers;
 static_assert(kPfRows % 2 == 0, "storing waves take rows in pairs");
 static_assert(kPfQuarters % 2 == 0, "the two accumulator sets alternate evenly over a tile");
-constexpr int kPfMinWgs = 2 * 256 * 16 / kPfWaves;  // two rounds of 4 waves a SIMD
+constexpr int kPfMinWgs = 4 * 256 * 16 / kPfWaves;  // four rounds of 4 waves a SIMD
 constexpr int kPfAhead = 4;  // operand fragments read ahead of their product
 
 template <bool Fp8>
@@ -684,15 +684,23 @@ hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, c
         }
         if (rows >= kPfRows) {  // rows share key tiles: 8 rows a workgroup
             // Keys per workgroup: the whole causal row when the row blocks alone
-            // give enough workgroups (each block then loads its query rows once
-            // and its prologue is paid once), halved while there are fewer than
-            // 512 of them.
+            // give enough workgroups with work (each block then loads its query
+            // rows once and pays its prologue once), halved while there are
+            // fewer than kPfMinWgs of them.  Without explicit positions the rows
+            // of this launch end at position S - T + row0 + rows - 1, so key
+            // chunks past that hold no work (unless -inf must be written there).
+            const long long nrb = (long long)B * ceil_div(rows, kPfRows);
+            const long long keys_hi =
+                q_pos ? S : std::min<long long>(S, (long long)(S - T) + row0 + rows);
+            const long long keys_avg =
+                q_pos ? S : std::max<long long>(1, (long long)(S - T) + row0 + rows / 2);
             int kchunk = 4096;
-            while (kchunk < S) kchunk <<= 1;
-            while (kchunk > 4096 && (long long)B * ceil_div(rows, kPfRows) * ceil_div(S, kchunk) < kPfMinWgs)
+            while (kchunk < keys_hi) kchunk <<= 1;
+            while (kchunk > 4096 && nrb * ((keys_avg + kchunk - 1) / kchunk) < kPfMinWgs)
                 kchunk >>= 1;
-            const int nkc = ceil_div(S, kchunk);
-            const long long wgs = (long long)B * ceil_div(rows, kPfRows) * nkc;
+            const int nkc = write_masked ? ceil_div(S, kchunk)
+                                         : (int)((keys_hi + kchunk - 1) / kchunk);
+            const long long wgs = nrb * nkc;
             if (idx_dtype == DSA_BF16)
                 hipLaunchKernelGGL((indexer_prefill_kernel<false>), dim3((unsigned)wgs),
                                    dim3(kPfWaves * 64), 0, stream,

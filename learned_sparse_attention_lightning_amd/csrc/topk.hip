@@ -274,7 +274,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
         // the range reduction's barriers also publish the keys
         block_key_range([&](auto f) { f(vlo); f(vhi); }, sm.sel, lo, hi);
     }
-    auto key_at = [&](int p) -> uint32_t { return cached ? sm.keys[p] : ordered_key(row[p]); };
     auto each = [&](auto f) {
         if (cached) {
             const int n16 = (n + 3) / 4;
@@ -285,7 +284,26 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
                     if (4 * j + e < n) f(v[e]);
             }
         } else {
-            for (int p = tid; p < n; p += kTkThreads) f(ordered_key(row[p]));
+            // a row longer than the cache is re-read on every pass: 16-byte
+            // loads, eight in flight per thread, so a pass costs a few memory
+            // latencies rather than one per key a thread reads
+            constexpr int U = 8;
+            const int n16 = aligned ? n / 4 : 0;
+            for (int j0 = tid; j0 < n16; j0 += U * kTkThreads) {
+                f32x4 v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int j = j0 + u * kTkThreads;
+                    if (j < n16) v[u] = reinterpret_cast<const f32x4 *>(row)[j];
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (j0 + u * kTkThreads < n16) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) f(ordered_key(v[u][e]));
+                    }
+            }
+            for (int p = 4 * n16 + tid; p < n; p += kTkThreads) f(ordered_key(row[p]));
         }
     };
     if (!cached) block_key_range(each, sm.sel, lo, hi);
@@ -314,10 +332,18 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
 #pragma unroll
             for (int it = 0; it < kMaxIt; ++it)
                 if (it < nit) body(kv[it], w0 + 64 * it + lane);
-        } else {
-            for (int it = 0; it < nit; ++it) {
-                const int p = w0 + 64 * it + lane;
-                body(p < w1 ? key_at(p) : 0u, p);
+        } else {  // keys from memory, eight loads ahead of their use
+            constexpr int U = 8;
+            for (int it0 = 0; it0 < nit; it0 += U) {
+                uint32_t kk[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int p = w0 + 64 * (it0 + u) + lane;
+                    kk[u] = it0 + u < nit && p < w1 ? ordered_key(row[p]) : 0u;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (it0 + u < nit) body(kk[u], w0 + 64 * (it0 + u) + lane);
             }
         }
     };
