@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4"])
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "p128k"])
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = auto)")
     ap.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
     ap.add_argument("--cpu-baseline", type=int, default=1)
@@ -243,17 +243,36 @@ def main():
             stage_ms.append(a.elapsed_time(b) / nst)
 
     else:
-        # prefill: each entry point once over all query rows (the step runs the
-        # same kernels on row chunks); two timed runs after a warm one
-        sc = torch.empty((w.B, w.T, w.S), dtype=torch.float32, device=dev)
+        # prefill: each entry point over all query rows (the step runs the same
+        # kernels on row chunks), in row chunks of at most 4 GiB of scores with
+        # explicit positions; two timed runs after a warm one
+        ch = max(1, min(w.T, (4 << 30) // (w.B * w.S * 4)))
+        sc = torch.empty((w.B, ch, w.S), dtype=torch.float32, device=dev)
         x = reps[0]
-        stages = [
-            lambda: dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"], scores=sc),
-            lambda: dsa.dsa_topk(sc, w.index_topk, idx=idx),
-            lambda: dsa.dsa_sparse_attention(desc, x["q"], x["kv"], x["v"], idx, out=out),
-        ]
+        chunks = []
+        for r0 in range(0, w.T, ch):
+            r1 = min(w.T, r0 + ch)
+            pos = None if ch == w.T else (torch.arange(w.S - w.T + r0, w.S - w.T + r1,
+                                                       dtype=torch.int32, device=dev)
+                                          .view(1, -1).repeat(w.B, 1))
+            chunks.append((r0, r1, pos))
+
+        def st_indexer():
+            for r0, r1, pos in chunks:
+                dsa.dsa_indexer_scores(x["q_idx"][:, r0:r1], x["k_idx"], x["w"][:, r0:r1],
+                                       q_pos=pos, scores=sc[:, : r1 - r0])
+
+        def st_topk():
+            for r0, r1, pos in chunks:
+                dsa.dsa_topk(sc[:, : r1 - r0], w.index_topk, q_pos=pos, idx=idx[:, r0:r1])
+
+        def st_attention():
+            for r0, r1, pos in chunks:
+                dsa.dsa_sparse_attention(desc, x["q"][:, r0:r1], x["kv"], x["v"],
+                                         idx[:, r0:r1], out=out[:, r0:r1])
+
         stage_ms = []
-        for f in stages:
+        for f in (st_indexer, st_topk, st_attention):
             f()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -74,6 +74,15 @@ WORKLOADS = {
         B=8, T=1, S=131072, index_n_heads=64, index_head_dim=128, index_topk=2048,
         idx_dtype="fp8", int_lo=-4, int_hi=4, w_den=16, form="mla", num_heads=128, d_qk=576,
         d_v=512, dtype="bf16", out_dtype="bf16", scale=1.0 / math.sqrt(192.0)),
+    # 128K-context prefill: the 32K prefill shape at n = 131072 (the score
+    # matrix of the whole sequence, 64 GiB, is never held at once: the forward
+    # pass runs query rows in chunks)
+    "p128k": Workload(
+        name="p128k", description="MLA prefill at 128K context: n=131072, indexer 64x128 "
+        "bf16, k=2048, 128 heads, latent 576/512 bf16",
+        B=1, T=131072, S=131072, index_n_heads=64, index_head_dim=128, index_topk=2048,
+        idx_dtype="bf16", int_lo=-4, int_hi=4, w_den=16, form="mla", num_heads=128, d_qk=576,
+        d_v=512, dtype="bf16", out_dtype="bf16", scale=1.0 / math.sqrt(192.0)),
 }
 
 

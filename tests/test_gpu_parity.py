@@ -402,6 +402,27 @@ def test_forward_c2_sampled_rows():
     assert err <= TOL["bf16"]
 
 
+def test_forward_p128k_sampled_rows():
+    """128K-context prefill: the forward pass runs the rows in chunks (the
+    scores of one chunk at a time); sampled rows across the sequence, at chunk
+    and top-k boundaries, against the oracle."""
+    w = configs.get("p128k")
+    x, idx, out = _forward(w, seed=11)
+    rows = [0, 2047, 2048, 65535, 65536, 100000, 131071]
+    _say(f"p128k: oracle over rows {rows}")
+    pos = np.array([rows])
+    sc = oracle.indexer_scores(x["q_idx"][:, rows], x["k_idx"], x["w"][:, rows], q_pos=pos)
+    ref_idx = oracle.topk(sc, w.index_topk, q_pos=pos)
+    assert_selection_equal(idx[:, rows], ref_idx, "p128k")
+    ref = oracle.sparse_attention("mla", x["q"][:, rows], x["kv"], None, ref_idx, w.scale,
+                                  d_v=w.d_v)
+    err = max_abs_err(out[:, rows], ref)
+    _say(f"p128k: max-abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+    del x, idx, out
+    torch.cuda.empty_cache()
+
+
 def test_forward_short_last_chunk():
     """Rows beyond one score block run in chunks; a short last chunk takes the
     split-entry attention path (partials in the workspace) and the wide top-k."""
