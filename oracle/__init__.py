@@ -44,7 +44,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_indexer_scores.restype = None
     lib.oracle_indexer_scores_exact.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p]
     lib.oracle_indexer_scores_exact.restype = None
-    lib.oracle_topk.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _p]
+    lib.oracle_topk.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _i64, _p]
     lib.oracle_topk.restype = None
     lib.oracle_sparse_attention.argtypes = [ctypes.c_int, _p, _p, _p, _p, _i64, _i64, _i64,
                                             _i64, _i64, _i64, _i64, ctypes.c_double, _p, _p]
@@ -130,14 +130,17 @@ def indexer_scores_exact(q_idx, k_idx, w, den: int, q_pos=None) -> np.ndarray:
     return out
 
 
-def topk(scores, k: int, q_pos=None) -> np.ndarray:
+def topk(scores, k: int, q_pos=None, include_current: bool = False) -> np.ndarray:
     """Selected positions per row in rank order (score desc, position asc),
-    min(k, t+1) valid entries then -1.  scores [B,T,S] -> int32 [B,T,k]."""
+    min(k, t+1) valid entries then -1.  scores [B,T,S] -> int32 [B,T,k].
+    include_current: position t itself first, then the best k-1 of s < t
+    ([P1] section 3.4, the current-token variant)."""
     sc = as_f64(scores)
     B, T, S = sc.shape
     pos, pos_p = _pos(q_pos)
     out = np.empty((B, T, k), dtype=np.int32)
-    _get().oracle_topk(sc.ctypes.data, pos_p, B, T, S, k, out.ctypes.data)
+    _get().oracle_topk(sc.ctypes.data, pos_p, B, T, S, k, 1 if include_current else 0,
+                       out.ctypes.data)
     return out
 
 

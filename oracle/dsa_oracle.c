@@ -126,27 +126,36 @@ static int candidate_rank_order(const void *pa, const void *pb) {
  *   S_t = the k candidates s in 0..t with the highest I[t,s];
  * ties broken by the lower s.  A row keeps n_sel = min(k, t+1) entries
  * ([P1] section 7.2), written in rank order; slots n_sel..k-1 hold -1.
+ *
+ * include_current != 0 is the variant [P1] section 3.4 mentions (the current
+ * token always kept): the query's own position t takes the first slot and
+ * the other k-1 slots go to the best candidates among s in 0..t-1, by the
+ * same order; n_sel is still min(k, t+1).
  * Layouts: scores [B,T,S], idx [B,T,k].
  */
 ORACLE_API void oracle_topk(const double *scores, const int64_t *q_pos,
                             int64_t B, int64_t T, int64_t S, int64_t k,
-                            int32_t *idx) {
+                            int64_t include_current, int32_t *idx) {
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
     for (int64_t b = 0; b < B; ++b) {
         for (int64_t i = 0; i < T; ++i) {
             const int64_t t = query_position(q_pos, b, i, T, S);
             const double *row = scores + (b * T + i) * S;
             int32_t *out = idx + (b * T + i) * k;
-            const int64_t n_cand = t + 1;
-            candidate_t *cand = (candidate_t *)malloc(sizeof(candidate_t) * (size_t)n_cand);
+            /* the forced slot, then the ranked candidates after it */
+            const int64_t forced = (include_current && t >= 0) ? 1 : 0;
+            const int64_t n_cand = t + 1 - forced;
+            int64_t r = 0;
+            if (forced) out[r++] = (int32_t)t;
+            const size_t n_alloc = n_cand > 0 ? (size_t)n_cand : 1;
+            candidate_t *cand = (candidate_t *)malloc(sizeof(candidate_t) * n_alloc);
             for (int64_t s = 0; s < n_cand; ++s) {
                 cand[s].score = row[s];
                 cand[s].pos = s;
             }
-            qsort(cand, (size_t)n_cand, sizeof(candidate_t), candidate_rank_order);
-            const int64_t n_sel = n_cand < k ? n_cand : k;
-            for (int64_t r = 0; r < k; ++r)
-                out[r] = r < n_sel ? (int32_t)cand[r].pos : -1;
+            if (n_cand > 1) qsort(cand, (size_t)n_cand, sizeof(candidate_t), candidate_rank_order);
+            for (int64_t c = 0; r < k; ++r, ++c)
+                out[r] = c < n_cand ? (int32_t)cand[c].pos : -1;
             free(cand);
         }
     }

@@ -68,6 +68,50 @@ def test_worked_example_tie_lower_index_wins(oracle):
     assert list(oracle.topk(sc, 4, q_pos=pos)[0, 0]) == [3, 9, 8, 10]
 
 
+def test_worked_example_include_current(oracle):
+    # [P1] section 3.4: the current token (10) is outside the plain top-3; the
+    # variant that always keeps it fills the other two slots with the two best
+    # earlier positions of the section 3.2 ranking (3, then 9)
+    ex, q, k, w, pos = _example_inputs([-1.0, 0.0])
+    sc = oracle.indexer_scores(q, k, w, q_pos=pos)
+    assert list(oracle.topk(sc, 3, q_pos=pos, include_current=True)[0, 0]) == [10, 3, 9]
+    assert list(oracle.topk(sc, 1, q_pos=pos, include_current=True)[0, 0]) == [10]
+
+
+@pytest.mark.parametrize("levels", [None, 3])
+def test_include_current_is_topk_with_current_scored_highest(oracle, levels):
+    """For finite scores, keeping the current token is the plain top-k of the
+    same row with I[t,t] raised above every other score; rows with t+1 <= k
+    keep everything either way."""
+    B, n = 2, 40
+    sc = synth.random_scores((B, n, n), seed=21, levels=levels).double().numpy()
+    raised = sc.copy()
+    for t in range(n):
+        raised[:, t, t] = np.inf
+    for k in (1, 2, 7, 40):
+        got = oracle.topk(sc, k, include_current=True)
+        want = oracle.topk(raised, k)
+        assert np.array_equal(got, want), k
+        for b, t in itertools.product(range(B), range(n)):
+            row = got[b, t]
+            nsel = min(k, t + 1)
+            assert row[0] == t and np.all(row[nsel:] == -1)
+            assert len(set(row[:nsel].tolist())) == nsel
+
+
+def test_include_current_keeps_plain_set_when_current_selected(oracle):
+    sc = synth.random_scores((1, 30, 30), seed=4, levels=4).double().numpy()
+    k = 6
+    plain = oracle.topk(sc, k)
+    cur = oracle.topk(sc, k, include_current=True)
+    hits = 0
+    for t in range(30):
+        if t in plain[0, t].tolist():
+            hits += 1
+            assert set(plain[0, t].tolist()) == set(cur[0, t].tolist())
+    assert hits >= 5
+
+
 def test_causal_mask_and_positions(oracle):
     w = configs.get("c0")
     q, k, wt = synth.indexer_inputs(w)
