@@ -25,7 +25,9 @@ MUTANTS = {
     "causal_excludes_self": ("if (s > t) {\n                    row[s] = -INFINITY;", "if (s >= t) {\n                    row[s] = -INFINITY;"),
     "tie_higher_index": ("return (a->pos < b->pos) ? -1 : (a->pos > b->pos);", "return (a->pos > b->pos) ? -1 : (a->pos < b->pos);"),
     "ascending_scores": ("if (a->score > b->score) return -1;\n    if (a->score < b->score) return 1;", "if (a->score < b->score) return -1;\n    if (a->score > b->score) return 1;"),
-    "candidates_exclude_self": ("const int64_t n_cand = t + 1;", "const int64_t n_cand = t > 0 ? t : 1;"),
+    "candidates_exclude_self": ("const int64_t n_cand = t + 1 - forced;", "const int64_t n_cand = (t > 0 ? t : 1) - forced;"),
+    "current_not_forced": ("const int64_t forced = (include_current && t >= 0) ? 1 : 0;", "const int64_t forced = 0;"),
+    "current_budget_not_reduced": ("const int64_t n_cand = t + 1 - forced;", "const int64_t n_cand = t + 1;"),
     "scale_dropped": ("logit[r] = scale * dot;", "logit[r] = dot;"),
     "not_normalised": ("for (int64_t d = 0; d < dv; ++d) o[d] /= denom;", ""),
     "mla_value_tail": ("    return kv + (b * S + s) * dqk;\n}\n\n/*\n * Attention restricted", "    return kv + (b * S + s) * dqk + (dqk - dv);\n}\n\n/*\n * Attention restricted"),
