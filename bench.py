@@ -38,7 +38,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "p128k"])
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c2-fp8", "c3", "c4", "p128k", "short2k"])
+    ap.add_argument("--include-current", type=int, default=0,
+                    help="always keep the current token (dsa_forward_ex flag)")
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = auto)")
     ap.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
     ap.add_argument("--cpu-baseline", type=int, default=1)
@@ -74,6 +76,8 @@ def algorithmic(w):
     ib = eb[w.idx_dtype]
     idx_bytes = B * S * D * ib + B * T * H * D * ib + B * T * H * 4
     idx_flops = pairs * 2 * H * D
+    if S <= k:  # the dense limit: no scores are needed to select everything
+        idx_bytes = idx_flops = 0
     if w.form == "mla":
         attn_flops = entries * 2 * w.num_heads * (w.d_qk + w.d_v)
         attn_bytes = entries * w.d_qk * 2 + B * T * w.num_heads * (w.d_qk * 2 + w.d_v * 2)
@@ -176,10 +180,15 @@ def main():
                               w.index_head_dim, w.index_topk)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
 
+    cur = bool(args.include_current)
+    # a context no longer than the budget selects everything: the forward pass
+    # runs only the selection fill and the attention
+    dense = w.S <= w.index_topk
+
     def step(r):
         x = reps[r]
         dsa.dsa_forward(desc, x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"], x["v"],
-                        w.index_topk, out=out, idx_out=idx, workspace=ws)
+                        w.index_topk, out=out, idx_out=idx, workspace=ws, include_current=cur)
 
     for s in range(args.warmup):
         step(s % R)
@@ -225,7 +234,7 @@ def main():
         nst = max(20, args.steps)
         stages = [
             lambda x: dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"], scores=sc),
-            lambda x: dsa.dsa_topk(sc, w.index_topk, idx=idx),
+            lambda x: dsa.dsa_topk(sc, w.index_topk, idx=idx, include_current=cur),
             lambda x: dsa.dsa_sparse_attention(desc, x["q"], x["kv"], x["v"], idx, out=out),
         ]
         for f in stages:  # inputs for the later stages, and warm launches
@@ -264,7 +273,8 @@ def main():
 
         def st_topk():
             for r0, r1, pos in chunks:
-                dsa.dsa_topk(sc[:, : r1 - r0], w.index_topk, q_pos=pos, idx=idx[:, r0:r1])
+                dsa.dsa_topk(sc[:, : r1 - r0], w.index_topk, q_pos=pos, idx=idx[:, r0:r1],
+                             include_current=cur)
 
         def st_attention():
             for r0, r1, pos in chunks:
@@ -273,6 +283,9 @@ def main():
 
         stage_ms = []
         for f in (st_indexer, st_topk, st_attention):
+            if dense and f is not st_attention:
+                stage_ms.append(0.0)  # skipped by the forward pass
+                continue
             f()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -308,10 +321,13 @@ def main():
                 "algorithmic_flops_per_launch": alg["attn_flops"],
                 "avg_launch_ms": round(stage_ms[2], 4)}
         ipk = FP8_PEAK_TFLOPS if w.idx_dtype == "fp8" else BF16_PEAK_TFLOPS
-        ind = alg["indexer_flops"] / (stage_ms[0] * 1e-3) / 1e12
-        indexer_roof = {"bound": "mfma", "achieved": round(ind, 2), "peak": ipk,
-                        "unit": "TFLOP/s", "frac": round(ind / ipk, 4),
-                        "avg_launch_ms": round(stage_ms[0], 4)}
+        if dense or not stage_ms[0] > 0:
+            indexer_roof = None
+        else:
+            ind = alg["indexer_flops"] / (stage_ms[0] * 1e-3) / 1e12
+            indexer_roof = {"bound": "mfma", "achieved": round(ind, 2), "peak": ipk,
+                            "unit": "TFLOP/s", "frac": round(ind / ipk, 4),
+                            "avg_launch_ms": round(stage_ms[0], 4)}
 
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
@@ -323,6 +339,7 @@ def main():
                    "index_head_dim": w.index_head_dim, "index_topk": w.index_topk,
                    "form": w.form, "heads": w.num_heads, "d_qk": w.d_qk, "d_v": w.d_v,
                    "input_replicas": R, "launch": "hip-graph" if graphs else "eager",
+                   "include_current": cur, "dense_limit": dense,
                    "parallelism": "single-gpu"},
         "roofline": roof,
         "host_ms_per_step": round(wall_ms, 5),

@@ -8,9 +8,13 @@
  *   2. per-query top-k selection     dsa_topk
  *   3. attention over the selection  dsa_sparse_attention (MHA or MLA latent)
  *   1+2+3                            dsa_forward
+ * dsa_topk_ex and dsa_forward_ex take selection flags (the current-token
+ * variant).
  *
  * Page references (titles as published):
  *   [P1] "DeepSeek Sparse Attention: Learned Token Selection from Scratch"
+ *   [P3] "Sparse Attention LLM Design: Native Sparse Attention and DeepSeek
+ *        Sparse Attention"
  *   [P4] "DeepSeek NSA and DSA: From Native Sparse Attention to Fine-Grained
  *        Token Selection"
  *
@@ -45,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 typedef enum {
     DSA_F32 = 0,      /* IEEE binary32 */
@@ -115,12 +119,30 @@ dsa_status_t dsa_indexer_scores(const void *q_idx, const void *k_idx, int idx_dt
  *   scores  [B,T,S] fp32 (entries s > t are never read)
  *   idx     [B,T,k] int32 output: the n_sel selected positions in ASCENDING
  *           order, then -1 in the remaining k - n_sel slots.
- * index_topk (k) in 1..S.  Needs dsa_workspace_bytes(DSA_OP_TOPK, ...) bytes
- * of workspace (may be 0; then workspace may be NULL).
+ * index_topk (k) in 1..2^20; k may exceed S (rows then keep every candidate
+ * and the surplus slots hold -1).  Needs dsa_workspace_bytes(DSA_OP_TOPK, ...)
+ * bytes of workspace (may be 0; then workspace may be NULL).
  */
 dsa_status_t dsa_topk(const float *scores, const int32_t *q_pos, int B, int T, int S,
                       int index_topk, int32_t *idx, void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/* Selection flags of the _ex calls. */
+enum {
+    /* Always keep the current token ([P1] section 3.4 names this variant):
+     * row i selects its own position t, and the other k-1 slots go to the
+     * best candidates among s in 0..t-1 by the order above.  n_sel is still
+     * min(k, t+1); the output stays ascending, so t is the last valid entry. */
+    DSA_SEL_INCLUDE_CURRENT = 1
+};
+
+/*
+ * dsa_topk with selection flags (DSA_SEL_*; 0 is dsa_topk).  Unknown flag
+ * bits return DSA_ERR_UNSUPPORTED.  Same workspace as dsa_topk.
+ */
+dsa_status_t dsa_topk_ex(const float *scores, const int32_t *q_pos, int B, int T, int S,
+                         int index_topk, int flags, int32_t *idx, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 /*
  * Softmax attention restricted to the selected rows, [P1] sections 3.3 and
@@ -156,6 +178,22 @@ dsa_status_t dsa_forward(const dsa_attn_desc_t *desc, const void *q_idx, const v
                          int index_n_heads, int index_head_dim, int index_topk, void *out,
                          int32_t *idx_out, void *workspace, size_t workspace_bytes,
                          void *stream);
+
+/*
+ * dsa_forward with selection flags (DSA_SEL_*; 0 is dsa_forward).  When the
+ * context is no longer than the budget (S <= k) every causal position is
+ * selected in every row -- the dense limit ([P1] section 7.6, the entry-count
+ * table; [P3] section "Trade-offs, Gotchas, and What Goes Wrong" on short
+ * inputs) -- so the indexer and the top-k are skipped and
+ * attention runs over the whole prefix; dsa_forward does the same.  Same
+ * workspace as dsa_forward.
+ */
+dsa_status_t dsa_forward_ex(const dsa_attn_desc_t *desc, const void *q_idx, const void *k_idx,
+                            int idx_dtype, const float *w, const void *q, const void *kv,
+                            const void *v, const int32_t *q_pos, int B, int T, int S,
+                            int index_n_heads, int index_head_dim, int index_topk, int flags,
+                            void *out, int32_t *idx_out, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 enum { DSA_OP_TOPK = 0, DSA_OP_ATTENTION = 1, DSA_OP_FORWARD = 2 };
 

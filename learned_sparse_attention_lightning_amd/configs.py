@@ -62,6 +62,22 @@ WORKLOADS = {
         B=1, T=32768, S=32768, index_n_heads=64, index_head_dim=128, index_topk=2048,
         idx_dtype="bf16", int_lo=-4, int_hi=4, w_den=16, form="mla", num_heads=128, d_qk=576,
         d_v=512, dtype="bf16", out_dtype="bf16", scale=1.0 / math.sqrt(192.0)),
+    # the 32K prefill with the indexer's q_I and k_I in fp8 (the pages' indexer
+    # precision; exact here, the inputs are small integers)
+    "c2-fp8": Workload(
+        name="c2-fp8", description="MLA prefill: n=32768, indexer 64x128 fp8, k=2048, "
+        "128 heads, latent 576/512 bf16",
+        B=1, T=32768, S=32768, index_n_heads=64, index_head_dim=128, index_topk=2048,
+        idx_dtype="fp8", int_lo=-4, int_hi=4, w_den=16, form="mla", num_heads=128, d_qk=576,
+        d_v=512, dtype="bf16", out_dtype="bf16", scale=1.0 / math.sqrt(192.0)),
+    # a context no longer than the budget: every causal position is selected
+    # (the dense limit), so the forward pass skips the indexer and the top-k
+    "short2k": Workload(
+        name="short2k", description="MLA prefill at the dense limit: n=2048 = k, "
+        "128 heads, latent 576/512 bf16 (indexer and top-k skipped)",
+        B=1, T=2048, S=2048, index_n_heads=64, index_head_dim=128, index_topk=2048,
+        idx_dtype="bf16", int_lo=-4, int_hi=4, w_den=16, form="mla", num_heads=128, d_qk=576,
+        d_v=512, dtype="bf16", out_dtype="bf16", scale=1.0 / math.sqrt(192.0)),
     "c3": Workload(
         name="c3", description="MLA batched decode: 64 sequences x 32768 cached tokens, "
         "bf16 indexer keys, k=2048",

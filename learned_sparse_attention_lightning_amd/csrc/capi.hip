@@ -16,6 +16,11 @@ constexpr size_t kAlign = 256;  // workspace carve-out alignment
 // this bounds that block (it then stays in the 256 MB last-level cache).
 constexpr size_t kScoreChunkBytes = 256ull << 20;
 
+// Largest selection budget accepted (k may exceed S: the surplus slots hold -1).
+constexpr int kMaxTopk = 1 << 20;
+
+bool valid_topk(int k) { return k >= 1 && k <= kMaxTopk; }
+
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -102,7 +107,7 @@ DSA_EXPORT size_t dsa_workspace_bytes(int op, const dsa_attn_desc_t *desc, int B
                                       int index_n_heads, int index_head_dim, int index_topk) {
     (void)index_n_heads;
     (void)index_head_dim;
-    if (B < 1 || T < 1 || S < 1 || index_topk < 1 || index_topk > S) return (size_t)-1;
+    if (B < 1 || T < 1 || S < 1 || !valid_topk(index_topk)) return (size_t)-1;
     switch (op) {
         case DSA_OP_TOPK: return topk_workspace_bytes(B, T, S, index_topk);
         case DSA_OP_ATTENTION:
@@ -130,18 +135,27 @@ DSA_EXPORT dsa_status_t dsa_indexer_scores(const void *q_idx, const void *k_idx,
                                      0, (hipStream_t)stream));
 }
 
-DSA_EXPORT dsa_status_t dsa_topk(const float *scores, const int32_t *q_pos, int B, int T, int S,
-                                 int index_topk, int32_t *idx, void *workspace,
-                                 size_t workspace_bytes, void *stream) {
+DSA_EXPORT dsa_status_t dsa_topk_ex(const float *scores, const int32_t *q_pos, int B, int T,
+                                    int S, int index_topk, int flags, int32_t *idx,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
     dsa_status_t st = check_sizes(B, T, S, q_pos != nullptr);
     if (st != DSA_OK) return st;
     if (!scores || !idx) return DSA_ERR_NULL;
-    if (index_topk < 1 || index_topk > S) return DSA_ERR_SHAPE;
+    if (!valid_topk(index_topk)) return DSA_ERR_SHAPE;
+    if (flags & ~DSA_SEL_INCLUDE_CURRENT) return DSA_ERR_UNSUPPORTED;
     if (!aligned16(scores) || !aligned16(idx)) return DSA_ERR_ALIGN;
     const size_t need = topk_workspace_bytes(B, T, S, index_topk);
     if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
     return hip_status(launch_topk(scores, (size_t)T * S, q_pos, B, T, S, 0, T, index_topk, idx,
-                                  workspace, false, (hipStream_t)stream));
+                                  workspace, false, (hipStream_t)stream,
+                                  (flags & DSA_SEL_INCLUDE_CURRENT) != 0));
+}
+
+DSA_EXPORT dsa_status_t dsa_topk(const float *scores, const int32_t *q_pos, int B, int T, int S,
+                                 int index_topk, int32_t *idx, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    return dsa_topk_ex(scores, q_pos, B, T, S, index_topk, 0, idx, workspace, workspace_bytes,
+                       stream);
 }
 
 DSA_EXPORT dsa_status_t dsa_sparse_attention(const dsa_attn_desc_t *desc, const void *q,
@@ -154,7 +168,7 @@ DSA_EXPORT dsa_status_t dsa_sparse_attention(const dsa_attn_desc_t *desc, const 
     st = check_attention(desc, q, kv, v, out);
     if (st != DSA_OK) return st;
     if (!idx) return DSA_ERR_NULL;
-    if (index_topk < 1 || index_topk > S) return DSA_ERR_SHAPE;
+    if (!valid_topk(index_topk)) return DSA_ERR_SHAPE;
     if (!aligned16(idx) || (lse && !aligned16(lse))) return DSA_ERR_ALIGN;
     const size_t need = attention_workspace_bytes(*desc, B, T, S, index_topk);
     if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
@@ -162,26 +176,28 @@ DSA_EXPORT dsa_status_t dsa_sparse_attention(const dsa_attn_desc_t *desc, const 
                                        workspace, (hipStream_t)stream));
 }
 
-DSA_EXPORT dsa_status_t dsa_forward(const dsa_attn_desc_t *desc, const void *q_idx,
-                                    const void *k_idx, int idx_dtype, const float *w,
-                                    const void *q, const void *kv, const void *v,
-                                    const int32_t *q_pos, int B, int T, int S,
-                                    int index_n_heads, int index_head_dim, int index_topk,
-                                    void *out, int32_t *idx_out, void *workspace,
-                                    size_t workspace_bytes, void *stream) {
+DSA_EXPORT dsa_status_t dsa_forward_ex(const dsa_attn_desc_t *desc, const void *q_idx,
+                                       const void *k_idx, int idx_dtype, const float *w,
+                                       const void *q, const void *kv, const void *v,
+                                       const int32_t *q_pos, int B, int T, int S,
+                                       int index_n_heads, int index_head_dim, int index_topk,
+                                       int flags, void *out, int32_t *idx_out, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
     dsa_status_t st = check_sizes(B, T, S, q_pos != nullptr);
     if (st != DSA_OK) return st;
     st = check_indexer(q_idx, k_idx, idx_dtype, w, index_n_heads, index_head_dim);
     if (st != DSA_OK) return st;
     st = check_attention(desc, q, kv, v, out);
     if (st != DSA_OK) return st;
-    if (index_topk < 1 || index_topk > S) return DSA_ERR_SHAPE;
+    if (!valid_topk(index_topk)) return DSA_ERR_SHAPE;
+    if (flags & ~DSA_SEL_INCLUDE_CURRENT) return DSA_ERR_UNSUPPORTED;
     if (idx_out && !aligned16(idx_out)) return DSA_ERR_ALIGN;
     const size_t need = forward_workspace(desc, B, T, S, index_topk);
     if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return DSA_ERR_ALIGN;
 
     hipStream_t s = (hipStream_t)stream;
+    const bool include_current = (flags & DSA_SEL_INCLUDE_CURRENT) != 0;
     const int rows = forward_chunk_rows(B, T, S);
     char *ws = static_cast<char *>(workspace);
     float *score_block = reinterpret_cast<float *>(ws);
@@ -193,21 +209,42 @@ DSA_EXPORT dsa_status_t dsa_forward(const dsa_attn_desc_t *desc, const void *q_i
     void *attn_ws = ws;
     if (idx_out) sel = idx_out;
 
+    // A context no longer than the budget selects every causal position in
+    // every row (with or without the current-token flag): the indexer and
+    // the top-k are skipped and the attention runs over the whole prefix.
+    const bool dense = S <= index_topk;
     const size_t batch_stride = (size_t)rows * S;
     for (int row0 = 0; row0 < T; row0 += rows) {
         const int n = T - row0 < rows ? T - row0 : rows;
-        // the indexer launch also clears the top-k counters
-        const size_t clear_words = topk_clear_words(B, n, S);
-        hipError_t e = launch_indexer(q_idx, k_idx, idx_dtype, w, q_pos, B, T, S, index_n_heads,
-                                      index_head_dim, row0, n, score_block, batch_stride, false,
-                                      static_cast<uint32_t *>(topk_ws), clear_words, s);
-        if (e != hipSuccess) return DSA_ERR_HIP;
-        e = launch_topk(score_block, batch_stride, q_pos, B, T, S, row0, n, index_topk, sel,
-                        topk_ws, clear_words > 0, s);
+        hipError_t e;
+        if (dense) {
+            e = launch_select_all(q_pos, B, T, S, row0, n, index_topk, sel, s);
+        } else {
+            // the indexer launch also clears the top-k counters
+            const size_t clear_words = topk_clear_words(B, n, S);
+            e = launch_indexer(q_idx, k_idx, idx_dtype, w, q_pos, B, T, S, index_n_heads,
+                               index_head_dim, row0, n, score_block, batch_stride, false,
+                               static_cast<uint32_t *>(topk_ws), clear_words, s);
+            if (e != hipSuccess) return DSA_ERR_HIP;
+            e = launch_topk(score_block, batch_stride, q_pos, B, T, S, row0, n, index_topk, sel,
+                            topk_ws, clear_words > 0, s, include_current);
+        }
         if (e != hipSuccess) return DSA_ERR_HIP;
         e = launch_attention(*desc, q, kv, v, sel, B, T, S, row0, n, index_topk, out, nullptr,
                              attn_ws, s);
         if (e != hipSuccess) return DSA_ERR_HIP;
     }
     return DSA_OK;
+}
+
+DSA_EXPORT dsa_status_t dsa_forward(const dsa_attn_desc_t *desc, const void *q_idx,
+                                    const void *k_idx, int idx_dtype, const float *w,
+                                    const void *q, const void *kv, const void *v,
+                                    const int32_t *q_pos, int B, int T, int S,
+                                    int index_n_heads, int index_head_dim, int index_topk,
+                                    void *out, int32_t *idx_out, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    return dsa_forward_ex(desc, q_idx, k_idx, idx_dtype, w, q, kv, v, q_pos, B, T, S,
+                          index_n_heads, index_head_dim, index_topk, 0, out, idx_out, workspace,
+                          workspace_bytes, stream);
 }

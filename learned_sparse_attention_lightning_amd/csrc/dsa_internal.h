@@ -112,9 +112,14 @@ bool indexer_shape_supported(int H, int D);
 
 size_t topk_workspace_bytes(int B, int T, int S, int k);
 size_t topk_clear_words(int B, int rows, int S);
+// include_current: the query's own position is always selected and the
+// other k-1 slots are ranked among the earlier positions.
 hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *q_pos, int B,
                        int T, int S, int row0, int rows, int k, int32_t *idx, void *workspace,
-                       bool workspace_cleared, hipStream_t stream);
+                       bool workspace_cleared, hipStream_t stream, bool include_current);
+// Selection of every candidate (for rows whose causal length is at most k).
+hipError_t launch_select_all(const int32_t *q_pos, int B, int T, int S, int row0, int rows,
+                             int k, int32_t *idx, hipStream_t stream);
 
 bool mha_dense_path(const dsa_attn_desc_t &d, int rows, int S, int k);
 size_t mha_workspace_bytes(int B, int rows, int S);

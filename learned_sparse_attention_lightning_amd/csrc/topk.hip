@@ -220,14 +220,14 @@ struct RowSmem {
 // writes the wave's selected positions in order (ballot prefix counts).
 __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
     const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
-    int T, int S, int row0, int k, int32_t *__restrict__ idx) {
+    int T, int S, int row0, int k, int cur, int ostride, int32_t *__restrict__ idx) {
     __shared__ RowSmem sm;
     const int r = blockIdx.x;
     const int b = blockIdx.y;
     const int i = row0 + r;
-    const int t = query_pos(q_pos, b, i, T, S);
+    const int t = query_pos(q_pos, b, i, T, S) - cur;  // last candidate position
     const float *row = scores + (size_t)b * batch_stride + (size_t)r * S;
-    int32_t *out = idx + ((size_t)b * T + i) * k;
+    int32_t *out = idx + ((size_t)b * T + i) * ostride;
     const int n = t < 0 ? 0 : t + 1;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -441,10 +441,10 @@ __device__ __forceinline__ void load8_keys(const float *row, int p0, int n, uint
 // grid: x = slice, y = row in chunk, z = batch
 __global__ __launch_bounds__(kWideThreads) void topk_wide_hist_kernel(
     const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
-    int T, int S, int row0, int rows, int k, WideLayout L) {
+    int T, int S, int row0, int rows, int k, int cur, WideLayout L) {
     __shared__ uint32_t hist[kDigits];
     const int r = blockIdx.y, b = blockIdx.z;
-    const int t = query_pos(q_pos, b, row0 + r, T, S);
+    const int t = query_pos(q_pos, b, row0 + r, T, S) - cur;
     const int n = t < 0 ? 0 : t + 1;
     const int base = blockIdx.x * kWideSlice;
     if (n <= k || base >= n) return;
@@ -466,12 +466,12 @@ __global__ __launch_bounds__(kWideThreads) void topk_wide_hist_kernel(
 // grid: x = slice, y = row in chunk, z = batch
 __global__ __launch_bounds__(kWideThreads) void topk_wide_scan_kernel(
     const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
-    int T, int S, int row0, int rows, int k, WideLayout L) {
+    int T, int S, int row0, int rows, int k, int cur, WideLayout L) {
     __shared__ uint32_t scratch[kWideThreads / 64];
     __shared__ uint32_t d1_s, above_s;
     __shared__ uint32_t h2[kDigits];  // second-digit counts when a slice has many candidates
     const int r = blockIdx.y, b = blockIdx.z;
-    const int t = query_pos(q_pos, b, row0 + r, T, S);
+    const int t = query_pos(q_pos, b, row0 + r, T, S) - cur;
     const int n = t < 0 ? 0 : t + 1;
     const int base = blockIdx.x * kWideSlice;
     if (n <= k || base >= n) return;
@@ -576,14 +576,14 @@ constexpr int kResolvePairs = kMaxSlices * kResolveSub / kTkThreads;  // (slice,
 // ahead of it (larger key, or equal key at a lower position).  A group too
 // large for that (massive ties) goes through the general threshold search.
 __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
-    const int32_t *__restrict__ q_pos, int T, int S, int row0, int rows, int k,
-    int32_t *__restrict__ idx, WideLayout L) {
+    const int32_t *__restrict__ q_pos, int T, int S, int row0, int rows, int k, int cur,
+    int ostride, int32_t *__restrict__ idx, WideLayout L) {
     __shared__ ResolveSmem sm;
     const int r = blockIdx.x, b = blockIdx.y;
     const int i = row0 + r;
-    const int t = query_pos(q_pos, b, i, T, S);
+    const int t = query_pos(q_pos, b, i, T, S) - cur;
     const int n = t < 0 ? 0 : t + 1;
-    int32_t *out = idx + ((size_t)b * T + i) * k;
+    int32_t *out = idx + ((size_t)b * T + i) * ostride;
     const int tid = threadIdx.x;
     if (n <= k) {
         for (int p = tid; p < k; p += kTkThreads) out[p] = p < n ? p : -1;
@@ -758,6 +758,39 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
     }
 }
 
+// The current-token variant: the selection kernels ran with budget k-1 over
+// the positions before t, writing slots 0..k-2 of each k-wide row (ascending,
+// -1 after the n_sel = min(k-1, t) selected).  Position t is the largest of
+// the set, so it goes right after them; slot k-1 gets -1 when unused.
+__global__ __launch_bounds__(256) void topk_current_fix_kernel(
+    const int32_t *__restrict__ q_pos, int B, int T, int S, int row0, int rows, int k,
+    int32_t *__restrict__ idx) {
+    const int g = blockIdx.x * 256 + threadIdx.x;
+    if (g >= B * rows) return;
+    const int b = g / rows, i = row0 + g % rows;
+    const int t = query_pos(q_pos, b, i, T, S);
+    int32_t *out = idx + ((size_t)b * T + i) * k;
+    if (t < 0) {
+        out[k - 1] = -1;
+        return;
+    }
+    const int n_sel = t < k - 1 ? t : k - 1;
+    out[n_sel] = t;
+    if (n_sel < k - 1) out[k - 1] = -1;
+}
+
+// Every candidate selected (at most k of them in every row): positions
+// 0..t ascending, then -1.  grid: x = slot block, y = row in chunk, z = batch.
+__global__ __launch_bounds__(256) void topk_select_all_kernel(
+    const int32_t *__restrict__ q_pos, int T, int S, int row0, int k,
+    int32_t *__restrict__ idx) {
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (p >= k) return;
+    const int b = blockIdx.z, i = row0 + blockIdx.y;
+    const int t = query_pos(q_pos, b, i, T, S);
+    idx[((size_t)b * T + i) * k + p] = p <= t ? p : -1;
+}
+
 bool use_wide(int B, int rows, int S) {
     return S >= kWideMinS && S <= kWideMaxS && (long long)B * rows <= kWideMaxRows;
 }
@@ -780,8 +813,11 @@ size_t topk_clear_words(int B, int rows, int S) {
 
 hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *q_pos, int B,
                        int T, int S, int row0, int rows, int k, int32_t *idx, void *workspace,
-                       bool workspace_cleared, hipStream_t stream) {
-    if (use_wide(B, rows, S) && workspace) {
+                       bool workspace_cleared, hipStream_t stream, bool include_current) {
+    // the current-token variant selects k-1 among the positions before t
+    const int cur = include_current ? 1 : 0;
+    const int kk = k - cur;
+    if (kk >= 1 && use_wide(B, rows, S) && workspace) {
         const WideLayout L = wide_layout(workspace, B * rows, S);
         const int nrows = B * rows;
         if (!workspace_cleared)
@@ -790,16 +826,25 @@ hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *
                                dim3(256), 0, stream, L.hist, L.meta, nrows);
         const dim3 g(ceil_div(S, kWideSlice), rows, B);
         hipLaunchKernelGGL(topk_wide_hist_kernel, g, dim3(kWideThreads), 0, stream, scores,
-                           batch_stride, q_pos, T, S, row0, rows, k, L);
+                           batch_stride, q_pos, T, S, row0, rows, kk, cur, L);
         hipLaunchKernelGGL(topk_wide_scan_kernel, g, dim3(kWideThreads), 0, stream, scores,
-                           batch_stride, q_pos, T, S, row0, rows, k, L);
+                           batch_stride, q_pos, T, S, row0, rows, kk, cur, L);
         hipLaunchKernelGGL(topk_wide_resolve_kernel, dim3(rows, B), dim3(kTkThreads), 0, stream,
-                           q_pos, T, S, row0, rows, k, idx, L);
-        return hipGetLastError();
+                           q_pos, T, S, row0, rows, kk, cur, k, idx, L);
+    } else if (kk >= 1) {
+        hipLaunchKernelGGL(topk_row_kernel, dim3(rows, B), dim3(kTkThreads), 0, stream, scores,
+                           batch_stride, q_pos, T, S, row0, kk, cur, k, idx);
     }
-    dim3 grid(rows, B);
-    hipLaunchKernelGGL(topk_row_kernel, grid, dim3(kTkThreads), 0, stream, scores, batch_stride,
-                       q_pos, T, S, row0, k, idx);
+    if (include_current)
+        hipLaunchKernelGGL(topk_current_fix_kernel, dim3(ceil_div(B * rows, 256)), dim3(256), 0,
+                           stream, q_pos, B, T, S, row0, rows, k, idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_all(const int32_t *q_pos, int B, int T, int S, int row0, int rows,
+                             int k, int32_t *idx, hipStream_t stream) {
+    hipLaunchKernelGGL(topk_select_all_kernel, dim3(ceil_div(k, 256), rows, B), dim3(256), 0,
+                       stream, q_pos, T, S, row0, k, idx);
     return hipGetLastError();
 }
 

@@ -26,7 +26,9 @@ DTYPE_CODES = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16,
 NAME_CODES = {"f32": DSA_F32, "bf16": DSA_BF16, "fp8": DSA_FP8_E4M3}
 FORM_CODES = {"mha": DSA_MHA, "mla": DSA_MLA}
 EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_indexer_scores", "dsa_topk",
-            "dsa_sparse_attention", "dsa_forward", "dsa_workspace_bytes")
+            "dsa_topk_ex", "dsa_sparse_attention", "dsa_forward", "dsa_forward_ex",
+            "dsa_workspace_bytes")
+DSA_SEL_INCLUDE_CURRENT = 1
 
 
 class DSAError(RuntimeError):
@@ -68,12 +70,17 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.dsa_indexer_scores.argtypes = [_p, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p, _p]
     lib.dsa_topk.restype = _i
     lib.dsa_topk.argtypes = [_p, _p, _i, _i, _i, _i, _p, _p, ctypes.c_size_t, _p]
+    lib.dsa_topk_ex.restype = _i
+    lib.dsa_topk_ex.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _p, ctypes.c_size_t, _p]
     lib.dsa_sparse_attention.restype = _i
     lib.dsa_sparse_attention.argtypes = [ctypes.POINTER(AttnDesc), _p, _p, _p, _p, _i, _i, _i,
                                          _i, _p, _p, _p, ctypes.c_size_t, _p]
     lib.dsa_forward.restype = _i
     lib.dsa_forward.argtypes = [ctypes.POINTER(AttnDesc), _p, _p, _i, _p, _p, _p, _p, _p, _i,
                                 _i, _i, _i, _i, _i, _p, _p, _p, ctypes.c_size_t, _p]
+    lib.dsa_forward_ex.restype = _i
+    lib.dsa_forward_ex.argtypes = [ctypes.POINTER(AttnDesc), _p, _p, _i, _p, _p, _p, _p, _p,
+                                   _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, ctypes.c_size_t, _p]
     lib.dsa_workspace_bytes.restype = ctypes.c_size_t
     lib.dsa_workspace_bytes.argtypes = [_i, ctypes.POINTER(AttnDesc), _i, _i, _i, _i, _i, _i]
     if path is None:
@@ -148,8 +155,9 @@ def dsa_indexer_scores(q_idx, k_idx, w, q_pos=None, scores=None, stream=None):
     return scores
 
 
-def dsa_topk(scores, k: int, q_pos=None, idx=None, stream=None):
-    """idx [B,T,k] int32: selected positions ascending, -1 padded."""
+def dsa_topk(scores, k: int, q_pos=None, idx=None, stream=None, include_current=False):
+    """idx [B,T,k] int32: selected positions ascending, -1 padded.
+    include_current: the query's own position is always kept (dsa_topk_ex)."""
     _need(scores, "scores", dtype=torch.float32, ndim=3)
     B, T, S = scores.shape
     if idx is None:
@@ -159,8 +167,13 @@ def dsa_topk(scores, k: int, q_pos=None, idx=None, stream=None):
         _need(q_pos, "q_pos", dtype=torch.int32, ndim=2)
     nws = workspace_bytes(DSA_OP_TOPK, None, B, T, S, 1, 1, k)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=scores.device)
-    _check(load().dsa_topk(_ptr(scores), _ptr(q_pos), B, T, S, k, _ptr(idx), _ptr(ws), nws,
-                           _stream(stream)))
+    if include_current:
+        _check(load().dsa_topk_ex(_ptr(scores), _ptr(q_pos), B, T, S, k,
+                                  DSA_SEL_INCLUDE_CURRENT, _ptr(idx), _ptr(ws), nws,
+                                  _stream(stream)))
+    else:
+        _check(load().dsa_topk(_ptr(scores), _ptr(q_pos), B, T, S, k, _ptr(idx), _ptr(ws), nws,
+                               _stream(stream)))
     return idx
 
 
@@ -189,8 +202,9 @@ def dsa_sparse_attention(desc: AttnDesc, q, kv, v, idx, out=None, lse=None, stre
 
 
 def dsa_forward(desc: AttnDesc, q_idx, k_idx, w, q, kv, v, k: int, q_pos=None, out=None,
-                idx_out=None, workspace=None, stream=None):
-    """Indexer -> top-k -> sparse attention; returns out (and fills idx_out)."""
+                idx_out=None, workspace=None, stream=None, include_current=False):
+    """Indexer -> top-k -> sparse attention; returns out (and fills idx_out).
+    include_current: the query's own position is always kept (dsa_forward_ex)."""
     _need(q_idx, "q_idx", ndim=4)
     _need(k_idx, "k_idx", dtype=q_idx.dtype, ndim=3)
     _need(w, "w", dtype=torch.float32, ndim=3)
@@ -208,8 +222,15 @@ def dsa_forward(desc: AttnDesc, q_idx, k_idx, w, q, kv, v, k: int, q_pos=None, o
     nws = workspace_bytes(DSA_OP_FORWARD, desc, B, T, S, H_I, D_I, k)
     if workspace is None or workspace.numel() < nws:
         workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
-    _check(load().dsa_forward(ctypes.byref(desc), _ptr(q_idx), _ptr(k_idx),
-                              DTYPE_CODES[q_idx.dtype], _ptr(w), _ptr(q), _ptr(kv), _ptr(v),
-                              _ptr(q_pos), B, T, S, H_I, D_I, k, _ptr(out), _ptr(idx_out),
-                              _ptr(workspace), workspace.numel(), _stream(stream)))
+    if include_current:
+        _check(load().dsa_forward_ex(ctypes.byref(desc), _ptr(q_idx), _ptr(k_idx),
+                                     DTYPE_CODES[q_idx.dtype], _ptr(w), _ptr(q), _ptr(kv),
+                                     _ptr(v), _ptr(q_pos), B, T, S, H_I, D_I, k,
+                                     DSA_SEL_INCLUDE_CURRENT, _ptr(out), _ptr(idx_out),
+                                     _ptr(workspace), workspace.numel(), _stream(stream)))
+    else:
+        _check(load().dsa_forward(ctypes.byref(desc), _ptr(q_idx), _ptr(k_idx),
+                                  DTYPE_CODES[q_idx.dtype], _ptr(w), _ptr(q), _ptr(kv), _ptr(v),
+                                  _ptr(q_pos), B, T, S, H_I, D_I, k, _ptr(out), _ptr(idx_out),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)))
     return out

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
     for s in range(8):
         assert lib.dsa_status_string(s)
     assert lib.dsa_status_string(99) == b"unknown status"
@@ -57,7 +57,8 @@ def test_workspace_sizes(lib):
     assert ws(dsa.DSA_OP_FORWARD, 1, 4096, 4096, 64, 128, 2048) >= 4096 * 4096 * 4
     # the score block is bounded for long prefill
     assert ws(dsa.DSA_OP_FORWARD, 1, 32768, 32768, 64, 128, 2048) < (1 << 30)
-    assert ws(dsa.DSA_OP_FORWARD, 1, 16, 16, 2, 2, 17) == bad  # k > S
+    assert ws(dsa.DSA_OP_FORWARD, 1, 16, 16, 2, 2, 17) != bad  # k > S is allowed
+    assert ws(dsa.DSA_OP_FORWARD, 1, 16, 16, 2, 2, (1 << 20) + 1) == bad
     assert ws(dsa.DSA_OP_FORWARD, 0, 16, 16, 2, 2, 3) == bad
     assert lib.dsa_workspace_bytes(dsa.DSA_OP_FORWARD, None, 1, 16, 16, 2, 2, 3) == bad
     assert ws(7, 1, 16, 16, 2, 2, 3) == bad
@@ -81,9 +82,18 @@ def test_topk_argument_checks(lib):
     f = lib.dsa_topk
     assert f(None, None, 1, 4, 4, 2, A, None, 0, None) == NULL
     assert f(A, None, 1, 4, 4, 0, A, None, 0, None) == SHAPE
-    assert f(A, None, 1, 4, 4, 5, A, None, 0, None) == SHAPE
+    assert f(A, None, 1, 4, 4, (1 << 20) + 1, A, None, 0, None) == SHAPE  # k may exceed S, to 2^20
     assert f(A, None, 1, 4, 4, 2, M, None, 0, None) == ALIGN
     assert f(A, None, 70000, 4, 4, 2, A, None, 0, None) == SHAPE
+
+
+def test_topk_ex_argument_checks(lib):
+    f = lib.dsa_topk_ex
+    cur = dsa.DSA_SEL_INCLUDE_CURRENT
+    assert f(None, None, 1, 4, 4, 2, cur, A, None, 0, None) == NULL
+    assert f(A, None, 1, 4, 4, 0, cur, A, None, 0, None) == SHAPE
+    assert f(A, None, 1, 4, 4, 2, 2, A, None, 0, None) == UNSUP  # unknown flag bit
+    assert f(A, None, 1, 4, 4, 2, cur, M, None, 0, None) == ALIGN
 
 
 def test_attention_argument_checks(lib):
@@ -100,7 +110,8 @@ def test_attention_argument_checks(lib):
     d5 = _desc(dqk=600)
     assert f(ctypes.byref(d5), A, A, None, A, 1, 1, 8, 2, A, None, None, 0, None) == SHAPE
     assert f(ctypes.byref(d), M, A, None, A, 1, 1, 8, 2, A, None, None, 0, None) == ALIGN
-    assert f(ctypes.byref(d), A, A, None, A, 1, 1, 8, 9, A, None, None, 0, None) == SHAPE
+    assert f(ctypes.byref(d), A, A, None, A, 1, 1, 8, (1 << 20) + 1, A, None, None, 0,
+             None) == SHAPE
     d6 = _desc(form=5)
     assert f(ctypes.byref(d6), A, A, None, A, 1, 1, 8, 2, A, None, None, 0, None) == SHAPE
 
@@ -117,6 +128,18 @@ def test_forward_argument_checks(lib):
     bad = list(args)
     bad[15] = M
     assert f(*bad, A, 1 << 40, None) == ALIGN
+
+
+def test_forward_ex_argument_checks(lib):
+    f = lib.dsa_forward_ex
+    d = _desc()
+    head = [ctypes.byref(d), A, A, 1, A, A, A, None, None, 1, 1, 8, 64, 128, 2]
+    cur = dsa.DSA_SEL_INCLUDE_CURRENT
+    assert f(*head, cur, A, None, None, 0, None) == WS
+    assert f(*head, 4, A, None, A, 1 << 40, None) == UNSUP
+    bad = list(head)
+    bad[1] = None
+    assert f(*bad, cur, A, None, A, 1 << 40, None) == NULL
 
 
 def test_binding_refuses_cpu_tensors():

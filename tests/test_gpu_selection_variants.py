@@ -1,0 +1,155 @@
+"""The selection variants of the HIP path against the CPU oracle: the
+current-token flag (the query's own position always kept, the other k-1
+slots ranked among earlier positions) and contexts no longer than the
+budget (every causal position selected; the forward pass skips the indexer
+and the top-k).  Bar as for the plain path: index sets bit-exact, attention
+outputs within max-abs 2e-2 (bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import TOL, assert_selection_equal, max_abs_err
+
+from learned_sparse_attention_lightning_amd import configs, dsa, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsa.load()
+    oracle.build()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _current_kept(idx, pos):
+    """Every row with a position t >= 0 holds t as its last valid entry."""
+    g = idx.cpu().numpy()
+    p = np.asarray(pos)
+    nvalid = (g >= 0).sum(-1)
+    for b, i in np.ndindex(p.shape):
+        if p[b, i] >= 0:
+            assert g[b, i, nvalid[b, i] - 1] == p[b, i], (b, i)
+
+
+# ------------------------------------------------------------------- top-k --
+
+@pytest.mark.parametrize("levels", [None, 3])
+@pytest.mark.parametrize("k", [1, 2, 7, 64, 300, 400])
+def test_topk_include_current_rows(levels, k):
+    B, T, S = 2, 300, 300
+    sc = synth.random_scores((B, T, S), seed=k * 3 + (levels or 0), levels=levels)
+    idx = dsa.dsa_topk(sc.to(DEV), k, include_current=True)
+    assert_selection_equal(idx, oracle.topk(sc, k, include_current=True),
+                           f"current levels={levels} k={k}")
+    _current_kept(idx, np.arange(T)[None, :].repeat(B, 0))
+
+
+@pytest.mark.parametrize("S", [32768, 131072])
+def test_topk_include_current_wide_rows(S):
+    B, k = 4, 2048
+    pos = torch.tensor([[S - 1], [S // 2], [2048], [0]], dtype=torch.int32)
+    sc = synth.random_scores((B, 1, S), seed=S + 1, levels=None)
+    sc[1, 0, : S // 4] = 0.5  # a block of ties
+    sc[0, 0, S - 1] = -10.0   # the current token far below the threshold
+    idx = dsa.dsa_topk(sc.to(DEV), k, q_pos=pos.to(DEV), include_current=True)
+    assert_selection_equal(idx, oracle.topk(sc, k, q_pos=pos, include_current=True),
+                           f"current wide S={S}")
+    _current_kept(idx, pos.numpy())
+
+
+def test_topk_include_current_many_long_rows():
+    B, T, S, k = 1, 520, 40001, 2048
+    pos = torch.tensor([[S - 1 - 37 * j for j in range(T)]], dtype=torch.int32)
+    sc = synth.random_scores((B, T, S), seed=12, levels=None)
+    idx = dsa.dsa_topk(sc.to(DEV), k, q_pos=pos.to(DEV), include_current=True)
+    rows = [0, 1, 100, 519]
+    ref = oracle.topk(sc[:, rows], k, q_pos=pos[:, rows], include_current=True)
+    assert_selection_equal(idx[:, rows], ref, "current many long rows")
+    _current_kept(idx, pos.numpy())
+
+
+def test_topk_budget_above_context():
+    B, T, S, k = 2, 50, 50, 80
+    sc = synth.random_scores((B, T, S), seed=3, levels=4)
+    idx = dsa.dsa_topk(sc.to(DEV), k)
+    assert_selection_equal(idx, oracle.topk(sc, k), "k > S")
+
+
+# ----------------------------------------------------------------- forward --
+
+def _run_forward(w, seed, include_current):
+    x = synth.make_inputs(w, device=DEV, seed=seed)
+    idx = torch.empty((w.B, w.T, w.index_topk), dtype=torch.int32, device=DEV)
+    out = dsa.dsa_forward(dsa.desc_for(w), x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"],
+                          x["v"], w.index_topk, idx_out=idx, include_current=include_current)
+    torch.cuda.synchronize()
+    return x, idx, out
+
+
+def _oracle_forward(w, x, include_current):
+    sc = oracle.indexer_scores(x["q_idx"], x["k_idx"], x["w"])
+    ref_idx = oracle.topk(sc, w.index_topk, include_current=include_current)
+    ref = oracle.sparse_attention(w.form, x["q"], x["kv"], x["v"], ref_idx, w.scale, d_v=w.d_v)
+    return ref_idx, ref
+
+
+CURRENT_CASES = {
+    "mla-prefill": ("c2", dict(B=2, T=700, S=700, index_topk=64, num_heads=16)),
+    "mha-prefill": ("c1", dict(B=1, T=1500, S=1500, index_topk=256)),
+    "mla-decode-fp8": ("c4", dict(B=2, T=1, S=40000, num_heads=16)),
+}
+
+
+@pytest.mark.parametrize("case", list(CURRENT_CASES))
+def test_forward_include_current(case):
+    base, kw = CURRENT_CASES[case]
+    w = configs.get(base).with_(name=f"current-{case}", **kw)
+    x, idx, out = _run_forward(w, 17, True)
+    ref_idx, ref = _oracle_forward(w, x, True)
+    assert_selection_equal(idx, ref_idx, case)
+    pos = np.arange(w.S - w.T, w.S)[None, :].repeat(w.B, 0)
+    _current_kept(idx, pos)
+    err = max_abs_err(out, ref)
+    _say(f"{case} with the current token: max-abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+DENSE_CASES = {
+    "mla-n1000-k2048": ("c2", dict(B=1, T=1000, S=1000, index_topk=2048, num_heads=16)),
+    "mla-k-equals-n": ("c2", dict(B=2, T=256, S=256, index_topk=256, num_heads=16)),
+    "mha-n777-k1024": ("c1", dict(B=1, T=777, S=777, index_topk=1024)),
+    "mla-decode-n1500": ("c4", dict(B=3, T=1, S=1500, num_heads=16)),
+}
+
+
+@pytest.mark.parametrize("case", list(DENSE_CASES))
+def test_forward_dense_when_context_within_budget(case):
+    """S <= k: every causal position is selected (the dense limit); the result
+    equals the oracle's top-k path, and the current-token flag changes
+    nothing."""
+    base, kw = DENSE_CASES[case]
+    w = configs.get(base).with_(name=f"dense-{case}", **kw)
+    x, idx, out = _run_forward(w, 23, False)
+    ref_idx, ref = _oracle_forward(w, x, False)
+    assert_selection_equal(idx, ref_idx, case)
+    g = idx.cpu().numpy()
+    for b in range(w.B):
+        for i in range(w.T):
+            t = w.S - w.T + i
+            assert np.array_equal(g[b, i, : t + 1], np.arange(t + 1))
+    err = max_abs_err(out, ref)
+    _say(f"{case} dense: max-abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+    idx2 = torch.empty_like(idx)
+    out2 = dsa.dsa_forward(dsa.desc_for(w), x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"],
+                           x["v"], w.index_topk, idx_out=idx2, include_current=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx) and torch.equal(out2, out)
