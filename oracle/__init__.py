@@ -59,6 +59,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_warmup_target.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i64,
                                          ctypes.c_double, _p]
     lib.oracle_warmup_target.restype = None
+    lib.oracle_sparse_target.argtypes = [ctypes.c_int, _p, _p, _p, _i64, _i64, _i64, _i64,
+                                         _i64, _i64, ctypes.c_double, _p]
+    lib.oracle_sparse_target.restype = None
     lib.oracle_indexer_kl.argtypes = [_p, _p, _p, _i64, _i64]
     lib.oracle_indexer_kl.restype = ctypes.c_double
     return lib
@@ -224,6 +227,44 @@ def warmup_target(q, K, scale: float, q_pos=None) -> np.ndarray:
     _get().oracle_warmup_target(qq.ctypes.data, kk.ctypes.data, pos_p, B, T, S, H, d,
                                 float(scale), out.ctypes.data)
     return out
+
+
+def sparse_target(form, q, kv, idx, scale: float) -> np.ndarray:
+    """Head-mean of the sparse attention weights over the selected set
+    ([P1] sections 5.2, 6.2-6.3).  MHA: kv = K [B,S,H,d]; MLA: kv = latent
+    [B,S,d].  -> p [B,T,S], zero outside the set."""
+    f = _form(form)
+    qq = as_f64(q)
+    kk = as_f64(kv)
+    B, T, H, dqk = qq.shape
+    S = kk.shape[1]
+    ix = np.ascontiguousarray(np.asarray(
+        idx.detach().cpu().numpy() if hasattr(idx, "detach") else idx, dtype=np.int32))
+    out = np.empty((B, T, S), dtype=np.float64)
+    _get().oracle_sparse_target(f, qq.ctypes.data, kk.ctypes.data, ix.ctypes.data, B, T, S, H,
+                                dqk, ix.shape[-1], float(scale), out.ctypes.data)
+    return out
+
+
+def selection_mask(idx, S: int) -> np.ndarray:
+    """[B,T,k] selection -> [B,T,S] int8 membership mask."""
+    ix = np.asarray(idx.detach().cpu().numpy() if hasattr(idx, "detach") else idx)
+    B, T, _ = ix.shape
+    m = np.zeros((B, T, S), dtype=np.int8)
+    for b in range(B):
+        for i in range(T):
+            v = ix[b, i][ix[b, i] >= 0]
+            m[b, i, v] = 1
+    return m
+
+
+def indexer_kl_rows(p, scores, mask) -> np.ndarray:
+    """KL(p || softmax(I)) of every row separately -> [B,T] float64."""
+    pp, sc = as_f64(p), as_f64(scores)
+    mk = np.asarray(mask)
+    B, T, _ = pp.shape
+    return np.array([[indexer_kl(pp[b, i:i + 1], sc[b, i:i + 1], mk[b, i:i + 1])
+                      for i in range(T)] for b in range(B)])
 
 
 def indexer_kl(p, scores, mask) -> float:

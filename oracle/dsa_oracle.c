@@ -369,6 +369,52 @@ ORACLE_API void oracle_warmup_target(const double *q, const double *K,
 }
 
 /*
+ * Sparse-stage target of the indexer, [P1] sections 6.2-6.3 with the head
+ * aggregation of section 5.2: the main attention runs over the selected set
+ * only, so its weights alpha^(h)[t,s] exist for s in S_t (the entries of
+ * idx[b,i,:] that are >= 0); they are averaged over the H heads,
+ *   p[t,s] = (1/H) sum_h alpha^(h)[t,s]  for s in S_t,  0 elsewhere,
+ * which sums to 1 over S_t.  Keys as in oracle_sparse_attention (MHA: K per
+ * head; MLA: the shared latent row).  p [B,T,S]; a row with an empty set is
+ * all zero.
+ */
+ORACLE_API void oracle_sparse_target(int form, const double *q, const double *kv,
+                                     const int32_t *idx, int64_t B, int64_t T,
+                                     int64_t S, int64_t H, int64_t dqk, int64_t k,
+                                     double scale, double *p) {
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t i = 0; i < T; ++i) {
+            const int32_t *sel = idx + (b * T + i) * k;
+            double *prow = p + (b * T + i) * S;
+            double *alpha = (double *)malloc(sizeof(double) * (size_t)k);
+            for (int64_t s = 0; s < S; ++s) prow[s] = 0.0;
+            for (int64_t h = 0; h < H; ++h) {
+                const double *qv = q + ((b * T + i) * H + h) * dqk;
+                double m = -INFINITY;
+                for (int64_t r = 0; r < k; ++r) {
+                    if (sel[r] < 0) continue;
+                    const double *key = key_row(form, kv, b, sel[r], h, S, H, dqk);
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < dqk; ++d) dot += qv[d] * key[d];
+                    alpha[r] = scale * dot;
+                    if (alpha[r] > m) m = alpha[r];
+                }
+                double z = 0.0;
+                for (int64_t r = 0; r < k; ++r) {
+                    if (sel[r] < 0) continue;
+                    alpha[r] = exp(alpha[r] - m);
+                    z += alpha[r];
+                }
+                for (int64_t r = 0; r < k; ++r)
+                    if (sel[r] >= 0) prow[sel[r]] += alpha[r] / z / (double)H;
+            }
+            free(alpha);
+        }
+    }
+}
+
+/*
  * Indexer distillation loss of one query row, [P1] sections 5.4 and 6.2:
  *   KL( p || softmax(I) ) = sum_s p_s (log p_s - log q_s),  q = softmax of I,
  * taken over the positions where mask[s] != 0 (all s <= t in the dense

@@ -26,6 +26,8 @@ MUTANTS = {
     "tie_higher_index": ("return (a->pos < b->pos) ? -1 : (a->pos > b->pos);", "return (a->pos > b->pos) ? -1 : (a->pos < b->pos);"),
     "ascending_scores": ("if (a->score > b->score) return -1;\n    if (a->score < b->score) return 1;", "if (a->score < b->score) return -1;\n    if (a->score > b->score) return 1;"),
     "candidates_exclude_self": ("const int64_t n_cand = t + 1 - forced;", "const int64_t n_cand = (t > 0 ? t : 1) - forced;"),
+    "sparse_target_head_sum": ("if (sel[r] >= 0) prow[sel[r]] += alpha[r] / z / (double)H;", "if (sel[r] >= 0) prow[sel[r]] += alpha[r] / z;"),
+    "sparse_target_unscaled": ("                    alpha[r] = scale * dot;", "                    alpha[r] = dot;"),
     "current_not_forced": ("const int64_t forced = (include_current && t >= 0) ? 1 : 0;", "const int64_t forced = 0;"),
     "current_budget_not_reduced": ("const int64_t n_cand = t + 1 - forced;", "const int64_t n_cand = t + 1;"),
     "scale_dropped": ("logit[r] = scale * dot;", "logit[r] = dot;"),

@@ -372,3 +372,51 @@ def test_indexer_kl_against_library(oracle):
         pr = p[r, [1, 4, 7]] / p[r, [1, 4, 7]].sum()
         want_sub += rel_entr(pr, softmax(sc[r, [1, 4, 7]])).sum()
     assert abs(oracle.indexer_kl(p, sc, sub) - want_sub) < 1e-12
+
+
+def test_sparse_target_with_full_selection_is_warmup_target(oracle):
+    """When S_t holds every s <= t (k >= t+1), the sparse-stage target is the
+    dense warm-up target; it sums to 1 over the set and is zero outside."""
+    q, K, V = _mha(T=9, H=3, d=4, dv=4, seed=14)
+    sel = oracle.topk(np.random.default_rng(1).standard_normal((1, 9, 9)), 9)
+    p = oracle.sparse_target("mha", q, K, sel, 0.5)
+    assert np.allclose(p, oracle.warmup_target(q, K, 0.5), atol=1e-14, rtol=0)
+
+
+def test_sparse_target_against_library_softmax(oracle):
+    """Restricted set: per-head softmax (library) over the selected keys only,
+    averaged over heads; MLA keys are the latent row shared by every head."""
+    g = torch.Generator().manual_seed(3)
+    B, T, S, H, d = 2, 6, 12, 4, 8
+    q = torch.randn(B, T, H, d, generator=g, dtype=torch.float64)
+    lat = torch.randn(B, S, d, generator=g, dtype=torch.float64)
+    sc = np.random.default_rng(2).standard_normal((B, T, S))
+    sel = oracle.topk(sc, 3, q_pos=np.full((B, T), S - 1))
+    sel[1, 2, 1:] = -1   # a single selection: all mass on it
+    sel[0, 4, :] = -1    # an empty selection: all zero
+    p = oracle.sparse_target("mla", q, lat, sel, 0.3)
+    for b in range(B):
+        for i in range(T):
+            s = [v for v in sel[b, i] if v >= 0]
+            want = np.zeros(S)
+            if s:
+                logits = 0.3 * (q[b, i] @ lat[b, s].T)          # [H, |s|]
+                want[s] = torch.softmax(logits, -1).mean(0).numpy()
+            assert np.allclose(p[b, i], want, atol=1e-14, rtol=0), (b, i)
+    assert p[1, 2, sel[1, 2, 0]] == 1.0 and np.all(p[0, 4] == 0)
+    # MLA equals MHA with the latent broadcast to every head
+    K = lat[:, :, None, :].expand(B, S, H, d).contiguous()
+    assert np.allclose(oracle.sparse_target("mha", q, K, sel, 0.3), p, atol=1e-15, rtol=0)
+
+
+def test_indexer_kl_rows_sum_to_total(oracle):
+    rng = np.random.default_rng(8)
+    p = rng.random((2, 3, 7))
+    sc = rng.standard_normal((2, 3, 7))
+    mask = (rng.random((2, 3, 7)) < 0.6).astype(np.int8)
+    mask[..., 0] = 1
+    rows = oracle.indexer_kl_rows(p, sc, mask)
+    assert rows.shape == (2, 3) and np.all(rows >= -1e-15)
+    assert abs(rows.sum() - oracle.indexer_kl(p, sc, mask)) < 1e-12
+    assert np.array_equal(oracle.selection_mask(np.array([[[2, -1, 0]]]), 4),
+                          np.array([[[1, 0, 1, 0]]], dtype=np.int8))
