@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c2-fp8", "c3", "c4", "p128k", "short2k"])
+    ap.add_argument("--kl", type=int, default=0,
+                    help="prefill: also time the indexer distillation loss (forward) per chunk")
     ap.add_argument("--include-current", type=int, default=0,
                     help="always keep the current token (dsa_forward_ex flag)")
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = auto)")
@@ -227,6 +229,7 @@ def main():
     # duration (plus the launch gaps), not the cost of an event pair.
     alg = algorithmic(w)
     stage_ms = None
+    kl_roof = None
     if not args.stages:
         stage_ms = [float("nan")] * 3
     elif w.decode:
@@ -295,6 +298,34 @@ def main():
             b.record()
             torch.cuda.synchronize()
             stage_ms.append(a.elapsed_time(b) / 2)
+        if args.kl and w.form == "mla":
+            # the loss kernel needs each chunk's scores and the attention's
+            # log-sum-exp: both computed untimed, then the loss launch timed
+            lse = torch.empty((w.B, ch, w.num_heads), dtype=torch.float32, device=dev)
+            loss = torch.empty((w.B, ch), dtype=torch.float32, device=dev)
+            kl_ms = 0.0
+            for rep in range(2):
+                tot = 0.0
+                for r0, r1, pos in chunks:
+                    n = r1 - r0
+                    dsa.dsa_indexer_scores(x["q_idx"][:, r0:r1], x["k_idx"], x["w"][:, r0:r1],
+                                           q_pos=pos, scores=sc[:, :n])
+                    dsa.dsa_sparse_attention(desc, x["q"][:, r0:r1], x["kv"], x["v"],
+                                             idx[:, r0:r1], out=out[:, r0:r1], lse=lse[:, :n])
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    dsa.dsa_indexer_kl(desc, x["q"][:, r0:r1], x["kv"], idx[:, r0:r1],
+                                       lse[:, :n], sc[:, :n], loss=loss[:, :n])
+                    b.record()
+                    torch.cuda.synchronize()
+                    tot += a.elapsed_time(b)
+                kl_ms = tot  # the second pass (warm) is kept
+            kl_flops = alg["entries"] * 2 * w.num_heads * w.d_qk
+            kl_tf = kl_flops / (kl_ms * 1e-3) / 1e12
+            kl_roof = {"bound": "mfma", "achieved": round(kl_tf, 2), "peak": BF16_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(kl_tf / BF16_PEAK_TFLOPS, 4),
+                       "ms": round(kl_ms, 4), "kernel": "mla_indexer_kl_kernel",
+                       "algorithmic_flops": kl_flops}
         del sc
 
     if w.decode:
@@ -352,6 +383,8 @@ def main():
         res["tokens_per_s"] = round(value * w.B, 1)
     else:
         res["indexer_roofline"] = indexer_roof
+    if kl_roof is not None:
+        res["indexer_kl_roofline"] = kl_roof
     if args.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, reps[0], args.cpu_seconds)
     else:

@@ -176,6 +176,23 @@ DSA_EXPORT dsa_status_t dsa_sparse_attention(const dsa_attn_desc_t *desc, const 
                                        workspace, (hipStream_t)stream));
 }
 
+DSA_EXPORT dsa_status_t dsa_indexer_kl(const dsa_attn_desc_t *desc, const void *q,
+                                       const void *kv, const int32_t *idx, const float *lse,
+                                       const float *scores, int B, int T, int S,
+                                       int index_topk, float *loss, void *stream) {
+    dsa_status_t st = check_sizes(B, T, S, true);
+    if (st != DSA_OK) return st;
+    if (!desc) return DSA_ERR_NULL;
+    if (!indexer_kl_supported(*desc)) return DSA_ERR_UNSUPPORTED;
+    st = check_attention(desc, q, kv, nullptr, loss);
+    if (st != DSA_OK) return st;
+    if (!idx || !lse || !scores) return DSA_ERR_NULL;
+    if (!valid_topk(index_topk)) return DSA_ERR_SHAPE;
+    if (!aligned16(idx) || !aligned16(lse) || !aligned16(scores)) return DSA_ERR_ALIGN;
+    return hip_status(launch_indexer_kl(*desc, q, kv, idx, lse, scores, B, T, S, index_topk,
+                                        loss, (hipStream_t)stream));
+}
+
 DSA_EXPORT dsa_status_t dsa_forward_ex(const dsa_attn_desc_t *desc, const void *q_idx,
                                        const void *k_idx, int idx_dtype, const float *w,
                                        const void *q, const void *kv, const void *v,

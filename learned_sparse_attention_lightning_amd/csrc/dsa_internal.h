@@ -121,6 +121,11 @@ hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *
 hipError_t launch_select_all(const int32_t *q_pos, int B, int T, int S, int row0, int rows,
                              int k, int32_t *idx, hipStream_t stream);
 
+bool indexer_kl_supported(const dsa_attn_desc_t &d);
+hipError_t launch_indexer_kl(const dsa_attn_desc_t &d, const void *q, const void *kv,
+                             const int32_t *idx, const float *lse, const float *scores, int B,
+                             int T, int S, int k, float *loss, hipStream_t stream);
+
 bool mha_dense_path(const dsa_attn_desc_t &d, int rows, int S, int k);
 size_t mha_workspace_bytes(int B, int rows, int S);
 hipError_t launch_mha_dense(const dsa_attn_desc_t &d, const void *q, const void *kv,

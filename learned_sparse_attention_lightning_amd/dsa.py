@@ -27,7 +27,7 @@ NAME_CODES = {"f32": DSA_F32, "bf16": DSA_BF16, "fp8": DSA_FP8_E4M3}
 FORM_CODES = {"mha": DSA_MHA, "mla": DSA_MLA}
 EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_indexer_scores", "dsa_topk",
             "dsa_topk_ex", "dsa_sparse_attention", "dsa_forward", "dsa_forward_ex",
-            "dsa_workspace_bytes")
+            "dsa_indexer_kl", "dsa_workspace_bytes")
 DSA_SEL_INCLUDE_CURRENT = 1
 
 
@@ -81,6 +81,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.dsa_forward_ex.restype = _i
     lib.dsa_forward_ex.argtypes = [ctypes.POINTER(AttnDesc), _p, _p, _i, _p, _p, _p, _p, _p,
                                    _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, ctypes.c_size_t, _p]
+    lib.dsa_indexer_kl.restype = _i
+    lib.dsa_indexer_kl.argtypes = [ctypes.POINTER(AttnDesc), _p, _p, _p, _p, _p, _i, _i, _i, _i,
+                                   _p, _p]
     lib.dsa_workspace_bytes.restype = ctypes.c_size_t
     lib.dsa_workspace_bytes.argtypes = [_i, ctypes.POINTER(AttnDesc), _i, _i, _i, _i, _i, _i]
     if path is None:
@@ -234,3 +237,29 @@ def dsa_forward(desc: AttnDesc, q_idx, k_idx, w, q, kv, v, k: int, q_pos=None, o
                                   _ptr(q_pos), B, T, S, H_I, D_I, k, _ptr(out), _ptr(idx_out),
                                   _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def dsa_indexer_kl(desc: AttnDesc, q, kv, idx, lse, scores, loss=None, stream=None):
+    """Per-row KL(head-mean attention weights || softmax of the indexer
+    scores) over each row's selected set -> loss [B,T] fp32 (MLA form)."""
+    _need(q, "q", dtype=torch.bfloat16, ndim=4)
+    _need(kv, "kv", dtype=torch.bfloat16, ndim=3)
+    _need(idx, "idx", dtype=torch.int32, ndim=3)
+    _need(lse, "lse", dtype=torch.float32, ndim=3)
+    _need(scores, "scores", dtype=torch.float32, ndim=3)
+    B, T, H, D = q.shape
+    S = kv.shape[1]
+    k = idx.shape[-1]
+    if H != desc.num_heads or D != desc.d_qk or tuple(kv.shape) != (B, S, D):
+        raise ValueError("q [B,T,H,d_qk] and kv [B,S,d_qk] must match desc")
+    if tuple(idx.shape[:2]) != (B, T) or tuple(lse.shape) != (B, T, H) or \
+            tuple(scores.shape) != (B, T, S):
+        raise ValueError("idx [B,T,k], lse [B,T,H] and scores [B,T,S] must match q and kv")
+    if loss is None:
+        loss = torch.empty((B, T), dtype=torch.float32, device=q.device)
+    _need(loss, "loss", dtype=torch.float32, ndim=2)
+    if tuple(loss.shape) != (B, T):
+        raise ValueError("loss must be [B,T]")
+    _check(load().dsa_indexer_kl(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(idx), _ptr(lse),
+                                 _ptr(scores), B, T, S, k, _ptr(loss), _stream(stream)))
+    return loss

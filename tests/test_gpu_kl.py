@@ -1,0 +1,111 @@
+"""The indexer's distillation loss (forward) on the GPU against the oracle.
+
+The GPU pipeline (indexer scores, top-k, attention with its log-sum-exp, then
+the loss kernel) runs on seeded inputs; the oracle computes its own scores,
+selection, head-mean target over the set and per-row KL in fp64.  Scores and
+selections are bit-exact (integer indexer inputs), so the rows compare term
+by term.  Tolerance: the logits are fp32 sums of bf16 products recomputed
+beside the attention's own, so p carries ~1e-6 relative error per entry and
+the fp32 sums over <= 2048 entries add ~1e-5 relative: |gpu - ref| <=
+1e-3 * max(1, |ref|)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+from learned_sparse_attention_lightning_amd import configs, dsa, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsa.load()
+    oracle.build()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _gpu_loss(w, x, k, include_current=False):
+    desc = dsa.desc_for(w)
+    sc = dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"])
+    idx = dsa.dsa_topk(sc, k, include_current=include_current)
+    lse = torch.empty((w.B, w.T, w.num_heads), dtype=torch.float32, device=DEV)
+    dsa.dsa_sparse_attention(desc, x["q"], x["kv"], None, idx, lse=lse)
+    loss = dsa.dsa_indexer_kl(desc, x["q"], x["kv"], idx, lse, sc)
+    torch.cuda.synchronize()
+    return sc, idx, loss
+
+
+def _oracle_loss(w, x, rows, k, include_current=False):
+    pos = np.array([[w.S - w.T + r for r in rows]] * w.B)
+    sc = oracle.indexer_scores(x["q_idx"][:, rows], x["k_idx"], x["w"][:, rows], q_pos=pos)
+    sel = oracle.topk(sc, k, q_pos=pos, include_current=include_current)
+    p = oracle.sparse_target("mla", x["q"][:, rows], x["kv"], sel, w.scale)
+    return sel, oracle.indexer_kl_rows(p, sc, oracle.selection_mask(sel, w.S))
+
+
+def _check(loss, ref, where):
+    g = loss.double().cpu().numpy()
+    err = np.abs(g - ref) / np.maximum(1.0, np.abs(ref))
+    _say(f"{where}: loss range {ref.min():.4g}..{ref.max():.4g}, max rel err {err.max():.3e}")
+    assert np.all(np.isfinite(g)) and err.max() <= 1e-3, where
+
+
+@pytest.mark.parametrize("heads", [32, 64, 128])
+def test_indexer_kl_sparse_stage(heads):
+    w = configs.get("c2").with_(name=f"kl-{heads}", B=2, T=300, S=300, index_topk=64,
+                                num_heads=heads)
+    x = synth.make_inputs(w, device=DEV, seed=31 + heads)
+    sc, idx, loss = _gpu_loss(w, x, w.index_topk)
+    rows = list(range(w.T))
+    _, ref = _oracle_loss(w, x, rows, w.index_topk)
+    _check(loss, ref, f"sparse stage H={heads}")
+    # row 0 selects only itself: p = softmax = 1 there, KL = 0
+    assert np.abs(loss[:, 0].cpu().numpy()).max() <= 1e-5
+
+
+def test_indexer_kl_dense_warmup():
+    """Every causal position selected (k >= S): the warm-up loss."""
+    w = configs.get("c2").with_(name="kl-dense", B=1, T=200, S=200, index_topk=256,
+                                num_heads=32)
+    x = synth.make_inputs(w, device=DEV, seed=5)
+    sc, idx, loss = _gpu_loss(w, x, w.index_topk)
+    _, ref = _oracle_loss(w, x, list(range(w.T)), w.index_topk)
+    _check(loss, ref, "dense warm-up")
+
+
+def test_indexer_kl_long_rows_sampled():
+    """k = 2048 over 6000 keys at 128 heads: several tile pairs per wave."""
+    w = configs.get("c2").with_(name="kl-long", B=1, T=6000, S=6000)
+    x = synth.make_inputs(w, device=DEV, seed=8)
+    sc, idx, loss = _gpu_loss(w, x, w.index_topk, include_current=True)
+    rows = [0, 1, 2047, 2048, 4000, 5999]
+    sel, ref = _oracle_loss(w, x, rows, w.index_topk, include_current=True)
+    _check(loss[:, rows], ref, "long rows")
+
+
+def test_indexer_kl_unit_scale_scores():
+    """Scores of unit scale (softmax far from one-hot): every term of the
+    divergence matters; the selection is the top-k of those scores."""
+    w = configs.get("c2").with_(name="kl-unit", B=2, T=400, S=400, index_topk=128,
+                                num_heads=64)
+    x = synth.make_inputs(w, device=DEV, seed=12)
+    sc = synth.random_scores((w.B, w.T, w.S), seed=4)
+    desc = dsa.desc_for(w)
+    idx = dsa.dsa_topk(sc.to(DEV), w.index_topk)
+    lse = torch.empty((w.B, w.T, w.num_heads), dtype=torch.float32, device=DEV)
+    dsa.dsa_sparse_attention(desc, x["q"], x["kv"], None, idx, lse=lse)
+    loss = dsa.dsa_indexer_kl(desc, x["q"], x["kv"], idx, lse, sc.to(DEV))
+    torch.cuda.synchronize()
+    sel = oracle.topk(sc, w.index_topk)
+    p = oracle.sparse_target("mla", x["q"], x["kv"], sel, w.scale)
+    ref = oracle.indexer_kl_rows(p, sc, oracle.selection_mask(sel, w.S))
+    _check(loss, ref, "unit-scale scores")
+    assert ref[:, 50:].min() > 0.05  # far from zero: p and softmax differ
