@@ -386,8 +386,9 @@ def test_mla_mfma_empty_and_single_rows():
     assert max_abs_err(out[:, 2:], ref) <= TOL["bf16"]
 
 
-def test_forward_c2_sampled_rows():
-    w = configs.get("c2")
+@pytest.mark.parametrize("name", ["c2", "c2-fp8"])
+def test_forward_c2_sampled_rows(name):
+    w = configs.get(name)
     x, idx, out = _forward(w)
     rows = [0, 1, 2047, 2048, 2049, 4095, 4096, 16383, 30000, 32767]
     _say(f"c2: oracle over rows {rows}")
