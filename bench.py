@@ -238,7 +238,8 @@ def main():
         stages = [
             lambda x: dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"], scores=sc),
             lambda x: dsa.dsa_topk(sc, w.index_topk, idx=idx, include_current=cur),
-            lambda x: dsa.dsa_sparse_attention(desc, x["q"], x["kv"], x["v"], idx, out=out),
+            lambda x: dsa.dsa_sparse_attention(desc, x["q"], x["kv"], x["v"], idx, out=out,
+                                               causal_prefix=True),
         ]
         for f in stages:  # inputs for the later stages, and warm launches
             for r in range(R):
@@ -281,8 +282,13 @@ def main():
 
         def st_attention():
             for r0, r1, pos in chunks:
+                # the forward pass's attention stops at each row's selected count
                 dsa.dsa_sparse_attention(desc, x["q"][:, r0:r1], x["kv"], x["v"],
-                                         idx[:, r0:r1], out=out[:, r0:r1])
+                                         idx[:, r0:r1], out=out[:, r0:r1], causal_prefix=True,
+                                         q_pos=(pos if pos is not None else
+                                                torch.arange(w.S - w.T + r0, w.S - w.T + r1,
+                                                             dtype=torch.int32, device=dev)
+                                                .view(1, -1).repeat(w.B, 1)))
 
         stage_ms = []
         for f in (st_indexer, st_topk, st_attention):

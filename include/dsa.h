@@ -165,6 +165,26 @@ dsa_status_t dsa_sparse_attention(const dsa_attn_desc_t *desc, const void *q, co
                                   int index_topk, void *out, float *lse, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* Attention flags of dsa_sparse_attention_ex. */
+enum {
+    /* Every row's idx holds its min(k, t+1) selected positions first and -1
+     * in every later slot (what dsa_topk and dsa_topk_ex write); the kernel
+     * then reads no slot past that count.  t comes from q_pos (or the
+     * default positions, which need T <= S). */
+    DSA_ATTN_CAUSAL_PREFIX = 1
+};
+
+/*
+ * dsa_sparse_attention with the query positions and attention flags
+ * (DSA_ATTN_*; 0 is dsa_sparse_attention, and q_pos is then unused).
+ * Unknown flag bits return DSA_ERR_UNSUPPORTED.  Same workspace.
+ */
+dsa_status_t dsa_sparse_attention_ex(const dsa_attn_desc_t *desc, const void *q, const void *kv,
+                                     const void *v, const int32_t *idx, const int32_t *q_pos,
+                                     int flags, int B, int T, int S, int index_topk, void *out,
+                                     float *lse, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
 /*
  * The whole forward path ([P4] section 3.2, three steps): indexer scores,
  * top-k, then attention over the selection, on one stream.  Query rows are

@@ -140,7 +140,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ lat,
     const int32_t *__restrict__ idx, int T, int S, int H, int k, float scale, int row0,
     int rows, int B, int splits, int per_split, Tout *__restrict__ out, float *__restrict__ lse,
-    Tout *__restrict__ o_part, float *__restrict__ lse_part) {
+    Tout *__restrict__ o_part, float *__restrict__ lse_part, const int32_t *__restrict__ q_pos,
+    int causal_tail) {
     __shared__ MlaSmem sm;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -177,8 +178,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     const int i = row0 + r;
     const int head0 = hg * kHg;
     const int e_begin = split * per_split;
-    const int len = min(k, e_begin + per_split) - e_begin;  // entries of this split
-    const int ntiles = (len + kKt - 1) / kKt;
+    int len = min(k, e_begin + per_split) - e_begin;  // entries of this split
+    if (causal_tail) {
+        // the selection is min(k, t+1) positions followed by -1 only: tiles
+        // past that are empty (a split left with none runs one masked tile)
+        const int t = query_pos(q_pos, b, i, T, S);
+        const int nvalid = t < 0 ? 0 : min(k, t + 1);
+        len = max(0, min(len, nvalid - e_begin));
+    }
+    const int ntiles = max(1, (len + kKt - 1) / kKt);
     const int32_t *sel_row = idx + ((size_t)b * T + i) * k + e_begin;
     const uint8_t *lat_b = reinterpret_cast<const uint8_t *>(lat) + (size_t)b * S * kLatRowBytes;
     const size_t rowq = (size_t)b * T + i;
@@ -692,7 +700,8 @@ size_t mla_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int k) {
 
 hipError_t launch_mla(const dsa_attn_desc_t &d, const void *q, const void *kv,
                       const int32_t *idx, int B, int T, int S, int row0, int rows, int k,
-                      void *out, float *lse, void *workspace, hipStream_t stream) {
+                      void *out, float *lse, void *workspace, hipStream_t stream,
+                      const int32_t *q_pos, bool causal_tail) {
     const int H = d.num_heads;
     for (int r0 = 0; r0 < rows; r0 += kMaxGridY) {
         const int n = min(kMaxGridY, rows - r0);
@@ -708,13 +717,15 @@ hipError_t launch_mla(const dsa_attn_desc_t &d, const void *q, const void *kv,
                                idx, T, S, H, k, d.scale, row0 + r0, n, B, used_splits, per_split,
                                static_cast<uint16_t *>(out), lse,
                                static_cast<uint16_t *>(workspace),
-                               reinterpret_cast<float *>(static_cast<uint16_t *>(workspace) + part_elems));
+                               reinterpret_cast<float *>(static_cast<uint16_t *>(workspace) + part_elems),
+                               q_pos, causal_tail ? 1 : 0);
         else
             hipLaunchKernelGGL(mla_attention_kernel<float>, grid, dim3(kThreads), 0, stream,
                                static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),
                                idx, T, S, H, k, d.scale, row0 + r0, n, B, used_splits, per_split,
                                static_cast<float *>(out), lse, static_cast<float *>(workspace),
-                               static_cast<float *>(workspace) + part_elems);
+                               static_cast<float *>(workspace) + part_elems, q_pos,
+                               causal_tail ? 1 : 0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (used_splits > 1) {

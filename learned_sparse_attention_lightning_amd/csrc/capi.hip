@@ -158,22 +158,34 @@ DSA_EXPORT dsa_status_t dsa_topk(const float *scores, const int32_t *q_pos, int 
                        stream);
 }
 
-DSA_EXPORT dsa_status_t dsa_sparse_attention(const dsa_attn_desc_t *desc, const void *q,
-                                             const void *kv, const void *v, const int32_t *idx,
-                                             int B, int T, int S, int index_topk, void *out,
-                                             float *lse, void *workspace,
-                                             size_t workspace_bytes, void *stream) {
-    dsa_status_t st = check_sizes(B, T, S, true);
+DSA_EXPORT dsa_status_t dsa_sparse_attention_ex(const dsa_attn_desc_t *desc, const void *q,
+                                                const void *kv, const void *v,
+                                                const int32_t *idx, const int32_t *q_pos,
+                                                int flags, int B, int T, int S, int index_topk,
+                                                void *out, float *lse, void *workspace,
+                                                size_t workspace_bytes, void *stream) {
+    dsa_status_t st = check_sizes(B, T, S, q_pos != nullptr || !(flags & DSA_ATTN_CAUSAL_PREFIX));
     if (st != DSA_OK) return st;
     st = check_attention(desc, q, kv, v, out);
     if (st != DSA_OK) return st;
     if (!idx) return DSA_ERR_NULL;
     if (!valid_topk(index_topk)) return DSA_ERR_SHAPE;
+    if (flags & ~DSA_ATTN_CAUSAL_PREFIX) return DSA_ERR_UNSUPPORTED;
     if (!aligned16(idx) || (lse && !aligned16(lse))) return DSA_ERR_ALIGN;
     const size_t need = attention_workspace_bytes(*desc, B, T, S, index_topk);
     if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
     return hip_status(launch_attention(*desc, q, kv, v, idx, B, T, S, 0, T, index_topk, out, lse,
-                                       workspace, (hipStream_t)stream));
+                                       workspace, (hipStream_t)stream, q_pos,
+                                       (flags & DSA_ATTN_CAUSAL_PREFIX) != 0));
+}
+
+DSA_EXPORT dsa_status_t dsa_sparse_attention(const dsa_attn_desc_t *desc, const void *q,
+                                             const void *kv, const void *v, const int32_t *idx,
+                                             int B, int T, int S, int index_topk, void *out,
+                                             float *lse, void *workspace,
+                                             size_t workspace_bytes, void *stream) {
+    return dsa_sparse_attention_ex(desc, q, kv, v, idx, nullptr, 0, B, T, S, index_topk, out,
+                                   lse, workspace, workspace_bytes, stream);
 }
 
 DSA_EXPORT dsa_status_t dsa_indexer_kl(const dsa_attn_desc_t *desc, const void *q,
@@ -247,8 +259,9 @@ DSA_EXPORT dsa_status_t dsa_forward_ex(const dsa_attn_desc_t *desc, const void *
                             topk_ws, clear_words > 0, s, include_current);
         }
         if (e != hipSuccess) return DSA_ERR_HIP;
+        // the selection just written is min(k, t+1) positions then -1 per row
         e = launch_attention(*desc, q, kv, v, sel, B, T, S, row0, n, index_topk, out, nullptr,
-                             attn_ws, s);
+                             attn_ws, s, q_pos, true);
         if (e != hipSuccess) return DSA_ERR_HIP;
     }
     return DSA_OK;

@@ -134,14 +134,18 @@ hipError_t launch_mha_dense(const dsa_attn_desc_t &d, const void *q, const void 
                             hipStream_t stream);
 bool mla_fast_path(const dsa_attn_desc_t &d);
 size_t mla_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int k);
+// causal_tail: every row's selection is min(k, t+1) positions followed by -1
+// only (what the top-k writes), so the kernel stops at that count.
 hipError_t launch_mla(const dsa_attn_desc_t &d, const void *q, const void *kv,
                       const int32_t *idx, int B, int T, int S, int row0, int rows, int k,
-                      void *out, float *lse, void *workspace, hipStream_t stream);
+                      void *out, float *lse, void *workspace, hipStream_t stream,
+                      const int32_t *q_pos = nullptr, bool causal_tail = false);
 
 size_t attention_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int S, int k);
 hipError_t launch_attention(const dsa_attn_desc_t &d, const void *q, const void *kv,
                             const void *v, const int32_t *idx, int B, int T, int S, int row0,
                             int rows, int k, void *out, float *lse, void *workspace,
-                            hipStream_t stream);
+                            hipStream_t stream, const int32_t *q_pos = nullptr,
+                            bool causal_tail = false);
 
 }  // namespace dsa

@@ -26,9 +26,11 @@ DTYPE_CODES = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16,
 NAME_CODES = {"f32": DSA_F32, "bf16": DSA_BF16, "fp8": DSA_FP8_E4M3}
 FORM_CODES = {"mha": DSA_MHA, "mla": DSA_MLA}
 EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_indexer_scores", "dsa_topk",
-            "dsa_topk_ex", "dsa_sparse_attention", "dsa_forward", "dsa_forward_ex",
+            "dsa_topk_ex", "dsa_sparse_attention", "dsa_sparse_attention_ex", "dsa_forward",
+            "dsa_forward_ex",
             "dsa_indexer_kl", "dsa_workspace_bytes")
 DSA_SEL_INCLUDE_CURRENT = 1
+DSA_ATTN_CAUSAL_PREFIX = 1
 
 
 class DSAError(RuntimeError):
@@ -75,6 +77,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.dsa_sparse_attention.restype = _i
     lib.dsa_sparse_attention.argtypes = [ctypes.POINTER(AttnDesc), _p, _p, _p, _p, _i, _i, _i,
                                          _i, _p, _p, _p, ctypes.c_size_t, _p]
+    lib.dsa_sparse_attention_ex.restype = _i
+    lib.dsa_sparse_attention_ex.argtypes = [ctypes.POINTER(AttnDesc), _p, _p, _p, _p, _p, _i, _i,
+                                            _i, _i, _i, _p, _p, _p, ctypes.c_size_t, _p]
     lib.dsa_forward.restype = _i
     lib.dsa_forward.argtypes = [ctypes.POINTER(AttnDesc), _p, _p, _i, _p, _p, _p, _p, _p, _i,
                                 _i, _i, _i, _i, _i, _p, _p, _p, ctypes.c_size_t, _p]
@@ -180,8 +185,11 @@ def dsa_topk(scores, k: int, q_pos=None, idx=None, stream=None, include_current=
     return idx
 
 
-def dsa_sparse_attention(desc: AttnDesc, q, kv, v, idx, out=None, lse=None, stream=None):
-    """out [B,T,H,d_v] over the selected rows idx [B,T,k]."""
+def dsa_sparse_attention(desc: AttnDesc, q, kv, v, idx, out=None, lse=None, stream=None,
+                         causal_prefix=False, q_pos=None):
+    """out [B,T,H,d_v] over the selected rows idx [B,T,k].  causal_prefix:
+    idx rows are min(k, t+1) positions then -1, as dsa_topk writes them
+    (dsa_sparse_attention_ex; q_pos gives t, else the default positions)."""
     _need(q, "q", ndim=4)
     _need(kv, "kv", dtype=q.dtype)
     if v is not None:
@@ -198,9 +206,17 @@ def dsa_sparse_attention(desc: AttnDesc, q, kv, v, idx, out=None, lse=None, stre
         _need(lse, "lse", dtype=torch.float32, ndim=3)
     nws = workspace_bytes(DSA_OP_ATTENTION, desc, B, T, S, 1, 1, k)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
-    _check(load().dsa_sparse_attention(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(v), _ptr(idx),
-                                       B, T, S, k, _ptr(out), _ptr(lse), _ptr(ws), nws,
-                                       _stream(stream)))
+    if causal_prefix:
+        if q_pos is not None:
+            _need(q_pos, "q_pos", dtype=torch.int32, ndim=2)
+        _check(load().dsa_sparse_attention_ex(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(v),
+                                              _ptr(idx), _ptr(q_pos), DSA_ATTN_CAUSAL_PREFIX, B,
+                                              T, S, k, _ptr(out), _ptr(lse), _ptr(ws), nws,
+                                              _stream(stream)))
+    else:
+        _check(load().dsa_sparse_attention(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(v),
+                                           _ptr(idx), B, T, S, k, _ptr(out), _ptr(lse),
+                                           _ptr(ws), nws, _stream(stream)))
     return out
 
 

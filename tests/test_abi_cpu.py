@@ -158,3 +158,14 @@ def test_indexer_kl_argument_checks(lib):
     assert f(ctypes.byref(d), A, A, None, A, A, 1, 4, 8, 2, A, None) == NULL
     assert f(ctypes.byref(d), A, A, A, A, A, 1, 4, 8, 0, A, None) == SHAPE
     assert f(ctypes.byref(d), A, A, A, M, A, 1, 4, 8, 2, A, None) == ALIGN
+
+
+def test_attention_ex_argument_checks(lib):
+    f = lib.dsa_sparse_attention_ex
+    d = _desc()
+    pre = dsa.DSA_ATTN_CAUSAL_PREFIX
+    assert f(None, A, A, None, A, None, pre, 1, 1, 8, 2, A, None, None, 0, None) == NULL
+    assert f(ctypes.byref(d), A, A, None, A, None, 2, 1, 1, 8, 2, A, None, None, 0, None) == UNSUP
+    # default positions need T <= S
+    assert f(ctypes.byref(d), A, A, None, A, None, pre, 1, 9, 8, 2, A, None, None, 0, None) == SHAPE
+    assert f(ctypes.byref(d), M, A, None, A, None, pre, 1, 1, 8, 2, A, None, None, 0, None) == ALIGN

@@ -153,3 +153,31 @@ def test_forward_dense_when_context_within_budget(case):
                            x["v"], w.index_topk, idx_out=idx2, include_current=True)
     torch.cuda.synchronize()
     assert torch.equal(idx2, idx) and torch.equal(out2, out)
+
+
+@pytest.mark.parametrize("case", ["prefill", "decode-splits"])
+def test_attention_causal_prefix_matches_plain(case):
+    """Stopping at each row's selected count (dsa_sparse_attention_ex with
+    DSA_ATTN_CAUSAL_PREFIX) skips only empty tiles: outputs and lse are
+    bitwise those of the plain call, and both match the oracle."""
+    if case == "prefill":
+        w = configs.get("c2").with_(name="prefix", B=1, T=3000, S=3000, num_heads=32)
+        pos = None
+    else:
+        w = configs.get("c4").with_(name="prefix-dec", B=4, T=1, S=3000, num_heads=16)
+        pos = torch.tensor([[2999], [100], [2047], [0]], dtype=torch.int32, device=DEV)
+    x = synth.make_inputs(w, device=DEV, seed=29)
+    sc = dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"], q_pos=pos)
+    idx = dsa.dsa_topk(sc, w.index_topk, q_pos=pos)
+    desc = dsa.desc_for(w)
+    lse0 = torch.empty((w.B, w.T, w.num_heads), dtype=torch.float32, device=DEV)
+    lse1 = torch.empty_like(lse0)
+    out0 = dsa.dsa_sparse_attention(desc, x["q"], x["kv"], None, idx, lse=lse0)
+    out1 = dsa.dsa_sparse_attention(desc, x["q"], x["kv"], None, idx, lse=lse1,
+                                    causal_prefix=True, q_pos=pos)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
+    rows = [0, 1, 2047, w.T - 1] if w.T > 1 else [0]
+    ref = oracle.sparse_attention("mla", x["q"][:, rows], x["kv"], None, idx[:, rows].cpu(),
+                                  w.scale, d_v=w.d_v)
+    assert max_abs_err(out1[:, rows], ref) <= TOL["bf16"]
