@@ -90,10 +90,22 @@ __global__ __launch_bounds__(kKlThreads, 1) void mla_indexer_kl_kernel(
     constexpr float kLog2e = 1.4426950408889634f;
 
     const uint16_t *qrow = q + row * (size_t)H * kKlDqk;
-    for (int p = tid; p < H * kKlPieces; p += kKlThreads) {
-        const int h = p / kKlPieces, c = p - h * kKlPieces;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(qrow + (size_t)h * kKlDqk + c * 8);
-        *reinterpret_cast<u32x4 *>(qs + h * kQPitch + c * 16) = v;
+    {  // every load of the query block in flight before the first LDS write
+        constexpr int kQIters = H * kKlPieces / kKlThreads;
+        static_assert(H * kKlPieces % kKlThreads == 0, "query pieces must tile the workgroup");
+        u32x4 qv[kQIters];
+#pragma unroll
+        for (int it = 0; it < kQIters; ++it) {
+            const int p = tid + it * kKlThreads;
+            const int h = p / kKlPieces, c = p - h * kKlPieces;
+            qv[it] = *reinterpret_cast<const u32x4 *>(qrow + (size_t)h * kKlDqk + c * 8);
+        }
+#pragma unroll
+        for (int it = 0; it < kQIters; ++it) {
+            const int p = tid + it * kKlThreads;
+            const int h = p / kKlPieces, c = p - h * kKlPieces;
+            *reinterpret_cast<u32x4 *>(qs + h * kQPitch + c * 16) = qv[it];
+        }
     }
     for (int h = tid; h < H; h += kKlThreads) lse2[h] = lse[row * H + h] * kLog2e;
     __syncthreads();
@@ -105,35 +117,47 @@ __global__ __launch_bounds__(kKlThreads, 1) void mla_indexer_kl_kernel(
     KlState st = {-INFINITY, 0.f, 0.f, 0.f, 0.f};
 
     const int npairs = (k + 63) / 64;
-    for (int pr = wave; pr < npairs; pr += kKlWaves) {
-        const int e0 = pr * 64 + n, e1 = e0 + 32, me = pr * 64 + lane;
-        const int s0 = e0 < k ? sel[e0] : -1;
-        const int s1 = e1 < k ? sel[e1] : -1;
-        const int sme = me < k ? sel[me] : -1;
-        if (__ballot(sme >= 0) == 0) continue;  // the whole pair is unused
+    auto sel_at = [&](int e) -> int { return e < k ? sel[e] : -1; };
+    auto kptr = [&](int s) { return kbase + (size_t)(s < 0 ? 0 : s) * (kKlDqk * 2); };
+    bf16x8 bg[2][kKlGroup][2];
+    auto load_group = [&](bf16x8 (&dst)[kKlGroup][2], const char *p0, const char *p1, int g) {
+#pragma unroll
+        for (int j = 0; j < kKlGroup; ++j) {
+            dst[j][0] = *reinterpret_cast<const bf16x8 *>(p0 + (g * kKlGroup + j) * 32);
+            dst[j][1] = *reinterpret_cast<const bf16x8 *>(p1 + (g * kKlGroup + j) * 32);
+        }
+    };
+    // the selection of a wave's next pair and that pair's first key group are
+    // in flight while the current pair is multiplied
+    int pr = wave;
+    int s0 = -1, s1 = -1, sme = -1;
+    if (pr < npairs) {
+        s0 = sel_at(pr * 64 + n);
+        s1 = sel_at(pr * 64 + 32 + n);
+        sme = sel_at(pr * 64 + lane);
+    }
+    for (; pr < npairs; pr += kKlWaves) {
+        const int nx = pr + kKlWaves;
+        int s0n = -1, s1n = -1, smen = -1;
+        if (nx < npairs) {
+            s0n = sel_at(nx * 64 + n);
+            s1n = sel_at(nx * 64 + 32 + n);
+            smen = sel_at(nx * 64 + lane);
+        }
+        const char *k0 = kptr(s0), *k1 = kptr(s1);
+        if (__ballot(sme >= 0) == 0) {  // the whole pair is unused
+            s0 = s0n, s1 = s1n, sme = smen;
+            continue;
+        }
         const float Ime = sme >= 0 ? irow[sme] : 0.f;
-        const char *k0 = kbase + (size_t)(s0 < 0 ? 0 : s0) * (kKlDqk * 2);
-        const char *k1 = kbase + (size_t)(s1 < 0 ? 0 : s1) * (kKlDqk * 2);
+        load_group(bg[0], k0, k1, 0);
 
         f32x16 acc[HT][2];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) acc[ht][0] = acc[ht][1] = f32x16{};
-        bf16x8 bg[2][kKlGroup][2];
-#pragma unroll
-        for (int j = 0; j < kKlGroup; ++j) {
-            bg[0][j][0] = *reinterpret_cast<const bf16x8 *>(k0 + j * 32);
-            bg[0][j][1] = *reinterpret_cast<const bf16x8 *>(k1 + j * 32);
-        }
 #pragma unroll
         for (int g = 0; g < kKlGroups; ++g) {
-            if (g + 1 < kKlGroups) {
-#pragma unroll
-                for (int j = 0; j < kKlGroup; ++j) {
-                    const int ks = (g + 1) * kKlGroup + j;
-                    bg[(g + 1) & 1][j][0] = *reinterpret_cast<const bf16x8 *>(k0 + ks * 32);
-                    bg[(g + 1) & 1][j][1] = *reinterpret_cast<const bf16x8 *>(k1 + ks * 32);
-                }
-            }
+            if (g + 1 < kKlGroups) load_group(bg[(g + 1) & 1], k0, k1, g + 1);
 #pragma unroll
             for (int j = 0; j < kKlGroup; ++j) {
                 const int ks = g * kKlGroup + j;
@@ -167,6 +191,7 @@ __global__ __launch_bounds__(kKlThreads, 1) void mla_indexer_kl_kernel(
         const float recv = __shfl_xor(half ? pa0 : pa1, 32);
         const float p = ((half ? pa1 : pa0) + recv) * (1.0f / H);
         if (sme >= 0) kl_push(st, p, Ime);
+        s0 = s0n, s1 = s1n, sme = smen;
     }
 
 #pragma unroll
