@@ -109,3 +109,29 @@ def test_indexer_kl_unit_scale_scores():
     ref = oracle.indexer_kl_rows(p, sc, oracle.selection_mask(sel, w.S))
     _check(loss, ref, "unit-scale scores")
     assert ref[:, 50:].min() > 0.05  # far from zero: p and softmax differ
+
+
+def test_indexer_kl_unordered_selection_with_holes():
+    """Any set of distinct positions in any slot order, unused slots anywhere
+    (the loss is a function of the set): permuted rows with holes punched in."""
+    w = configs.get("c2").with_(name="kl-holes", B=1, T=256, S=256, index_topk=96,
+                                num_heads=32)
+    x = synth.make_inputs(w, device=DEV, seed=41)
+    sc = synth.random_scores((w.B, w.T, w.S), seed=6)
+    sel = oracle.topk(sc, w.index_topk)           # rank order, -1 padded
+    rng = np.random.default_rng(2)
+    for i in range(w.T):
+        sel[0, i] = sel[0, i, rng.permutation(w.index_topk)]
+        holes = rng.choice(w.index_topk, size=10, replace=False)
+        sel[0, i, holes] = -1
+    sel[0, 7, :] = -1                             # an empty row: loss 0
+    idx = torch.from_numpy(sel).to(DEV)
+    desc = dsa.desc_for(w)
+    lse = torch.empty((w.B, w.T, w.num_heads), dtype=torch.float32, device=DEV)
+    dsa.dsa_sparse_attention(desc, x["q"], x["kv"], None, idx, lse=lse)
+    loss = dsa.dsa_indexer_kl(desc, x["q"], x["kv"], idx, lse, sc.to(DEV))
+    torch.cuda.synchronize()
+    p = oracle.sparse_target("mla", x["q"], x["kv"], sel, w.scale)
+    ref = oracle.indexer_kl_rows(p, sc, oracle.selection_mask(sel, w.S))
+    _check(loss, ref, "unordered with holes")
+    assert loss[0, 7].item() == 0.0

@@ -181,3 +181,17 @@ def test_attention_causal_prefix_matches_plain(case):
     ref = oracle.sparse_attention("mla", x["q"][:, rows], x["kv"], None, idx[:, rows].cpu(),
                                   w.scale, d_v=w.d_v)
     assert max_abs_err(out1[:, rows], ref) <= TOL["bf16"]
+
+
+def test_forward_include_current_c4_full():
+    """The 128K decode workload at full size with the current token kept."""
+    w = configs.get("c4")
+    x, idx, out = _run_forward(w, None, True)
+    sc = oracle.indexer_scores(x["q_idx"], x["k_idx"], x["w"])
+    ref_idx = oracle.topk(sc, w.index_topk, include_current=True)
+    assert_selection_equal(idx, ref_idx, "c4 current")
+    _current_kept(idx, np.full((w.B, 1), w.S - 1))
+    ref = oracle.sparse_attention("mla", x["q"], x["kv"], None, ref_idx, w.scale, d_v=w.d_v)
+    err = max_abs_err(out, ref)
+    _say(f"c4 with the current token: max-abs err {err:.3e}")
+    assert err <= TOL["bf16"]
