@@ -127,8 +127,8 @@ __global__ __launch_bounds__(kKlThreads, 1) void mla_indexer_kl_kernel(
             dst[j][1] = *reinterpret_cast<const bf16x8 *>(p1 + (g * kKlGroup + j) * 32);
         }
     };
-    // the selection of a wave's next pair and that pair's first key group are
-    // in flight while the current pair is multiplied
+    // the selection of a wave's next pair is in flight while the current pair
+    // is multiplied
     int pr = wave;
     int s0 = -1, s1 = -1, sme = -1;
     if (pr < npairs) {
