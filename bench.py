@@ -304,7 +304,7 @@ def main():
             b.record()
             torch.cuda.synchronize()
             stage_ms.append(a.elapsed_time(b) / 2)
-        if args.kl and w.form == "mla":
+        if args.kl:
             # the loss kernel needs each chunk's scores and the attention's
             # log-sum-exp: both computed untimed, then the loss launch timed
             lse = torch.empty((w.B, ch, w.num_heads), dtype=torch.float32, device=dev)
@@ -328,9 +328,13 @@ def main():
                 kl_ms = tot  # the second pass (warm) is kept
             kl_flops = alg["entries"] * 2 * w.num_heads * w.d_qk
             kl_tf = kl_flops / (kl_ms * 1e-3) / 1e12
-            kl_roof = {"bound": "mfma", "achieved": round(kl_tf, 2), "peak": BF16_PEAK_TFLOPS,
-                       "unit": "TFLOP/s", "frac": round(kl_tf / BF16_PEAK_TFLOPS, 4),
-                       "ms": round(kl_ms, 4), "kernel": "mla_indexer_kl_kernel",
+            # MLA: matrix-core products; MHA: per-head dot products on the
+            # vector ALUs (fp32 FMA peak)
+            kpk, kb = (BF16_PEAK_TFLOPS, "mfma") if w.form == "mla" else (157.3, "alu")
+            kl_roof = {"bound": kb, "achieved": round(kl_tf, 2), "peak": kpk,
+                       "unit": "TFLOP/s", "frac": round(kl_tf / kpk, 4),
+                       "ms": round(kl_ms, 4),
+                       "kernel": f"{w.form}_indexer_kl_kernel",
                        "algorithmic_flops": kl_flops}
         del sc
 

@@ -219,24 +219,26 @@ dsa_status_t dsa_forward_ex(const dsa_attn_desc_t *desc, const void *q_idx, cons
  * Forward value of the indexer's distillation loss over a selected set,
  * [P1] sections 5.2-5.4 (target and loss) and 6.2 (restricted to S_t).  For
  * each query row, with S = the entries of idx[b,i,:] that are >= 0:
- *   p_s     = (1/H) sum_h softmax_{s in S}( scale * q[b,i,h,:] . latent[b,s,:] )
- *             (the head mean of the attention weights over S),
+ *   p_s     = (1/H) sum_h softmax_{s in S}( scale * q[b,i,h,:] . key(s,h) )
+ *             (the head mean of the attention weights over S; key(s,h) as in
+ *             dsa_sparse_attention),
  *   loss[b,i] = KL( p || softmax_{s in S}( scores[b,i,s] ) )
  *             = sum_{s in S} p_s ( log p_s - log softmax(scores)_s ),
  * with p renormalised over S.  A row with an empty set gets 0.  The dense
  * warm-up loss of [P1] section 5.4 is the same call with every causal
  * position selected (k >= S; dsa_topk writes that selection).
- *   MLA latent form only: desc->form DSA_MLA, dtype DSA_BF16, d_qk 576,
- *   num_heads 32, 64 or 128 (else DSA_ERR_UNSUPPORTED); desc->scale is the
- *   attention's softmax scale.
- *   q      [B,T,H,576] bf16;  kv  [B,S,576] bf16 latent rows
+ *   MLA: desc->form DSA_MLA, dtype DSA_BF16, d_qk 576, num_heads 32, 64 or
+ *   128; MHA: DSA_MHA, dtype DSA_BF16 or DSA_F32, d_qk 64 or 128, num_heads
+ *   <= 64 (else DSA_ERR_UNSUPPORTED).  desc->scale is the attention's scale.
+ *   q      [B,T,H,d_qk] desc->dtype
+ *   kv     MLA: [B,S,576] bf16 latent rows; MHA: K [B,S,H,d_qk]
  *   idx    [B,T,k] int32 distinct positions < S, -1 = unused slot
  *   lse    [B,T,H] fp32 natural-log sum of exp of the scaled logits over the
  *          same set, as dsa_sparse_attention writes it for q, kv, idx
  *   scores [B,T,S] fp32 indexer scores (read at the selected positions)
  *   loss   [B,T] fp32 output (the total is its sum)
- * Logits in fp32 from bf16 products; p, the log-sum-exp of the scores and the
- * sums in fp32.  No workspace.
+ * Logits in fp32 (bf16 or fp32 inputs); p, the log-sum-exp of the scores and
+ * the sums in fp32.  No workspace.
  */
 dsa_status_t dsa_indexer_kl(const dsa_attn_desc_t *desc, const void *q, const void *kv,
                             const int32_t *idx, const float *lse, const float *scores, int B,

@@ -196,7 +196,8 @@ DSA_EXPORT dsa_status_t dsa_indexer_kl(const dsa_attn_desc_t *desc, const void *
     if (st != DSA_OK) return st;
     if (!desc) return DSA_ERR_NULL;
     if (!indexer_kl_supported(*desc)) return DSA_ERR_UNSUPPORTED;
-    st = check_attention(desc, q, kv, nullptr, loss);
+    // the loss reads keys only (MHA: K in kv; the value tensor is not needed)
+    st = check_attention(desc, q, kv, desc->form == DSA_MHA ? kv : nullptr, loss);
     if (st != DSA_OK) return st;
     if (!idx || !lse || !scores) return DSA_ERR_NULL;
     if (!valid_topk(index_topk)) return DSA_ERR_SHAPE;

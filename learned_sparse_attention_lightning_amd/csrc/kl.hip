@@ -1,6 +1,6 @@
 // kl.hip -- forward value of the indexer's distillation loss over a selected
 // set ("DeepSeek Sparse Attention: Learned Token Selection from Scratch",
-// sections 5.2-5.4 and 6.2), MLA latent form.
+// sections 5.2-5.4 and 6.2), MLA latent form and MHA form.
 //
 // For query row t with selected set S_t and per-head log-sum-exp lse_h of
 // the scaled logits over S_t (what the attention step writes), the target is
@@ -60,6 +60,23 @@ __device__ __forceinline__ KlState kl_merge(KlState a, KlState b) {
     r.A = a.A + b.A;
     r.Bd = a.Bd - a.P * (r.m - a.m) + b.Bd - b.P * (r.m - b.m);
     return r;
+}
+
+__device__ __forceinline__ float load_as_float(const float *p) { return *p; }
+__device__ __forceinline__ float load_as_float(const uint16_t *p) {
+    return __uint_as_float((uint32_t)*p << 16);
+}
+// 16 bytes of keys to fp32: four floats or eight bf16
+__device__ __forceinline__ void unpack16(u32x4 raw, float (&out)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = __uint_as_float(raw[j]);
+}
+__device__ __forceinline__ void unpack16(u32x4 raw, float (&out)[8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        out[2 * j] = __uint_as_float(raw[j] << 16);
+        out[2 * j + 1] = __uint_as_float(raw[j] & 0xffff0000u);
+    }
 }
 
 __device__ __forceinline__ KlState kl_shfl_xor(KlState s, int mask) {
@@ -206,9 +223,76 @@ __global__ __launch_bounds__(kKlThreads, 1) void mla_indexer_kl_kernel(
     }
 }
 
+
+// MHA form: every head has its own key row, so the logits are 2-operand dot
+// products per (entry, head) rather than one shared-operand product.  One
+// workgroup per query row, one lane per selected entry: the lane streams its
+// entry's H key rows (16-byte loads) against the query block, broadcast from
+// LDS as fp32, and sums exp(scale q_h.K[s,h] - lse_h) over the heads.
+constexpr int kMhaKlThreads = 256;
+constexpr int kMhaKlMaxH = 64;
+constexpr int kMhaKlMaxD = 128;
+
+template <typename Tin>
+__global__ __launch_bounds__(kMhaKlThreads) void mha_indexer_kl_kernel(
+    const Tin *__restrict__ q, const Tin *__restrict__ K, const int32_t *__restrict__ idx,
+    const float *__restrict__ lse, const float *__restrict__ scores, int T, int S, int H, int D,
+    int k, float scale, float *__restrict__ loss) {
+    __shared__ __attribute__((aligned(16))) float qf[kMhaKlMaxH * kMhaKlMaxD];
+    __shared__ float lse2[kMhaKlMaxH];
+    __shared__ KlState red[kMhaKlThreads / kWave];
+    const int i = blockIdx.x, b = blockIdx.y;
+    const size_t row = (size_t)b * T + i;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr float kLog2e = 1.4426950408889634f;
+    constexpr int kPer = 16 / sizeof(Tin);  // elements per 16-byte load
+
+    const Tin *qrow = q + row * (size_t)H * D;
+    for (int e = tid; e < H * D; e += kMhaKlThreads) qf[e] = load_as_float(qrow + e);
+    for (int h = tid; h < H; h += kMhaKlThreads) lse2[h] = lse[row * H + h] * kLog2e;
+    __syncthreads();
+
+    const float c1 = scale * kLog2e;
+    const int32_t *sel = idx + row * (size_t)k;
+    const float *irow = scores + row * (size_t)S;
+    KlState st = {-INFINITY, 0.f, 0.f, 0.f, 0.f};
+    for (int e = tid; e < k; e += kMhaKlThreads) {
+        const int s = sel[e];
+        if (s < 0) continue;
+        const Tin *krow = K + ((size_t)b * S + s) * (size_t)H * D;
+        float pacc = 0.f;
+        for (int h = 0; h < H; ++h) {
+            const Tin *kh = krow + (size_t)h * D;
+            const float *qh = qf + h * D;
+            float dot = 0.f;
+            for (int d0 = 0; d0 < D; d0 += kPer) {
+                const u32x4 raw = *reinterpret_cast<const u32x4 *>(kh + d0);
+                float kv[kPer];
+                unpack16(raw, kv);
+#pragma unroll
+                for (int j = 0; j < kPer; ++j) dot = fmaf(qh[d0 + j], kv[j], dot);
+            }
+            pacc += exp2f(fmaf(dot, c1, -lse2[h]));
+        }
+        kl_push(st, pacc / (float)H, irow[s]);
+    }
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) st = kl_merge(st, kl_shfl_xor(st, mask));
+    if (lane == 0) red[wave] = st;
+    __syncthreads();
+    if (tid == 0) {
+        KlState r = red[0];
+        for (int w = 1; w < kMhaKlThreads / kWave; ++w) r = kl_merge(r, red[w]);
+        loss[row] = r.P > 0.f ? r.A / r.P - __logf(r.P) - r.Bd / r.P + __logf(r.z) : 0.f;
+    }
+}
+
 }  // namespace
 
 bool indexer_kl_supported(const dsa_attn_desc_t &d) {
+    if (d.form == DSA_MHA)
+        return (d.dtype == DSA_BF16 || d.dtype == DSA_F32) && (d.d_qk == 64 || d.d_qk == 128) &&
+               d.num_heads <= kMhaKlMaxH;
     return d.form == DSA_MLA && d.dtype == DSA_BF16 && d.d_qk == kKlDqk &&
            (d.num_heads == 32 || d.num_heads == 64 || d.num_heads == 128);
 }
@@ -217,6 +301,19 @@ hipError_t launch_indexer_kl(const dsa_attn_desc_t &d, const void *q, const void
                              const int32_t *idx, const float *lse, const float *scores, int B,
                              int T, int S, int k, float *loss, hipStream_t stream) {
     const dim3 grid(T, B);
+    if (d.form == DSA_MHA) {
+        if (d.dtype == DSA_BF16)
+            hipLaunchKernelGGL(mha_indexer_kl_kernel<uint16_t>, grid, dim3(kMhaKlThreads), 0,
+                               stream, static_cast<const uint16_t *>(q),
+                               static_cast<const uint16_t *>(kv), idx, lse, scores, T, S,
+                               d.num_heads, d.d_qk, k, d.scale, loss);
+        else
+            hipLaunchKernelGGL(mha_indexer_kl_kernel<float>, grid, dim3(kMhaKlThreads), 0,
+                               stream, static_cast<const float *>(q),
+                               static_cast<const float *>(kv), idx, lse, scores, T, S,
+                               d.num_heads, d.d_qk, k, d.scale, loss);
+        return hipGetLastError();
+    }
     const uint16_t *qq = static_cast<const uint16_t *>(q);
     const uint16_t *kk = static_cast<const uint16_t *>(kv);
     switch (d.num_heads) {

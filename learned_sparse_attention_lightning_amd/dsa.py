@@ -257,17 +257,20 @@ def dsa_forward(desc: AttnDesc, q_idx, k_idx, w, q, kv, v, k: int, q_pos=None, o
 
 def dsa_indexer_kl(desc: AttnDesc, q, kv, idx, lse, scores, loss=None, stream=None):
     """Per-row KL(head-mean attention weights || softmax of the indexer
-    scores) over each row's selected set -> loss [B,T] fp32 (MLA form)."""
-    _need(q, "q", dtype=torch.bfloat16, ndim=4)
-    _need(kv, "kv", dtype=torch.bfloat16, ndim=3)
+    scores) over each row's selected set -> loss [B,T] fp32 (MLA or MHA)."""
+    mha = desc.form == DSA_MHA
+    _need(q, "q", ndim=4)
+    _need(kv, "kv", dtype=q.dtype, ndim=4 if mha else 3)
     _need(idx, "idx", dtype=torch.int32, ndim=3)
     _need(lse, "lse", dtype=torch.float32, ndim=3)
     _need(scores, "scores", dtype=torch.float32, ndim=3)
     B, T, H, D = q.shape
     S = kv.shape[1]
     k = idx.shape[-1]
-    if H != desc.num_heads or D != desc.d_qk or tuple(kv.shape) != (B, S, D):
-        raise ValueError("q [B,T,H,d_qk] and kv [B,S,d_qk] must match desc")
+    want_kv = (B, S, H, D) if mha else (B, S, D)
+    if H != desc.num_heads or D != desc.d_qk or tuple(kv.shape) != want_kv:
+        raise ValueError("q [B,T,H,d_qk] and kv (MLA [B,S,d_qk], MHA [B,S,H,d_qk]) must "
+                         "match desc")
     if tuple(idx.shape[:2]) != (B, T) or tuple(lse.shape) != (B, T, H) or \
             tuple(scores.shape) != (B, T, S):
         raise ValueError("idx [B,T,k], lse [B,T,H] and scores [B,T,S] must match q and kv")

@@ -153,8 +153,10 @@ def test_indexer_kl_argument_checks(lib):
     f = lib.dsa_indexer_kl
     d = _desc()
     assert f(None, A, A, A, A, A, 1, 4, 8, 2, A, None) == NULL
-    d2 = _desc(form=dsa.DSA_MHA, H=4, dqk=64, dv=64)
+    d2 = _desc(form=dsa.DSA_MHA, H=4, dqk=96, dv=96)
     assert f(ctypes.byref(d2), A, A, A, A, A, 1, 4, 8, 2, A, None) == UNSUP
+    d3 = _desc(form=dsa.DSA_MHA, H=65, dqk=64, dv=64)
+    assert f(ctypes.byref(d3), A, A, A, A, A, 1, 4, 8, 2, A, None) == UNSUP
     assert f(ctypes.byref(d), A, A, None, A, A, 1, 4, 8, 2, A, None) == NULL
     assert f(ctypes.byref(d), A, A, A, A, A, 1, 4, 8, 0, A, None) == SHAPE
     assert f(ctypes.byref(d), A, A, A, M, A, 1, 4, 8, 2, A, None) == ALIGN

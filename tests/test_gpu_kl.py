@@ -135,3 +135,42 @@ def test_indexer_kl_unordered_selection_with_holes():
     ref = oracle.indexer_kl_rows(p, sc, oracle.selection_mask(sel, w.S))
     _check(loss, ref, "unordered with holes")
     assert loss[0, 7].item() == 0.0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_indexer_kl_mha_sparse_stage(dtype):
+    """MHA form (a key row per head): the pipeline's loss against the oracle."""
+    w = configs.get("c1").with_(name=f"kl-mha-{dtype}", B=2, T=300, S=300, index_topk=64,
+                                dtype=dtype, out_dtype=dtype)
+    x = synth.make_inputs(w, device=DEV, seed=51)
+    desc = dsa.desc_for(w)
+    sc = dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"])
+    idx = dsa.dsa_topk(sc, w.index_topk)
+    lse = torch.empty((w.B, w.T, w.num_heads), dtype=torch.float32, device=DEV)
+    dsa.dsa_sparse_attention(desc, x["q"], x["kv"], x["v"], idx, lse=lse)
+    loss = dsa.dsa_indexer_kl(desc, x["q"], x["kv"], idx, lse, sc)
+    torch.cuda.synchronize()
+    rsc = oracle.indexer_scores(x["q_idx"], x["k_idx"], x["w"])
+    sel = oracle.topk(rsc, w.index_topk)
+    p = oracle.sparse_target("mha", x["q"], x["kv"], sel, w.scale)
+    ref = oracle.indexer_kl_rows(p, rsc, oracle.selection_mask(sel, w.S))
+    _check(loss, ref, f"MHA {dtype}")
+
+
+def test_indexer_kl_mha_dense_warmup_target():
+    """Every causal position selected: the GPU loss against KL(p || softmax(I))
+    with p the oracle's dense warm-up target ([P1] section 5.2)."""
+    w = configs.get("c1").with_(name="kl-mha-warm", B=1, T=200, S=200, index_topk=256)
+    x = synth.make_inputs(w, device=DEV, seed=52)
+    desc = dsa.desc_for(w)
+    sc = dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"])
+    idx = dsa.dsa_topk(sc, w.index_topk)
+    lse = torch.empty((w.B, w.T, w.num_heads), dtype=torch.float32, device=DEV)
+    dsa.dsa_sparse_attention(desc, x["q"], x["kv"], x["v"], idx, lse=lse)
+    loss = dsa.dsa_indexer_kl(desc, x["q"], x["kv"], idx, lse, sc)
+    torch.cuda.synchronize()
+    rsc = oracle.indexer_scores(x["q_idx"], x["k_idx"], x["w"])
+    p = oracle.warmup_target(x["q"], x["kv"], w.scale)
+    causal = np.tril(np.ones((w.T, w.S), dtype=np.int8))[None]
+    ref = oracle.indexer_kl_rows(p, rsc, causal)
+    _check(loss, ref, "MHA dense warm-up")
