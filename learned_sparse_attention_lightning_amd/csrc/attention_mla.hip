@@ -29,14 +29,13 @@
 // Decode rows split their entries over several workgroups; each writes a
 // normalised partial output and its log-sum-exp, merged by a second kernel.
 #include "dsa_internal.h"
+#include "mla_schedule.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kDqk = 576;
-constexpr int kDv = 512;
-constexpr int kHg = 64;            // heads per workgroup
-constexpr int kKsteps = kDqk / 16; // 36
+using namespace mla;  // shapes, tile schedule and addressing (mla_schedule.h)
+
 constexpr float kRescaleLog2 = 8.0f;  // reference-max slack, base-2 units
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -97,20 +96,9 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float v) {
 // The S and PV waves share each SIMD, so one role's latencies are covered by
 // the other's matrix work.  The kh = 1 waves read the rope dims of tile it+1
 // from registers loaded one iteration earlier.
-constexpr int kKt = 32;                          // entries per tile
-constexpr int kRing = 4;                         // tiles resident in LDS
-constexpr int kVRowBytes = kDv * 2;              // 1024: the latent dims of a row in LDS
-constexpr int kRowPitch = kVRowBytes + 16;       // 1040 (bank shift of 4 dwords a row)
-constexpr int kTileBytes = kKt * kRowPitch;      // 33280
 constexpr int kPPitch = kKt * 2 + 16;            // 80 bytes per head row of P
-constexpr int kHalfSteps = kKsteps / 2;          // 18
-constexpr int kRopeSteps = (kDqk - kDv) / 16;    // 4 k-steps of rope dims (kh = 1)
 constexpr int kLdsSteps1 = kHalfSteps - kRopeSteps;  // 14 k-steps of kh = 1 read from LDS
 constexpr int kThreads = 512;
-constexpr int kOutPitch = 136;  // floats per head row of the output staging block
-constexpr int kStageRows = kKt / 4;              // rows of a tile each PV wave gathers
-constexpr int kSelRing = 8;                      // tiles of the selection kept in LDS
-constexpr int kLatRowBytes = kDqk * 2;           // 1152: a latent row in memory
 
 // LDS row of entry m of a tile: within each block of 16 entries, entry
 // 4a + b sits in row 4b + a.  A row is 1040 bytes (16 bytes past a multiple
@@ -150,43 +138,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     const int l32 = lane & 31;
     const int hgs = H / kHg;
     const int id = blockIdx.x;
-    int hg, split, qidx;
-    if ((rows * B) % 8 == 0) {
-        // XCD x (= id mod 8) takes the query rows qidx = x mod 8, each with all
-        // its head groups and splits: the two head groups share the gathered
-        // rows and the query block in that XCD's L2, and the split partials
-        // are written where the merge reads them.
-        const int x = id & 7, j = id >> 3;
-        const int per = hgs * splits;
-        const int qg = j / per, rem = j - qg * per;
-        hg = rem % hgs;
-        split = rem / hgs;
-        qidx = 8 * qg + x;
-    } else if ((rows * B * splits) % 8 == 0) {
-        const int slot = id >> 3;
-        hg = slot % hgs;
-        const int unit = (slot / hgs) * 8 + (id & 7);
-        qidx = unit / splits;
-        split = unit % splits;
-    } else {
-        hg = id % hgs;
-        split = (id / hgs) % splits;
-        qidx = id / (hgs * splits);
-    }
-    const int r = qidx % rows;
-    const int b = qidx / rows;
+    // XCD-aware order: the two head groups of a query row share the gathered
+    // rows and the query block in one XCD's L2, and the split partials are
+    // written where the merge reads them
+    const Work wk = work_of(id, rows, B, hgs, splits);
+    const int hg = wk.hg, split = wk.split, qidx = wk.qidx, r = wk.r, b = wk.b;
     const int i = row0 + r;
     const int head0 = hg * kHg;
     const int e_begin = split * per_split;
-    int len = min(k, e_begin + per_split) - e_begin;  // entries of this split
-    if (causal_tail) {
-        // the selection is min(k, t+1) positions followed by -1 only: tiles
-        // past that are empty (a split left with none runs one masked tile)
-        const int t = query_pos(q_pos, b, i, T, S);
-        const int nvalid = t < 0 ? 0 : min(k, t + 1);
-        len = max(0, min(len, nvalid - e_begin));
-    }
-    const int ntiles = max(1, (len + kKt - 1) / kKt);
+    // entries of this split; with causal_tail the tiles past the row's
+    // min(k, t+1) selected positions are empty and not visited
+    const int len = split_len(split, per_split, k, causal_tail != 0,
+                              causal_tail ? query_pos(q_pos, b, i, T, S) : 0);
+    const int ntiles = split_tiles(len);
     const int32_t *sel_row = idx + ((size_t)b * T + i) * k + e_begin;
     const uint8_t *lat_b = reinterpret_cast<const uint8_t *>(lat) + (size_t)b * S * kLatRowBytes;
     const size_t rowq = (size_t)b * T + i;
@@ -200,26 +164,23 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         const int ht = wave & 1, kh = wave >> 1;
         bf16x8 qb[kHalfSteps];
         {
-            const uint16_t *qp = q + (rowq * H + head0 + ht * 32 + l32) * kDqk + 8 * half +
-                                 16 * kHalfSteps * kh;
 #pragma unroll
             for (int ks = 0; ks < kHalfSteps; ++ks)
-                qb[ks] = *reinterpret_cast<const bf16x8 *>(qp + ks * 16);
+                qb[ks] = *reinterpret_cast<const bf16x8 *>(
+                    q + q_offset(rowq, H, head0, ht, l32, half, kh, ks));
         }
         // rope fragments (kh = 1) of tile t: k-steps 14..17 of this half
         auto rope_load = [&](int t, bf16x8 (&rp)[kRopeSteps]) {
-            const int32_t s = sm.sel[t % kSelRing][l32];
-            const uint8_t *src = lat_b + (uint32_t)max(s, 0) * (uint64_t)kLatRowBytes +
-                                 kVRowBytes + 16 * half;
+            const int32_t s = sm.sel[sel_slot(t)][l32];
 #pragma unroll
             for (int j = 0; j < kRopeSteps; ++j)
-                rp[j] = *reinterpret_cast<const bf16x8 *>(src + 32 * j);
+                rp[j] = *reinterpret_cast<const bf16x8 *>(lat_b + rope_offset(s, half, j));
         };
         // this wave's half of S^T(t): K fragments from the LDS ring (and, for
         // kh = 1, the rope registers)
         auto s_read = [&](int t, bf16x8 (&af)[kHalfSteps], const bf16x8 (&rp)[kRopeSteps]) {
             const uint8_t *arow =
-                sm.kv[t % kRing] + tile_row(l32) * kRowPitch + 16 * half + 576 * kh;
+                sm.kv[ring_slot(t)] + tile_row(l32) * kRowPitch + 16 * half + 576 * kh;
             if (kh == 0) {
 #pragma unroll
                 for (int ks = 0; ks < kHalfSteps; ++ks) af[ks] = lds_b128(arow + ks * 32);
@@ -241,7 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         // the sum with the partner's half is -inf too.  Whole tiles are the
         // rule; the branch is uniform.
         auto mask_tile = [&](int t, f32x16 &acc) {
-            const uint32_t vmask = (uint32_t)__ballot(sm.sel[t % kSelRing][l32] >= 0);
+            const uint32_t vmask = (uint32_t)__ballot(sm.sel[sel_slot(t)][l32] >= 0);
             if (vmask != 0xffffffffu) {
                 const uint32_t mh = vmask >> (4 * half);
 #pragma unroll
@@ -308,16 +269,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         // written at iteration it from a load issued one iteration earlier
         // (the wave has no other memory loads, so that wait is free), ahead of
         // every reader: the gathering waves (tile it+4), the rope loads (tile
-        // it+2) and the softmax mask (tile it).
+        // it+2) and the mask (tile it+1).
         int32_t sel_next = 0;
         if (wave == 0) {
-            int32_t sv[5];
+            int32_t sv[kSelPrologue];
 #pragma unroll
-            for (int t = 0; t < 5; ++t) sv[t] = sel_of(t * kKt + l32);
-            sel_next = sel_of(5 * kKt + l32);
+            for (int t = 0; t < kSelPrologue; ++t) sv[t] = sel_of(t * kKt + l32);
+            sel_next = sel_of(kSelAhead * kKt + l32);
 #pragma unroll
-            for (int t = 0; t < 5; ++t)
-                if (half == 0) sm.sel[t][l32] = sv[t];
+            for (int t = 0; t < kSelPrologue; ++t)
+                if (half == 0) sm.sel[sel_slot(t)][l32] = sv[t];
         }
         lds_barrier();  // selection of tiles 0..4
         bf16x8 rp[2][kRopeSteps];  // kh = 1: rope of tiles it+1 (in use) and it+2
@@ -343,22 +304,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         // tile it+1 in rp[c], loads of tile it+2 into rp[c ^ 1]
         auto s_step = [&](const int it, bf16x8 (&rcur)[kRopeSteps],
                           bf16x8 (&rnext)[kRopeSteps]) {
-            const bool more = it + 1 < ntiles;
+            const bool more = it + kSAhead < ntiles;
             if (wave == 0) {
-                if (half == 0) sm.sel[(it + 5) % kSelRing][l32] = sel_next;
-                sel_next = sel_of((it + 6) * kKt + l32);
+                if (half == 0) sm.sel[sel_slot(it + kSelAhead)][l32] = sel_next;
+                sel_next = sel_of((it + kSelAhead + 1) * kKt + l32);
             }
             if (kh == 0) {
                 if (more) {
                     bf16x8 af[kHalfSteps];
-                    s_read(it + 1, af, rcur);
+                    s_read(it + kSAhead, af, rcur);
                     f32x16 nx = {};
 #pragma unroll
                     for (int ks = 0; ks < kHalfSteps; ++ks)
                         nx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qb[ks], nx, 0, 0, 0);
                     softmax(it, s_cur);
                     interleave(std::integral_constant<int, 5>{});
-                    mask_tile(it + 1, nx);
+                    mask_tile(it + kSAhead, nx);
                     s_cur = nx;
                 } else {
                     softmax(it, s_cur);
@@ -366,15 +327,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             } else {
                 if (more) {
                     bf16x8 af[kHalfSteps];
-                    s_read(it + 1, af, rcur);
+                    s_read(it + kSAhead, af, rcur);
                     f32x16 nx = {};
 #pragma unroll
                     for (int ks = 0; ks < kHalfSteps; ++ks)
                         nx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qb[ks], nx, 0, 0, 0);
                     interleave(std::integral_constant<int, 0>{});
-                    put_part(it + 1, nx);
+                    put_part(it + kSAhead, nx);
                 }
-                if (it + 2 < ntiles) rope_load(it + 2, rnext);
+                if (it + kRopeAhead < ntiles) rope_load(it + kRopeAhead, rnext);
             }
             lds_barrier();
         };
@@ -398,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             if (splits == 1) {
                 if (lse) lse[rowq * H + head0 + hl] = ls;
             } else {
-                lse_part[(prow * splits + split) * H + head0 + hl] = ls;
+                lse_part[lse_part_offset(prow, splits, split, H, head0 + hl)] = ls;
             }
         }
     } else {
@@ -408,31 +369,30 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         // gather: rows 8d..8d+7 of tile t, one row a load (lane = 16-byte
         // piece); the rows come from the selection ring
         auto stage_load = [&](int t, u32x4 (&st)[kStageRows]) {
-            const int32_t *sr = sm.sel[t % kSelRing] + 8 * d;
+            const int32_t *sr = sm.sel[sel_slot(t)] + kStageRows * d;
             int32_t rowv[kStageRows];
 #pragma unroll
             for (int m = 0; m < kStageRows; ++m) rowv[m] = sr[m];
 #pragma unroll
             for (int m = 0; m < kStageRows; ++m) {
                 const int32_t s = __builtin_amdgcn_readfirstlane(rowv[m]);
-                st[m] = *reinterpret_cast<const u32x4 *>(
-                    lat_b + (uint32_t)max(s, 0) * (uint64_t)kLatRowBytes + 16 * lane);
+                st[m] = *reinterpret_cast<const u32x4 *>(lat_b + gather_offset(s, lane));
             }
         };
         auto stage_store = [&](int t, const u32x4 (&st)[kStageRows]) {
-            uint8_t *dst = sm.kv[t % kRing] + 16 * lane;
+            uint8_t *dst = sm.kv[ring_slot(t)] + 16 * lane;
 #pragma unroll
             for (int m = 0; m < kStageRows; ++m)
-                *reinterpret_cast<u32x4 *>(dst + tile_row(8 * d + m) * kRowPitch) = st[m];
+                *reinterpret_cast<u32x4 *>(dst + tile_row(kStageRows * d + m) * kRowPitch) = st[m];
         };
         // the first tiles take their rows straight from the selection in memory
         // (uniform loads), so their gathers start before the ring is filled
         auto stage_load_first = [&](int t, u32x4 (&st)[kStageRows]) {
 #pragma unroll
             for (int m = 0; m < kStageRows; ++m) {
-                const int32_t s = __builtin_amdgcn_readfirstlane(sel_of(t * kKt + 8 * d + m));
-                st[m] = *reinterpret_cast<const u32x4 *>(
-                    lat_b + (uint32_t)max(s, 0) * (uint64_t)kLatRowBytes + 16 * lane);
+                const int32_t s =
+                    __builtin_amdgcn_readfirstlane(sel_of(t * kKt + kStageRows * d + m));
+                st[m] = *reinterpret_cast<const u32x4 *>(lat_b + gather_offset(s, lane));
             }
         };
         u32x4 stg[2][kStageRows];
@@ -459,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         // Operands of one 16-entry k-step of tile `tile`: P (A, 32 heads x 16
         // entries per head tile) and V (B, 16 entries x 32 dims per column tile).
         auto pv_read = [&](int tile, int ks, bf16x8 (&pa)[2], bf16x8 (&vb)[4]) {
-            const uint8_t *kvt = sm.kv[tile % kRing];
+            const uint8_t *kvt = sm.kv[ring_slot(tile)];
             const uint8_t *pt = sm.p[tile & 1];
 #pragma unroll
             for (int a = 0; a < 2; ++a)
@@ -485,8 +445,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         // issued before the parking, so their latency overlaps it; the gathers
         // and the second k-step's reads follow the first k-step's products.
         auto o_step = [&](const int it, u32x4 (&st)[kStageRows]) {
-            const int tp = it - 1;
-            const bool pv = it >= 1;
+            const int tp = it - kPvBehind;
+            const bool pv = tp >= 0;
             int32_t f0 = 0, f1 = 0;
             bf16x8 pa[2], vb[4];
             if (pv) {
@@ -495,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
                 pv_read(tp, 0, pa, vb);
             }
             __builtin_amdgcn_sched_barrier(0);
-            stage_store(it + 2, st);
+            stage_store(it + kParkAhead, st);
             __builtin_amdgcn_sched_barrier(0);
             if (pv) {
 #pragma unroll
@@ -515,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
                 pv_mfma(pa, vb);
             }
             __builtin_amdgcn_sched_barrier(0);
-            stage_load(it + 4, st);
+            stage_load(it + kGatherAhead, st);
             __builtin_amdgcn_sched_barrier(0);
             if (pv) {
                 pv_read(tp, 1, pa, vb);
@@ -563,16 +523,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             for (int m = 0; m < 16; ++m)
                 v[m] = *reinterpret_cast<const f32x4 *>(blk + (2 * m + half) * kOutPitch + 4 * l32);
             const int dd = dv0 + 4 * l32;
-            if (splits == 1) {
+            // heads head0 + a*32 + half + 2m
+            Tout *ob = splits == 1
+                           ? out + out_offset(rowq, H, head0 + a * 32 + half, dd)
+                           : o_part + part_offset(prow, splits, split, H, head0 + a * 32 + half, dd);
 #pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    store_out4(out + (rowq * H + head0 + a * 32 + 2 * m + half) * kDv + dd, v[m]);
-            } else {
-#pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    store_out4(o_part + ((prow * splits + split) * H + head0 + a * 32 + 2 * m + half) *
-                                            kDv + dd, v[m]);
-            }
+            for (int m = 0; m < 16; ++m) store_out4(ob + m * kHeadPairStride, v[m]);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();  // block reused by the second half
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -600,33 +556,23 @@ __device__ __forceinline__ f32x4 load_out4<uint16_t>(const uint16_t *p) {
 // of 16 whose loads are all issued before any is used (clamped indices, zero
 // weight past the last split), merged online across batches, so a row costs
 // one memory latency per 16 splits.
-constexpr int kCombineBatch = 16;
-
 template <typename Tout>
 __global__ __launch_bounds__(256) void mla_combine_kernel(
     const Tout *__restrict__ o_part, const float *__restrict__ lse_part, int T, int H,
     int row0, int rows, int B, int splits, Tout *__restrict__ out, float *__restrict__ lse) {
     // workgroup = (query row, head pair); with a multiple of 8 rows the rows
     // map to XCDs as in the attention kernel, so the partials come from L2
-    const int hps = H / 2;
-    const int id = blockIdx.x;
-    int hp, qidx;
-    if ((rows * B) % 8 == 0) {
-        const int x = id & 7, j = id >> 3;
-        hp = j % hps;
-        qidx = 8 * (j / hps) + x;
-    } else {
-        hp = id % hps;
-        qidx = id / hps;
-    }
+    const CombineWork cw = combine_work_of(blockIdx.x, rows, B, H);
+    const int hp = cw.hp, qidx = cw.qidx;
     const int h = hp * 2 + (threadIdx.x >> 7);
     const int d = (threadIdx.x & 127) * 4;
     const int r = qidx % rows;
     const int b = qidx / rows;
     const size_t rowq = (size_t)b * T + row0 + r;
     const size_t prow = (size_t)b * rows + r;  // row of the launch's split partials
-    const float *lp = lse_part + prow * splits * H + h;  // split s at lp[s * H]
-    const Tout *op = o_part + (prow * splits * H + h) * kDv + d;  // split s at op[s * H * kDv]
+    // split s at lp[s * lse_split_stride] and op[s * part_split_stride]
+    const float *lp = lse_part + lse_part_offset(prow, splits, 0, H, h);
+    const Tout *op = o_part + part_offset(prow, splits, 0, H, h, d);
     float mx = -INFINITY, wsum = 0.0f;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int s0 = 0; s0 < splits; s0 += kCombineBatch) {
@@ -634,9 +580,9 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(
         f32x4 ov[kCombineBatch];
 #pragma unroll
         for (int j = 0; j < kCombineBatch; ++j) {
-            const size_t sc = (size_t)min(s0 + j, splits - 1);
-            ls[j] = lp[sc * H];
-            ov[j] = load_out4(op + sc * H * kDv);
+            const size_t sc = (size_t)combine_split(s0, j, splits);
+            ls[j] = lp[sc * lse_split_stride(H)];
+            ov[j] = load_out4(op + sc * part_split_stride(H));
         }
         float bmx = -INFINITY;
 #pragma unroll
@@ -656,21 +602,10 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(
         }
     }
     const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-    Tout *o = out + (rowq * H + h) * kDv + d;
+    Tout *o = out + out_offset(rowq, H, h, d);
 #pragma unroll
     for (int e = 0; e < 4; ++e) store_out(o + e, acc[e] * inv);
     if (lse && d == 0) lse[rowq * H + h] = wsum > 0.0f ? mx + __logf(wsum) : -INFINITY;
-}
-
-// Entry splits per query row: enough workgroups to cover the CUs, but at least
-// two tiles per split so the two-stage gather pipeline has work to overlap.
-int mla_splits(int B, int rows, int H, int k) {
-    const long long wgs = (long long)B * rows * (H / kHg);
-    const int max_splits = ceil_div(k, 4 * kKt);
-    long long s = (256 + wgs - 1) / wgs;
-    if (s > max_splits) s = max_splits;
-    if (s < 1) s = 1;
-    return (int)s;
 }
 
 }  // namespace
@@ -689,11 +624,9 @@ size_t mla_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int k) {
     const int top = min(T, kMaxGridY);
     for (int n = 1; n <= top; ++n) {
         if ((long long)B * n * hgs >= 256) break;
-        const int splits = mla_splits(B, n, d.num_heads, k);
-        if (splits > 1) {
-            const size_t need = (size_t)B * n * splits * d.num_heads * (kDv + 1) * 4 + 256;
-            total = need > total ? need : total;
-        }
+        const Plan p = launch_plan(B, n, d.num_heads, k);
+        const size_t need = launch_workspace_bytes(B, n, p.splits, d.num_heads, 4) + 256;
+        if (p.splits > 1) total = need > total ? need : total;
     }
     return total;
 }
@@ -705,10 +638,9 @@ hipError_t launch_mla(const dsa_attn_desc_t &d, const void *q, const void *kv,
     const int H = d.num_heads;
     for (int r0 = 0; r0 < rows; r0 += kMaxGridY) {
         const int n = min(kMaxGridY, rows - r0);
-        const int splits = mla_splits(B, n, H, k);
-        const int per_split = ceil_div(ceil_div(k, splits), kKt) * kKt;
-        const int used_splits = ceil_div(k, per_split);
-        const size_t part_elems = (size_t)B * n * used_splits * H * kDv;
+        const Plan p = launch_plan(B, n, H, k);
+        const int used_splits = p.splits, per_split = p.per_split;
+        const size_t pe = part_elems(B, n, used_splits, H);
         const long long nwg = (long long)(H / kHg) * used_splits * n * B;
         dim3 grid((unsigned)nwg);
         if (d.out_dtype == DSA_BF16)
@@ -717,14 +649,14 @@ hipError_t launch_mla(const dsa_attn_desc_t &d, const void *q, const void *kv,
                                idx, T, S, H, k, d.scale, row0 + r0, n, B, used_splits, per_split,
                                static_cast<uint16_t *>(out), lse,
                                static_cast<uint16_t *>(workspace),
-                               reinterpret_cast<float *>(static_cast<uint16_t *>(workspace) + part_elems),
+                               reinterpret_cast<float *>(static_cast<uint16_t *>(workspace) + pe),
                                q_pos, causal_tail ? 1 : 0);
         else
             hipLaunchKernelGGL(mla_attention_kernel<float>, grid, dim3(kThreads), 0, stream,
                                static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kv),
                                idx, T, S, H, k, d.scale, row0 + r0, n, B, used_splits, per_split,
                                static_cast<float *>(out), lse, static_cast<float *>(workspace),
-                               static_cast<float *>(workspace) + part_elems, q_pos,
+                               static_cast<float *>(workspace) + pe, q_pos,
                                causal_tail ? 1 : 0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -734,13 +666,13 @@ hipError_t launch_mla(const dsa_attn_desc_t &d, const void *q, const void *kv,
                 hipLaunchKernelGGL(mla_combine_kernel<uint16_t>, cg, dim3(256), 0, stream,
                                    static_cast<const uint16_t *>(workspace),
                                    reinterpret_cast<const float *>(
-                                       static_cast<const uint16_t *>(workspace) + part_elems),
+                                       static_cast<const uint16_t *>(workspace) + pe),
                                    T, H, row0 + r0, n, B, used_splits,
                                    static_cast<uint16_t *>(out), lse);
             else
                 hipLaunchKernelGGL(mla_combine_kernel<float>, cg, dim3(256), 0, stream,
                                    static_cast<const float *>(workspace),
-                                   static_cast<const float *>(workspace) + part_elems, T, H,
+                                   static_cast<const float *>(workspace) + pe, T, H,
                                    row0 + r0, n, B, used_splits,
                                    static_cast<float *>(out), lse);
             e = hipGetLastError();
