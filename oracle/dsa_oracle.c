@@ -29,10 +29,15 @@
 #define ORACLE_API __attribute__((visibility("default")))
 
 /* Absolute position of query row i of batch b: q_pos[b*T+i] if given, else
- * the last T positions of a length-S sequence (prefill T==S, decode T==1). */
+ * the last T positions of a length-S sequence (prefill T==S, decode T==1).
+ * The candidates of position t are the cached positions s <= t ([P1] section
+ * 2.1); the cache holds 0..S-1, so a position t >= S has the same candidates
+ * as t = S-1 and is taken as S-1 (the position convention of the library's
+ * interface).  A negative position has no candidates. */
 static int64_t query_position(const int64_t *q_pos, int64_t b, int64_t i,
                               int64_t T, int64_t S) {
-    return q_pos ? q_pos[b * T + i] : (S - T + i);
+    const int64_t t = q_pos ? q_pos[b * T + i] : (S - T + i);
+    return t >= S ? S - 1 : t;
 }
 
 /*

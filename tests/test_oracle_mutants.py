@@ -34,6 +34,8 @@ MUTANTS = {
     "not_normalised": ("for (int64_t d = 0; d < dv; ++d) o[d] /= denom;", ""),
     "mla_value_tail": ("    return kv + (b * S + s) * dqk;\n}\n\n/*\n * Attention restricted", "    return kv + (b * S + s) * dqk + (dqk - dv);\n}\n\n/*\n * Attention restricted"),
     "mha_key_head_transposed": ("if (form == 0) return kv + ((b * S + s) * H + h) * dqk;", "if (form == 0) return kv + ((b * S + s) * H + (H - 1 - h)) * dqk;"),
+    "warmup_target_head_sum": ("for (int64_t s = 0; s <= t; ++s) prow[s] /= total;", ""),
+    "position_not_clamped": ("return t >= S ? S - 1 : t;", "return t;"),
     "dense_excludes_self": ("for (int64_t s = 0; s <= t; ++s) {\n                    const double *key = key_row", "for (int64_t s = 0; s < t; ++s) {\n                    const double *key = key_row"),
 }
 

@@ -346,10 +346,52 @@ def test_warmup_target_is_head_mean_of_dense_weights(oracle):
     assert np.allclose(p[0], want, atol=1e-14, rtol=0)
 
 
-def test_head_mean_worked_number():
-    # section 5.3: eight head weights at (t=10, s=3) sum to 0.91 and average to 0.11375
-    a = [0.15, 0.02, 0.30, 0.05, 0.10, 0.01, 0.20, 0.08]
-    assert abs(sum(a) - 0.91) < 1e-15 and abs(sum(a) / 8 - 0.11375) < 1e-15
+def test_head_mean_worked_number(oracle):
+    """Section 5.3 numerical check: with 8 heads whose weights for query t=10
+    at key s=3 are 0.15, 0.02, 0.30, 0.05, 0.10, 0.01, 0.20, 0.08, the target
+    is p[10,3] = 0.91 / 8 = 0.11375.  Queries and one-hot keys are built so
+    that head h's softmax over s = 0..10 puts exactly that weight on s = 3
+    (the rest spread evenly), and the oracle's warm-up target must return the
+    printed number."""
+    a = np.array([0.15, 0.02, 0.30, 0.05, 0.10, 0.01, 0.20, 0.08])
+    H, T, scale = 8, 11, 0.25
+    # logits of head h at t = 10: log a_h at s = 3, log((1 - a_h)/10) elsewhere
+    logits = np.log((1.0 - a)[:, None] / 10.0) * np.ones((H, T))
+    logits[:, 3] = np.log(a)
+    K = np.zeros((1, T, H, T))
+    for s in range(T):
+        K[0, s, :, s] = 1.0            # one-hot key: q . K[s] picks entry s of q
+    q = np.zeros((1, T, H, T))
+    q[0, 10] = logits / scale
+    p = oracle.warmup_target(q, K, scale)
+    assert abs(p[0, 10, 3] - 0.11375) < 1e-14
+    assert abs(p[0, 10].sum() - 1.0) < 1e-14
+    # and the sparse-stage target over the full set is the same distribution
+    idx = np.arange(T, dtype=np.int32)[None, None, :].repeat(T, 1)
+    idx[0] = np.where(idx[0] <= np.arange(T)[:, None], idx[0], -1)
+    ps = oracle.sparse_target("mha", q, K, idx, scale)
+    assert abs(ps[0, 10, 3] - 0.11375) < 1e-14
+
+
+def test_positions_past_the_cache_are_the_last_one(oracle):
+    """A query position t >= S sees every cached position, as t = S-1 does
+    (the library's position convention): scores, selection and dense
+    attention are those of t = S-1."""
+    g = np.random.default_rng(8)
+    S, H, D = 12, 2, 3
+    q = g.integers(-3, 3, (1, 2, H, D), endpoint=True).astype(np.float64)
+    k = g.integers(-3, 3, (1, S, D), endpoint=True).astype(np.float64)
+    w = g.integers(0, 8, (1, 2, H), endpoint=True) / 8.0
+    past = np.array([[S + 3, S]])
+    last = np.array([[S - 1, S - 1]])
+    sc_past = oracle.indexer_scores(q, k, w, q_pos=past)
+    sc_last = oracle.indexer_scores(q, k, w, q_pos=last)
+    assert np.array_equal(sc_past, sc_last) and np.all(np.isfinite(sc_past))
+    assert np.array_equal(oracle.topk(sc_past, 5, q_pos=past), oracle.topk(sc_last, 5, q_pos=last))
+    qa, Ka, Va = _mha(T=2, H=2, d=4, dv=4, seed=3)
+    Ka, Va = torch.cat([Ka] * 6, 1), torch.cat([Va] * 6, 1)  # S = 12
+    assert np.array_equal(oracle.dense_causal_attention("mha", qa, Ka, Va, 0.5, q_pos=past),
+                          oracle.dense_causal_attention("mha", qa, Ka, Va, 0.5, q_pos=last))
 
 
 def test_indexer_kl_against_library(oracle):
