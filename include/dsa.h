@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 
 typedef enum {
     DSA_F32 = 0,      /* IEEE binary32 */
@@ -110,6 +110,23 @@ dsa_status_t dsa_indexer_scores(const void *q_idx, const void *k_idx, int idx_dt
                                 const float *w, const int32_t *q_pos, int B, int T, int S,
                                 int index_n_heads, int index_head_dim, float *scores,
                                 void *stream);
+
+/* Indexer flags of dsa_indexer_scores_ex. */
+enum {
+    /* Write only the candidates s <= t of each row; entries s > t are left
+     * as they were (dsa_topk never reads them).  This is what dsa_forward
+     * does with its score block. */
+    DSA_IDX_CAUSAL_ONLY = 1
+};
+
+/*
+ * dsa_indexer_scores with indexer flags (DSA_IDX_*; 0 is
+ * dsa_indexer_scores).  Unknown flag bits return DSA_ERR_UNSUPPORTED.
+ */
+dsa_status_t dsa_indexer_scores_ex(const void *q_idx, const void *k_idx, int idx_dtype,
+                                   const float *w, const int32_t *q_pos, int B, int T, int S,
+                                   int index_n_heads, int index_head_dim, int flags,
+                                   float *scores, void *stream);
 
 /*
  * Top-k selection, [P1] section 3.1: row i keeps the n_sel = min(k, t+1)

@@ -1,5 +1,7 @@
 """Build libdsa.so: every HIP source under csrc/ compiled for gfx950 with
-hipcc, then linked into one shared library placed next to this file.
+hipcc, then linked into one shared library placed next to this file; and
+libdsa_probes.so from probes/ (device peak probes the benchmark uses for its
+roofline fractions; not part of the forward path).
 
     python -m learned_sparse_attention_lightning_amd.build
 """
@@ -16,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
+PROBES = os.path.join(PKG, "probes")
+PROBE_LIB = os.path.join(PKG, "libdsa_probes.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -29,8 +33,8 @@ FLAGS = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=h
 EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(d=CSRC):
+    return sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
@@ -46,17 +50,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=jobs or min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     r = subprocess.run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int | None = None) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = sources()
+    probe_srcs = sources(PROBES)
+    with cf.ThreadPoolExecutor(max_workers=jobs or min(8, len(srcs) + len(probe_srcs))) as ex:
+        objs = list(ex.map(_compile, srcs + probe_srcs))
+    _link(objs[: len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     return LIB
 
 

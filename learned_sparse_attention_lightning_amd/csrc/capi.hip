@@ -13,8 +13,10 @@ using namespace dsa;
 
 constexpr size_t kAlign = 256;  // workspace carve-out alignment
 // The forward pass keeps one fp32 block of scores for a chunk of query rows;
-// this bounds that block (it then stays in the 256 MB last-level cache).
-constexpr size_t kScoreChunkBytes = 256ull << 20;
+// this bounds that block.  Larger chunks give the prefill indexer launches
+// with more workgroups (less tail per launch); the per-row top-k that reads
+// the block back runs at the same speed from 256 MiB to 1 GiB blocks.
+constexpr size_t kScoreChunkBytes = 1ull << 30;
 
 // Largest selection budget accepted (k may exceed S: the surplus slots hold -1).
 constexpr int kMaxTopk = 1 << 20;
@@ -85,6 +87,72 @@ size_t forward_workspace(const dsa_attn_desc_t *d, int B, int T, int S, int k) {
 
 dsa_status_t hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
+dsa_status_t check_forward(const dsa_attn_desc_t *desc, const void *q_idx, const void *k_idx,
+                           int idx_dtype, const float *w, const void *q, const void *kv,
+                           const void *v, const int32_t *q_pos, int B, int T, int S,
+                           int index_n_heads, int index_head_dim, int index_topk, int flags,
+                           const void *out, const int32_t *idx_out) {
+    dsa_status_t st = check_sizes(B, T, S, q_pos != nullptr);
+    if (st != DSA_OK) return st;
+    st = check_indexer(q_idx, k_idx, idx_dtype, w, index_n_heads, index_head_dim);
+    if (st != DSA_OK) return st;
+    st = check_attention(desc, q, kv, v, out);
+    if (st != DSA_OK) return st;
+    if (!valid_topk(index_topk)) return DSA_ERR_SHAPE;
+    if (flags & ~DSA_SEL_INCLUDE_CURRENT) return DSA_ERR_UNSUPPORTED;
+    if (idx_out && !aligned16(idx_out)) return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+// The three steps over chunks of query rows, in `workspace` (checked by the
+// caller to hold forward_workspace(...) bytes, 16-byte aligned).
+dsa_status_t forward_run(const dsa_attn_desc_t *desc, const void *q_idx, const void *k_idx,
+                         int idx_dtype, const float *w, const void *q, const void *kv,
+                         const void *v, const int32_t *q_pos, int B, int T, int S,
+                         int index_n_heads, int index_head_dim, int index_topk, int flags,
+                         void *out, int32_t *idx_out, void *workspace, hipStream_t s) {
+    const bool include_current = (flags & DSA_SEL_INCLUDE_CURRENT) != 0;
+    const int rows = forward_chunk_rows(B, T, S);
+    char *ws = static_cast<char *>(workspace);
+    float *score_block = reinterpret_cast<float *>(ws);
+    ws += round_up((size_t)B * rows * S * sizeof(float));
+    int32_t *sel = reinterpret_cast<int32_t *>(ws);
+    ws += round_up((size_t)B * T * index_topk * sizeof(int32_t));
+    void *topk_ws = ws;
+    ws += round_up(topk_workspace_bytes(B, rows, S, index_topk));
+    void *attn_ws = ws;
+    if (idx_out) sel = idx_out;
+
+    // A context no longer than the budget selects every causal position in
+    // every row (with or without the current-token flag): the indexer and
+    // the top-k are skipped and the attention runs over the whole prefix.
+    const bool dense = S <= index_topk;
+    const size_t batch_stride = (size_t)rows * S;
+    for (int row0 = 0; row0 < T; row0 += rows) {
+        const int n = T - row0 < rows ? T - row0 : rows;
+        hipError_t e;
+        if (dense) {
+            e = launch_select_all(q_pos, B, T, S, row0, n, index_topk, sel, s);
+        } else {
+            // the indexer launch also clears the top-k counters (a kernel, not
+            // a memset, so the step can be captured in a graph)
+            const size_t clear_words = topk_clear_words(B, n, S);
+            e = launch_indexer(q_idx, k_idx, idx_dtype, w, q_pos, B, T, S, index_n_heads,
+                               index_head_dim, row0, n, score_block, batch_stride, false,
+                               static_cast<uint32_t *>(topk_ws), clear_words, s);
+            if (e != hipSuccess) return DSA_ERR_HIP;
+            e = launch_topk(score_block, batch_stride, q_pos, B, T, S, row0, n, index_topk, sel,
+                            topk_ws, clear_words > 0, s, include_current);
+        }
+        if (e != hipSuccess) return DSA_ERR_HIP;
+        // the selection just written is min(k, t+1) positions then -1 per row
+        e = launch_attention(*desc, q, kv, v, sel, B, T, S, row0, n, index_topk, out, nullptr,
+                             attn_ws, s, q_pos, true);
+        if (e != hipSuccess) return DSA_ERR_HIP;
+    }
+    return DSA_OK;
+}
+
 }  // namespace
 
 DSA_EXPORT int dsa_abi_version(void) { return DSA_ABI_VERSION; }
@@ -120,19 +188,30 @@ DSA_EXPORT size_t dsa_workspace_bytes(int op, const dsa_attn_desc_t *desc, int B
     }
 }
 
-DSA_EXPORT dsa_status_t dsa_indexer_scores(const void *q_idx, const void *k_idx, int idx_dtype,
-                                           const float *w, const int32_t *q_pos, int B, int T,
-                                           int S, int index_n_heads, int index_head_dim,
-                                           float *scores, void *stream) {
+DSA_EXPORT dsa_status_t dsa_indexer_scores_ex(const void *q_idx, const void *k_idx,
+                                              int idx_dtype, const float *w,
+                                              const int32_t *q_pos, int B, int T, int S,
+                                              int index_n_heads, int index_head_dim, int flags,
+                                              float *scores, void *stream) {
     dsa_status_t st = check_sizes(B, T, S, q_pos != nullptr);
     if (st != DSA_OK) return st;
     if (!scores) return DSA_ERR_NULL;
     st = check_indexer(q_idx, k_idx, idx_dtype, w, index_n_heads, index_head_dim);
     if (st != DSA_OK) return st;
+    if (flags & ~DSA_IDX_CAUSAL_ONLY) return DSA_ERR_UNSUPPORTED;
     if (!aligned16(scores)) return DSA_ERR_ALIGN;
+    const bool write_masked = (flags & DSA_IDX_CAUSAL_ONLY) == 0;
     return hip_status(launch_indexer(q_idx, k_idx, idx_dtype, w, q_pos, B, T, S, index_n_heads,
-                                     index_head_dim, 0, T, scores, (size_t)T * S, true, nullptr,
-                                     0, (hipStream_t)stream));
+                                     index_head_dim, 0, T, scores, (size_t)T * S, write_masked,
+                                     nullptr, 0, (hipStream_t)stream));
+}
+
+DSA_EXPORT dsa_status_t dsa_indexer_scores(const void *q_idx, const void *k_idx, int idx_dtype,
+                                           const float *w, const int32_t *q_pos, int B, int T,
+                                           int S, int index_n_heads, int index_head_dim,
+                                           float *scores, void *stream) {
+    return dsa_indexer_scores_ex(q_idx, k_idx, idx_dtype, w, q_pos, B, T, S, index_n_heads,
+                                 index_head_dim, 0, scores, stream);
 }
 
 DSA_EXPORT dsa_status_t dsa_topk_ex(const float *scores, const int32_t *q_pos, int B, int T,
@@ -213,59 +292,16 @@ DSA_EXPORT dsa_status_t dsa_forward_ex(const dsa_attn_desc_t *desc, const void *
                                        int index_n_heads, int index_head_dim, int index_topk,
                                        int flags, void *out, int32_t *idx_out, void *workspace,
                                        size_t workspace_bytes, void *stream) {
-    dsa_status_t st = check_sizes(B, T, S, q_pos != nullptr);
+    dsa_status_t st = check_forward(desc, q_idx, k_idx, idx_dtype, w, q, kv, v, q_pos, B, T, S,
+                                    index_n_heads, index_head_dim, index_topk, flags, out,
+                                    idx_out);
     if (st != DSA_OK) return st;
-    st = check_indexer(q_idx, k_idx, idx_dtype, w, index_n_heads, index_head_dim);
-    if (st != DSA_OK) return st;
-    st = check_attention(desc, q, kv, v, out);
-    if (st != DSA_OK) return st;
-    if (!valid_topk(index_topk)) return DSA_ERR_SHAPE;
-    if (flags & ~DSA_SEL_INCLUDE_CURRENT) return DSA_ERR_UNSUPPORTED;
-    if (idx_out && !aligned16(idx_out)) return DSA_ERR_ALIGN;
     const size_t need = forward_workspace(desc, B, T, S, index_topk);
     if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return DSA_ERR_ALIGN;
-
-    hipStream_t s = (hipStream_t)stream;
-    const bool include_current = (flags & DSA_SEL_INCLUDE_CURRENT) != 0;
-    const int rows = forward_chunk_rows(B, T, S);
-    char *ws = static_cast<char *>(workspace);
-    float *score_block = reinterpret_cast<float *>(ws);
-    ws += round_up((size_t)B * rows * S * sizeof(float));
-    int32_t *sel = reinterpret_cast<int32_t *>(ws);
-    ws += round_up((size_t)B * T * index_topk * sizeof(int32_t));
-    void *topk_ws = ws;
-    ws += round_up(topk_workspace_bytes(B, rows, S, index_topk));
-    void *attn_ws = ws;
-    if (idx_out) sel = idx_out;
-
-    // A context no longer than the budget selects every causal position in
-    // every row (with or without the current-token flag): the indexer and
-    // the top-k are skipped and the attention runs over the whole prefix.
-    const bool dense = S <= index_topk;
-    const size_t batch_stride = (size_t)rows * S;
-    for (int row0 = 0; row0 < T; row0 += rows) {
-        const int n = T - row0 < rows ? T - row0 : rows;
-        hipError_t e;
-        if (dense) {
-            e = launch_select_all(q_pos, B, T, S, row0, n, index_topk, sel, s);
-        } else {
-            // the indexer launch also clears the top-k counters
-            const size_t clear_words = topk_clear_words(B, n, S);
-            e = launch_indexer(q_idx, k_idx, idx_dtype, w, q_pos, B, T, S, index_n_heads,
-                               index_head_dim, row0, n, score_block, batch_stride, false,
-                               static_cast<uint32_t *>(topk_ws), clear_words, s);
-            if (e != hipSuccess) return DSA_ERR_HIP;
-            e = launch_topk(score_block, batch_stride, q_pos, B, T, S, row0, n, index_topk, sel,
-                            topk_ws, clear_words > 0, s, include_current);
-        }
-        if (e != hipSuccess) return DSA_ERR_HIP;
-        // the selection just written is min(k, t+1) positions then -1 per row
-        e = launch_attention(*desc, q, kv, v, sel, B, T, S, row0, n, index_topk, out, nullptr,
-                             attn_ws, s, q_pos, true);
-        if (e != hipSuccess) return DSA_ERR_HIP;
-    }
-    return DSA_OK;
+    return forward_run(desc, q_idx, k_idx, idx_dtype, w, q, kv, v, q_pos, B, T, S,
+                       index_n_heads, index_head_dim, index_topk, flags, out, idx_out, workspace,
+                       (hipStream_t)stream);
 }
 
 DSA_EXPORT dsa_status_t dsa_forward(const dsa_attn_desc_t *desc, const void *q_idx,

@@ -25,12 +25,14 @@ DTYPE_CODES = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16,
                torch.float8_e4m3fn: DSA_FP8_E4M3}
 NAME_CODES = {"f32": DSA_F32, "bf16": DSA_BF16, "fp8": DSA_FP8_E4M3}
 FORM_CODES = {"mha": DSA_MHA, "mla": DSA_MLA}
-EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_indexer_scores", "dsa_topk",
+EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_indexer_scores",
+            "dsa_indexer_scores_ex", "dsa_topk",
             "dsa_topk_ex", "dsa_sparse_attention", "dsa_sparse_attention_ex", "dsa_forward",
             "dsa_forward_ex",
             "dsa_indexer_kl", "dsa_workspace_bytes")
 DSA_SEL_INCLUDE_CURRENT = 1
 DSA_ATTN_CAUSAL_PREFIX = 1
+DSA_IDX_CAUSAL_ONLY = 1
 
 
 class DSAError(RuntimeError):
@@ -70,6 +72,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.dsa_status_string.argtypes = [_i]
     lib.dsa_indexer_scores.restype = _i
     lib.dsa_indexer_scores.argtypes = [_p, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p, _p]
+    lib.dsa_indexer_scores_ex.restype = _i
+    lib.dsa_indexer_scores_ex.argtypes = [_p, _p, _i, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p]
     lib.dsa_topk.restype = _i
     lib.dsa_topk.argtypes = [_p, _p, _i, _i, _i, _i, _p, _p, ctypes.c_size_t, _p]
     lib.dsa_topk_ex.restype = _i
@@ -145,8 +149,10 @@ def workspace_bytes(op: int, desc: AttnDesc | None, B: int, T: int, S: int, H_I:
     return n
 
 
-def dsa_indexer_scores(q_idx, k_idx, w, q_pos=None, scores=None, stream=None):
-    """scores [B,T,S] fp32 = sum_j w ReLU(q_idx . k_idx) for s <= t, -inf after."""
+def dsa_indexer_scores(q_idx, k_idx, w, q_pos=None, scores=None, stream=None,
+                       causal_only=False):
+    """scores [B,T,S] fp32 = sum_j w ReLU(q_idx . k_idx) for s <= t, -inf after.
+    causal_only: entries s > t are left unwritten (dsa_indexer_scores_ex)."""
     _need(q_idx, "q_idx", ndim=4)
     _need(k_idx, "k_idx", dtype=q_idx.dtype, ndim=3)
     _need(w, "w", dtype=torch.float32, ndim=3)
@@ -157,9 +163,14 @@ def dsa_indexer_scores(q_idx, k_idx, w, q_pos=None, scores=None, stream=None):
     _need(scores, "scores", dtype=torch.float32, ndim=3)
     if q_pos is not None:
         _need(q_pos, "q_pos", dtype=torch.int32, ndim=2)
-    _check(load().dsa_indexer_scores(_ptr(q_idx), _ptr(k_idx), DTYPE_CODES[q_idx.dtype],
-                                     _ptr(w), _ptr(q_pos), B, T, S, H, D, _ptr(scores),
-                                     _stream(stream)))
+    if causal_only:
+        _check(load().dsa_indexer_scores_ex(_ptr(q_idx), _ptr(k_idx), DTYPE_CODES[q_idx.dtype],
+                                            _ptr(w), _ptr(q_pos), B, T, S, H, D,
+                                            DSA_IDX_CAUSAL_ONLY, _ptr(scores), _stream(stream)))
+    else:
+        _check(load().dsa_indexer_scores(_ptr(q_idx), _ptr(k_idx), DTYPE_CODES[q_idx.dtype],
+                                         _ptr(w), _ptr(q_pos), B, T, S, H, D, _ptr(scores),
+                                         _stream(stream)))
     return scores
 
 

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsa_abi_version() == 2
+    assert lib.dsa_abi_version() == 3
     for s in range(8):
         assert lib.dsa_status_string(s)
     assert lib.dsa_status_string(99) == b"unknown status"
@@ -55,8 +55,10 @@ def test_workspace_sizes(lib):
     bad = ctypes.c_size_t(-1).value
     assert ws(dsa.DSA_OP_TOPK, 1, 16, 16, 2, 2, 3) != bad
     assert ws(dsa.DSA_OP_FORWARD, 1, 4096, 4096, 64, 128, 2048) >= 4096 * 4096 * 4
-    # the score block is bounded for long prefill
-    assert ws(dsa.DSA_OP_FORWARD, 1, 32768, 32768, 64, 128, 2048) < (1 << 30)
+    # the score block is bounded (1 GiB) for long prefill: 32K and 128K
+    # contexts need the score block, the selection and a little more
+    assert ws(dsa.DSA_OP_FORWARD, 1, 32768, 32768, 64, 128, 2048) < (1 << 30) + (512 << 20)
+    assert ws(dsa.DSA_OP_FORWARD, 1, 131072, 131072, 64, 128, 2048) < (3 << 30)
     assert ws(dsa.DSA_OP_FORWARD, 1, 16, 16, 2, 2, 17) != bad  # k > S is allowed
     assert ws(dsa.DSA_OP_FORWARD, 1, 16, 16, 2, 2, (1 << 20) + 1) == bad
     assert ws(dsa.DSA_OP_FORWARD, 0, 16, 16, 2, 2, 3) == bad
@@ -76,6 +78,13 @@ def test_indexer_argument_checks(lib):
     assert f(A, A, 1, A, None, 1, 4, 4, 128, 256, A, None) == UNSUP
     assert f(M, A, 1, A, None, 1, 4, 4, 64, 128, A, None) == ALIGN
     assert f(A, A, 1, A, None, 1, 4, 4, 64, 128, M, None) == ALIGN
+
+
+def test_indexer_ex_flags(lib):
+    f = lib.dsa_indexer_scores_ex
+    assert f(A, A, 1, A, None, 1, 4, 4, 64, 128, 2, A, None) == UNSUP   # unknown flag bit
+    assert f(None, A, 1, A, None, 1, 4, 4, 64, 128, 1, A, None) == NULL
+    assert f(A, A, 1, A, None, 1, 4, 4, 64, 128, 1, M, None) == ALIGN
 
 
 def test_topk_argument_checks(lib):

@@ -126,6 +126,24 @@ def test_indexer_signed_weights_and_max_magnitude():
     assert torch.all(torch.isneginf(sc[0][~low]))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_indexer_causal_only_leaves_the_tail(dtype):
+    """dsa_indexer_scores_ex with DSA_IDX_CAUSAL_ONLY (the forward pass's
+    launch): candidates s <= t exact, entries s > t untouched."""
+    B, S, H, D = 1, 3000, 64, 128
+    for T, pos in ((40, torch.arange(2000, 2040, dtype=torch.int32).view(1, -1)),
+                   (5, torch.tensor([[2999, 0, 31, 1000, 2048]], dtype=torch.int32)),
+                   (1, torch.tensor([[1777]], dtype=torch.int32))):
+        q, k, wt = _int_indexer(B, T, S, H, D, dtype, seed=T)
+        sc = torch.full((B, T, S), 7.5, dtype=torch.float32, device=DEV)
+        dsa.dsa_indexer_scores(q, k, wt, q_pos=pos.to(DEV), scores=sc, causal_only=True)
+        ref = oracle.indexer_scores(q, k, wt, q_pos=pos)
+        g = sc.cpu().numpy().astype(np.float64)
+        tail = np.isneginf(ref)
+        assert np.all(g[tail] == 7.5), f"T={T}: an entry past t was written"
+        assert np.array_equal(g[~tail], ref[~tail]), f"T={T}: scores differ"
+
+
 def test_indexer_c1_sampled_rows():
     w = configs.get("c1")
     q, k, wt = synth.indexer_inputs(w, device=DEV)
@@ -301,21 +319,24 @@ def test_forward_c0_all_rows():
     assert max_abs_err(out, ref) <= TOL["f32"]
 
 
-def test_forward_c1_sets_all_rows_outputs_sampled():
+@pytest.mark.timeout(600)
+def test_forward_c1_every_row():
+    """The 4K MHA prefill: oracle scores, oracle top-k and oracle attention on
+    every row, against the forward pass's selection and output and the
+    indexer's scores."""
     w = configs.get("c1")
     x, idx, out = _forward(w)
     sc = dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"])
-    rows = [0, 5, 2046, 2047, 2048, 4095]
-    ref_rows = oracle.indexer_scores(x["q_idx"][:, rows], x["k_idx"], x["w"][:, rows],
-                                     q_pos=np.array([rows]))
-    _assert_scores_equal(sc[:, rows], ref_rows, "c1 forward scores")
-    _say("c1: oracle top-k over every row")
-    ref_idx = oracle.topk(sc, w.index_topk)
+    _say("c1: oracle scores over every row")
+    ref_sc = oracle.indexer_scores(x["q_idx"], x["k_idx"], x["w"])
+    _assert_scores_equal(sc, ref_sc, "c1 scores")
+    ref_idx = oracle.topk(ref_sc, w.index_topk)
     assert_selection_equal(idx, ref_idx, "c1")
-    sample = [0, 1, 100, 2047, 2048, 3333, 4095]
-    ref = oracle.sparse_attention("mha", x["q"][:, sample], x["kv"], x["v"],
-                                  ref_idx[:, sample], w.scale)
-    assert max_abs_err(out[:, sample], ref) <= TOL["bf16"]
+    _say("c1: oracle attention over every row")
+    ref = oracle.sparse_attention("mha", x["q"], x["kv"], x["v"], ref_idx, w.scale)
+    err = max_abs_err(out, ref)
+    _say(f"c1: max-abs err {err:.3e} over all {w.T} rows")
+    assert err <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("name", ["c3", "c4"])
@@ -329,6 +350,27 @@ def test_forward_decode_full(name):
     err = max_abs_err(out, ref)
     _say(f"{name}: max-abs err {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+def test_positions_past_the_cache():
+    """A query position t >= S is taken as S-1 (every cached position is a
+    candidate): indexer, top-k and attention against the oracle, which
+    applies the same convention."""
+    B, T, S, H, D, k = 2, 3, 3000, 64, 128, 2048
+    pos = torch.tensor([[S, S + 7, S - 1], [2 * S, 5, S + 1]], dtype=torch.int32)
+    q, kk, wt = _int_indexer(B, T, S, H, D, "bf16", seed=41)
+    sc = dsa.dsa_indexer_scores(q, kk, wt, q_pos=pos.to(DEV))
+    ref_sc = oracle.indexer_scores(q, kk, wt, q_pos=pos)
+    _assert_scores_equal(sc, ref_sc, "past the cache")
+    idx = dsa.dsa_topk(sc, k, q_pos=pos.to(DEV))
+    ref_idx = oracle.topk(ref_sc, k, q_pos=pos)
+    assert_selection_equal(idx, ref_idx, "past the cache")
+    w = configs.get("c2").with_(name="past", B=B, T=T, S=S, index_topk=k)
+    x = synth.make_inputs(w, device=DEV, seed=42)
+    out = dsa.dsa_sparse_attention(dsa.desc_for(w), x["q"], x["kv"], None, idx,
+                                   causal_prefix=True, q_pos=pos.to(DEV))
+    ref = oracle.sparse_attention("mla", x["q"], x["kv"], None, ref_idx, w.scale, d_v=w.d_v)
+    assert max_abs_err(out, ref) <= TOL["bf16"]
 
 
 def test_forward_repeatable_bitwise():
@@ -386,40 +428,72 @@ def test_mla_mfma_empty_and_single_rows():
     assert max_abs_err(out[:, 2:], ref) <= TOL["bf16"]
 
 
+def stratified_rows(T: int, n: int, k: int, seed: int) -> list:
+    """n query rows spread over 0..T-1: one random row in each of n - 8
+    equal strata, plus the edges (0, 1, k-1, k, k+1, T/2, T-2, T-1)."""
+    g = np.random.default_rng(seed)
+    m = n - 8
+    edges = np.linspace(0, T, m + 1).astype(np.int64)
+    rows = {int(g.integers(edges[j], max(edges[j] + 1, edges[j + 1]))) for j in range(m)}
+    rows |= {0, 1, k - 1, k, k + 1, T // 2, T - 2, T - 1}
+    return sorted(r for r in rows if 0 <= r < T)
+
+
+def check_prefill_every_row(w, x, idx, out, n_sample, chunk_rows, seed):
+    """Selection of every row: the oracle's top-k over the exact fp32 score
+    rows the GPU indexer produces, chunk by chunk (scores are exact, so these
+    are the oracle's scores wherever the sample below checks them).  On a
+    stratified sample of rows: the oracle's own scores (bit-exact against the
+    GPU's), its top-k and its attention output."""
+    T, S, k = w.T, w.S, w.index_topk
+    rows = stratified_rows(T, n_sample, k, seed)
+    sample_scores = {}
+    for r0 in range(0, T, chunk_rows):
+        r1 = min(T, r0 + chunk_rows)
+        pos = torch.arange(S - T + r0, S - T + r1, dtype=torch.int32, device=DEV).view(1, -1)
+        sc = dsa.dsa_indexer_scores(x["q_idx"][:, r0:r1], x["k_idx"], x["w"][:, r0:r1],
+                                    q_pos=pos)
+        sc_h = sc.cpu()
+        ref_idx = oracle.topk(sc_h, k, q_pos=pos.cpu())
+        assert_selection_equal(idx[:, r0:r1], ref_idx, f"{w.name} rows {r0}..{r1 - 1}")
+        for r in rows:
+            if r0 <= r < r1:
+                sample_scores[r] = sc_h[:, r - r0].numpy().astype(np.float64)
+        del sc, sc_h
+        if r0 // chunk_rows % 16 == 0:
+            _say(f"{w.name}: selections of rows {r0}..{r1 - 1} equal the oracle's top-k")
+    _say(f"{w.name}: oracle scores, top-k and attention on {len(rows)} stratified rows")
+    pos = np.array([[S - T + r for r in rows]])
+    ref_sc = oracle.indexer_scores(x["q_idx"][:, rows], x["k_idx"], x["w"][:, rows], q_pos=pos)
+    got = np.stack([sample_scores[r] for r in rows], axis=1)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref_sc)), f"{w.name}: mask differs"
+    fin = np.isfinite(ref_sc)
+    assert np.array_equal(got[fin], ref_sc[fin]), f"{w.name}: sampled scores differ"
+    ref_idx = oracle.topk(ref_sc, k, q_pos=pos)
+    assert_selection_equal(idx[:, rows], ref_idx, f"{w.name} sampled rows")
+    ref = oracle.sparse_attention("mla", x["q"][:, rows], x["kv"], None, ref_idx, w.scale,
+                                  d_v=w.d_v)
+    err = max_abs_err(out[:, rows], ref)
+    _say(f"{w.name}: max-abs err {err:.3e} over {len(rows)} rows")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["c2", "c2-fp8"])
-def test_forward_c2_sampled_rows(name):
+def test_forward_c2_every_row(name):
     w = configs.get(name)
     x, idx, out = _forward(w)
-    rows = [0, 1, 2047, 2048, 2049, 4095, 4096, 16383, 30000, 32767]
-    _say(f"c2: oracle over rows {rows}")
-    pos = np.array([rows])
-    sc = oracle.indexer_scores(x["q_idx"][:, rows], x["k_idx"], x["w"][:, rows], q_pos=pos)
-    ref_idx = oracle.topk(sc, w.index_topk, q_pos=pos)
-    assert_selection_equal(idx[:, rows], ref_idx, "c2")
-    ref = oracle.sparse_attention("mla", x["q"][:, rows], x["kv"], None, ref_idx, w.scale,
-                                  d_v=w.d_v)
-    err = max_abs_err(out[:, rows], ref)
-    _say(f"c2: max-abs err {err:.3e}")
-    assert err <= TOL["bf16"]
+    check_prefill_every_row(w, x, idx, out, n_sample=256, chunk_rows=2048, seed=2)
 
 
-def test_forward_p128k_sampled_rows():
+@pytest.mark.timeout(1200)
+def test_forward_p128k_every_row():
     """128K-context prefill: the forward pass runs the rows in chunks (the
-    scores of one chunk at a time); sampled rows across the sequence, at chunk
-    and top-k boundaries, against the oracle."""
+    scores of one chunk at a time); every row's selection against the
+    oracle's top-k, and scores and outputs on 128 stratified rows."""
     w = configs.get("p128k")
     x, idx, out = _forward(w, seed=11)
-    rows = [0, 2047, 2048, 65535, 65536, 100000, 131071]
-    _say(f"p128k: oracle over rows {rows}")
-    pos = np.array([rows])
-    sc = oracle.indexer_scores(x["q_idx"][:, rows], x["k_idx"], x["w"][:, rows], q_pos=pos)
-    ref_idx = oracle.topk(sc, w.index_topk, q_pos=pos)
-    assert_selection_equal(idx[:, rows], ref_idx, "p128k")
-    ref = oracle.sparse_attention("mla", x["q"][:, rows], x["kv"], None, ref_idx, w.scale,
-                                  d_v=w.d_v)
-    err = max_abs_err(out[:, rows], ref)
-    _say(f"p128k: max-abs err {err:.3e}")
-    assert err <= TOL["bf16"]
+    check_prefill_every_row(w, x, idx, out, n_sample=128, chunk_rows=1024, seed=3)
     del x, idx, out
     torch.cuda.empty_cache()
 

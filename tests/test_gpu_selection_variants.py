@@ -101,10 +101,13 @@ def _oracle_forward(w, x, include_current):
     return ref_idx, ref
 
 
+# 128 heads run the MLA matrix-core kernel; 16 heads the gather kernel
 CURRENT_CASES = {
-    "mla-prefill": ("c2", dict(B=2, T=700, S=700, index_topk=64, num_heads=16)),
+    "mla-prefill-h16": ("c2", dict(B=2, T=700, S=700, index_topk=64, num_heads=16)),
+    "mla-prefill-h128": ("c2", dict(B=2, T=700, S=700, index_topk=64)),
     "mha-prefill": ("c1", dict(B=1, T=1500, S=1500, index_topk=256)),
-    "mla-decode-fp8": ("c4", dict(B=2, T=1, S=40000, num_heads=16)),
+    "mla-decode-fp8-h16": ("c4", dict(B=2, T=1, S=40000, num_heads=16)),
+    "mla-decode-fp8-h128": ("c4", dict(B=2, T=1, S=40000)),
 }
 
 
@@ -123,10 +126,13 @@ def test_forward_include_current(case):
 
 
 DENSE_CASES = {
-    "mla-n1000-k2048": ("c2", dict(B=1, T=1000, S=1000, index_topk=2048, num_heads=16)),
-    "mla-k-equals-n": ("c2", dict(B=2, T=256, S=256, index_topk=256, num_heads=16)),
+    "mla-n1000-k2048-h16": ("c2", dict(B=1, T=1000, S=1000, index_topk=2048, num_heads=16)),
+    "mla-n1000-k2048-h128": ("c2", dict(B=1, T=1000, S=1000, index_topk=2048)),
+    "mla-k-equals-n-h16": ("c2", dict(B=2, T=256, S=256, index_topk=256, num_heads=16)),
+    "mla-k-equals-n-h128": ("c2", dict(B=2, T=256, S=256, index_topk=256)),
     "mha-n777-k1024": ("c1", dict(B=1, T=777, S=777, index_topk=1024)),
-    "mla-decode-n1500": ("c4", dict(B=3, T=1, S=1500, num_heads=16)),
+    "mla-decode-n1500-h16": ("c4", dict(B=3, T=1, S=1500, num_heads=16)),
+    "mla-decode-n1500-h128": ("c4", dict(B=3, T=1, S=1500)),
 }
 
 
@@ -155,16 +161,37 @@ def test_forward_dense_when_context_within_budget(case):
     assert torch.equal(idx2, idx) and torch.equal(out2, out)
 
 
-@pytest.mark.parametrize("case", ["prefill", "decode-splits"])
+def test_forward_dense_limit_2048_h128():
+    """The dense-limit workload as benchmarked (n = k = 2048, 128 heads): the
+    selection fill on every row and the matrix-core attention against the
+    oracle's textbook dense causal attention on a stratified row sample."""
+    w = configs.get("short2k")
+    x, idx, out = _run_forward(w, 23, False)
+    g = idx.cpu().numpy()
+    for i in range(w.T):
+        assert np.array_equal(g[0, i, : i + 1], np.arange(i + 1)) and np.all(g[0, i, i + 1:] == -1)
+    rows = sorted({0, 1, 31, 32, 1000, 2046, 2047} | set(range(3, 2047, 41)))
+    _say(f"dense limit 2048 x 128 heads: oracle dense attention on {len(rows)} rows")
+    ref = oracle.dense_causal_attention("mla", x["q"][:, rows], x["kv"], None, w.scale,
+                                        d_v=w.d_v, q_pos=np.array([rows]))
+    err = max_abs_err(out[:, rows], ref)
+    _say(f"dense limit 2048: max-abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("case", ["prefill-h32", "decode-splits-h16", "prefill-h128",
+                                  "decode-splits-h128"])
 def test_attention_causal_prefix_matches_plain(case):
     """Stopping at each row's selected count (dsa_sparse_attention_ex with
     DSA_ATTN_CAUSAL_PREFIX) skips only empty tiles: outputs and lse are
     bitwise those of the plain call, and both match the oracle."""
-    if case == "prefill":
-        w = configs.get("c2").with_(name="prefix", B=1, T=3000, S=3000, num_heads=32)
+    heads = int(case.rsplit("-h", 1)[1])
+    if case.startswith("prefill"):
+        w = configs.get("c2").with_(name="prefix", B=1, T=3000, S=3000, num_heads=heads)
         pos = None
     else:
-        w = configs.get("c4").with_(name="prefix-dec", B=4, T=1, S=3000, num_heads=16)
+        # t < k leaves whole entry splits empty (each runs one masked tile)
+        w = configs.get("c4").with_(name="prefix-dec", B=4, T=1, S=3000, num_heads=heads)
         pos = torch.tensor([[2999], [100], [2047], [0]], dtype=torch.int32, device=DEV)
     x = synth.make_inputs(w, device=DEV, seed=29)
     sc = dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"], q_pos=pos)
@@ -177,10 +204,12 @@ def test_attention_causal_prefix_matches_plain(case):
                                     causal_prefix=True, q_pos=pos)
     torch.cuda.synchronize()
     assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
-    rows = [0, 1, 2047, w.T - 1] if w.T > 1 else [0]
-    ref = oracle.sparse_attention("mla", x["q"][:, rows], x["kv"], None, idx[:, rows].cpu(),
-                                  w.scale, d_v=w.d_v)
+    rows = [0, 1, 100, 2046, 2047, 2048, w.T - 1] if w.T > 1 else [0]
+    ref, ref_lse = oracle.sparse_attention("mla", x["q"][:, rows], x["kv"], None,
+                                           idx[:, rows].cpu(), w.scale, d_v=w.d_v,
+                                           with_lse=True)
     assert max_abs_err(out1[:, rows], ref) <= TOL["bf16"]
+    assert np.abs(lse1[:, rows].cpu().numpy() - ref_lse).max() < 1e-3
 
 
 def test_forward_include_current_c4_full():
