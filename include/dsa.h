@@ -22,9 +22,11 @@
  * --------------------------------
  * Memory.  Every tensor argument is caller-owned DEVICE memory (for instance a
  *   torch tensor's data pointer), dense row-major in the layout given, and
- *   16-byte aligned.  The library allocates nothing, keeps no pointer after a
- *   call returns and holds no mutable global state.  Buffers must stay alive
- *   until the work queued on `stream` has finished.
+ *   16-byte aligned.  The library allocates nothing and keeps no pointer
+ *   after a call returns.  Its only mutable global state is the scratch
+ *   array of dsa_forward_ex_noalloc (below) and the per-device address of
+ *   that array.  Buffers must stay alive until the work queued on `stream`
+ *   has finished.
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
  *   stream).  Every call only enqueues work; none synchronises the host.
  * Positions.  q_pos [B,T] int32 gives the absolute position t of each query
@@ -231,6 +233,30 @@ dsa_status_t dsa_forward_ex(const dsa_attn_desc_t *desc, const void *q_idx, cons
                             int index_n_heads, int index_head_dim, int index_topk, int flags,
                             void *out, int32_t *idx_out, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/*
+ * dsa_forward_ex without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The intermediate buffers (the score
+ * block, the selection when idx_out is NULL, the top-k counters and the
+ * attention's split partials) live in a static device array of
+ * DSA_NOALLOC_SCRATCH_BYTES (128 MiB) that each GPU the library runs on holds
+ * until the process ends; the call itself allocates nothing.  Sizes whose
+ * dsa_workspace_bytes(DSA_OP_FORWARD, ...) exceed that return
+ * DSA_ERR_WORKSPACE before anything is enqueued (the decode workloads fit:
+ * 8 x 131072 and 64 x 32768 contexts at k = 2048, 128 heads).  Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (several
+ * streams, several host threads) race and must be serialised by the caller;
+ * the array keeps the last call's contents (whatever must start at zero is
+ * cleared by the call's own kernels).  Results equal dsa_forward_ex's.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (128u << 20)
+dsa_status_t dsa_forward_ex_noalloc(const dsa_attn_desc_t *desc, const void *q_idx,
+                                    const void *k_idx, int idx_dtype, const float *w,
+                                    const void *q, const void *kv, const void *v,
+                                    const int32_t *q_pos, int B, int T, int S,
+                                    int index_n_heads, int index_head_dim, int index_topk,
+                                    int flags, void *out, int32_t *idx_out, void *stream);
 
 /*
  * Forward value of the indexer's distillation loss over a selected set,

@@ -3,6 +3,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "dsa_internal.h"
 
 #define DSA_EXPORT extern "C" __attribute__((visibility("default")))
@@ -86,6 +88,32 @@ size_t forward_workspace(const dsa_attn_desc_t *d, int B, int T, int S, int k) {
 }
 
 dsa_status_t hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+// ---- scratch of the allocation-free entry point (dsa_forward_ex_noalloc) --
+// Each GPU the library runs on holds its own copy of this array, allocated
+// with the code object and kept until the process ends.  Host code never uses
+// the array's name as an address: the device address is resolved once per
+// device with hipGetSymbolAddress and kept below.
+constexpr size_t kScratchBytes = (size_t)DSA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// Device address of the current device's scratch array.
+dsa_status_t scratch_of_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DSA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSA_OK;
+}
 
 dsa_status_t check_forward(const dsa_attn_desc_t *desc, const void *q_idx, const void *k_idx,
                            int idx_dtype, const float *w, const void *q, const void *kv,
@@ -301,6 +329,26 @@ DSA_EXPORT dsa_status_t dsa_forward_ex(const dsa_attn_desc_t *desc, const void *
     if (!aligned16(workspace)) return DSA_ERR_ALIGN;
     return forward_run(desc, q_idx, k_idx, idx_dtype, w, q, kv, v, q_pos, B, T, S,
                        index_n_heads, index_head_dim, index_topk, flags, out, idx_out, workspace,
+                       (hipStream_t)stream);
+}
+
+DSA_EXPORT dsa_status_t dsa_forward_ex_noalloc(const dsa_attn_desc_t *desc, const void *q_idx,
+                                               const void *k_idx, int idx_dtype, const float *w,
+                                               const void *q, const void *kv, const void *v,
+                                               const int32_t *q_pos, int B, int T, int S,
+                                               int index_n_heads, int index_head_dim,
+                                               int index_topk, int flags, void *out,
+                                               int32_t *idx_out, void *stream) {
+    dsa_status_t st = check_forward(desc, q_idx, k_idx, idx_dtype, w, q, kv, v, q_pos, B, T, S,
+                                    index_n_heads, index_head_dim, index_topk, flags, out,
+                                    idx_out);
+    if (st != DSA_OK) return st;
+    if (forward_workspace(desc, B, T, S, index_topk) > kScratchBytes) return DSA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != DSA_OK) return st;
+    return forward_run(desc, q_idx, k_idx, idx_dtype, w, q, kv, v, q_pos, B, T, S,
+                       index_n_heads, index_head_dim, index_topk, flags, out, idx_out, ws,
                        (hipStream_t)stream);
 }
 

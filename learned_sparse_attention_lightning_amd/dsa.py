@@ -28,7 +28,7 @@ FORM_CODES = {"mha": DSA_MHA, "mla": DSA_MLA}
 EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_indexer_scores",
             "dsa_indexer_scores_ex", "dsa_topk",
             "dsa_topk_ex", "dsa_sparse_attention", "dsa_sparse_attention_ex", "dsa_forward",
-            "dsa_forward_ex",
+            "dsa_forward_ex", "dsa_forward_ex_noalloc",
             "dsa_indexer_kl", "dsa_workspace_bytes")
 DSA_SEL_INCLUDE_CURRENT = 1
 DSA_ATTN_CAUSAL_PREFIX = 1
@@ -90,6 +90,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.dsa_forward_ex.restype = _i
     lib.dsa_forward_ex.argtypes = [ctypes.POINTER(AttnDesc), _p, _p, _i, _p, _p, _p, _p, _p,
                                    _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, ctypes.c_size_t, _p]
+    lib.dsa_forward_ex_noalloc.restype = _i
+    lib.dsa_forward_ex_noalloc.argtypes = [ctypes.POINTER(AttnDesc), _p, _p, _i, _p, _p, _p, _p,
+                                           _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p]
     lib.dsa_indexer_kl.restype = _i
     lib.dsa_indexer_kl.argtypes = [ctypes.POINTER(AttnDesc), _p, _p, _p, _p, _p, _i, _i, _i, _i,
                                    _p, _p]
@@ -263,6 +266,32 @@ def dsa_forward(desc: AttnDesc, q_idx, k_idx, w, q, kv, v, k: int, q_pos=None, o
                                   DTYPE_CODES[q_idx.dtype], _ptr(w), _ptr(q), _ptr(kv), _ptr(v),
                                   _ptr(q_pos), B, T, S, H_I, D_I, k, _ptr(out), _ptr(idx_out),
                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def dsa_forward_noalloc(desc: AttnDesc, q_idx, k_idx, w, q, kv, v, k: int, q_pos=None,
+                        out=None, idx_out=None, stream=None, include_current=False):
+    """dsa_forward through dsa_forward_ex_noalloc: no workspace, the library's
+    per-device scratch array instead (sizes up to its 128 MiB)."""
+    _need(q_idx, "q_idx", ndim=4)
+    _need(k_idx, "k_idx", dtype=q_idx.dtype, ndim=3)
+    _need(w, "w", dtype=torch.float32, ndim=3)
+    _need(q, "q", ndim=4)
+    _need(kv, "kv", dtype=q.dtype)
+    B, T, H_I, D_I = q_idx.shape
+    S = k_idx.shape[1]
+    odt = {DSA_F32: torch.float32, DSA_BF16: torch.bfloat16}[desc.out_dtype]
+    if out is None:
+        out = torch.empty((B, T, desc.num_heads, desc.d_v), dtype=odt, device=q.device)
+    if idx_out is not None:
+        _need(idx_out, "idx_out", dtype=torch.int32, ndim=3)
+    if q_pos is not None:
+        _need(q_pos, "q_pos", dtype=torch.int32, ndim=2)
+    _check(load().dsa_forward_ex_noalloc(ctypes.byref(desc), _ptr(q_idx), _ptr(k_idx),
+                                         DTYPE_CODES[q_idx.dtype], _ptr(w), _ptr(q), _ptr(kv),
+                                         _ptr(v), _ptr(q_pos), B, T, S, H_I, D_I, k,
+                                         DSA_SEL_INCLUDE_CURRENT if include_current else 0,
+                                         _ptr(out), _ptr(idx_out), _stream(stream)))
     return out
 
 

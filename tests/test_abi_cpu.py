@@ -87,6 +87,22 @@ def test_indexer_ex_flags(lib):
     assert f(A, A, 1, A, None, 1, 4, 4, 64, 128, 1, M, None) == ALIGN
 
 
+def test_noalloc_forward_rejects_sizes_beyond_its_scratch(lib):
+    """dsa_forward_ex_noalloc: sizes whose forward workspace exceeds the
+    128 MiB scratch are rejected on the host before anything is enqueued."""
+    d = _desc()
+    f = lib.dsa_forward_ex_noalloc
+    need = lib.dsa_workspace_bytes(dsa.DSA_OP_FORWARD, ctypes.byref(d), 1, 32768, 32768, 64,
+                                   128, 2048)
+    assert need > (128 << 20)
+    assert f(ctypes.byref(d), A, A, 1, A, A, A, None, None, 1, 32768, 32768, 64, 128, 2048, 0,
+             A, None, None) == WS
+    assert f(ctypes.byref(d), None, A, 1, A, A, A, None, None, 8, 1, 131072, 64, 128, 2048, 0,
+             A, None, None) == NULL
+    assert f(ctypes.byref(d), A, A, 1, A, A, A, None, None, 8, 1, 131072, 64, 128, 2048, 2,
+             A, None, None) == UNSUP
+
+
 def test_topk_argument_checks(lib):
     f = lib.dsa_topk
     assert f(None, None, 1, 4, 4, 2, A, None, 0, None) == NULL
