@@ -147,7 +147,7 @@ def measure_peaks(read_bytes: int):
         raise RuntimeError(f"{hb.PROBE_LIB} is missing: build with __graft_entry__.build()")
     lib = ctypes.CDLL(hb.PROBE_LIB)
     lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                      ctypes.c_int, ctypes.c_void_p]
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     for f in (lib.probe_mfma_bf16, lib.probe_mfma_fp8):
         f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -166,20 +166,28 @@ def measure_peaks(read_bytes: int):
 
     out = {}
     for nbytes in sorted({read_bytes // 16 * 16, 1 << 30}):
-        # 4 buffers rotated, so a launch never finds its data in the 256 MB cache
+        # 4 buffers rotated, so a launch never finds its data in the 256 MB cache;
+        # the best of a few launch shapes is the device's achievable read rate
         bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(4)]
         for bb in bufs:
             bb.fill_(1)
         it = [0]
-
-        def rd():
-            bb = bufs[it[0] % 4]
-            it[0] += 1
-            rc = lib.probe_stream_read(ctypes.c_void_p(bb.data_ptr()), nbytes,
-                                       ctypes.c_void_p(sink.data_ptr()), 2048, stream)
-            assert rc == 0, rc
-        ms = timed(rd, 20)
-        out[f"stream_read_{nbytes}"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        best, shapes = 0.0, {}
+        for blocks in (1024, 2048, 4096, 8192):
+            for inflight in (4, 8):
+                def rd():
+                    bb = bufs[it[0] % 4]
+                    it[0] += 1
+                    rc = lib.probe_stream_read(ctypes.c_void_p(bb.data_ptr()), nbytes,
+                                               ctypes.c_void_p(sink.data_ptr()), blocks,
+                                               inflight, stream)
+                    assert rc == 0, rc
+                ms = timed(rd, 20)
+                gbs = nbytes / (ms * 1e-3) / 1e9
+                shapes[f"{blocks}x{inflight}"] = round(gbs, 1)
+                best = max(best, gbs)
+        out[f"stream_read_{nbytes}"] = round(best, 1)
+        out[f"stream_read_{nbytes}_shapes"] = shapes
         del bufs
     iters, blocks = 4000, 512
     for name, fn, flop in (("mfma_bf16", lib.probe_mfma_bf16, 32768),

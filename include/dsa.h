@@ -83,7 +83,8 @@ typedef struct {
     int d_qk;       /* query/key width: MHA 64 or 128; MLA 576 */
     int d_v;        /* value width: MHA == d_qk; MLA 512 (first d_v entries
                        of the latent row) */
-    float scale;    /* softmax scale, 1/sqrt(d_k) on [P1] section 3.3 */
+    float scale;    /* softmax scale, 1/sqrt(d_k) on [P1] section 3.3; finite and
+                       > 0 (else DSA_ERR_SHAPE) */
     int dtype;      /* dtype of q, K/V or latent: DSA_F32 or DSA_BF16
                        (MLA: DSA_BF16 only) */
     int out_dtype;  /* dtype of out: DSA_F32 or DSA_BF16 */

@@ -56,7 +56,7 @@ dsa_status_t check_attention(const dsa_attn_desc_t *d, const void *q, const void
     if (d->dtype == DSA_FP8_E4M3 || d->out_dtype == DSA_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
     if (d->num_heads < 1 || d->num_heads > 4096) return DSA_ERR_SHAPE;
     if (d->d_qk < 1 || d->d_qk > 576 || d->d_v < 1 || d->d_v > 512) return DSA_ERR_SHAPE;
-    if (!(d->scale == d->scale) || isinf(d->scale)) return DSA_ERR_SHAPE;
+    if (!(d->scale > 0.0f) || isinf(d->scale)) return DSA_ERR_SHAPE;  // finite, positive
     if (d->form == DSA_MHA) {
         if (!v) return DSA_ERR_NULL;
         if (!aligned16(v)) return DSA_ERR_ALIGN;

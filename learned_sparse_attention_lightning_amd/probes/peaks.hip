@@ -1,8 +1,8 @@
 // peaks.hip -- what this device actually sustains, for the roofline
 // fractions reported beside the vendor peaks:
-//   probe_stream_read   coalesced 16-byte nontemporal reads of a buffer, four
-//                       loads in flight per thread (the access pattern of the
-//                       decode key stream), one word written per workgroup;
+//   probe_stream_read   coalesced 16-byte nontemporal reads of a buffer, four or
+//                       eight loads in flight per thread (the access pattern of
+//                       the decode key stream), one word written per workgroup;
 //   probe_mfma_bf16     back-to-back v_mfma_f32_32x32x16_bf16 on register
 //                       operands, four independent accumulators per wave;
 //   probe_mfma_fp8      the same with the fp8 e4m3 32x32x64 scaled form.
@@ -21,20 +21,20 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kReadThreads = 256;
-constexpr int kInFlight = 4;
 
+template <int InFlight>
 __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4 *__restrict__ p,
                                                                    size_t n16,
                                                                    uint32_t *__restrict__ sink) {
     const size_t stride = (size_t)gridDim.x * kReadThreads;
     uint32_t acc = 0u;
     size_t j = (size_t)blockIdx.x * kReadThreads + threadIdx.x;
-    for (; j + (kInFlight - 1) * stride < n16; j += kInFlight * stride) {
-        u32x4 v[kInFlight];
+    for (; j + (InFlight - 1) * stride < n16; j += InFlight * stride) {
+        u32x4 v[InFlight];
 #pragma unroll
-        for (int u = 0; u < kInFlight; ++u) v[u] = __builtin_nontemporal_load(p + j + u * stride);
+        for (int u = 0; u < InFlight; ++u) v[u] = __builtin_nontemporal_load(p + j + u * stride);
 #pragma unroll
-        for (int u = 0; u < kInFlight; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+        for (int u = 0; u < InFlight; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
     }
     for (; j < n16; j += stride) {
         const u32x4 v = __builtin_nontemporal_load(p + j);
@@ -81,11 +81,16 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float *__restrict__ sink
 
 }  // namespace
 
-// Reads `bytes` (a multiple of 16) from `buf` once; sink holds `blocks` words.
+// Reads `bytes` (a multiple of 16) from `buf` once, `inflight` (4 or 8)
+// 16-byte loads in flight per thread; sink holds `blocks` words.
 PROBE_EXPORT int probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks,
-                                   void *stream) {
-    hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(kReadThreads), 0,
-                       (hipStream_t)stream, static_cast<const u32x4 *>(buf), bytes / 16, sink);
+                                   int inflight, void *stream) {
+    if (inflight == 8)
+        hipLaunchKernelGGL(stream_read_kernel<8>, dim3(blocks), dim3(kReadThreads), 0,
+                           (hipStream_t)stream, static_cast<const u32x4 *>(buf), bytes / 16, sink);
+    else
+        hipLaunchKernelGGL(stream_read_kernel<4>, dim3(blocks), dim3(kReadThreads), 0,
+                           (hipStream_t)stream, static_cast<const u32x4 *>(buf), bytes / 16, sink);
     return (int)hipGetLastError();
 }
 

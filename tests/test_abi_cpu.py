@@ -87,6 +87,13 @@ def test_indexer_ex_flags(lib):
     assert f(A, A, 1, A, None, 1, 4, 4, 64, 128, 1, M, None) == ALIGN
 
 
+def test_attention_scale_must_be_positive(lib):
+    f = lib.dsa_sparse_attention
+    for bad_scale in (0.0, -0.5, float("inf"), float("nan")):
+        d = dsa.AttnDesc(dsa.DSA_MLA, 128, 576, 512, bad_scale, dsa.DSA_BF16, dsa.DSA_BF16)
+        assert f(ctypes.byref(d), A, A, None, A, 1, 4, 4, 2, A, None, None, 0, None) == SHAPE
+
+
 def test_noalloc_forward_rejects_sizes_beyond_its_scratch(lib):
     """dsa_forward_ex_noalloc: sizes whose forward workspace exceeds the
     128 MiB scratch are rejected on the host before anything is enqueued."""
