@@ -490,7 +490,7 @@ def run_prefill(w, args, dev, peaks, with_cpu):
     apk = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_VECTOR_TFLOPS
     apk_meas = peaks.get("mfma_bf16_tflops") if w.dtype == "bf16" else None
     att_kernel = ("mla_attention_kernel" if w.form == "mla" else
-                  "mha_dense_kernel" if w.dtype == "bf16" else "attention_gather_kernel")
+                  "mha_fa_kernel" if w.dtype == "bf16" else "attention_gather_kernel")
     rec = {
         "workload": f"{w.name}: {w.description}",
         "value": round(w.B * w.T / (ms * 1e-3), 1), "unit": "tokens/s",

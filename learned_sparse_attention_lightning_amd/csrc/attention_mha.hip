@@ -41,6 +41,8 @@ constexpr int kFaWaves = kFaQ / 32;  // waves of a group (one per 32 queries)
 constexpr int kFaGroups = 2;       // groups over alternate key tiles
 constexpr int kFaThreads = 64 * kFaWaves * kFaGroups;
 constexpr int kFaKeys = 64;        // keys per tile
+// s_waitcnt immediate: vmcnt 0, expcnt and lgkmcnt at their maxima (no wait)
+constexpr int kWaitVm0 = 0x0F70;
 constexpr int kMaxS = 65536;       // bitmap row of a row kept in LDS by the bitmap kernel (8 KB)
 constexpr float kRescaleLog2 = 8.0f;
 
@@ -84,14 +86,23 @@ __global__ __launch_bounds__(256) void mha_bitmap_kernel(const int32_t *__restri
     __syncthreads();
     const int32_t *sel = idx + ((size_t)b * T + row0 + r) * k;
     int hi = -1;
-    for (int e = threadIdx.x; e < k; e += 256) {
-        const int s = sel[e];
-        if (s >= 0 && s < S) {
-            atomicOr(&w[s >> 5], 1u << (s & 31));
-            hi = max(hi, s);
+    // eight loads in flight per thread before any of them is used
+    for (int e0 = threadIdx.x; e0 < k; e0 += 8 * 256) {
+        int sv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sv[u] = e0 + 256 * u < k ? sel[e0 + 256 * u] : -1;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int s = sv[u];
+            if (s >= 0 && s < S) {
+                atomicOr(&w[s >> 5], 1u << (s & 31));
+                hi = max(hi, s);
+            }
         }
     }
-    atomicMax(&hi_s, hi);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) hi = max(hi, __shfl_xor(hi, off, 64));
+    if ((threadIdx.x & 63) == 0) atomicMax(&hi_s, hi);
     __syncthreads();
     uint32_t *out = bits + ((size_t)b * rows + r) * words;
     for (int j = threadIdx.x; j < words; j += 256) out[j] = w[j];
@@ -267,7 +278,12 @@ __global__ __launch_bounds__(kFaThreads, 1) void mha_fa_kernel(
     auto step = [&](auto G, auto BUF, const int i) __attribute__((always_inline)) {
         constexpr int g = decltype(G)::value, nbuf = 1 - decltype(BUF)::value;
         const int j = 2 * i + g;
-        __syncthreads();  // tile j in LDS (this wave's loads done, every wave past step i-1)
+        // tile j in LDS: this wave's loads have landed (the wait is explicit:
+        // the barrier's fence does not reliably wait for direct-to-LDS
+        // loads); after the barrier every wave's have, and every wave is past
+        // step i-1
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __syncthreads();
         mw0 = nw0;
         mw1 = nw1;
         if (j + 2 < ntiles) {
@@ -304,11 +320,14 @@ __global__ __launch_bounds__(kFaThreads, 1) void mha_fa_kernel(
         if (__ballot((mw0 & mw1) != 0xffffffffu)) {  // some key of the tile not selected
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const uint32_t mw = u == 0 ? mw0 : mw1;
+                const uint32_t mw = (u == 0 ? mw0 : mw1) >> (4 * half);
 #pragma unroll
                 for (int rg = 0; rg < 16; ++rg) {
-                    const int bit = 8 * (rg >> 2) + 4 * half + (rg & 3);
-                    s[u][rg] = (mw >> bit) & 1u ? s[u][rg] : -INFINITY;
+                    // all ones when key rg is selected, else zero
+                    const uint32_t keep =
+                        (uint32_t)__builtin_amdgcn_sbfe((int)mw, 8 * (rg >> 2) + (rg & 3), 1);
+                    s[u][rg] = __uint_as_float((__float_as_uint(s[u][rg]) & keep) |
+                                               (0xff800000u & ~keep));
                 }
             }
         }
