@@ -489,8 +489,11 @@ def run_prefill(w, args, dev, peaks, with_cpu):
     ipk_meas = peaks.get("mfma_fp8_tflops" if w.idx_dtype == "fp8" else "mfma_bf16_tflops")
     apk = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_VECTOR_TFLOPS
     apk_meas = peaks.get("mfma_bf16_tflops") if w.dtype == "bf16" else None
+    # the stage time covers every launch of one attention call (for the MHA
+    # masked-dense form: the selection bitmap, then the attention)
     att_kernel = ("mla_attention_kernel" if w.form == "mla" else
-                  "mha_fa_kernel" if w.dtype == "bf16" else "attention_gather_kernel")
+                  "mha_bitmap_kernel+mha_fa_kernel" if w.dtype == "bf16" else
+                  "attention_gather_kernel")
     rec = {
         "workload": f"{w.name}: {w.description}",
         "value": round(w.B * w.T / (ms * 1e-3), 1), "unit": "tokens/s",

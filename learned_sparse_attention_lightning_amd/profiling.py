@@ -5,8 +5,13 @@
         --kernel-fetch DIR --kernel-write DIR --copy-fetch DIR --copy-write DIR \
         --copy-bytes N --kernel REGEX --source FILE --out OUT.json --command "..."
 
+    python -m learned_sparse_attention_lightning_amd.profiling counters \
+        --run DIR [--run DIR ...] --kernel NAME=REGEX [...] --out OUT.md --command "..."
+
 `trace` turns the kernel table of a `rocprofv3 --kernel-trace --stats` run
-(the rocpd SQLite database) into a short markdown table.  `traffic` turns two
+(the rocpd SQLite database) into a short markdown table.  `counters` turns
+`rocprofv3 --pmc` runs (one per counter set) into per-dispatch averages per
+kernel, with the matrix-core busy fractions they imply.  `traffic` turns two
 `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of a kernel into HBM bytes per
 dispatch, each counter scaled by what it reads for a plain copy of a known
 number of bytes (the copy reads and writes exactly that many bytes).
@@ -63,6 +68,73 @@ def counter_per_dispatch(run_dir: str, counter: str, kernel_regex: str) -> float
     return sum(vals.values()) / len(vals)
 
 
+def counter_table(run_dirs, kernel_regex: str):
+    """{counter: mean per dispatch} of the dispatches whose name matches."""
+    out = {}
+    for d in run_dirs:
+        per = {}
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(fn)):
+                if not re.search(kernel_regex, r["Kernel_Name"]):
+                    continue
+                key = (r["Counter_Name"], r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        sums = {}
+        for (c, _), v in per.items():
+            sums.setdefault(c, []).append(v)
+        for c, vs in sums.items():
+            out[c] = (sum(vs) / len(vs), len(vs))
+    return out
+
+
+# SIMDs and XCDs of the device: the matrix-core busy cycles are summed over
+# SIMDs, GRBM_GUI_ACTIVE over XCDs, SQ_BUSY_CU_CYCLES over SIMDs in
+# quad-cycles.
+DEVICE_SIMDS = 1024
+DEVICE_XCDS = 8
+
+
+def write_counters(a):
+    kernels = [k.split("=", 1) for k in a.kernel]
+    lines = [f"# {a.title}", "", "Commands (one rocprofv3 run per counter set):", "", "```"]
+    lines += a.command
+    lines += ["```", ""]
+    for label, regex in kernels:
+        tab = counter_table(a.run, regex)
+        if not tab:
+            raise ValueError(f"no samples for {label} (/{regex}/)")
+        lines += [f"## `{label}`", "", "| counter | per dispatch | dispatches |", "|---|---|---|"]
+        for c in sorted(tab):
+            v, n = tab[c]
+            lines.append(f"| {c} | {v:,.0f} | {n} |")
+        derived = []
+        mf = tab.get("SQ_VALU_MFMA_BUSY_CYCLES", (None,))[0]
+        busy = tab.get("SQ_BUSY_CU_CYCLES", (None,))[0]
+        grbm = tab.get("GRBM_GUI_ACTIVE", (None,))[0]
+        co = tab.get("SQ_VALU_MFMA_COEXEC_CYCLES", (None,))[0]
+        if mf is not None and busy:
+            derived.append(f"matrix cores busy, share of SIMD-busy cycles: "
+                           f"{mf / (4 * busy):.3f} (SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES))")
+        if mf is not None and grbm:
+            cyc = grbm / DEVICE_XCDS
+            derived.append(f"matrix cores busy, share of the kernel's cycles: "
+                           f"{mf / (DEVICE_SIMDS * cyc):.3f} (over {DEVICE_SIMDS} SIMDs x "
+                           f"GRBM_GUI_ACTIVE / {DEVICE_XCDS} = {cyc:,.0f} cycles)")
+        if mf and co is not None:
+            derived.append(f"VALU issued while the matrix cores are busy: {co / mf:.3f} of their "
+                           f"busy cycles (SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES)")
+        if "FETCH_SIZE" in tab:
+            derived.append(f"FETCH_SIZE: {tab['FETCH_SIZE'][0] / 1024:,.1f} MiB per dispatch "
+                           f"(uncalibrated counter units of KiB)")
+        if derived:
+            lines += [""] + [f"- {d}" for d in derived]
+        lines.append("")
+    if a.note:
+        lines += [a.note, ""]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def source_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
@@ -104,9 +176,18 @@ def main():
     tr.add_argument("--source", required=True)
     tr.add_argument("--out", required=True)
     tr.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--run", action="append", required=True)
+    c.add_argument("--kernel", action="append", required=True, help="LABEL=REGEX")
+    c.add_argument("--out", required=True)
+    c.add_argument("--command", action="append", required=True)
+    c.add_argument("--title", default="Counters")
+    c.add_argument("--note", default="")
     a = ap.parse_args()
     if a.cmd == "trace":
         write_trace(a.db, a.out, a.command, a.title)
+    elif a.cmd == "counters":
+        write_counters(a)
     else:
         print(json.dumps(write_traffic(a), indent=1))
 
