@@ -444,11 +444,19 @@ def time_kl(w, x, desc, out, idx, chunks, dev):
     alg = algorithmic(w)
     kl_flops = alg["entries"] * 2 * w.num_heads * w.d_qk
     kl_tf = kl_flops / (kl_ms * 1e-3) / 1e12
-    # MLA: matrix-core products; MHA: per-head dot products on the vector ALUs
-    kpk, kb = (BF16_PEAK_TFLOPS, "mfma") if w.form == "mla" else (FP32_VECTOR_TFLOPS, "alu")
+    # MLA and the MHA masked-dense form (bf16, k >= S/4): matrix-core
+    # products; other MHA shapes: per-head dot products on the vector ALUs
+    dense = dsa.workspace_bytes(dsa.DSA_OP_KL, desc, w.B, ch, w.S, 1, 1, w.index_topk) > 0
+    if w.form == "mla":
+        kpk, kb, kname = BF16_PEAK_TFLOPS, "mfma", "mla_indexer_kl_kernel"
+    elif dense:
+        kpk, kb = BF16_PEAK_TFLOPS, "mfma"
+        kname = "mha_bitmap_kernel+mha_kl_dense_kernel+kl_split_merge_kernel"
+    else:
+        kpk, kb, kname = FP32_VECTOR_TFLOPS, "alu", "mha_indexer_kl_kernel"
     return {"bound": kb, "achieved": round(kl_tf, 2), "peak": kpk, "unit": "TFLOP/s",
             "frac": round(kl_tf / kpk, 4), "ms": round(kl_ms, 4),
-            "kernel": f"{w.form}_indexer_kl_kernel", "algorithmic_flops": kl_flops}
+            "kernel": kname, "algorithmic_flops": kl_flops}
 
 
 def mfma_roof(flops, ms, peak, measured, kernel, launches):

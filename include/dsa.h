@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 
 typedef enum {
     DSA_F32 = 0,      /* IEEE binary32 */
@@ -282,17 +282,35 @@ dsa_status_t dsa_forward_ex_noalloc(const dsa_attn_desc_t *desc, const void *q_i
  *   scores [B,T,S] fp32 indexer scores (read at the selected positions)
  *   loss   [B,T] fp32 output (the total is its sum)
  * Logits in fp32 (bf16 or fp32 inputs); p, the log-sum-exp of the scores and
- * the sums in fp32.  No workspace.
+ * the sums in fp32.  No workspace (dsa_indexer_kl_ex takes one).
  */
 dsa_status_t dsa_indexer_kl(const dsa_attn_desc_t *desc, const void *q, const void *kv,
                             const int32_t *idx, const float *lse, const float *scores, int B,
                             int T, int S, int index_topk, float *loss, void *stream);
 
-enum { DSA_OP_TOPK = 0, DSA_OP_ATTENTION = 1, DSA_OP_FORWARD = 2 };
+/*
+ * dsa_indexer_kl with a workspace (same loss, [P1] sections 5.2-5.4 and
+ * 6.2).  When dsa_workspace_bytes(DSA_OP_KL, ...) is non-zero -- MHA, bf16,
+ * d_qk 64 or 128, 8 or 16 heads, S <= 65536 and k >= S/4, the prefill
+ * regime where the selection covers much of every causal prefix -- and a
+ * workspace of at least that many bytes (16-byte aligned, caller-owned,
+ * contents not preserved) is given, the target p_s is computed for every key
+ * of the causal area on the matrix cores and the selection, turned into one
+ * bit per (row, key), decides which keys enter the loss; otherwise (NULL
+ * workspace, or a shape outside that set) the call is dsa_indexer_kl.  A
+ * workspace smaller than needed gives DSA_ERR_WORKSPACE.
+ */
+dsa_status_t dsa_indexer_kl_ex(const dsa_attn_desc_t *desc, const void *q, const void *kv,
+                               const int32_t *idx, const float *lse, const float *scores, int B,
+                               int T, int S, int index_topk, float *loss, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+enum { DSA_OP_TOPK = 0, DSA_OP_ATTENTION = 1, DSA_OP_FORWARD = 2, DSA_OP_KL = 3 };
 
 /*
  * Workspace bytes needed by one call of `op` with these sizes (desc may be
- * NULL for DSA_OP_TOPK).  Returns (size_t)-1 when the sizes are invalid.
+ * NULL for DSA_OP_TOPK; DSA_OP_KL: the bytes dsa_indexer_kl_ex uses, 0 when
+ * it runs without one).  Returns (size_t)-1 when the sizes are invalid.
  */
 size_t dsa_workspace_bytes(int op, const dsa_attn_desc_t *desc, int B, int T, int S,
                            int index_n_heads, int index_head_dim, int index_topk);

@@ -469,6 +469,20 @@ size_t mha_workspace_bytes(int B, int rows, int S) {
     return align256((size_t)B * rows * words * 4) + align256((size_t)B * rows * 4);
 }
 
+hipError_t launch_selection_bitmap(const int32_t *idx, int B, int T, int S, int row0, int rows,
+                                   int k, uint32_t *bits, int32_t *row_hi, hipStream_t stream) {
+    if (S > kMaxS) return hipErrorInvalidValue;
+    const size_t words = (size_t)(S + 31) / 32;
+    for (int r0 = 0; r0 < rows; r0 += kMaxGridY) {
+        const int n = min(kMaxGridY, rows - r0);
+        hipLaunchKernelGGL(mha_bitmap_kernel, dim3(n, B), dim3(256), 0, stream, idx, T, S,
+                           row0 + r0, rows, k, bits + (size_t)r0 * words, row_hi + r0);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_mha_dense(const dsa_attn_desc_t &d, const void *q, const void *kv,
                             const void *v, const int32_t *idx, int B, int T, int S, int row0,
                             int rows, int k, void *out, float *lse, void *workspace,
@@ -477,13 +491,8 @@ hipError_t launch_mha_dense(const dsa_attn_desc_t &d, const void *q, const void 
     uint32_t *bits = static_cast<uint32_t *>(workspace);
     int32_t *row_hi = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) +
                                                   align256((size_t)B * rows * words * 4));
-    for (int r0 = 0; r0 < rows; r0 += kMaxGridY) {
-        const int n = min(kMaxGridY, rows - r0);
-        hipLaunchKernelGGL(mha_bitmap_kernel, dim3(n, B), dim3(256), 0, stream, idx, T, S,
-                           row0 + r0, rows, k, bits + (size_t)r0 * words, row_hi + r0);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    hipError_t e = launch_selection_bitmap(idx, B, T, S, row0, rows, k, bits, row_hi, stream);
+    if (e != hipSuccess) return e;
     const int nqb = (rows + kFaQ - 1) / kFaQ;
     const long long units = (long long)B * nqb * d.num_heads;
     const dim3 grid((unsigned)units);

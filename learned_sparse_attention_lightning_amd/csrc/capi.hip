@@ -212,6 +212,9 @@ DSA_EXPORT size_t dsa_workspace_bytes(int op, const dsa_attn_desc_t *desc, int B
         case DSA_OP_FORWARD:
             if (!desc) return (size_t)-1;
             return forward_workspace(desc, B, T, S, index_topk);
+        case DSA_OP_KL:
+            if (!desc) return (size_t)-1;
+            return kl_workspace_bytes(*desc, B, T, S, index_topk);
         default: return (size_t)-1;
     }
 }
@@ -295,10 +298,11 @@ DSA_EXPORT dsa_status_t dsa_sparse_attention(const dsa_attn_desc_t *desc, const 
                                    lse, workspace, workspace_bytes, stream);
 }
 
-DSA_EXPORT dsa_status_t dsa_indexer_kl(const dsa_attn_desc_t *desc, const void *q,
-                                       const void *kv, const int32_t *idx, const float *lse,
-                                       const float *scores, int B, int T, int S,
-                                       int index_topk, float *loss, void *stream) {
+DSA_EXPORT dsa_status_t dsa_indexer_kl_ex(const dsa_attn_desc_t *desc, const void *q,
+                                          const void *kv, const int32_t *idx, const float *lse,
+                                          const float *scores, int B, int T, int S,
+                                          int index_topk, float *loss, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
     dsa_status_t st = check_sizes(B, T, S, true);
     if (st != DSA_OK) return st;
     if (!desc) return DSA_ERR_NULL;
@@ -309,8 +313,19 @@ DSA_EXPORT dsa_status_t dsa_indexer_kl(const dsa_attn_desc_t *desc, const void *
     if (!idx || !lse || !scores) return DSA_ERR_NULL;
     if (!valid_topk(index_topk)) return DSA_ERR_SHAPE;
     if (!aligned16(idx) || !aligned16(lse) || !aligned16(scores)) return DSA_ERR_ALIGN;
+    const size_t need = kl_workspace_bytes(*desc, B, T, S, index_topk);
+    if (workspace && (workspace_bytes < need || !aligned16(workspace))) return DSA_ERR_WORKSPACE;
     return hip_status(launch_indexer_kl(*desc, q, kv, idx, lse, scores, B, T, S, index_topk,
-                                        loss, (hipStream_t)stream));
+                                        loss, need > 0 ? workspace : nullptr,
+                                        (hipStream_t)stream));
+}
+
+DSA_EXPORT dsa_status_t dsa_indexer_kl(const dsa_attn_desc_t *desc, const void *q,
+                                       const void *kv, const int32_t *idx, const float *lse,
+                                       const float *scores, int B, int T, int S,
+                                       int index_topk, float *loss, void *stream) {
+    return dsa_indexer_kl_ex(desc, q, kv, idx, lse, scores, B, T, S, index_topk, loss, nullptr,
+                             0, stream);
 }
 
 DSA_EXPORT dsa_status_t dsa_forward_ex(const dsa_attn_desc_t *desc, const void *q_idx,

@@ -122,9 +122,17 @@ hipError_t launch_select_all(const int32_t *q_pos, int B, int T, int S, int row0
                              int k, int32_t *idx, hipStream_t stream);
 
 bool indexer_kl_supported(const dsa_attn_desc_t &d);
+// workspace: kl_workspace_bytes(...) bytes (or NULL: the per-entry form)
+size_t kl_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int S, int k);
 hipError_t launch_indexer_kl(const dsa_attn_desc_t &d, const void *q, const void *kv,
                              const int32_t *idx, const float *lse, const float *scores, int B,
-                             int T, int S, int k, float *loss, hipStream_t stream);
+                             int T, int S, int k, float *loss, void *workspace,
+                             hipStream_t stream);
+// One bit per (row, key) of the selection idx[b, row0 + r, :] (rows r of
+// the launch, bits[(b * rows + r) * ceil(S/32) + s/32] bit s%32) and each
+// row's largest selected position (-1: none).  S <= 65536.
+hipError_t launch_selection_bitmap(const int32_t *idx, int B, int T, int S, int row0, int rows,
+                                   int k, uint32_t *bits, int32_t *row_hi, hipStream_t stream);
 
 bool mha_dense_path(const dsa_attn_desc_t &d, int rows, int S, int k);
 size_t mha_workspace_bytes(int B, int rows, int S);

@@ -287,7 +287,188 @@ __global__ __launch_bounds__(kMhaKlThreads) void mha_indexer_kl_kernel(
     }
 }
 
+// MHA masked-dense form (bf16, d_qk 64 or 128, 8 or 16 heads, a selection
+// that covers a large share of the causal prefix): the target p_s of every
+// key of the causal area is computed on the matrix cores and the bitmap of
+// the selection decides which keys enter the loss.  Workgroup = 32 query
+// rows x one range of 512 keys (a split) x every head: wave w multiplies
+// heads HPW w .. HPW w + HPW-1 (their query fragments in registers, B
+// operand) with the key rows of one 32-key tile at a time (A operand,
+// loaded from memory straight into registers, three head-tiles in flight),
+// and adds exp2(S^T scale log2e - lse_h log2e) over its heads; the eight
+// waves' sums meet in LDS (one barrier a tile, two buffers), where each
+// thread takes 2 (key, query) pairs and folds the selected ones into its
+// running KL state.  The splits of a row are merged by a second kernel.
+// The splits of one query block sit on consecutive workgroup ids, so with 8
+// splits a key range stays on one XCD and its keys in that XCD's L2.
+constexpr int kDkWaves = 8;
+constexpr int kDkThreads = kDkWaves * kWave;
+constexpr int kDkQ = 32;            // query rows per workgroup
+constexpr int kDkKeys = 32;         // keys per tile
+constexpr int kDkSplitTiles = 16;   // tiles per split (512 keys)
+constexpr int kDkRing = 3;          // head-tiles of key fragments in flight
+constexpr int kDkUnroll = 6;        // head-tiles per unrolled body: a multiple of 3, 2 and 1
+
+template <int D, int HPW>
+__global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
+    const uint32_t *__restrict__ bits, const int32_t *__restrict__ row_hi,
+    const float *__restrict__ lse, const float *__restrict__ scores, int T, int S, float scale,
+    int nqb, int nsplit, KlState *__restrict__ part) {
+    constexpr int H = kDkWaves * HPW;
+    constexpr int KS = D / 16;  // 16-dim k-steps
+    static_assert(kDkUnroll % kDkRing == 0 && kDkUnroll % HPW == 0, "static ring and head");
+    __shared__ float red[2][kDkWaves][16][kWave];  // per-wave sums of a tile, two buffers
+    __shared__ KlState fin[kDkWaves][kDkQ];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const int split = blockIdx.x % nsplit;
+    const int rest = blockIdx.x / nsplit;
+    const int qb = nqb - 1 - rest % nqb;  // longest query blocks first
+    const int b = rest / nqb;
+    const int words = (S + 31) / 32;
+    const int my_r = qb * kDkQ + l32;  // this lane's query row (queries are lanes mod 32)
+    const bool live = my_r < T;
+    const int rr = live ? my_r : T - 1;
+    const size_t row = (size_t)b * T + rr;
+    int hi = live ? row_hi[row] : -1;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) hi = max(hi, __shfl_xor(hi, off, 64));
+    const int ntiles = hi < 0 ? 0 : hi / kDkKeys + 1;  // the same in every wave
+    const int t0 = split * kDkSplitTiles;
+    const int t1 = min(ntiles, t0 + kDkSplitTiles);
+    const int njt = t1 > t0 ? (t1 - t0) * HPW : 0;  // head-tiles of this wave
+
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float c1 = scale * kLog2e;
+    // query fragments (B operand): lane (query l32, half) holds dims 16 ks + 8 half .. +8
+    bf16x8 qf[HPW][KS];
+    float lse2[HPW];
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+        const uint16_t *qp = q + (row * H + wave * HPW + h) * D + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[h][ks] = *reinterpret_cast<const bf16x8 *>(qp + 16 * ks);
+        lse2[h] = lse[row * H + wave * HPW + h] * kLog2e;
+    }
+    // key fragments (A operand) of head-tile j: lane (key l32 of the tile,
+    // half) holds dims 16 ks + 8 half .. +8 of head wave*HPW + j%HPW; keys
+    // past the cache read the last row (never selected)
+    const uint16_t *kb = K + (size_t)b * S * H * D + 8 * half;
+    auto load_kt = [&](int j, bf16x8 (&dst)[KS]) {
+        const int t = t0 + j / HPW;
+        const int key = min(t * kDkKeys + l32, S - 1);
+        const uint16_t *kp = kb + ((size_t)key * H + wave * HPW + j % HPW) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) dst[ks] = *reinterpret_cast<const bf16x8 *>(kp + 16 * ks);
+    };
+    // the pairs this thread folds: lane L = `lane`, registers 2 wave, 2 wave + 1
+    // of every wave's tile sums: query l32, keys kin and kin + 1 of the tile
+    const int kin = 8 * (wave >> 1) + 4 * half + 2 * (wave & 1);
+    const uint32_t *my_bits = bits + row * words;
+    const float *my_scores = scores + row * (size_t)S;
+    KlState st = {-INFINITY, 0.f, 0.f, 0.f, 0.f};
+    bf16x8 kr[kDkRing][KS];
+    f32x16 pacc = {};
+    float inext[2] = {0.f, 0.f};
+    uint32_t bnext = 0u;
+    auto fetch_pairs = [&](int t) {  // scores and selection word of tile t for this thread
+        const int key = t * kDkKeys + kin;
+        bnext = my_bits[t];
+        inext[0] = my_scores[min(key, S - 1)];
+        inext[1] = my_scores[min(key + 1, S - 1)];
+    };
+    // Head-tiles past the last (up to the unrolled body's end) are computed
+    // on the last one's keys and not folded: every load and every barrier of
+    // the body is then unconditional, so the waits for one head-tile's
+    // fragments never count the loads issued after them.
+    auto tile_done = [&](int t, bool valid) {
+        const int par = t & 1;
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg) red[par][wave][rg][lane] = pacc[rg];
+        pacc = f32x16{};
+        const uint32_t bw = bnext;
+        const float i0 = inext[0], i1 = inext[1];
+        fetch_pairs(min(t + 1, t1 - 1));
+        lds_barrier();
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < kDkWaves; ++v) {
+            s0 += red[par][v][2 * wave][lane];
+            s1 += red[par][v][2 * wave + 1][lane];
+        }
+        if (valid && live) {
+            if ((bw >> kin) & 1u) kl_push(st, s0 * (1.0f / H), i0);
+            if ((bw >> (kin + 1)) & 1u) kl_push(st, s1 * (1.0f / H), i1);
+        }
+    };
+    if (njt > 0) {  // uniform over the workgroup
+        fetch_pairs(t0);
+        load_kt(0, kr[0]);
+        load_kt(min(1, njt - 1), kr[1]);
+        for (int j0 = 0; j0 < njt; j0 += kDkUnroll) {
+#pragma unroll
+            for (int u = 0; u < kDkUnroll; ++u) {
+                const int j = j0 + u;
+                load_kt(min(j + 2, njt - 1), kr[(u + 2) % kDkRing]);
+                const int h = u % HPW;
+                f32x16 acc = {};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[u % kDkRing][ks], qf[h][ks],
+                                                                  acc, 0, 0, 0);
+#pragma unroll
+                for (int rg = 0; rg < 16; ++rg)
+                    pacc[rg] += __builtin_amdgcn_exp2f(fmaf(acc[rg], c1, -lse2[h]));
+                if (h == HPW - 1) tile_done(t0 + min(j, njt - 1) / HPW, j < njt);
+            }
+        }
+    }
+    // this row's state: lanes l32 and l32 + 32 of every wave hold parts of it
+    st = kl_merge(st, kl_shfl_xor(st, 32));
+    if (half == 0) fin[wave][l32] = st;
+    __syncthreads();
+    if (wave == 0 && half == 0 && live) {
+        KlState r = fin[0][l32];
+#pragma unroll
+        for (int v = 1; v < kDkWaves; ++v) r = kl_merge(r, fin[v][l32]);
+        part[row * nsplit + split] = r;
+    }
+}
+
+// Loss of each row from the states of its splits.
+__global__ __launch_bounds__(256) void kl_split_merge_kernel(const KlState *__restrict__ part,
+                                                             int rows, int nsplit,
+                                                             float *__restrict__ loss) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= rows) return;
+    KlState m = part[(size_t)r * nsplit];
+    for (int s = 1; s < nsplit; ++s) m = kl_merge(m, part[(size_t)r * nsplit + s]);
+    loss[r] = m.P > 0.f ? m.A / m.P - __logf(m.P) - m.Bd / m.P + __logf(m.z) : 0.f;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// The masked-dense form: bf16, d_qk 64 or 128, 8 or 16 heads, S within the
+// bitmap's reach, and a selection of at least a quarter of the keys.
+bool kl_dense_path(const dsa_attn_desc_t &d, int S, int k) {
+    return d.form == DSA_MHA && d.dtype == DSA_BF16 && (d.d_qk == 64 || d.d_qk == 128) &&
+           (d.num_heads == 8 || d.num_heads == 16) && S <= 65536 && 4LL * k >= (long long)S;
+}
+
+int kl_splits(int S) { return (S + kDkSplitTiles * kDkKeys - 1) / (kDkSplitTiles * kDkKeys); }
+
 }  // namespace
+
+size_t kl_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int S, int k) {
+    if (!kl_dense_path(d, S, k)) return 0;
+    const size_t rows = (size_t)B * T;
+    const size_t words = (size_t)(S + 31) / 32;
+    return align256(rows * words * 4) + align256(rows * 4) +
+           align256(rows * kl_splits(S) * sizeof(KlState));
+}
 
 bool indexer_kl_supported(const dsa_attn_desc_t &d) {
     if (d.form == DSA_MHA)
@@ -299,8 +480,42 @@ bool indexer_kl_supported(const dsa_attn_desc_t &d) {
 
 hipError_t launch_indexer_kl(const dsa_attn_desc_t &d, const void *q, const void *kv,
                              const int32_t *idx, const float *lse, const float *scores, int B,
-                             int T, int S, int k, float *loss, hipStream_t stream) {
+                             int T, int S, int k, float *loss, void *workspace,
+                             hipStream_t stream) {
     const dim3 grid(T, B);
+    if (workspace && kl_dense_path(d, S, k)) {
+        const size_t rows = (size_t)B * T;
+        const size_t words = (size_t)(S + 31) / 32;
+        char *ws = static_cast<char *>(workspace);
+        uint32_t *bits = reinterpret_cast<uint32_t *>(ws);
+        int32_t *row_hi = reinterpret_cast<int32_t *>(ws + align256(rows * words * 4));
+        KlState *part = reinterpret_cast<KlState *>(ws + align256(rows * words * 4) +
+                                                    align256(rows * 4));
+        hipError_t e = launch_selection_bitmap(idx, B, T, S, 0, T, k, bits, row_hi, stream);
+        if (e != hipSuccess) return e;
+        const int nqb = (T + kDkQ - 1) / kDkQ;
+        const int nsplit = kl_splits(S);
+        const dim3 g((unsigned)((long long)B * nqb * nsplit));
+        const uint16_t *qq = static_cast<const uint16_t *>(q);
+        const uint16_t *kk = static_cast<const uint16_t *>(kv);
+        if (d.d_qk == 128 && d.num_heads == 16)
+            hipLaunchKernelGGL((mha_kl_dense_kernel<128, 2>), g, dim3(kDkThreads), 0, stream, qq,
+                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, part);
+        else if (d.d_qk == 128)
+            hipLaunchKernelGGL((mha_kl_dense_kernel<128, 1>), g, dim3(kDkThreads), 0, stream, qq,
+                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, part);
+        else if (d.num_heads == 16)
+            hipLaunchKernelGGL((mha_kl_dense_kernel<64, 2>), g, dim3(kDkThreads), 0, stream, qq,
+                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, part);
+        else
+            hipLaunchKernelGGL((mha_kl_dense_kernel<64, 1>), g, dim3(kDkThreads), 0, stream, qq,
+                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, part);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kl_split_merge_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256),
+                           0, stream, part, (int)rows, nsplit, loss);
+        return hipGetLastError();
+    }
     if (d.form == DSA_MHA) {
         if (d.dtype == DSA_BF16)
             hipLaunchKernelGGL(mha_indexer_kl_kernel<uint16_t>, grid, dim3(kMhaKlThreads), 0,

@@ -19,7 +19,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so"
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 DSA_MHA, DSA_MLA = 0, 1
-DSA_OP_TOPK, DSA_OP_ATTENTION, DSA_OP_FORWARD = 0, 1, 2
+DSA_OP_TOPK, DSA_OP_ATTENTION, DSA_OP_FORWARD, DSA_OP_KL = 0, 1, 2, 3
 
 DTYPE_CODES = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16,
                torch.float8_e4m3fn: DSA_FP8_E4M3}
@@ -29,7 +29,7 @@ EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_indexer_scores",
             "dsa_indexer_scores_ex", "dsa_topk",
             "dsa_topk_ex", "dsa_sparse_attention", "dsa_sparse_attention_ex", "dsa_forward",
             "dsa_forward_ex", "dsa_forward_ex_noalloc",
-            "dsa_indexer_kl", "dsa_workspace_bytes")
+            "dsa_indexer_kl", "dsa_indexer_kl_ex", "dsa_workspace_bytes")
 DSA_SEL_INCLUDE_CURRENT = 1
 DSA_ATTN_CAUSAL_PREFIX = 1
 DSA_IDX_CAUSAL_ONLY = 1
@@ -96,6 +96,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.dsa_indexer_kl.restype = _i
     lib.dsa_indexer_kl.argtypes = [ctypes.POINTER(AttnDesc), _p, _p, _p, _p, _p, _i, _i, _i, _i,
                                    _p, _p]
+    lib.dsa_indexer_kl_ex.restype = _i
+    lib.dsa_indexer_kl_ex.argtypes = [ctypes.POINTER(AttnDesc), _p, _p, _p, _p, _p, _i, _i, _i,
+                                      _i, _p, _p, ctypes.c_size_t, _p]
     lib.dsa_workspace_bytes.restype = ctypes.c_size_t
     lib.dsa_workspace_bytes.argtypes = [_i, ctypes.POINTER(AttnDesc), _i, _i, _i, _i, _i, _i]
     if path is None:
@@ -295,9 +298,12 @@ def dsa_forward_noalloc(desc: AttnDesc, q_idx, k_idx, w, q, kv, v, k: int, q_pos
     return out
 
 
-def dsa_indexer_kl(desc: AttnDesc, q, kv, idx, lse, scores, loss=None, stream=None):
+def dsa_indexer_kl(desc: AttnDesc, q, kv, idx, lse, scores, loss=None, stream=None,
+                   workspace=None):
     """Per-row KL(head-mean attention weights || softmax of the indexer
-    scores) over each row's selected set -> loss [B,T] fp32 (MLA or MHA)."""
+    scores) over each row's selected set -> loss [B,T] fp32 (MLA or MHA).
+    Through dsa_indexer_kl_ex with the workspace it asks for (allocated here
+    when not given), so the MHA masked-dense form runs where it applies."""
     mha = desc.form == DSA_MHA
     _need(q, "q", ndim=4)
     _need(kv, "kv", dtype=q.dtype, ndim=4 if mha else 3)
@@ -319,6 +325,10 @@ def dsa_indexer_kl(desc: AttnDesc, q, kv, idx, lse, scores, loss=None, stream=No
     _need(loss, "loss", dtype=torch.float32, ndim=2)
     if tuple(loss.shape) != (B, T):
         raise ValueError("loss must be [B,T]")
-    _check(load().dsa_indexer_kl(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(idx), _ptr(lse),
-                                 _ptr(scores), B, T, S, k, _ptr(loss), _stream(stream)))
+    nws = workspace_bytes(DSA_OP_KL, desc, B, T, S, 1, 1, k)
+    if nws and (workspace is None or workspace.numel() < nws):
+        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    _check(load().dsa_indexer_kl_ex(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(idx), _ptr(lse),
+                                    _ptr(scores), B, T, S, k, _ptr(loss),
+                                    _ptr(workspace) if nws else None, nws, _stream(stream)))
     return loss

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsa_abi_version() == 3
+    assert lib.dsa_abi_version() == 4
     for s in range(8):
         assert lib.dsa_status_string(s)
     assert lib.dsa_status_string(99) == b"unknown status"
@@ -192,6 +192,31 @@ def test_indexer_kl_argument_checks(lib):
     assert f(ctypes.byref(d), A, A, None, A, A, 1, 4, 8, 2, A, None) == NULL
     assert f(ctypes.byref(d), A, A, A, A, A, 1, 4, 8, 0, A, None) == SHAPE
     assert f(ctypes.byref(d), A, A, A, M, A, 1, 4, 8, 2, A, None) == ALIGN
+
+
+def test_indexer_kl_ex_workspace(lib):
+    """dsa_indexer_kl_ex: the masked-dense MHA form asks for a workspace (one
+    bit per (row, key), the rows' last selected positions, the split states);
+    other shapes ask for none; a workspace below the need is refused on the
+    host."""
+    ws = lib.dsa_workspace_bytes
+    mha = _desc(form=dsa.DSA_MHA, H=16, dqk=128, dv=128)
+    need = ws(dsa.DSA_OP_KL, ctypes.byref(mha), 1, 4096, 4096, 1, 1, 2048)
+    rows, words, splits = 4096, 4096 // 32, 4096 // 512
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert need == r256(rows * words * 4) + r256(rows * 4) + r256(rows * splits * 20)
+    # a sparse selection (k < S/4), the MLA form, fp32 and 32 heads: the
+    # per-entry form, no workspace
+    assert ws(dsa.DSA_OP_KL, ctypes.byref(mha), 1, 4096, 4096, 1, 1, 1000) == 0
+    assert ws(dsa.DSA_OP_KL, ctypes.byref(_desc()), 1, 4096, 4096, 1, 1, 2048) == 0
+    f32 = _desc(form=dsa.DSA_MHA, H=16, dqk=128, dv=128, dt=dsa.DSA_F32, odt=dsa.DSA_F32)
+    assert ws(dsa.DSA_OP_KL, ctypes.byref(f32), 1, 4096, 4096, 1, 1, 2048) == 0
+    h32 = _desc(form=dsa.DSA_MHA, H=32, dqk=128, dv=128)
+    assert ws(dsa.DSA_OP_KL, ctypes.byref(h32), 1, 4096, 4096, 1, 1, 2048) == 0
+    f = lib.dsa_indexer_kl_ex
+    assert f(ctypes.byref(mha), A, A, A, A, A, 1, 4096, 4096, 2048, A, A, need - 1, None) == WS
+    assert f(ctypes.byref(mha), A, A, A, A, A, 1, 4096, 4096, 2048, A, M, need, None) == WS
+    assert f(None, A, A, A, A, A, 1, 4, 8, 2, A, None, 0, None) == NULL
 
 
 def test_attention_ex_argument_checks(lib):

@@ -174,3 +174,73 @@ def test_indexer_kl_mha_dense_warmup_target():
     causal = np.tril(np.ones((w.T, w.S), dtype=np.int8))[None]
     ref = oracle.indexer_kl_rows(p, rsc, causal)
     _check(loss, ref, "MHA dense warm-up")
+
+
+def _mha_dense_case(w, seed, holes=False):
+    """Seeded inputs, integer-valued scores and the oracle's own selection
+    (ranked, or shuffled with holes), the GPU attention's lse over it, then
+    the GPU loss and the oracle's."""
+    x = synth.make_inputs(w, device=DEV, seed=seed)
+    desc = dsa.desc_for(w)
+    g = torch.Generator().manual_seed(seed)
+    sc = torch.randint(-64, 64, (w.B, w.T, w.S), generator=g).to(torch.float32) / 8
+    sel = oracle.topk(sc, w.index_topk)
+    if holes:  # unordered rows, a few entries dropped (still distinct positions)
+        rng = np.random.default_rng(seed)
+        for b in range(w.B):
+            for i in range(w.T):
+                rng.shuffle(sel[b, i])
+                sel[b, i, rng.random(w.index_topk) < 0.05] = -1
+    idx = torch.from_numpy(sel).to(DEV)
+    assert dsa.workspace_bytes(dsa.DSA_OP_KL, desc, w.B, w.T, w.S, 1, 1, w.index_topk) > 0
+    lse = torch.empty((w.B, w.T, w.num_heads), dtype=torch.float32, device=DEV)
+    dsa.dsa_sparse_attention(desc, x["q"], x["kv"], x["v"], idx, lse=lse)
+    loss = dsa.dsa_indexer_kl(desc, x["q"], x["kv"], idx, lse, sc.to(DEV))
+    torch.cuda.synchronize()
+    p = oracle.sparse_target("mha", x["q"], x["kv"], sel, w.scale)
+    ref = oracle.indexer_kl_rows(p, sc, oracle.selection_mask(sel, w.S))
+    return loss, ref
+
+
+@pytest.mark.parametrize("heads,dim", [(16, 128), (8, 128), (16, 64), (8, 64)])
+def test_indexer_kl_mha_masked_dense(heads, dim):
+    """The masked-dense MHA form (k >= S/4): 1500 rows and keys, so the query
+    blocks of 32 rows, the 32-key tiles and the splits of 512 keys all end
+    ragged; against the oracle's loss over the same selection."""
+    w = configs.get("c1").with_(name=f"kl-mha-dense-{heads}x{dim}", B=2, T=1500, S=1500,
+                                index_topk=512, num_heads=heads, d_qk=dim, d_v=dim,
+                                index_n_heads=4, index_head_dim=32)
+    loss, ref = _mha_dense_case(w, seed=61)
+    _check(loss, ref, f"MHA masked-dense {heads}x{dim}")
+
+
+def test_indexer_kl_mha_masked_dense_holes():
+    """Unordered selection rows with holes through the masked-dense form."""
+    w = configs.get("c1").with_(name="kl-mha-dense-holes", B=1, T=700, S=700, index_topk=256,
+                                index_n_heads=4, index_head_dim=32)
+    loss, ref = _mha_dense_case(w, seed=62, holes=True)
+    _check(loss, ref, "MHA masked-dense, unordered with holes")
+
+
+@pytest.mark.timeout(600)
+def test_indexer_kl_c1_sampled_rows():
+    """The 4K MHA prefill (n = 4096, 16 heads x 128, k = 2048): the GPU
+    pipeline's scores, selection and lse, the masked-dense loss; the oracle's
+    loss over the GPU's selection and scores on 96 rows spread over the
+    causal range (sets and scores equal the oracle's bit for bit in the
+    parity tests)."""
+    w = configs.get("c1")
+    x = synth.make_inputs(w, device=DEV, seed=synth.default_seed(w))
+    desc = dsa.desc_for(w)
+    sc = dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"])
+    idx = dsa.dsa_topk(sc, w.index_topk)
+    lse = torch.empty((w.B, w.T, w.num_heads), dtype=torch.float32, device=DEV)
+    dsa.dsa_sparse_attention(desc, x["q"], x["kv"], x["v"], idx, lse=lse)
+    loss = dsa.dsa_indexer_kl(desc, x["q"], x["kv"], idx, lse, sc)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.linspace(8, w.T - 9, 80).astype(int),
+                                     np.arange(w.T - 8, w.T)]))
+    sel = idx[:, rows].cpu().numpy()
+    p = oracle.sparse_target("mha", x["q"][:, rows], x["kv"], sel, w.scale)
+    ref = oracle.indexer_kl_rows(p, sc[:, rows].cpu(), oracle.selection_mask(sel, w.S))
+    _check(loss[:, rows], ref, f"c1 masked-dense loss, {len(rows)} rows")
