@@ -73,40 +73,73 @@ __device__ __forceinline__ int fa_row(int m) {
     return (m & ~15) | ((m & 3) << 2) | ((m >> 2) & 3);
 }
 
-__global__ __launch_bounds__(256) void mha_bitmap_kernel(const int32_t *__restrict__ idx, int T,
-                                                         int S, int row0, int rows, int k,
-                                                         uint32_t *__restrict__ bits,
-                                                         int32_t *__restrict__ row_hi) {
-    __shared__ uint32_t w[kMaxS / 32];
-    __shared__ int hi_s;
-    const int r = blockIdx.x, b = blockIdx.y;
+// One wave per row (4 rows a workgroup): the wave zeroes its own bitmap row
+// in LDS, ORs in the selected positions (eight loads of the selection in
+// flight per lane), and writes the row out with its largest position.  The
+// wave is alone with its row, so no workgroup barrier is needed.
+constexpr int kBmRows = 4;
+// grid: x = group of 4 rows among the nr rows of this launch, y = batch;
+// rows = the row stride of bits and row_hi per batch
+__global__ __launch_bounds__(kBmRows * 64) void mha_bitmap_kernel(const int32_t *__restrict__ idx,
+                                                                  int T, int S, int row0, int nr,
+                                                                  int rows, int k,
+                                                                  uint32_t *__restrict__ bits,
+                                                                  int32_t *__restrict__ row_hi) {
+    __shared__ uint32_t w[kBmRows][kMaxS / 32];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = blockIdx.x * kBmRows + wave, b = blockIdx.y;
+    if (r >= nr) return;  // the whole wave
     const int words = (S + 31) / 32;
-    for (int j = threadIdx.x; j < words; j += 256) w[j] = 0u;
-    if (threadIdx.x == 0) hi_s = -1;
-    __syncthreads();
+    uint32_t *wr = w[wave];
+    for (int j = lane; j < words; j += 64) wr[j] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int32_t *sel = idx + ((size_t)b * T + row0 + r) * k;
     int hi = -1;
-    // eight loads in flight per thread before any of them is used
-    for (int e0 = threadIdx.x; e0 < k; e0 += 8 * 256) {
+    for (int e0 = lane; e0 < k; e0 += 8 * 64) {
         int sv[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) sv[u] = e0 + 256 * u < k ? sel[e0 + 256 * u] : -1;
+        for (int u = 0; u < 8; ++u) sv[u] = e0 + 64 * u < k ? sel[e0 + 64 * u] : -1;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
+            // the 64 lanes hold consecutive entries: within each row of 16
+            // lanes, runs of lanes with the same bitmap word (the rule for a
+            // top-k row, which is ascending) are merged with DPP row shifts
+            // first, and only the first lane of each run ORs into LDS -- the
+            // LDS atomics are the slow part; any order stays exact, only with
+            // more of them
             const int s = sv[u];
-            if (s >= 0 && s < S) {
-                atomicOr(&w[s >> 5], 1u << (s & 31));
-                hi = max(hi, s);
-            }
+            const bool valid = s >= 0 && s < S;
+            const int wd = valid ? s >> 5 : -1 - lane;  // a word of its own when unused
+            uint32_t acc = valid ? 1u << (s & 31) : 0u;
+            hi = valid ? max(hi, s) : hi;
+            const int lr = lane & 15;
+            // row_shl:n -- lane i reads lane i + n of its row
+#define DSA_MERGE_STEP(n, ctrl)                                                             \
+    {                                                                                       \
+        const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)acc, ctrl, 0xf, 0xf, false); \
+        const int ow = __builtin_amdgcn_mov_dpp(wd, ctrl, 0xf, 0xf, false);                \
+        if (lr + n < 16 && ow == wd) acc |= o;                                              \
+    }
+            DSA_MERGE_STEP(1, 0x101)
+            DSA_MERGE_STEP(2, 0x102)
+            DSA_MERGE_STEP(4, 0x104)
+            DSA_MERGE_STEP(8, 0x108)
+#undef DSA_MERGE_STEP
+            // row_shr:1 -- lane i reads lane i - 1 of its row
+            const int pw = __builtin_amdgcn_mov_dpp(wd, 0x111, 0xf, 0xf, false);
+            if (valid && (lr == 0 || pw != wd)) atomicOr(&wr[wd], acc);
         }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) hi = max(hi, __shfl_xor(hi, off, 64));
-    if ((threadIdx.x & 63) == 0) atomicMax(&hi_s, hi);
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     uint32_t *out = bits + ((size_t)b * rows + r) * words;
-    for (int j = threadIdx.x; j < words; j += 256) out[j] = w[j];
-    if (threadIdx.x == 0) row_hi[(size_t)b * rows + r] = hi_s;
+    for (int j = lane; j < words; j += 64) out[j] = wr[j];
+    if (lane == 0) row_hi[(size_t)b * rows + r] = hi;
 }
 
 // 4 consecutive outputs (8-byte aligned as bf16, 16-byte as fp32)
@@ -475,8 +508,9 @@ hipError_t launch_selection_bitmap(const int32_t *idx, int B, int T, int S, int 
     const size_t words = (size_t)(S + 31) / 32;
     for (int r0 = 0; r0 < rows; r0 += kMaxGridY) {
         const int n = min(kMaxGridY, rows - r0);
-        hipLaunchKernelGGL(mha_bitmap_kernel, dim3(n, B), dim3(256), 0, stream, idx, T, S,
-                           row0 + r0, rows, k, bits + (size_t)r0 * words, row_hi + r0);
+        hipLaunchKernelGGL(mha_bitmap_kernel, dim3((n + kBmRows - 1) / kBmRows, B),
+                           dim3(kBmRows * 64), 0, stream, idx, T, S, row0 + r0, n, rows, k,
+                           bits + (size_t)r0 * words, row_hi + r0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

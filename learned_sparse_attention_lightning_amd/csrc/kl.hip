@@ -291,21 +291,24 @@ __global__ __launch_bounds__(kMhaKlThreads) void mha_indexer_kl_kernel(
 // that covers a large share of the causal prefix): the target p_s of every
 // key of the causal area is computed on the matrix cores and the bitmap of
 // the selection decides which keys enter the loss.  Workgroup = 32 query
-// rows x one range of 512 keys (a split) x every head: wave w multiplies
+// rows x one range of 256 keys (a split) x every head: wave w multiplies
 // heads HPW w .. HPW w + HPW-1 (their query fragments in registers, B
-// operand) with the key rows of one 32-key tile at a time (A operand,
-// loaded from memory straight into registers, three head-tiles in flight),
+// operand) with the key rows of one 32-key tile at a time (A operand; each
+// head-tile's rows are loaded with whole-row 16-byte pieces, three
+// head-tiles in flight in registers, and pass through a wave-private LDS
+// tile into the operand layout),
 // and adds exp2(S^T scale log2e - lse_h log2e) over its heads; the eight
 // waves' sums meet in LDS (one barrier a tile, two buffers), where each
 // thread takes 2 (key, query) pairs and folds the selected ones into its
 // running KL state.  The splits of a row are merged by a second kernel.
-// The splits of one query block sit on consecutive workgroup ids, so with 8
-// splits a key range stays on one XCD and its keys in that XCD's L2.
+// The splits of one query block sit on consecutive workgroup ids, so with a
+// multiple of 8 splits a key range stays on one XCD and its keys in that
+// XCD's L2.
 constexpr int kDkWaves = 8;
 constexpr int kDkThreads = kDkWaves * kWave;
 constexpr int kDkQ = 32;            // query rows per workgroup
 constexpr int kDkKeys = 32;         // keys per tile
-constexpr int kDkSplitTiles = 16;   // tiles per split (512 keys)
+constexpr int kDkSplitTiles = 8;    // tiles per split (256 keys)
 constexpr int kDkRing = 3;          // head-tiles of key fragments in flight
 constexpr int kDkUnroll = 6;        // head-tiles per unrolled body: a multiple of 3, 2 and 1
 
@@ -318,8 +321,12 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
     constexpr int H = kDkWaves * HPW;
     constexpr int KS = D / 16;  // 16-dim k-steps
     static_assert(kDkUnroll % kDkRing == 0 && kDkUnroll % HPW == 0, "static ring and head");
+    constexpr int P = D / 8;                 // 16-byte pieces of a key's head row
+    constexpr int NL = kDkKeys * P / kWave;  // loads of a head-tile per lane
+    constexpr int kPitch = D * 2 + 16;       // LDS row pitch: rows 4 banks apart
     __shared__ float red[2][kDkWaves][16][kWave];  // per-wave sums of a tile, two buffers
     __shared__ KlState fin[kDkWaves][kDkQ];
+    __shared__ __align__(16) uint8_t ktile[kDkWaves][kDkKeys * kPitch];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
@@ -353,16 +360,39 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
         for (int ks = 0; ks < KS; ++ks) qf[h][ks] = *reinterpret_cast<const bf16x8 *>(qp + 16 * ks);
         lse2[h] = lse[row * H + wave * HPW + h] * kLog2e;
     }
-    // key fragments (A operand) of head-tile j: lane (key l32 of the tile,
-    // half) holds dims 16 ks + 8 half .. +8 of head wave*HPW + j%HPW; keys
-    // past the cache read the last row (never selected)
-    const uint16_t *kb = K + (size_t)b * S * H * D + 8 * half;
-    auto load_kt = [&](int j, bf16x8 (&dst)[KS]) {
+    // key rows of head-tile j (head wave*HPW + j%HPW): load i of a lane is
+    // piece q % P of tile key q / P, q = 64 i + lane, so one instruction reads
+    // whole rows; keys past the cache read the last row (never selected)
+    const uint8_t *kb = reinterpret_cast<const uint8_t *>(K) + (size_t)b * S * H * D * 2;
+    auto load_kt = [&](int j, u32x4 (&dst)[NL]) {
         const int t = t0 + j / HPW;
-        const int key = min(t * kDkKeys + l32, S - 1);
-        const uint16_t *kp = kb + ((size_t)key * H + wave * HPW + j % HPW) * D;
+        const int hh = wave * HPW + j % HPW;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) dst[ks] = *reinterpret_cast<const bf16x8 *>(kp + 16 * ks);
+        for (int i = 0; i < NL; ++i) {
+            const int qq = kWave * i + lane;
+            const int key = min(t * kDkKeys + qq / P, S - 1);
+            dst[i] = *reinterpret_cast<const u32x4 *>(kb + ((size_t)key * H + hh) * D * 2 +
+                                                      16 * (qq % P));
+        }
+    };
+    // through the wave's LDS tile into the A operand: lane (key l32, half)
+    // holds dims 16 ks + 8 half .. +8 (reads 4 banks apart a row: no conflict)
+    uint8_t *kt = ktile[wave];
+    auto to_operand = [&](const u32x4 (&src)[NL], bf16x8 (&af)[KS]) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int qq = kWave * i + lane;
+            *reinterpret_cast<u32x4 *>(kt + (qq / P) * kPitch + 16 * (qq % P)) = src[i];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            af[ks] = *reinterpret_cast<const bf16x8 *>(kt + l32 * kPitch + (16 * ks + 8 * half) * 2);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();  // the next head-tile's writes come after these reads
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
     // the pairs this thread folds: lane L = `lane`, registers 2 wave, 2 wave + 1
     // of every wave's tile sums: query l32, keys kin and kin + 1 of the tile
@@ -370,7 +400,7 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
     const uint32_t *my_bits = bits + row * words;
     const float *my_scores = scores + row * (size_t)S;
     KlState st = {-INFINITY, 0.f, 0.f, 0.f, 0.f};
-    bf16x8 kr[kDkRing][KS];
+    u32x4 kr[kDkRing][NL];
     f32x16 pacc = {};
     float inext[2] = {0.f, 0.f};
     uint32_t bnext = 0u;
@@ -414,11 +444,12 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
                 const int j = j0 + u;
                 load_kt(min(j + 2, njt - 1), kr[(u + 2) % kDkRing]);
                 const int h = u % HPW;
+                bf16x8 af[KS];
+                to_operand(kr[u % kDkRing], af);
                 f32x16 acc = {};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[u % kDkRing][ks], qf[h][ks],
-                                                                  acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[h][ks], acc, 0, 0, 0);
 #pragma unroll
                 for (int rg = 0; rg < 16; ++rg)
                     pacc[rg] += __builtin_amdgcn_exp2f(fmaf(acc[rg], c1, -lse2[h]));

@@ -202,7 +202,7 @@ def test_indexer_kl_ex_workspace(lib):
     ws = lib.dsa_workspace_bytes
     mha = _desc(form=dsa.DSA_MHA, H=16, dqk=128, dv=128)
     need = ws(dsa.DSA_OP_KL, ctypes.byref(mha), 1, 4096, 4096, 1, 1, 2048)
-    rows, words, splits = 4096, 4096 // 32, 4096 // 512
+    rows, words, splits = 4096, 4096 // 32, 4096 // 256
     r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert need == r256(rows * words * 4) + r256(rows * 4) + r256(rows * splits * 20)
     # a sparse selection (k < S/4), the MLA form, fp32 and 32 heads: the

@@ -205,7 +205,7 @@ def _mha_dense_case(w, seed, holes=False):
 @pytest.mark.parametrize("heads,dim", [(16, 128), (8, 128), (16, 64), (8, 64)])
 def test_indexer_kl_mha_masked_dense(heads, dim):
     """The masked-dense MHA form (k >= S/4): 1500 rows and keys, so the query
-    blocks of 32 rows, the 32-key tiles and the splits of 512 keys all end
+    blocks of 32 rows, the 32-key tiles and the splits of 256 keys all end
     ragged; against the oracle's loss over the same selection."""
     w = configs.get("c1").with_(name=f"kl-mha-dense-{heads}x{dim}", B=2, T=1500, S=1500,
                                 index_topk=512, num_heads=heads, d_qk=dim, d_v=dim,
