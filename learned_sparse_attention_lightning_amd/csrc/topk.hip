@@ -99,18 +99,21 @@ __device__ __forceinline__ uint32_t block_flag_scan(bool flag, uint32_t *scratch
     return before + lanes_below(m);
 }
 
-struct SelectSmem {
+template <int NT>  // threads of the workgroup
+struct SelectSmemT {
     uint32_t hist[kTkBins];
-    uint32_t red_lo[kTkWaves], red_hi[kTkWaves];
-    uint32_t scan[kTkWaves];
+    uint32_t red_lo[NT / 64], red_hi[NT / 64];
+    uint32_t scan[NT / 64];
     uint32_t found_bin, found_above;
 };
+using SelectSmem = SelectSmemT<kTkThreads>;
 
 // Smallest and largest of the keys this thread visits, reduced over the
 // workgroup (uniform result).  `each(f)` calls f(key) for every key the
 // calling thread owns.
-template <typename Each>
-__device__ void block_key_range(Each each, SelectSmem &sm, uint32_t &lo_out, uint32_t &hi_out) {
+template <typename Each, int NT>
+__device__ void block_key_range(Each each, SelectSmemT<NT> &sm, uint32_t &lo_out,
+                                uint32_t &hi_out) {
     const int tid = threadIdx.x;
     uint32_t lo = 0xffffffffu, hi = 0u;
     each([&](uint32_t u) {
@@ -130,7 +133,7 @@ __device__ void block_key_range(Each each, SelectSmem &sm, uint32_t &lo_out, uin
     lo = sm.red_lo[0];
     hi = sm.red_hi[0];
 #pragma unroll
-    for (int v = 1; v < kTkWaves; ++v) {
+    for (int v = 1; v < NT / 64; ++v) {
         lo = min(lo, sm.red_lo[v]);
         hi = max(hi, sm.red_hi[v]);
     }
@@ -143,23 +146,23 @@ __device__ void block_key_range(Each each, SelectSmem &sm, uint32_t &lo_out, uin
 // key of the set, over the workgroup), all of which lie in [lo, hi], and how
 // many keys equal to tau belong to the top `need` (need_out).  1 <= need <=
 // number of keys.  Called by all kTkThreads threads; the result is uniform.
-template <typename Each>
+template <typename Each, int NT>
 __device__ void block_select_in(Each each, uint32_t lo, uint32_t hi, uint32_t need,
-                                SelectSmem &sm, uint32_t &tau_out, uint32_t &need_out) {
+                                SelectSmemT<NT> &sm, uint32_t &tau_out, uint32_t &need_out) {
     const int tid = threadIdx.x;
     while (lo != hi) {  // invariant: keys > hi are taken; need more lie in [lo, hi]
         const uint32_t range = hi - lo;
         int shift = 0;
         while ((range >> shift) >= (uint32_t)kTkBins) ++shift;
         const int nb = (int)(range >> shift) + 1;
-        for (int j = tid; j < nb; j += kTkThreads) sm.hist[j] = 0u;
+        for (int j = tid; j < nb; j += NT) sm.hist[j] = 0u;
         __syncthreads();
         each([&](uint32_t u) {
             if (u >= lo && u <= hi) atomicAdd(&sm.hist[(u - lo) >> shift], 1u);
         });
         __syncthreads();
         {  // bin holding the need-th largest: suffix counts over thread-owned bin pairs
-            constexpr int kPer = kTkBins / kTkThreads;  // 2 bins per thread
+            constexpr int kPer = kTkBins / NT;  // bins per thread
             uint32_t hb[kPer], c = 0u;
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
@@ -168,7 +171,7 @@ __device__ void block_select_in(Each each, uint32_t lo, uint32_t hi, uint32_t ne
                 c += hb[j];
             }
             uint32_t tot;
-            const uint32_t pre = block_excl_scan<kTkWaves>(c, sm.scan, tot);
+            const uint32_t pre = block_excl_scan<NT / 64>(c, sm.scan, tot);
             uint32_t run = tot - pre - c;  // keys in bins above this thread's pair
 #pragma unroll
             for (int j = kPer - 1; j >= 0; --j) {
@@ -194,11 +197,11 @@ __device__ void block_select_in(Each each, uint32_t lo, uint32_t hi, uint32_t ne
 }
 
 // block_select_in over keys key_at(0..n-1), range found first.
-template <typename KeyAt>
-__device__ void block_select(KeyAt key_at, int n, uint32_t need, SelectSmem &sm,
+template <typename KeyAt, int NT>
+__device__ void block_select(KeyAt key_at, int n, uint32_t need, SelectSmemT<NT> &sm,
                              uint32_t &tau_out, uint32_t &need_out) {
     auto each = [&](auto f) {
-        for (int p = threadIdx.x; p < n; p += kTkThreads) f(key_at(p));
+        for (int p = threadIdx.x; p < n; p += NT) f(key_at(p));
     };
     uint32_t lo, hi;
     block_key_range(each, sm, lo, hi);
@@ -206,10 +209,11 @@ __device__ void block_select(KeyAt key_at, int n, uint32_t need, SelectSmem &sm,
 }
 
 // ------------------------------------------------------- per-row kernel ----
-struct RowSmem {
-    SelectSmem sel;
-    uint32_t cnt_gt[kTkWaves], cnt_eq[kTkWaves];
-    __align__(16) uint32_t keys[kRowCache];
+template <int NT, int CACHE>
+struct RowSmemT {
+    SelectSmemT<NT> sel;
+    uint32_t cnt_gt[NT / 64], cnt_eq[NT / 64];
+    __align__(16) uint32_t keys[CACHE];
 };
 
 // One workgroup per row.  A cached row is read with 16-byte loads, four in
@@ -218,10 +222,11 @@ struct RowSmem {
 // wave one contiguous segment of positions: a first sweep counts the keys
 // above tau and equal to tau per wave, and after one barrier a second sweep
 // writes the wave's selected positions in order (ballot prefix counts).
-__global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
+template <int NT, int CACHE>
+__global__ __launch_bounds__(NT) void topk_row_kernel(
     const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
     int T, int S, int row0, int k, int cur, int ostride, int32_t *__restrict__ idx) {
-    __shared__ RowSmem sm;
+    __shared__ RowSmemT<NT, CACHE> sm;
     const int r = blockIdx.x;
     const int b = blockIdx.y;
     const int i = row0 + r;
@@ -233,26 +238,26 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
     const int lane = tid & 63, wave = tid >> 6;
 
     if (n <= k) {  // every candidate is selected
-        for (int p = tid; p < k; p += kTkThreads) out[p] = p < n ? p : -1;
+        for (int p = tid; p < k; p += NT) out[p] = p < n ? p : -1;
         return;
     }
-    const bool cached = n <= kRowCache;
+    const bool cached = n <= CACHE;
     const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
     uint32_t lo, hi;
     if (cached) {
-        // 16-byte pieces j = tid + kTkThreads * (4 * it + u), four loads in flight
+        // 16-byte pieces j = tid + NT * (4 * it + u), four loads in flight
         const int n16 = aligned ? n / 4 : 0;  // whole pieces read as vectors
         uint32_t vlo = 0xffffffffu, vhi = 0u;
-        for (int j0 = tid; j0 < n16; j0 += 4 * kTkThreads) {
+        for (int j0 = tid; j0 < n16; j0 += 4 * NT) {
             f32x4 v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int j = j0 + u * kTkThreads;
+                const int j = j0 + u * NT;
                 if (j < n16) v[u] = reinterpret_cast<const f32x4 *>(row)[j];
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int j = j0 + u * kTkThreads;
+                const int j = j0 + u * NT;
                 if (j < n16) {
                     uint32_t kk[4];
 #pragma unroll
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
                 }
             }
         }
-        for (int p = 4 * n16 + tid; p < n; p += kTkThreads) {
+        for (int p = 4 * n16 + tid; p < n; p += NT) {
             const uint32_t u = ordered_key(row[p]);
             sm.keys[p] = u;
             vlo = min(vlo, u);
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
     auto each = [&](auto f) {
         if (cached) {
             const int n16 = (n + 3) / 4;
-            for (int j = tid; j < n16; j += kTkThreads) {
+            for (int j = tid; j < n16; j += NT) {
                 const u32x4 v = reinterpret_cast<const u32x4 *>(sm.keys)[j];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -289,21 +294,21 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
             // latencies rather than one per key a thread reads
             constexpr int U = 8;
             const int n16 = aligned ? n / 4 : 0;
-            for (int j0 = tid; j0 < n16; j0 += U * kTkThreads) {
+            for (int j0 = tid; j0 < n16; j0 += U * NT) {
                 f32x4 v[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int j = j0 + u * kTkThreads;
+                    const int j = j0 + u * NT;
                     if (j < n16) v[u] = reinterpret_cast<const f32x4 *>(row)[j];
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u)
-                    if (j0 + u * kTkThreads < n16) {
+                    if (j0 + u * NT < n16) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) f(ordered_key(v[u][e]));
                     }
             }
-            for (int p = 4 * n16 + tid; p < n; p += kTkThreads) f(ordered_key(row[p]));
+            for (int p = 4 * n16 + tid; p < n; p += NT) f(ordered_key(row[p]));
         }
     };
     if (!cached) block_key_range(each, sm.sel, lo, hi);
@@ -312,13 +317,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(
     block_select_in(each, lo, hi, (uint32_t)k, sm.sel, tau, need);
 
     // ordered selection: all keys > tau, plus the first `need` keys == tau
-    const int seg = ceil_div(ceil_div(n, kTkWaves), 64) * 64;  // positions per wave
+    const int seg = ceil_div(ceil_div(n, (NT / 64)), 64) * 64;  // positions per wave
     const int w0 = wave * seg, w1 = min(n, w0 + seg);
     // sweep 1 counts the wave's keys above and at tau; after the barrier,
     // sweep 2 writes the wave's selected positions from the same keys (a
     // cached row's keys stay in registers between the sweeps)
     const int nit = w1 > w0 ? ceil_div(w1 - w0, 64) : 0;
-    constexpr int kMaxIt = kRowCache / kTkThreads;  // seg <= 64 * kMaxIt when cached
+    constexpr int kMaxIt = CACHE / NT;  // seg <= 64 * kMaxIt when cached
     uint32_t kv[kMaxIt];
     if (cached) {
 #pragma unroll
@@ -832,8 +837,22 @@ hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *
         hipLaunchKernelGGL(topk_wide_resolve_kernel, dim3(rows, B), dim3(kTkThreads), 0, stream,
                            q_pos, T, S, row0, rows, kk, cur, k, idx, L);
     } else if (kk >= 1) {
-        hipLaunchKernelGGL(topk_row_kernel, dim3(rows, B), dim3(kTkThreads), 0, stream, scores,
-                           batch_stride, q_pos, T, S, row0, kk, cur, k, idx);
+        // the longest row of the launch picks the workgroup: short rows go to
+        // small workgroups with small caches, several rows a CU at once
+        const long long n_max = q_pos ? S : std::min<long long>(S, (long long)S - T + row0 + rows);
+        if (n_max <= 4096)
+            hipLaunchKernelGGL((topk_row_kernel<256, 4096>), dim3(rows, B), dim3(256), 0, stream,
+                               scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx);
+        else if (n_max <= 8192)
+            hipLaunchKernelGGL((topk_row_kernel<256, 8192>), dim3(rows, B), dim3(256), 0, stream,
+                               scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx);
+        else if (n_max <= 16384)
+            hipLaunchKernelGGL((topk_row_kernel<512, 16384>), dim3(rows, B), dim3(512), 0, stream,
+                               scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx);
+        else
+            hipLaunchKernelGGL((topk_row_kernel<kTkThreads, kRowCache>), dim3(rows, B),
+                               dim3(kTkThreads), 0, stream, scores, batch_stride, q_pos, T, S,
+                               row0, kk, cur, k, idx);
     }
     if (include_current)
         hipLaunchKernelGGL(topk_current_fix_kernel, dim3(ceil_div(B * rows, 256)), dim3(256), 0,
