@@ -216,6 +216,128 @@ struct RowSmemT {
     __align__(16) uint32_t keys[CACHE];
 };
 
+// Rows longer than the LDS cache: a threshold from a 1/16 sample of the row
+// (runs of 32 consecutive positions, so each sample run is one cache line),
+// then one pass over the row that keeps, per wave and in position order, the
+// keys at or above it; the exact selection then runs on those candidates
+// only, and the row is read about once instead of once per radix pass.
+// Exact whenever at least k keys reach the threshold (the k-th largest is
+// then among them, with all its ties) and every wave's candidates fit its
+// share of the cache; otherwise it returns false with nothing written and
+// the caller runs the full passes.
+constexpr int kSampleRun = 32;
+template <int NT, int CACHE>
+__device__ bool sampled_select(const float *__restrict__ row, int n, int k,
+                               int32_t *__restrict__ out, RowSmemT<NT, CACHE> &sm) {
+    constexpr int W = NT / 64;
+    constexpr int kCap = CACHE / 2 / W;        // candidates per wave
+    constexpr int kMaxRuns = CACHE / 2 / kSampleRun;
+    uint32_t *ck = sm.keys;                    // [W][kCap] keys (samples first)
+    uint32_t *cp = sm.keys + CACHE / 2;        // [W][kCap] positions
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // 1. sample: runs of kSampleRun positions every `stride` (>= 512)
+    int stride = 512;
+    while (n / stride > kMaxRuns) stride *= 2;
+    const int ns = (n / stride) * kSampleRun;
+    for (int m = tid; m < ns; m += NT)
+        ck[m] = ordered_key(row[(size_t)(m / kSampleRun) * stride + m % kSampleRun]);
+    __syncthreads();
+    // the need_s-th largest sample: 1.25 k of the row's share plus a margin
+    const uint32_t need_s =
+        (uint32_t)min((long long)ns, (long long)k * ns * 5 / (4LL * n) + 32);
+    uint32_t tau_s, unused;
+    block_select([&](int j) -> uint32_t { return ck[j]; }, ns, need_s, sm.sel, tau_s, unused);
+    __syncthreads();  // every thread is done with the samples
+    // 2. one pass over the row: each wave keeps its segment's keys >= tau_s
+    const int seg = ceil_div(ceil_div(n, W), 64) * 64;
+    const int w0 = wave * seg, w1 = min(n, w0 + seg);
+    uint32_t *myk = ck + wave * kCap, *myp = cp + wave * kCap;
+    uint32_t cnt = 0u;
+    constexpr int U = 8;
+    for (int p0 = w0; p0 < w1; p0 += 64 * U) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + 64 * u + lane;
+            v[u] = p < w1 ? row[p] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + 64 * u + lane;
+            const uint32_t key = ordered_key(v[u]);
+            const bool c = p < w1 && key >= tau_s;
+            const uint64_t m = __ballot(c);
+            if (c) {
+                const uint32_t slot = cnt + lanes_below(m);
+                if (slot < (uint32_t)kCap) {
+                    myk[slot] = key;
+                    myp[slot] = (uint32_t)p;
+                }
+            }
+            cnt += (uint32_t)__popcll(m);
+        }
+    }
+    if (lane == 0) {
+        sm.cnt_gt[wave] = cnt;
+        sm.cnt_eq[wave] = 0u;
+    }
+    __syncthreads();
+    uint32_t cw[W], total = 0u;
+    bool over = false;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+        cw[v] = sm.cnt_gt[v];
+        over |= cw[v] > (uint32_t)kCap;
+        total += cw[v];
+    }
+    __syncthreads();  // the counts are read before they are reused below
+    if (over || total < (uint32_t)k) return false;  // uniform
+    // 3. exact threshold among the candidates
+    auto each = [&](auto f) {
+        for (int j = tid; j < W * kCap; j += NT) {
+            const int v = j / kCap;
+            if ((uint32_t)(j - v * kCap) < cw[v]) f(ck[j]);
+        }
+    };
+    uint32_t lo, hi, tau, need;
+    block_key_range(each, sm.sel, lo, hi);
+    block_select_in(each, lo, hi, (uint32_t)k, sm.sel, tau, need);
+    // 4. in position order (wave regions in order, each in order): all keys
+    // > tau and the first `need` keys == tau
+    const uint32_t mine = cw[wave];
+    uint32_t c_gt = 0u, c_eq = 0u;
+    for (uint32_t j0 = 0; j0 < mine; j0 += 64) {
+        const uint32_t j = j0 + lane;
+        const uint32_t key = j < mine ? myk[j] : 0u;
+        c_gt += (uint32_t)__popcll(__ballot(j < mine && key > tau));
+        c_eq += (uint32_t)__popcll(__ballot(j < mine && key == tau));
+    }
+    if (lane == 0) {
+        sm.cnt_gt[wave] = c_gt;
+        sm.cnt_eq[wave] = c_eq;
+    }
+    __syncthreads();
+    uint32_t gt_before = 0u, eq_before = 0u;
+    for (int v = 0; v < wave; ++v) {
+        gt_before += sm.cnt_gt[v];
+        eq_before += sm.cnt_eq[v];
+    }
+    uint32_t written = gt_before + min(eq_before, need), ties = eq_before;
+    for (uint32_t j0 = 0; j0 < mine; j0 += 64) {
+        const uint32_t j = j0 + lane;
+        const uint32_t key = j < mine ? myk[j] : 0u;
+        const bool gt = j < mine && key > tau;
+        const bool eq = j < mine && key == tau;
+        const uint64_t eqm = __ballot(eq);
+        const bool take = gt || (eq && ties + lanes_below(eqm) < need);
+        const uint64_t tm = __ballot(take);
+        if (take) out[written + lanes_below(tm)] = (int32_t)myp[j];
+        written += (uint32_t)__popcll(tm);
+        ties += (uint32_t)__popcll(eqm);
+    }
+    return true;
+}
+
 // One workgroup per row.  A cached row is read with 16-byte loads, four in
 // flight per thread, converted to keys on the way into LDS; the threshold
 // search and the selection then read LDS only.  The selection gives each
@@ -243,6 +365,7 @@ __global__ __launch_bounds__(NT) void topk_row_kernel(
     }
     const bool cached = n <= CACHE;
     const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+    if (!cached && sampled_select(row, n, k, out, sm)) return;
     uint32_t lo, hi;
     if (cached) {
         // 16-byte pieces j = tid + NT * (4 * it + u), four loads in flight

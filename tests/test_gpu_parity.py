@@ -190,6 +190,30 @@ def test_topk_many_long_rows():
     assert_selection_equal(idx[:, rows], ref, "many long rows")
 
 
+@pytest.mark.parametrize("case", ["random", "levels", "local", "off-sample", "on-sample"])
+def test_topk_long_rows_every_row(case):
+    """Rows longer than the per-row cache, more rows than the split-row path
+    takes: the threshold comes from a 1/16 sample (runs of 32 positions every
+    512), one pass keeps the keys at or above it, the exact selection runs on
+    those.  Every row against the oracle, for random scores, heavy ties
+    ("levels"), and three distributions that defeat the sample and must take
+    the full passes: the top scores in one contiguous block (one wave's share
+    overflows), only off the sampled runs (far too many candidates), only on
+    them (too few)."""
+    B, T, S, k = 1, 520, 40001, 2048
+    pos = torch.tensor([[S - 1 - 37 * j for j in range(T)]], dtype=torch.int32)
+    sc = synth.random_scores((B, T, S), seed=21, levels=40 if case == "levels" else None)
+    p = torch.arange(S)
+    if case == "local":
+        sc[0, :, 5000:9000] += 8.0
+    elif case == "off-sample":
+        sc[0, :, (p % 512) < 32] -= 8.0
+    elif case == "on-sample":
+        sc[0, :, (p % 512) < 32] += 8.0
+    idx = dsa.dsa_topk(sc.to(DEV), k, q_pos=pos.to(DEV))
+    assert_selection_equal(idx, oracle.topk(sc, k, q_pos=pos), f"long rows {case}")
+
+
 def test_topk_ties_signed_zero_and_short_rows():
     sc = torch.zeros(1, 50, 50)
     sc[0, :, 1::2] = -0.0
