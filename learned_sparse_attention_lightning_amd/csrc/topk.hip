@@ -747,7 +747,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
 #pragma unroll
         for (int f = 0; f < kResolveFetch; ++f) {
             const uint32_t j = (uint32_t)(sub + kResolveSub * f);
-            pre[v][f] = j < cnt[v] ? gcand[(size_t)sl * kWideSlice + j] : make_uint2(0u, 0u);
+            // issued without waiting for the count (only the slice's range
+            // decides); entries past the count are read but never visited
+            const size_t ci = min((size_t)sl * kWideSlice + j, (size_t)S - 1);
+            pre[v][f] = sl < nslices ? gcand[ci] : make_uint2(0u, 0u);
         }
     }
 
