@@ -50,6 +50,24 @@ __device__ __forceinline__ void kl_push(KlState &st, float p, float I) {
     st.Bd += p * (I - st.m);
 }
 
+// kl_push when `take`, else no change, without a branch: a value loaded
+// for a pair that only a branch consumed could be moved into that branch,
+// i.e. next to its use, where its memory latency is no longer hidden.
+__device__ __forceinline__ void kl_push_if(KlState &st, bool take, float p, float I) {
+    const bool first = st.m == -INFINITY;
+    const float mn = fmaxf(st.m, I);
+    const float zr = first ? 0.f : st.z * __expf(st.m - mn);
+    const float bshift = first ? 0.f : st.P * (mn - st.m);
+    const float plogp = p > 0.f ? p * __logf(p) : 0.f;
+    const KlState nx = {mn, zr + __expf(I - mn), st.P + p, st.A + plogp,
+                        st.Bd - bshift + p * (I - mn)};
+    st.m = take ? nx.m : st.m;
+    st.z = take ? nx.z : st.z;
+    st.P = take ? nx.P : st.P;
+    st.A = take ? nx.A : st.A;
+    st.Bd = take ? nx.Bd : st.Bd;
+}
+
 __device__ __forceinline__ KlState kl_merge(KlState a, KlState b) {
     if (b.m == -INFINITY) return a;
     if (a.m == -INFINITY) return b;
@@ -294,9 +312,9 @@ __global__ __launch_bounds__(kMhaKlThreads) void mha_indexer_kl_kernel(
 // rows x one range of 256 keys (a split) x every head: wave w multiplies
 // heads HPW w .. HPW w + HPW-1 (their query fragments in registers, B
 // operand) with the key rows of one 32-key tile at a time (A operand; each
-// head-tile's rows are loaded with whole-row 16-byte pieces, three
-// head-tiles in flight in registers, and pass through a wave-private LDS
-// tile into the operand layout),
+// head-tile's rows are loaded with whole-row 16-byte pieces into one of two
+// register sets, which is refilled two head-tiles ahead as soon as it has
+// passed through a wave-private LDS tile into the operand layout),
 // and adds exp2(S^T scale log2e - lse_h log2e) over its heads; the eight
 // waves' sums meet in LDS (one barrier a tile, two buffers), where each
 // thread takes 2 (key, query) pairs and folds the selected ones into its
@@ -309,18 +327,30 @@ constexpr int kDkThreads = kDkWaves * kWave;
 constexpr int kDkQ = 32;            // query rows per workgroup
 constexpr int kDkKeys = 32;         // keys per tile
 constexpr int kDkSplitTiles = 8;    // tiles per split (256 keys)
-constexpr int kDkRing = 3;          // head-tiles of key fragments in flight
-constexpr int kDkUnroll = 6;        // head-tiles per unrolled body: a multiple of 3, 2 and 1
+constexpr int kDkRing = 2;          // register sets of key fragments (loads two head-tiles ahead)
+constexpr int kDkAhead = 3;         // tiles whose scores and selection words are in flight
+
+// First query block (of kDkQ rows) whose last row reaches split s (keys
+// 256 s ..), with row t at position off + t.  Every later block reaches it.
+__host__ __device__ inline int kl_first_block(int s, int off, int nqb) {
+    const int q = s * kDkSplitTiles * kDkKeys - off - (kDkQ - 1);
+    const int qb = q <= 0 ? 0 : (q + kDkQ - 1) / kDkQ;
+    return qb < nqb ? qb : nqb;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t kl_buffer(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
 
 template <int D, int HPW>
 __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
     const uint32_t *__restrict__ bits, const int32_t *__restrict__ row_hi,
     const float *__restrict__ lse, const float *__restrict__ scores, int T, int S, float scale,
-    int nqb, int nsplit, KlState *__restrict__ part) {
+    int nqb, int nsplit, int nslot, int per_xcd, KlState *__restrict__ part) {
     constexpr int H = kDkWaves * HPW;
     constexpr int KS = D / 16;  // 16-dim k-steps
-    static_assert(kDkUnroll % kDkRing == 0 && kDkUnroll % HPW == 0, "static ring and head");
     constexpr int P = D / 8;                 // 16-byte pieces of a key's head row
     constexpr int NL = kDkKeys * P / kWave;  // loads of a head-tile per lane
     constexpr int kPitch = D * 2 + 16;       // LDS row pitch: rows 4 banks apart
@@ -331,10 +361,31 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
     const int l32 = lane & 31;
-    const int split = blockIdx.x % nsplit;
-    const int rest = blockIdx.x / nsplit;
-    const int qb = nqb - 1 - rest % nqb;  // longest query blocks first
-    const int b = rest / nqb;
+    // workgroup -> (XCD x = id mod 8, batch, split, query block): XCD x
+    // takes the splits 16 m + x and 16 m + 15 - x (m = 0, 1, ...), a short
+    // and a long column of the causal triangle, so the XCDs get equal shares
+    // of the work while each keeps its own key ranges in its L2.  Only the
+    // (split, query block) pairs inside the causal area are launched, in one
+    // run per split, the longest query blocks first: consecutive workgroups
+    // of an XCD go to its shader engines in turn, so work and no-work
+    // workgroups must not alternate.
+    const int xcd = blockIdx.x % 8;
+    const int jx = blockIdx.x / 8;
+    const int b = jx / per_xcd;
+    int rem = jx % per_xcd;
+    int split = -1, qb = 0;
+    for (int k = 0; k < nslot; ++k) {
+        const int sp = 8 * k + ((k & 1) ? 7 - xcd : xcd);
+        if (sp >= nsplit) continue;
+        const int w = nqb - kl_first_block(sp, S - T, nqb);
+        if (rem < w) {
+            split = sp;
+            qb = nqb - 1 - rem;
+            break;
+        }
+        rem -= w;
+    }
+    if (split < 0) return;  // past this XCD's share
     const int words = (S + 31) / 32;
     const int my_r = qb * kDkQ + l32;  // this lane's query row (queries are lanes mod 32)
     const bool live = my_r < T;
@@ -343,10 +394,16 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
     int hi = live ? row_hi[row] : -1;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) hi = max(hi, __shfl_xor(hi, off, 64));
+    hi = __builtin_amdgcn_readfirstlane(hi);  // equal in every lane: keep it scalar
     const int ntiles = hi < 0 ? 0 : hi / kDkKeys + 1;  // the same in every wave
     const int t0 = split * kDkSplitTiles;
     const int t1 = min(ntiles, t0 + kDkSplitTiles);
     const int njt = t1 > t0 ? (t1 - t0) * HPW : 0;  // head-tiles of this wave
+    if (njt == 0) {  // nothing selected in the split by any row of the block
+        if (wave == 0 && half == 0 && live)
+            part[row * nsplit + split] = KlState{-INFINITY, 0.f, 0.f, 0.f, 0.f};
+        return;
+    }
 
     constexpr float kLog2e = 1.4426950408889634f;
     const float c1 = scale * kLog2e;
@@ -362,18 +419,21 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
     }
     // key rows of head-tile j (head wave*HPW + j%HPW): load i of a lane is
     // piece q % P of tile key q / P, q = 64 i + lane, so one instruction reads
-    // whole rows; keys past the cache read the last row (never selected)
-    const uint8_t *kb = reinterpret_cast<const uint8_t *>(K) + (size_t)b * S * H * D * 2;
+    // whole rows.  Buffer loads over this batch's keys: the lane's offset is
+    // fixed, the tile, head and load index only move the scalar offset, and
+    // keys past the cache read as zeros (never selected).
+    constexpr uint32_t kRow = (uint32_t)H * D * 2;  // bytes of one key (every head)
+    const __amdgpu_buffer_rsrc_t krs = kl_buffer(K + (size_t)b * S * H * D, (uint32_t)S * kRow);
+    const uint32_t kvoff = (uint32_t)(lane / P) * kRow + 16u * (uint32_t)(lane % P);
     auto load_kt = [&](int j, u32x4 (&dst)[NL]) {
-        const int t = t0 + j / HPW;
-        const int hh = wave * HPW + j % HPW;
+        const uint32_t t = (uint32_t)(t0 + j / HPW);
+        const uint32_t hh = (uint32_t)(wave * HPW + j % HPW);
+        const uint32_t base = t * kDkKeys * kRow + hh * D * 2;
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const int qq = kWave * i + lane;
-            const int key = min(t * kDkKeys + qq / P, S - 1);
-            dst[i] = *reinterpret_cast<const u32x4 *>(kb + ((size_t)key * H + hh) * D * 2 +
-                                                      16 * (qq % P));
-        }
+        for (int i = 0; i < NL; ++i)
+            dst[i] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           krs, kvoff, base + (uint32_t)i * (kWave / P) * kRow, 0));
     };
     // through the wave's LDS tile into the A operand: lane (key l32, half)
     // holds dims 16 ks + 8 half .. +8 (reads 4 banks apart a row: no conflict)
@@ -397,31 +457,44 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
     // the pairs this thread folds: lane L = `lane`, registers 2 wave, 2 wave + 1
     // of every wave's tile sums: query l32, keys kin and kin + 1 of the tile
     const int kin = 8 * (wave >> 1) + 4 * half + 2 * (wave & 1);
-    const uint32_t *my_bits = bits + row * words;
-    const float *my_scores = scores + row * (size_t)S;
+    // scores and selection words of the block's rows, over buffers that end
+    // at the block's last row (lanes past it read zeros)
+    const size_t brow0 = (size_t)b * T + (size_t)qb * kDkQ;
+    const uint32_t brows = (uint32_t)min(kDkQ, T - qb * kDkQ);
+    const __amdgpu_buffer_rsrc_t srs = kl_buffer(scores + brow0 * S, brows * (uint32_t)S * 4u);
+    const __amdgpu_buffer_rsrc_t brs = kl_buffer(bits + brow0 * words, brows * (uint32_t)words * 4u);
+    const uint32_t svoff = ((uint32_t)l32 * (uint32_t)S + (uint32_t)kin) * 4u;
+    const uint32_t bvoff = (uint32_t)l32 * (uint32_t)words * 4u;
     KlState st = {-INFINITY, 0.f, 0.f, 0.f, 0.f};
     u32x4 kr[kDkRing][NL];
     f32x16 pacc = {};
-    float inext[2] = {0.f, 0.f};
-    uint32_t bnext = 0u;
-    auto fetch_pairs = [&](int t) {  // scores and selection word of tile t for this thread
-        const int key = t * kDkKeys + kin;
-        bnext = my_bits[t];
-        inext[0] = my_scores[min(key, S - 1)];
-        inext[1] = my_scores[min(key + 1, S - 1)];
+    // Scores and selection words of this thread's pairs, TPB tiles ahead: the
+    // scores come from memory once, so their latency is the longest of the
+    // loop's.  The split's tiles are unrolled completely, so every ring slot
+    // is a fixed register set: no copies of registers with loads in flight
+    // (such a copy waits for every load issued before it).
+    constexpr int TPB = kDkAhead;
+    float isc[TPB][2];
+    uint32_t ibw[TPB];
+    auto fetch_pairs = [&](int slot, int t) {
+        const uint32_t so = (uint32_t)t * kDkKeys * 4u;
+        ibw[slot] = __builtin_amdgcn_raw_buffer_load_b32(brs, bvoff, (uint32_t)t * 4u, 0);
+        isc[slot][0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, svoff, so, 0));
+        isc[slot][1] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, svoff + 4u, so, 0));
     };
-    // Head-tiles past the last (up to the unrolled body's end) are computed
-    // on the last one's keys and not folded: every load and every barrier of
-    // the body is then unconditional, so the waits for one head-tile's
-    // fragments never count the loads issued after them.
-    auto tile_done = [&](int t, bool valid) {
+    // A split shorter than kDkSplitTiles tiles (the diagonal one) computes
+    // its last head-tile again in place of the missing ones and does not
+    // fold them: every load and barrier of the unrolled tiles is then
+    // unconditional, so the wait for one head-tile's fragments counts only
+    // the loads issued before them.
+    auto tile_done = [&](int t, bool valid, int slot) {
         const int par = t & 1;
 #pragma unroll
         for (int rg = 0; rg < 16; ++rg) red[par][wave][rg][lane] = pacc[rg];
         pacc = f32x16{};
-        const uint32_t bw = bnext;
-        const float i0 = inext[0], i1 = inext[1];
-        fetch_pairs(min(t + 1, t1 - 1));
+        const uint32_t bw = ibw[slot];
+        const float i0 = isc[slot][0], i1 = isc[slot][1];
+        fetch_pairs(slot, min(t + TPB, t1 - 1));
         lds_barrier();
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -429,32 +502,29 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
             s0 += red[par][v][2 * wave][lane];
             s1 += red[par][v][2 * wave + 1][lane];
         }
-        if (valid && live) {
-            if ((bw >> kin) & 1u) kl_push(st, s0 * (1.0f / H), i0);
-            if ((bw >> (kin + 1)) & 1u) kl_push(st, s1 * (1.0f / H), i1);
-        }
+        const bool fold = valid && live;
+        kl_push_if(st, fold && ((bw >> kin) & 1u), s0 * (1.0f / H), i0);
+        kl_push_if(st, fold && ((bw >> (kin + 1)) & 1u), s1 * (1.0f / H), i1);
     };
     if (njt > 0) {  // uniform over the workgroup
-        fetch_pairs(t0);
+#pragma unroll
+        for (int i = 0; i < TPB; ++i) fetch_pairs(i, min(t0 + i, t1 - 1));
         load_kt(0, kr[0]);
         load_kt(min(1, njt - 1), kr[1]);
-        for (int j0 = 0; j0 < njt; j0 += kDkUnroll) {
 #pragma unroll
-            for (int u = 0; u < kDkUnroll; ++u) {
-                const int j = j0 + u;
-                load_kt(min(j + 2, njt - 1), kr[(u + 2) % kDkRing]);
-                const int h = u % HPW;
-                bf16x8 af[KS];
-                to_operand(kr[u % kDkRing], af);
-                f32x16 acc = {};
+        for (int j = 0; j < kDkSplitTiles * HPW; ++j) {
+            const int h = j % HPW;
+            bf16x8 af[KS];
+            to_operand(kr[j % kDkRing], af);
+            load_kt(min(j + 2, njt - 1), kr[j % kDkRing]);
+            f32x16 acc = {};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[h][ks], acc, 0, 0, 0);
+            for (int ks = 0; ks < KS; ++ks)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[h][ks], acc, 0, 0, 0);
 #pragma unroll
-                for (int rg = 0; rg < 16; ++rg)
-                    pacc[rg] += __builtin_amdgcn_exp2f(fmaf(acc[rg], c1, -lse2[h]));
-                if (h == HPW - 1) tile_done(t0 + min(j, njt - 1) / HPW, j < njt);
-            }
+            for (int rg = 0; rg < 16; ++rg)
+                pacc[rg] += __builtin_amdgcn_exp2f(fmaf(acc[rg], c1, -lse2[h]));
+            if (h == HPW - 1) tile_done(t0 + min(j, njt - 1) / HPW, j < njt, (j / HPW) % TPB);
         }
     }
     // this row's state: lanes l32 and l32 + 32 of every wave hold parts of it
@@ -470,13 +540,16 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
 }
 
 // Loss of each row from the states of its splits.
+// Row t (position S - T + t) has a state in the splits that reach it.
 __global__ __launch_bounds__(256) void kl_split_merge_kernel(const KlState *__restrict__ part,
-                                                             int rows, int nsplit,
+                                                             int rows, int T, int S, int nsplit,
                                                              float *__restrict__ loss) {
     const int r = blockIdx.x * 256 + threadIdx.x;
     if (r >= rows) return;
+    const int pos = S - T + r % T;
+    const int ns = min(nsplit, pos / (kDkSplitTiles * kDkKeys) + 1);
     KlState m = part[(size_t)r * nsplit];
-    for (int s = 1; s < nsplit; ++s) m = kl_merge(m, part[(size_t)r * nsplit + s]);
+    for (int s = 1; s < ns; ++s) m = kl_merge(m, part[(size_t)r * nsplit + s]);
     loss[r] = m.P > 0.f ? m.A / m.P - __logf(m.P) - m.Bd / m.P + __logf(m.z) : 0.f;
 }
 
@@ -526,25 +599,35 @@ hipError_t launch_indexer_kl(const dsa_attn_desc_t &d, const void *q, const void
         if (e != hipSuccess) return e;
         const int nqb = (T + kDkQ - 1) / kDkQ;
         const int nsplit = kl_splits(S);
-        const dim3 g((unsigned)((long long)B * nqb * nsplit));
+        const int nslot = (nsplit + 7) / 8;  // splits per XCD, rounded up
+        int per_xcd = 0;  // launched (split, query block) pairs of the busiest XCD
+        for (int x = 0; x < 8; ++x) {
+            int n = 0;
+            for (int k = 0; k < nslot; ++k) {
+                const int sp = 8 * k + ((k & 1) ? 7 - x : x);
+                if (sp < nsplit) n += nqb - kl_first_block(sp, S - T, nqb);
+            }
+            per_xcd = n > per_xcd ? n : per_xcd;
+        }
+        const dim3 g((unsigned)((long long)B * per_xcd * 8));
         const uint16_t *qq = static_cast<const uint16_t *>(q);
         const uint16_t *kk = static_cast<const uint16_t *>(kv);
         if (d.d_qk == 128 && d.num_heads == 16)
             hipLaunchKernelGGL((mha_kl_dense_kernel<128, 2>), g, dim3(kDkThreads), 0, stream, qq,
-                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, part);
+                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, nslot, per_xcd, part);
         else if (d.d_qk == 128)
             hipLaunchKernelGGL((mha_kl_dense_kernel<128, 1>), g, dim3(kDkThreads), 0, stream, qq,
-                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, part);
+                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, nslot, per_xcd, part);
         else if (d.num_heads == 16)
             hipLaunchKernelGGL((mha_kl_dense_kernel<64, 2>), g, dim3(kDkThreads), 0, stream, qq,
-                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, part);
+                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, nslot, per_xcd, part);
         else
             hipLaunchKernelGGL((mha_kl_dense_kernel<64, 1>), g, dim3(kDkThreads), 0, stream, qq,
-                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, part);
+                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, nslot, per_xcd, part);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kl_split_merge_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256),
-                           0, stream, part, (int)rows, nsplit, loss);
+                           0, stream, part, (int)rows, T, S, nsplit, loss);
         return hipGetLastError();
     }
     if (d.form == DSA_MHA) {
