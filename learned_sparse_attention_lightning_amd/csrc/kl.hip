@@ -511,21 +511,35 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
         for (int i = 0; i < TPB; ++i) fetch_pairs(i, min(t0 + i, t1 - 1));
         load_kt(0, kr[0]);
         load_kt(min(1, njt - 1), kr[1]);
-#pragma unroll
-        for (int j = 0; j < kDkSplitTiles * HPW; ++j) {
-            const int h = j % HPW;
+        // Head-tile j's products go to acc[j & 1] and its exponentials are
+        // taken after head-tile j+1's products are issued: the matrix cores
+        // and the VALU work on different head-tiles.
+        constexpr int NJ = kDkSplitTiles * HPW;
+        f32x16 acc[2];
+        auto products = [&](int j) {
             bf16x8 af[KS];
             to_operand(kr[j % kDkRing], af);
             load_kt(min(j + 2, njt - 1), kr[j % kDkRing]);
-            f32x16 acc = {};
+            f32x16 a = {};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[h][ks], acc, 0, 0, 0);
+                a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], qf[j % HPW][ks], a, 0, 0, 0);
+            acc[j & 1] = a;
+        };
+        auto weights = [&](int j) {
+            const int h = j % HPW;
 #pragma unroll
             for (int rg = 0; rg < 16; ++rg)
-                pacc[rg] += __builtin_amdgcn_exp2f(fmaf(acc[rg], c1, -lse2[h]));
+                pacc[rg] += __builtin_amdgcn_exp2f(fmaf(acc[j & 1][rg], c1, -lse2[h]));
             if (h == HPW - 1) tile_done(t0 + min(j, njt - 1) / HPW, j < njt, (j / HPW) % TPB);
+        };
+        products(0);
+#pragma unroll
+        for (int j = 1; j < NJ; ++j) {
+            products(j);
+            weights(j - 1);
         }
+        weights(NJ - 1);
     }
     // this row's state: lanes l32 and l32 + 32 of every wave hold parts of it
     st = kl_merge(st, kl_shfl_xor(st, 32));
