@@ -498,7 +498,8 @@ def run_prefill(w, args, dev, peaks, with_cpu):
     apk = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_VECTOR_TFLOPS
     apk_meas = peaks.get("mfma_bf16_tflops") if w.dtype == "bf16" else None
     # the stage time covers every launch of one attention call (for the MHA
-    # masked-dense form: the selection bitmap, then the attention)
+    # masked-dense form: the selection bitmap, then the attention; inside the
+    # forward the top-k writes that bitmap and only the attention runs)
     att_kernel = ("mla_attention_kernel" if w.form == "mla" else
                   "mha_bitmap_kernel+mha_fa_kernel" if w.dtype == "bf16" else
                   "attention_gather_kernel")

@@ -140,13 +140,14 @@ size_t attention_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int S, 
 hipError_t launch_attention(const dsa_attn_desc_t &d, const void *q, const void *kv,
                             const void *v, const int32_t *idx, int B, int T, int S, int row0,
                             int rows, int k, void *out, float *lse, void *workspace,
-                            hipStream_t stream, const int32_t *q_pos, bool causal_tail) {
+                            hipStream_t stream, const int32_t *q_pos, bool causal_tail,
+                            bool bitmap_ready) {
     if (mla_fast_path(d))
         return launch_mla(d, q, kv, idx, B, T, S, row0, rows, k, out, lse, workspace, stream,
                           q_pos, causal_tail);
     if (mha_dense_path(d, rows, S, k) && workspace)
         return launch_mha_dense(d, q, kv, v, idx, B, T, S, row0, rows, k, out, lse, workspace,
-                                stream);
+                                stream, bitmap_ready);
     const bool in_bf16 = d.dtype == DSA_BF16;
     const bool out_bf16 = d.out_dtype == DSA_BF16;
     if (in_bf16 && out_bf16)

@@ -517,16 +517,25 @@ hipError_t launch_selection_bitmap(const int32_t *idx, int B, int T, int S, int 
     return hipSuccess;
 }
 
+void mha_bitmap_of(void *workspace, int B, int rows, int S, uint32_t **bits, int32_t **row_hi) {
+    const size_t words = (size_t)(S + 31) / 32;
+    *bits = static_cast<uint32_t *>(workspace);
+    *row_hi = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) +
+                                          align256((size_t)B * rows * words * 4));
+}
+
 hipError_t launch_mha_dense(const dsa_attn_desc_t &d, const void *q, const void *kv,
                             const void *v, const int32_t *idx, int B, int T, int S, int row0,
                             int rows, int k, void *out, float *lse, void *workspace,
-                            hipStream_t stream) {
-    const size_t words = (size_t)(S + 31) / 32;
-    uint32_t *bits = static_cast<uint32_t *>(workspace);
-    int32_t *row_hi = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) +
-                                                  align256((size_t)B * rows * words * 4));
-    hipError_t e = launch_selection_bitmap(idx, B, T, S, row0, rows, k, bits, row_hi, stream);
-    if (e != hipSuccess) return e;
+                            hipStream_t stream, bool bitmap_ready) {
+    uint32_t *bits;
+    int32_t *row_hi;
+    mha_bitmap_of(workspace, B, rows, S, &bits, &row_hi);
+    if (!bitmap_ready) {
+        const hipError_t e =
+            launch_selection_bitmap(idx, B, T, S, row0, rows, k, bits, row_hi, stream);
+        if (e != hipSuccess) return e;
+    }
     const int nqb = (rows + kFaQ - 1) / kFaQ;
     const long long units = (long long)B * nqb * d.num_heads;
     const dim3 grid((unsigned)units);

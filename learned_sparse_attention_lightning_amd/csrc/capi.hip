@@ -159,6 +159,7 @@ dsa_status_t forward_run(const dsa_attn_desc_t *desc, const void *q_idx, const v
     for (int row0 = 0; row0 < T; row0 += rows) {
         const int n = T - row0 < rows ? T - row0 : rows;
         hipError_t e;
+        bool bitmap_ready = false;
         if (dense) {
             e = launch_select_all(q_pos, B, T, S, row0, n, index_topk, sel, s);
         } else {
@@ -169,13 +170,22 @@ dsa_status_t forward_run(const dsa_attn_desc_t *desc, const void *q_idx, const v
                                index_head_dim, row0, n, score_block, batch_stride, false,
                                static_cast<uint32_t *>(topk_ws), clear_words, s);
             if (e != hipSuccess) return DSA_ERR_HIP;
+            // the masked-dense MHA attention takes the selection as a bitmap:
+            // where the per-row top-k runs, it writes that bitmap too, in
+            // place of a separate pass over the selection
+            uint32_t *bits = nullptr;
+            int32_t *row_hi = nullptr;
+            if (mha_dense_path(*desc, n, S, index_topk) &&
+                topk_writes_bitmap(B, n, S, index_topk, include_current))
+                mha_bitmap_of(attn_ws, B, n, S, &bits, &row_hi);
             e = launch_topk(score_block, batch_stride, q_pos, B, T, S, row0, n, index_topk, sel,
-                            topk_ws, clear_words > 0, s, include_current);
+                            topk_ws, clear_words > 0, s, include_current, bits, row_hi);
+            bitmap_ready = bits != nullptr;
         }
         if (e != hipSuccess) return DSA_ERR_HIP;
         // the selection just written is min(k, t+1) positions then -1 per row
         e = launch_attention(*desc, q, kv, v, sel, B, T, S, row0, n, index_topk, out, nullptr,
-                             attn_ws, s, q_pos, true);
+                             attn_ws, s, q_pos, true, bitmap_ready);
         if (e != hipSuccess) return DSA_ERR_HIP;
     }
     return DSA_OK;

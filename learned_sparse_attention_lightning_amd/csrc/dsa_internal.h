@@ -114,9 +114,14 @@ size_t topk_workspace_bytes(int B, int T, int S, int k);
 size_t topk_clear_words(int B, int rows, int S);
 // include_current: the query's own position is always selected and the
 // other k-1 slots are ranked among the earlier positions.
+// bits / row_hi (optional, where topk_writes_bitmap holds): the selection
+// also as the bitmap and per-row bound that launch_selection_bitmap writes
+// (row_hi = n - 1, an upper bound of the last selected position).
+bool topk_writes_bitmap(int B, int rows, int S, int k, bool include_current);
 hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *q_pos, int B,
                        int T, int S, int row0, int rows, int k, int32_t *idx, void *workspace,
-                       bool workspace_cleared, hipStream_t stream, bool include_current);
+                       bool workspace_cleared, hipStream_t stream, bool include_current,
+                       uint32_t *bits = nullptr, int32_t *row_hi = nullptr);
 // Selection of every candidate (for rows whose causal length is at most k).
 hipError_t launch_select_all(const int32_t *q_pos, int B, int T, int S, int row0, int rows,
                              int k, int32_t *idx, hipStream_t stream);
@@ -136,10 +141,14 @@ hipError_t launch_selection_bitmap(const int32_t *idx, int B, int T, int S, int 
 
 bool mha_dense_path(const dsa_attn_desc_t &d, int rows, int S, int k);
 size_t mha_workspace_bytes(int B, int rows, int S);
+// Where launch_mha_dense keeps the selection bitmap and per-row bound in its
+// workspace (for a launch of `rows` rows).
+void mha_bitmap_of(void *workspace, int B, int rows, int S, uint32_t **bits, int32_t **row_hi);
+// bitmap_ready: the workspace already holds them (written by the top-k)
 hipError_t launch_mha_dense(const dsa_attn_desc_t &d, const void *q, const void *kv,
                             const void *v, const int32_t *idx, int B, int T, int S, int row0,
                             int rows, int k, void *out, float *lse, void *workspace,
-                            hipStream_t stream);
+                            hipStream_t stream, bool bitmap_ready = false);
 bool mla_fast_path(const dsa_attn_desc_t &d);
 size_t mla_workspace_bytes(const dsa_attn_desc_t &d, int B, int T, int k);
 // causal_tail: every row's selection is min(k, t+1) positions followed by -1
@@ -154,6 +163,6 @@ hipError_t launch_attention(const dsa_attn_desc_t &d, const void *q, const void 
                             const void *v, const int32_t *idx, int B, int T, int S, int row0,
                             int rows, int k, void *out, float *lse, void *workspace,
                             hipStream_t stream, const int32_t *q_pos = nullptr,
-                            bool causal_tail = false);
+                            bool causal_tail = false, bool bitmap_ready = false);
 
 }  // namespace dsa

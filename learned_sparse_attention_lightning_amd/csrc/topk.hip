@@ -344,10 +344,16 @@ __device__ bool sampled_select(const float *__restrict__ row, int n, int k,
 // wave one contiguous segment of positions: a first sweep counts the keys
 // above tau and equal to tau per wave, and after one barrier a second sweep
 // writes the wave's selected positions in order (ballot prefix counts).
+//
+// bits (optional, rows no longer than CACHE): the selection also as one bit
+// per position, bits[(b * rows + r) * words + p / 32] bit p % 32 (every word
+// of the row written, zeros past the candidates), and row_hi[b * rows + r] =
+// n - 1 (no selected position lies beyond it; -1 for an empty row).
 template <int NT, int CACHE>
 __global__ __launch_bounds__(NT) void topk_row_kernel(
     const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
-    int T, int S, int row0, int k, int cur, int ostride, int32_t *__restrict__ idx) {
+    int T, int S, int row0, int k, int cur, int ostride, int32_t *__restrict__ idx,
+    uint32_t *__restrict__ bits, int32_t *__restrict__ row_hi, int words) {
     __shared__ RowSmemT<NT, CACHE> sm;
     const int r = blockIdx.x;
     const int b = blockIdx.y;
@@ -358,14 +364,23 @@ __global__ __launch_bounds__(NT) void topk_row_kernel(
     const int n = t < 0 ? 0 : t + 1;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    uint32_t *brow = bits ? bits + ((size_t)b * gridDim.x + r) * words : nullptr;
+    if (bits && tid == 0) row_hi[(size_t)b * gridDim.x + r] = n - 1;
 
     if (n <= k) {  // every candidate is selected
         for (int p = tid; p < k; p += NT) out[p] = p < n ? p : -1;
+        if (bits)
+            for (int wd = tid; wd < words; wd += NT) {
+                const int p0 = 32 * wd;
+                brow[wd] = p0 + 32 <= n ? 0xffffffffu : p0 >= n ? 0u : (1u << (n - p0)) - 1u;
+            }
         return;
     }
+    if (bits)  // words past the waves' 64-position runs below
+        for (int wd = 2 * ((n + 63) / 64) + tid; wd < words; wd += NT) brow[wd] = 0u;
     const bool cached = n <= CACHE;
     const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-    if (!cached && sampled_select(row, n, k, out, sm)) return;
+    if (!cached && !bits && sampled_select(row, n, k, out, sm)) return;
     uint32_t lo, hi;
     if (cached) {
         // 16-byte pieces j = tid + NT * (4 * it + u), four loads in flight
@@ -498,6 +513,11 @@ __global__ __launch_bounds__(NT) void topk_row_kernel(
         const bool take = gt || (eq && ties + lanes_below(eqm) < need);
         const uint64_t tm = __ballot(take);
         if (take) out[written + lanes_below(tm)] = p;
+        if (bits && lane == 0) {  // positions p - lane .. p - lane + 63: two words
+            const int wd = (p - lane) / 32;
+            brow[wd] = (uint32_t)tm;
+            if (wd + 1 < words) brow[wd + 1] = (uint32_t)(tm >> 32);
+        }
         written += (uint32_t)__popcll(tm);
         ties += (uint32_t)__popcll(eqm);
     });
@@ -942,12 +962,20 @@ size_t topk_clear_words(int B, int rows, int S) {
     return (size_t)B * rows * (2 * kDigits + kMetaWords);
 }
 
+bool topk_writes_bitmap(int B, int rows, int S, int k, bool include_current) {
+    return !include_current && k >= 1 && !use_wide(B, rows, S);
+}
+
 hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *q_pos, int B,
                        int T, int S, int row0, int rows, int k, int32_t *idx, void *workspace,
-                       bool workspace_cleared, hipStream_t stream, bool include_current) {
+                       bool workspace_cleared, hipStream_t stream, bool include_current,
+                       uint32_t *bits, int32_t *row_hi) {
     // the current-token variant selects k-1 among the positions before t
     const int cur = include_current ? 1 : 0;
     const int kk = k - cur;
+    const int words = (S + 31) / 32;
+    if (bits && !(topk_writes_bitmap(B, rows, S, k, include_current) && row_hi))
+        return hipErrorInvalidValue;
     if (kk >= 1 && use_wide(B, rows, S) && workspace) {
         const WideLayout L = wide_layout(workspace, B * rows, S);
         const int nrows = B * rows;
@@ -968,17 +996,20 @@ hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *
         const long long n_max = q_pos ? S : std::min<long long>(S, (long long)S - T + row0 + rows);
         if (n_max <= 4096)
             hipLaunchKernelGGL((topk_row_kernel<256, 4096>), dim3(rows, B), dim3(256), 0, stream,
-                               scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx);
+                               scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx, bits, row_hi,
+                               words);
         else if (n_max <= 8192)
             hipLaunchKernelGGL((topk_row_kernel<256, 8192>), dim3(rows, B), dim3(256), 0, stream,
-                               scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx);
+                               scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx, bits, row_hi,
+                               words);
         else if (n_max <= 16384)
             hipLaunchKernelGGL((topk_row_kernel<512, 16384>), dim3(rows, B), dim3(512), 0, stream,
-                               scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx);
+                               scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx, bits, row_hi,
+                               words);
         else
             hipLaunchKernelGGL((topk_row_kernel<kTkThreads, kRowCache>), dim3(rows, B),
                                dim3(kTkThreads), 0, stream, scores, batch_stride, q_pos, T, S,
-                               row0, kk, cur, k, idx);
+                               row0, kk, cur, k, idx, bits, row_hi, words);
     }
     if (include_current)
         hipLaunchKernelGGL(topk_current_fix_kernel, dim3(ceil_div(B * rows, 256)), dim3(256), 0,
