@@ -355,7 +355,9 @@ __global__ __launch_bounds__(NT) void topk_row_kernel(
     int T, int S, int row0, int k, int cur, int ostride, int32_t *__restrict__ idx,
     uint32_t *__restrict__ bits, int32_t *__restrict__ row_hi, int words) {
     __shared__ RowSmemT<NT, CACHE> sm;
-    const int r = blockIdx.x;
+    // the last rows first: without explicit positions they are the longest,
+    // so the short ones fill in at the end rather than trailing behind them
+    const int r = gridDim.x - 1 - blockIdx.x;
     const int b = blockIdx.y;
     const int i = row0 + r;
     const int t = query_pos(q_pos, b, i, T, S) - cur;  // last candidate position
