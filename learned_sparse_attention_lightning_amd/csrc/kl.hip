@@ -364,26 +364,30 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
     // workgroup -> (XCD x = id mod 8, batch, split, query block): XCD x
     // takes the splits 16 m + x and 16 m + 15 - x (m = 0, 1, ...), a short
     // and a long column of the causal triangle, so the XCDs get equal shares
-    // of the work while each keeps its own key ranges in its L2.  Only the
-    // (split, query block) pairs inside the causal area are launched, in one
-    // run per split, the longest query blocks first: consecutive workgroups
-    // of an XCD go to its shader engines in turn, so work and no-work
-    // workgroups must not alternate.
+    // of the work while each keeps its own key ranges in its L2.  First the
+    // (split, query block) pairs inside the causal area, one run per split,
+    // the longest query blocks first; then the pairs past it, which only a
+    // selection of later positions gives work (most end at once).
+    // Consecutive workgroups of an XCD go to its shader engines in turn, so
+    // work and no-work workgroups must not alternate.
     const int xcd = blockIdx.x % 8;
     const int jx = blockIdx.x / 8;
     const int b = jx / per_xcd;
     int rem = jx % per_xcd;
     int split = -1, qb = 0;
-    for (int k = 0; k < nslot; ++k) {
-        const int sp = 8 * k + ((k & 1) ? 7 - xcd : xcd);
-        if (sp >= nsplit) continue;
-        const int w = nqb - kl_first_block(sp, S - T, nqb);
-        if (rem < w) {
-            split = sp;
-            qb = nqb - 1 - rem;
-            break;
+    for (int pass = 0; pass < 2 && split < 0; ++pass) {
+        for (int k = 0; k < nslot; ++k) {
+            const int sp = 8 * k + ((k & 1) ? 7 - xcd : xcd);
+            if (sp >= nsplit) continue;
+            const int first = kl_first_block(sp, S - T, nqb);
+            const int w = pass == 0 ? nqb - first : first;
+            if (rem < w) {
+                split = sp;
+                qb = pass == 0 ? nqb - 1 - rem : rem;
+                break;
+            }
+            rem -= w;
         }
-        rem -= w;
     }
     if (split < 0) return;  // past this XCD's share
     const int words = (S + 31) / 32;
@@ -554,16 +558,13 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
 }
 
 // Loss of each row from the states of its splits.
-// Row t (position S - T + t) has a state in the splits that reach it.
 __global__ __launch_bounds__(256) void kl_split_merge_kernel(const KlState *__restrict__ part,
-                                                             int rows, int T, int S, int nsplit,
+                                                             int rows, int nsplit,
                                                              float *__restrict__ loss) {
     const int r = blockIdx.x * 256 + threadIdx.x;
     if (r >= rows) return;
-    const int pos = S - T + r % T;
-    const int ns = min(nsplit, pos / (kDkSplitTiles * kDkKeys) + 1);
     KlState m = part[(size_t)r * nsplit];
-    for (int s = 1; s < ns; ++s) m = kl_merge(m, part[(size_t)r * nsplit + s]);
+    for (int s = 1; s < nsplit; ++s) m = kl_merge(m, part[(size_t)r * nsplit + s]);
     loss[r] = m.P > 0.f ? m.A / m.P - __logf(m.P) - m.Bd / m.P + __logf(m.z) : 0.f;
 }
 
@@ -614,13 +615,11 @@ hipError_t launch_indexer_kl(const dsa_attn_desc_t &d, const void *q, const void
         const int nqb = (T + kDkQ - 1) / kDkQ;
         const int nsplit = kl_splits(S);
         const int nslot = (nsplit + 7) / 8;  // splits per XCD, rounded up
-        int per_xcd = 0;  // launched (split, query block) pairs of the busiest XCD
+        int per_xcd = 0;  // (split, query block) pairs of the XCD with the most splits
         for (int x = 0; x < 8; ++x) {
             int n = 0;
-            for (int k = 0; k < nslot; ++k) {
-                const int sp = 8 * k + ((k & 1) ? 7 - x : x);
-                if (sp < nsplit) n += nqb - kl_first_block(sp, S - T, nqb);
-            }
+            for (int k = 0; k < nslot; ++k)
+                if (8 * k + ((k & 1) ? 7 - x : x) < nsplit) n += nqb;
             per_xcd = n > per_xcd ? n : per_xcd;
         }
         const dim3 g((unsigned)((long long)B * per_xcd * 8));
@@ -641,7 +640,7 @@ hipError_t launch_indexer_kl(const dsa_attn_desc_t &d, const void *q, const void
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kl_split_merge_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256),
-                           0, stream, part, (int)rows, T, S, nsplit, loss);
+                           0, stream, part, (int)rows, nsplit, loss);
         return hipGetLastError();
     }
     if (d.form == DSA_MHA) {

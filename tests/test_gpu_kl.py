@@ -176,15 +176,17 @@ def test_indexer_kl_mha_dense_warmup_target():
     _check(loss, ref, "MHA dense warm-up")
 
 
-def _mha_dense_case(w, seed, holes=False):
+def _mha_dense_case(w, seed, holes=False, any_position=False):
     """Seeded inputs, integer-valued scores and the oracle's own selection
-    (ranked, or shuffled with holes), the GPU attention's lse over it, then
-    the GPU loss and the oracle's."""
+    (ranked, or shuffled with holes; any_position: every row ranks all S
+    positions, so early rows also select later ones), the GPU attention's
+    lse over it, then the GPU loss and the oracle's."""
     x = synth.make_inputs(w, device=DEV, seed=seed)
     desc = dsa.desc_for(w)
     g = torch.Generator().manual_seed(seed)
     sc = torch.randint(-64, 64, (w.B, w.T, w.S), generator=g).to(torch.float32) / 8
-    sel = oracle.topk(sc, w.index_topk)
+    pos = np.full((w.B, w.T), w.S - 1, dtype=np.int32) if any_position else None
+    sel = oracle.topk(sc, w.index_topk, q_pos=pos)
     if holes:  # unordered rows, a few entries dropped (still distinct positions)
         rng = np.random.default_rng(seed)
         for b in range(w.B):
@@ -212,6 +214,27 @@ def test_indexer_kl_mha_masked_dense(heads, dim):
                                 index_n_heads=4, index_head_dim=32)
     loss, ref = _mha_dense_case(w, seed=61)
     _check(loss, ref, f"MHA masked-dense {heads}x{dim}")
+
+
+def test_indexer_kl_mha_masked_dense_rows_at_the_end():
+    """Rows at the end of a longer cache (row t at position S - T + t) and 20
+    key splits (three per XCD, the last XCD slot partly past the last
+    split): every launched (split, query block) pair and only those."""
+    w = configs.get("c1").with_(name="kl-mha-dense-offset", B=2, T=300, S=5000,
+                                index_topk=1300, num_heads=16, d_qk=64, d_v=64,
+                                index_n_heads=4, index_head_dim=32)
+    loss, ref = _mha_dense_case(w, seed=63)
+    _check(loss, ref, "MHA masked-dense, rows at the end of a 5000-key cache")
+
+
+def test_indexer_kl_mha_masked_dense_any_position():
+    """Selections that include positions past a row's own (the entry point
+    takes any distinct positions < S): the key ranges past the causal area
+    are launched too, after it, and fold what is selected there."""
+    w = configs.get("c1").with_(name="kl-mha-dense-any", B=1, T=700, S=700, index_topk=256,
+                                num_heads=8, d_qk=64, d_v=64, index_n_heads=4, index_head_dim=32)
+    loss, ref = _mha_dense_case(w, seed=64, any_position=True)
+    _check(loss, ref, "MHA masked-dense, selections past the row's position")
 
 
 def test_indexer_kl_mha_masked_dense_holes():
