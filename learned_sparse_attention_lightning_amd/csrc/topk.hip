@@ -1008,6 +1008,11 @@ hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *
             hipLaunchKernelGGL((topk_row_kernel<512, 16384>), dim3(rows, B), dim3(512), 0, stream,
                                scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx, bits, row_hi,
                                words);
+        else if (n_max > kRowCache)  // rows past any cache: the sampled path, two
+                                     // workgroups a CU with the smaller cache
+            hipLaunchKernelGGL((topk_row_kernel<512, 16384>), dim3(rows, B), dim3(512), 0, stream,
+                               scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx, bits,
+                               row_hi, words);
         else
             hipLaunchKernelGGL((topk_row_kernel<kTkThreads, kRowCache>), dim3(rows, B),
                                dim3(kTkThreads), 0, stream, scores, batch_stride, q_pos, T, S,
