@@ -31,7 +31,6 @@ namespace {
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kTkBins = 2048;
-constexpr int kRowCache = 32768;  // scores cached in LDS by the per-row kernel
 
 // wide-row path
 constexpr int kWideThreads = 256;
@@ -965,7 +964,9 @@ size_t topk_clear_words(int B, int rows, int S) {
 }
 
 bool topk_writes_bitmap(int B, int rows, int S, int k, bool include_current) {
-    return !include_current && k >= 1 && !use_wide(B, rows, S);
+    // per-row kernel with every row in its LDS cache (a longer row writes the
+    // bitmap only through the full passes, not the faster sampled path)
+    return !include_current && k >= 1 && !use_wide(B, rows, S) && S <= 16384;
 }
 
 hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *q_pos, int B,
@@ -994,7 +995,9 @@ hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *
                            q_pos, T, S, row0, rows, kk, cur, k, idx, L);
     } else if (kk >= 1) {
         // the longest row of the launch picks the workgroup: short rows go to
-        // small workgroups with small caches, several rows a CU at once
+        // small workgroups with small caches, several rows a CU at once; rows
+        // past 16384 keys take the sampled path of the 16384-key tier (two
+        // workgroups a CU), which beat caching them in a 128 KB workgroup
         const long long n_max = q_pos ? S : std::min<long long>(S, (long long)S - T + row0 + rows);
         if (n_max <= 4096)
             hipLaunchKernelGGL((topk_row_kernel<256, 4096>), dim3(rows, B), dim3(256), 0, stream,
@@ -1004,19 +1007,10 @@ hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *
             hipLaunchKernelGGL((topk_row_kernel<256, 8192>), dim3(rows, B), dim3(256), 0, stream,
                                scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx, bits, row_hi,
                                words);
-        else if (n_max <= 16384)
+        else
             hipLaunchKernelGGL((topk_row_kernel<512, 16384>), dim3(rows, B), dim3(512), 0, stream,
                                scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx, bits, row_hi,
                                words);
-        else if (n_max > kRowCache)  // rows past any cache: the sampled path, two
-                                     // workgroups a CU with the smaller cache
-            hipLaunchKernelGGL((topk_row_kernel<512, 16384>), dim3(rows, B), dim3(512), 0, stream,
-                               scores, batch_stride, q_pos, T, S, row0, kk, cur, k, idx, bits,
-                               row_hi, words);
-        else
-            hipLaunchKernelGGL((topk_row_kernel<kTkThreads, kRowCache>), dim3(rows, B),
-                               dim3(kTkThreads), 0, stream, scores, batch_stride, q_pos, T, S,
-                               row0, kk, cur, k, idx, bits, row_hi, words);
     }
     if (include_current)
         hipLaunchKernelGGL(topk_current_fix_kernel, dim3(ceil_div(B * rows, 256)), dim3(256), 0,

@@ -410,13 +410,14 @@ def test_forward_repeatable_bitwise():
     (2, 300, 300, 96, 64),       # S not a multiple of 64; rows with n <= k and n > k
     (1, 200, 1000, 256, 128),    # rows at the end of a longer cache
     (1, 1024, 1024, 256, 128),   # 8 query blocks of 128 rows
-    (1, 600, 40000, 10000, 64),  # rows longer than the top-k's LDS cache (not the wide path)
+    (1, 600, 40000, 10000, 64),  # rows past the top-k's LDS cache: the separate bitmap pass
 ])
 def test_forward_mha_bitmap_from_topk(B, T, S, k, d):
     """In the forward, the per-row top-k also writes the selection bitmap the
     masked-dense MHA attention reads (and the separate bitmap pass is
-    skipped): selection and output must equal the step-by-step path (scores,
-    top-k, attention through their own entry points) bit for bit."""
+    skipped) where every row fits its LDS cache: selection and output must
+    equal the step-by-step path (scores, top-k, attention through their own
+    entry points) bit for bit."""
     w = configs.get("c1").with_(name="mha-fused", B=B, T=T, S=S, index_topk=k, num_heads=2,
                                 d_qk=d, d_v=d, scale=1.0 / math.sqrt(d))
     _say(f"fused bitmap B={B} T={T} S={S} k={k} d={d}")
