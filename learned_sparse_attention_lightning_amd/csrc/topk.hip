@@ -238,8 +238,29 @@ __device__ bool sampled_select(const float *__restrict__ row, int n, int k,
     int stride = 512;
     while (n / stride > kMaxRuns) stride *= 2;
     const int ns = (n / stride) * kSampleRun;
-    for (int m = tid; m < ns; m += NT)
-        ck[m] = ordered_key(row[(size_t)(m / kSampleRun) * stride + m % kSampleRun]);
+    const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+    if (aligned) {  // 16-byte pieces of the runs, every load issued before any is used
+        constexpr int kVec = CACHE / 2 / 4 / NT;  // ns <= CACHE / 2
+        f32x4 sv[kVec];
+#pragma unroll
+        for (int u = 0; u < kVec; ++u) {
+            const int m = 4 * (tid + u * NT);
+            sv[u] = m < ns ? *reinterpret_cast<const f32x4 *>(
+                                 row + (size_t)(m / kSampleRun) * stride + m % kSampleRun)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < kVec; ++u) {
+            const int m = 4 * (tid + u * NT);
+            if (m < ns)
+                *reinterpret_cast<u32x4 *>(ck + m) =
+                    u32x4{ordered_key(sv[u][0]), ordered_key(sv[u][1]), ordered_key(sv[u][2]),
+                          ordered_key(sv[u][3])};
+        }
+    } else {
+        for (int m = tid; m < ns; m += NT)
+            ck[m] = ordered_key(row[(size_t)(m / kSampleRun) * stride + m % kSampleRun]);
+    }
     __syncthreads();
     // the need_s-th largest sample: 1.25 k of the row's share plus a margin
     const uint32_t need_s =
@@ -247,33 +268,78 @@ __device__ bool sampled_select(const float *__restrict__ row, int n, int k,
     uint32_t tau_s, unused;
     block_select([&](int j) -> uint32_t { return ck[j]; }, ns, need_s, sm.sel, tau_s, unused);
     __syncthreads();  // every thread is done with the samples
-    // 2. one pass over the row: each wave keeps its segment's keys >= tau_s
-    const int seg = ceil_div(ceil_div(n, W), 64) * 64;
+    // 2. one pass over the row: each wave keeps its segment's keys >= tau_s,
+    // in position order.  Segments are whole multiples of 256 positions, so
+    // with an aligned row every 16-byte piece but the row's last lies inside
+    // one wave's segment; a lane takes 4 consecutive keys per piece, eight
+    // pieces in flight.
+    const int seg = ceil_div(ceil_div(n, W), 256) * 256;
     const int w0 = wave * seg, w1 = min(n, w0 + seg);
     uint32_t *myk = ck + wave * kCap, *myp = cp + wave * kCap;
     uint32_t cnt = 0u;
-    constexpr int U = 8;
-    for (int p0 = w0; p0 < w1; p0 += 64 * U) {
-        float v[U];
+    if (aligned) {
+        constexpr int U = 8;
+        for (int p0 = w0; p0 < w1; p0 += 256 * U) {
+            f32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = p0 + 64 * u + lane;
-            v[u] = p < w1 ? row[p] : 0.0f;
-        }
+            for (int u = 0; u < U; ++u) {
+                const int p = p0 + 256 * u + 4 * lane;
+                if (p + 4 <= w1) {
+                    v[u] = *reinterpret_cast<const f32x4 *>(row + p);
+                } else {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = p0 + 64 * u + lane;
-            const uint32_t key = ordered_key(v[u]);
-            const bool c = p < w1 && key >= tau_s;
-            const uint64_t m = __ballot(c);
-            if (c) {
-                const uint32_t slot = cnt + lanes_below(m);
-                if (slot < (uint32_t)kCap) {
-                    myk[slot] = key;
-                    myp[slot] = (uint32_t)p;
+                    for (int e = 0; e < 4; ++e) v[u][e] = p + e < w1 ? row[p + e] : 0.0f;
                 }
             }
-            cnt += (uint32_t)__popcll(m);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int p = p0 + 256 * u + 4 * lane;
+                uint32_t key[4], take = 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    key[e] = ordered_key(v[u][e]);
+                    if (p + e < w1 && key[e] >= tau_s) take |= 1u << e;
+                }
+                // this lane's count and the wave's prefix of counts (three ballots)
+                const uint32_t c = (uint32_t)__popc(take);
+                const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
+                uint32_t slot = cnt + lanes_below(b0) + 2u * lanes_below(b1) + 4u * lanes_below(b2);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (take & (1u << e)) {
+                        if (slot < (uint32_t)kCap) {
+                            myk[slot] = key[e];
+                            myp[slot] = (uint32_t)(p + e);
+                        }
+                        ++slot;
+                    }
+                cnt += (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2));
+            }
+        }
+    } else {
+        constexpr int U = 8;
+        for (int p0 = w0; p0 < w1; p0 += 64 * U) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int p = p0 + 64 * u + lane;
+                v[u] = p < w1 ? row[p] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int p = p0 + 64 * u + lane;
+                const uint32_t key = ordered_key(v[u]);
+                const bool c = p < w1 && key >= tau_s;
+                const uint64_t m = __ballot(c);
+                if (c) {
+                    const uint32_t slot = cnt + lanes_below(m);
+                    if (slot < (uint32_t)kCap) {
+                        myk[slot] = key;
+                        myp[slot] = (uint32_t)p;
+                    }
+                }
+                cnt += (uint32_t)__popcll(m);
+            }
         }
     }
     if (lane == 0) {
