@@ -319,9 +319,8 @@ __global__ __launch_bounds__(kMhaKlThreads) void mha_indexer_kl_kernel(
 // waves' sums meet in LDS (one barrier a tile, two buffers), where each
 // thread takes 2 (key, query) pairs and folds the selected ones into its
 // running KL state.  The splits of a row are merged by a second kernel.
-// The splits of one query block sit on consecutive workgroup ids, so with a
-// multiple of 8 splits a key range stays on one XCD and its keys in that
-// XCD's L2.
+// Each key range is taken by one XCD (the workgroup order is described in
+// the kernel), so its keys stay in that XCD's L2.
 constexpr int kDkWaves = 8;
 constexpr int kDkThreads = kDkWaves * kWave;
 constexpr int kDkQ = 32;            // query rows per workgroup
