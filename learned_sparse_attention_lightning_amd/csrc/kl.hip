@@ -13,6 +13,7 @@
 #include <math.h>
 
 #include "dsa_internal.h"
+#include "kl_schedule.h"
 
 namespace dsa {
 namespace {
@@ -323,19 +324,11 @@ __global__ __launch_bounds__(kMhaKlThreads) void mha_indexer_kl_kernel(
 // the kernel), so its keys stay in that XCD's L2.
 constexpr int kDkWaves = 8;
 constexpr int kDkThreads = kDkWaves * kWave;
-constexpr int kDkQ = 32;            // query rows per workgroup
-constexpr int kDkKeys = 32;         // keys per tile
-constexpr int kDkSplitTiles = 8;    // tiles per split (256 keys)
+constexpr int kDkQ = kl::kQ;                  // query rows per workgroup
+constexpr int kDkKeys = kl::kKeys;            // keys per tile
+constexpr int kDkSplitTiles = kl::kSplitTiles;  // tiles per split (256 keys)
 constexpr int kDkRing = 2;          // register sets of key fragments (loads two head-tiles ahead)
 constexpr int kDkAhead = 3;         // tiles whose scores and selection words are in flight
-
-// First query block (of kDkQ rows) whose last row reaches split s (keys
-// 256 s ..), with row t at position off + t.  Every later block reaches it.
-__host__ __device__ inline int kl_first_block(int s, int off, int nqb) {
-    const int q = s * kDkSplitTiles * kDkKeys - off - (kDkQ - 1);
-    const int qb = q <= 0 ? 0 : (q + kDkQ - 1) / kDkQ;
-    return qb < nqb ? qb : nqb;
-}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t kl_buffer(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
@@ -347,7 +340,7 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
     const uint32_t *__restrict__ bits, const int32_t *__restrict__ row_hi,
     const float *__restrict__ lse, const float *__restrict__ scores, int T, int S, float scale,
-    int nqb, int nsplit, int nslot, int per_xcd, KlState *__restrict__ part) {
+    int nqb, int nsplit, int per_xcd, KlState *__restrict__ part) {
     constexpr int H = kDkWaves * HPW;
     constexpr int KS = D / 16;  // 16-dim k-steps
     constexpr int P = D / 8;                 // 16-byte pieces of a key's head row
@@ -360,35 +353,12 @@ __global__ __launch_bounds__(kDkThreads, 1) void mha_kl_dense_kernel(
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
     const int l32 = lane & 31;
-    // workgroup -> (XCD x = id mod 8, batch, split, query block): XCD x
-    // takes the splits 16 m + x and 16 m + 15 - x (m = 0, 1, ...), a short
-    // and a long column of the causal triangle, so the XCDs get equal shares
-    // of the work while each keeps its own key ranges in its L2.  First the
-    // (split, query block) pairs inside the causal area, one run per split,
-    // the longest query blocks first; then the pairs past it, which only a
-    // selection of later positions gives work (most end at once).
-    // Consecutive workgroups of an XCD go to its shader engines in turn, so
-    // work and no-work workgroups must not alternate.
-    const int xcd = blockIdx.x % 8;
-    const int jx = blockIdx.x / 8;
-    const int b = jx / per_xcd;
-    int rem = jx % per_xcd;
-    int split = -1, qb = 0;
-    for (int pass = 0; pass < 2 && split < 0; ++pass) {
-        for (int k = 0; k < nslot; ++k) {
-            const int sp = 8 * k + ((k & 1) ? 7 - xcd : xcd);
-            if (sp >= nsplit) continue;
-            const int first = kl_first_block(sp, S - T, nqb);
-            const int w = pass == 0 ? nqb - first : first;
-            if (rem < w) {
-                split = sp;
-                qb = pass == 0 ? nqb - 1 - rem : rem;
-                break;
-            }
-            rem -= w;
-        }
-    }
-    if (split < 0) return;  // past this XCD's share
+    // workgroup -> (batch, key split, query block): each XCD keeps its own
+    // key ranges in its L2 with equal shares of the causal triangle, the
+    // causal pairs first in runs, longest first (kl_schedule.h)
+    const kl::Work wk = kl::work_of(blockIdx.x, T, S, nqb, nsplit, per_xcd);
+    if (wk.split < 0) return;  // past this XCD's share
+    const int b = wk.b, split = wk.split, qb = wk.qb;
     const int words = (S + 31) / 32;
     const int my_r = qb * kDkQ + l32;  // this lane's query row (queries are lanes mod 32)
     const bool live = my_r < T;
@@ -576,7 +546,7 @@ bool kl_dense_path(const dsa_attn_desc_t &d, int S, int k) {
            (d.num_heads == 8 || d.num_heads == 16) && S <= 65536 && 4LL * k >= (long long)S;
 }
 
-int kl_splits(int S) { return (S + kDkSplitTiles * kDkKeys - 1) / (kDkSplitTiles * kDkKeys); }
+int kl_splits(int S) { return kl::splits_of(S); }
 
 }  // namespace
 
@@ -611,31 +581,24 @@ hipError_t launch_indexer_kl(const dsa_attn_desc_t &d, const void *q, const void
                                                     align256(rows * 4));
         hipError_t e = launch_selection_bitmap(idx, B, T, S, 0, T, k, bits, row_hi, stream);
         if (e != hipSuccess) return e;
-        const int nqb = (T + kDkQ - 1) / kDkQ;
+        const int nqb = kl::blocks_of(T);
         const int nsplit = kl_splits(S);
-        const int nslot = (nsplit + 7) / 8;  // splits per XCD, rounded up
-        int per_xcd = 0;  // (split, query block) pairs of the XCD with the most splits
-        for (int x = 0; x < 8; ++x) {
-            int n = 0;
-            for (int k = 0; k < nslot; ++k)
-                if (8 * k + ((k & 1) ? 7 - x : x) < nsplit) n += nqb;
-            per_xcd = n > per_xcd ? n : per_xcd;
-        }
-        const dim3 g((unsigned)((long long)B * per_xcd * 8));
+        const int per_xcd = kl::per_xcd(nqb, nsplit);
+        const dim3 g((unsigned)((long long)B * per_xcd * kl::kXcds));
         const uint16_t *qq = static_cast<const uint16_t *>(q);
         const uint16_t *kk = static_cast<const uint16_t *>(kv);
         if (d.d_qk == 128 && d.num_heads == 16)
             hipLaunchKernelGGL((mha_kl_dense_kernel<128, 2>), g, dim3(kDkThreads), 0, stream, qq,
-                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, nslot, per_xcd, part);
+                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, per_xcd, part);
         else if (d.d_qk == 128)
             hipLaunchKernelGGL((mha_kl_dense_kernel<128, 1>), g, dim3(kDkThreads), 0, stream, qq,
-                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, nslot, per_xcd, part);
+                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, per_xcd, part);
         else if (d.num_heads == 16)
             hipLaunchKernelGGL((mha_kl_dense_kernel<64, 2>), g, dim3(kDkThreads), 0, stream, qq,
-                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, nslot, per_xcd, part);
+                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, per_xcd, part);
         else
             hipLaunchKernelGGL((mha_kl_dense_kernel<64, 1>), g, dim3(kDkThreads), 0, stream, qq,
-                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, nslot, per_xcd, part);
+                               kk, bits, row_hi, lse, scores, T, S, d.scale, nqb, nsplit, per_xcd, part);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kl_split_merge_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256),
