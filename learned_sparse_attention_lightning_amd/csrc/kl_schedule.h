@@ -2,8 +2,8 @@
 // distillation-loss kernel (kl.hip, mha_kl_dense_kernel) and the splits its
 // merge reads.
 //
-// The kernel takes its (batch, key split, query block) from kl_work_of and
-// the launch is sized by kl_per_xcd, so a host program can replay every
+// The kernel takes its (batch, key split, query block) from kl::work_of and
+// the launch is sized by kl::per_xcd, so a host program can replay every
 // workgroup id of a launch and check that each (batch, split, block) pair is
 // taken exactly once.  The includer provides __host__ / __device__ (the HIP
 // runtime header on the device side; empty definitions in a host-only build).
@@ -39,7 +39,7 @@ __host__ __device__ inline int first_block(int s, int off, int nqb) {
 }
 
 // Workgroups per XCD and batch: all (split, block) pairs of the XCD with
-// the most splits.  The launch has kXcds * B * kl_per_xcd(...) workgroups.
+// the most splits.  The launch has kXcds * B * per_xcd(...) workgroups.
 __host__ __device__ inline int per_xcd(int nqb, int nsplit) {
     int most = 0;
     for (int x = 0; x < kXcds; ++x) {
