@@ -163,9 +163,10 @@ dsa_status_t forward_run(const dsa_attn_desc_t *desc, const void *q_idx, const v
         if (dense) {
             e = launch_select_all(q_pos, B, T, S, row0, n, index_topk, sel, s);
         } else {
-            // the indexer launch also clears the top-k counters (a kernel, not
-            // a memset, so the step can be captured in a graph)
-            const size_t clear_words = topk_clear_words(B, n, S);
+            // the indexer launch also clears the top-k counters where the
+            // top-k needs them (a kernel, not a memset, so the step can be
+            // captured in a graph)
+            const size_t clear_words = topk_clear_words(B, n, S, index_topk, include_current);
             e = launch_indexer(q_idx, k_idx, idx_dtype, w, q_pos, B, T, S, index_n_heads,
                                index_head_dim, row0, n, score_block, batch_stride, false,
                                static_cast<uint32_t *>(topk_ws), clear_words, s);

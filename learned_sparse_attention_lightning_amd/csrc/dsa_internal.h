@@ -111,7 +111,7 @@ hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, c
 bool indexer_shape_supported(int H, int D);
 
 size_t topk_workspace_bytes(int B, int T, int S, int k);
-size_t topk_clear_words(int B, int rows, int S);
+size_t topk_clear_words(int B, int rows, int S, int k, bool include_current);
 // include_current: the query's own position is always selected and the
 // other k-1 slots are ranked among the earlier positions.
 // bits / row_hi (optional, where topk_writes_bitmap holds): the selection

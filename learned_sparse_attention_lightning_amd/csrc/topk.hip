@@ -23,6 +23,9 @@
 //      resolve  one workgroup per row selects the remaining `need` candidates
 //               exactly (ties by lower position), ORs them into the bitmap and
 //               compacts the bitmap in position order.
+#include <algorithm>
+#include <cmath>
+
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -414,35 +417,15 @@ __device__ bool sampled_select(const float *__restrict__ row, int n, int k,
 // per position, bits[(b * rows + r) * words + p / 32] bit p % 32 (every word
 // of the row written, zeros past the candidates), and row_hi[b * rows + r] =
 // n - 1 (no selected position lies beyond it; -1 for an empty row).
+// The exact top-k of one row of n > k scores (in memory), written to out in
+// ascending position order by the NT threads of the workgroup; brow
+// (optional) receives the selection as bits, `words` words.
 template <int NT, int CACHE>
-__global__ __launch_bounds__(NT) void topk_row_kernel(
-    const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
-    int T, int S, int row0, int k, int cur, int ostride, int32_t *__restrict__ idx,
-    uint32_t *__restrict__ bits, int32_t *__restrict__ row_hi, int words) {
-    __shared__ RowSmemT<NT, CACHE> sm;
-    // the last rows first: without explicit positions they are the longest,
-    // so the short ones fill in at the end rather than trailing behind them
-    const int r = gridDim.x - 1 - blockIdx.x;
-    const int b = blockIdx.y;
-    const int i = row0 + r;
-    const int t = query_pos(q_pos, b, i, T, S) - cur;  // last candidate position
-    const float *row = scores + (size_t)b * batch_stride + (size_t)r * S;
-    int32_t *out = idx + ((size_t)b * T + i) * ostride;
-    const int n = t < 0 ? 0 : t + 1;
+__device__ void select_row(const float *__restrict__ row, int n, int k, int32_t *__restrict__ out,
+                           uint32_t *__restrict__ brow, int words, RowSmemT<NT, CACHE> &sm) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    uint32_t *brow = bits ? bits + ((size_t)b * gridDim.x + r) * words : nullptr;
-    if (bits && tid == 0) row_hi[(size_t)b * gridDim.x + r] = n - 1;
-
-    if (n <= k) {  // every candidate is selected
-        for (int p = tid; p < k; p += NT) out[p] = p < n ? p : -1;
-        if (bits)
-            for (int wd = tid; wd < words; wd += NT) {
-                const int p0 = 32 * wd;
-                brow[wd] = p0 + 32 <= n ? 0xffffffffu : p0 >= n ? 0u : (1u << (n - p0)) - 1u;
-            }
-        return;
-    }
+    const bool bits = brow != nullptr;
     if (bits)  // words past the waves' 64-position runs below
         for (int wd = 2 * ((n + 63) / 64) + tid; wd < words; wd += NT) brow[wd] = 0u;
     const bool cached = n <= CACHE;
@@ -588,6 +571,37 @@ __global__ __launch_bounds__(NT) void topk_row_kernel(
         written += (uint32_t)__popcll(tm);
         ties += (uint32_t)__popcll(eqm);
     });
+}
+
+template <int NT, int CACHE>
+__global__ __launch_bounds__(NT) void topk_row_kernel(
+    const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
+    int T, int S, int row0, int k, int cur, int ostride, int32_t *__restrict__ idx,
+    uint32_t *__restrict__ bits, int32_t *__restrict__ row_hi, int words) {
+    __shared__ RowSmemT<NT, CACHE> sm;
+    // the last rows first: without explicit positions they are the longest,
+    // so the short ones fill in at the end rather than trailing behind them
+    const int r = gridDim.x - 1 - blockIdx.x;
+    const int b = blockIdx.y;
+    const int i = row0 + r;
+    const int t = query_pos(q_pos, b, i, T, S) - cur;  // last candidate position
+    const float *row = scores + (size_t)b * batch_stride + (size_t)r * S;
+    int32_t *out = idx + ((size_t)b * T + i) * ostride;
+    const int n = t < 0 ? 0 : t + 1;
+    const int tid = threadIdx.x;
+    uint32_t *brow = bits ? bits + ((size_t)b * gridDim.x + r) * words : nullptr;
+    if (bits && tid == 0) row_hi[(size_t)b * gridDim.x + r] = n - 1;
+
+    if (n <= k) {  // every candidate is selected
+        for (int p = tid; p < k; p += NT) out[p] = p < n ? p : -1;
+        if (bits)
+            for (int wd = tid; wd < words; wd += NT) {
+                const int p0 = 32 * wd;
+                brow[wd] = p0 + 32 <= n ? 0xffffffffu : p0 >= n ? 0u : (1u << (n - p0)) - 1u;
+            }
+        return;
+    }
+    select_row<NT, CACHE>(row, n, k, out, brow, words, sm);
 }
 
 // ------------------------------------------------------- wide-row path -----
@@ -976,6 +990,424 @@ __global__ __launch_bounds__(kTkThreads) void topk_wide_resolve_kernel(
     }
 }
 
+// ------------------------------------------------------ partition path -----
+// Few wide rows with a budget small against the row (decode): the row's
+// 32-position tiles are dealt round-robin to P partitions of 64 tiles, one
+// workgroup each, and every workgroup keeps its partition's keys at or above
+// a threshold chosen with two rounds of a 256-bin histogram (the partition's
+// key range, then the bin where the count crosses) so that at most `cap`
+// remain; it records the threshold when it dropped keys.  The kept keys of a
+// partition are a prefix of it in the selection order.  Let theta be the
+// largest recorded threshold: every dropped key lies below it, so once at
+// least k kept keys reach theta the k-th largest kept key is >= theta, no
+// dropped key can belong to the top k, and the top k of the kept keys is
+// the row's.  The resolve checks exactly that and selects among the kept
+// keys; otherwise (a partition holding a large share of the top k, heavy
+// ties) it runs the exact per-row selection on the whole row.  Dealing tiles
+// round-robin puts a contiguous run of top scores (a local window) at one
+// tile per partition.
+constexpr int kPartTiles = 64;                         // 32-position tiles per partition
+constexpr int kPartKeys = kPartTiles * 32;             // 2048
+constexpr int kPartBins = 256;
+constexpr int kPartMax = 12288;                        // kept keys a row's resolve holds
+constexpr int kPartPieces = kPartMax / 2 / kTkThreads;  // 16-byte pieces per resolve thread
+constexpr int kPartMaxP = kWideMaxS / kPartKeys;       // 128
+constexpr int kPartTies = 1024;                        // keys equal to tau ranked pairwise
+
+struct PartLayout {
+    uint2 *meta;  // [rows][P] (kept count, threshold; 0 when nothing was dropped)
+    uint2 *cand;  // [rows][P][stride] (key, position) of the kept keys
+    int P;        // partitions a row; 0: the partition path does not apply
+    int stride;   // slots a partition (even, >= cap)
+    int cap;      // keys a partition keeps at most
+};
+
+// Over a 256-bin histogram hw of fewer than 4096 keys (every lane of the
+// wave active): the lowest bin `first` whose keys and those of every bin
+// above it number at most `room` (256: the top bin alone holds more); room
+// becomes what is left of it for bin first - 1.  Uniform.  The keys in the
+// bins of higher lanes come from one ballot per bit of the lanes' counts.
+__device__ __forceinline__ void part_first_bin(const uint32_t *hw, int lane, uint32_t &room,
+                                               uint32_t &first) {
+    const u32x4 hb = reinterpret_cast<const u32x4 *>(hw)[lane];  // bins 4 lane .. + 3
+    const uint32_t s4 = hb[0] + hb[1] + hb[2] + hb[3];
+    uint32_t higher = 0u;
+#pragma unroll
+    for (int bit = 0; bit < 12; ++bit) {
+        const uint32_t mine = (s4 >> bit) & 1u;
+        const uint64_t m = __ballot(mine);
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        higher += ((uint32_t)__popcll(m) - below - mine) << bit;
+    }
+    uint32_t above = higher + s4;  // keys in bins >= 4 lane
+    uint32_t at_bin = kPartBins, at_count = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (above <= room && at_bin == (uint32_t)kPartBins) {
+            at_bin = 4 * lane + j;
+            at_count = above;
+        }
+        above -= hb[j];
+    }
+    // the bins that qualify are all those from `first` up: the lowest lane
+    // holding one has it
+    const uint64_t q = __ballot(at_bin != (uint32_t)kPartBins);
+    if (q == 0u) {
+        first = kPartBins;
+        return;
+    }
+    const int src = __builtin_ctzll(q);
+    first = (uint32_t)__builtin_amdgcn_readlane((int)at_bin, src);
+    room -= (uint32_t)__builtin_amdgcn_readlane((int)at_count, src);
+}
+
+// grid: 1-D, 8 * ceil(B * rows / 8) * P workgroups, one a partition.
+// Workgroup id mod 8 (its XCD) takes the rows rr = b * rows + r with rr mod 8
+// equal to it, the XCD of the row's resolve workgroup.
+__global__ __launch_bounds__(256) void topk_part_kernel(
+    const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
+    int B, int T, int S, int row0, int rows, int k, int cur, PartLayout L) {
+    __shared__ __align__(16) uint32_t hist[kPartBins];
+    __shared__ uint32_t red[3][4];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int jx = (int)(blockIdx.x >> 3);
+    const int rr = (int)(blockIdx.x & 7) + 8 * (jx / L.P);
+    const int c = jx % L.P;
+    if (rr >= B * rows) return;
+    const int b = rr / rows, r = rr % rows;
+    const int t = query_pos(q_pos, b, row0 + r, T, S) - cur;
+    const int n = t < 0 ? 0 : t + 1;
+    if (n <= k) return;  // the resolve takes every position
+    const float *row = scores + (size_t)b * batch_stride + (size_t)r * S;
+    // the thread's 16-byte pieces j = tid and tid + 256 of the partition:
+    // piece j holds positions 4 (j % 8) .. + 3 of tile c + P (j / 8)
+    const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+    int p0[2];
+    f32x4 v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int j = tid + 256 * h;
+        p0[h] = 32 * (c + L.P * (j >> 3)) + 4 * (j & 7);
+        if (aligned && p0[h] + 4 <= n) {
+            v[h] = *reinterpret_cast<const f32x4 *>(row + p0[h]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[h][e] = p0[h] + e < n ? row[p0[h] + e] : 0.0f;
+        }
+    }
+    reinterpret_cast<uint32_t *>(hist)[tid] = 0u;  // 256 bins, one a thread
+    uint32_t key[8], valid = 0u, lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        key[e] = ordered_key(v[e >> 2][e & 3]);
+        if (p0[e >> 2] + (e & 3) < n) {
+            valid |= 1u << e;
+            lo = min(lo, key[e]);
+            hi = max(hi, key[e]);
+        }
+    }
+    uint32_t nvalid = (uint32_t)__popc(valid);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
+        nvalid += (uint32_t)__shfl_xor((int)nvalid, off, 64);
+    }
+    if (lane == 0) {
+        red[0][wave] = lo;
+        red[1][wave] = hi;
+        red[2][wave] = nvalid;
+    }
+    __syncthreads();
+    lo = min(min(red[0][0], red[0][1]), min(red[0][2], red[0][3]));
+    hi = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
+    nvalid = red[2][0] + red[2][1] + red[2][2] + red[2][3];
+    uint64_t theta = 0u;  // keys below it are dropped
+    if (nvalid > (uint32_t)L.cap) {  // uniform
+        int shift = 0;
+        while (((hi - lo) >> shift) >= (uint32_t)kPartBins) ++shift;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (valid & (1u << e)) atomicAdd(&hist[min((key[e] - lo) >> shift, 255u)], 1u);
+        __syncthreads();
+        // every wave reads the same histogram and reaches the same bin
+        uint32_t room = (uint32_t)L.cap, first;
+        part_first_bin(hist, lane, room, first);
+        theta = (uint64_t)lo + ((uint64_t)first << shift);
+        if (first >= 1 && shift > 0) {  // uniform: refine inside bin first - 1
+            // (it holds a key; the bins above it hold cap - room keys)
+            const uint32_t b1 = first - 1;
+            const uint32_t base = lo + (b1 << shift);
+            const int s2 = shift > 8 ? shift - 8 : 0;
+            __syncthreads();  // every wave has read the histogram
+            hist[tid] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if ((valid & (1u << e)) && ((key[e] - lo) >> shift) == b1)
+                    atomicAdd(&hist[min((key[e] - base) >> s2, 255u)], 1u);
+            __syncthreads();
+            uint32_t first2;
+            part_first_bin(hist, lane, room, first2);
+            theta = (uint64_t)base + ((uint64_t)first2 << s2);
+        }
+    }
+    uint32_t take = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if ((valid & (1u << e)) && (uint64_t)key[e] >= theta) take |= 1u << e;
+    // slots: the waves' totals, then a prefix of the lanes' counts (0..8, four ballots)
+    const uint32_t cnt = (uint32_t)__popc(take);
+    const uint64_t b0 = __ballot(cnt & 1u), b1 = __ballot(cnt & 2u), b2 = __ballot(cnt & 4u),
+                   b3 = __ballot(cnt & 8u);
+    const uint32_t wtot = (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2) +
+                                     8 * __popcll(b3));
+    __syncthreads();  // red is reused
+    if (lane == 0) red[0][wave] = wtot;
+    __syncthreads();
+    uint32_t slot = lanes_below(b0) + 2u * lanes_below(b1) + 4u * lanes_below(b2) +
+                    8u * lanes_below(b3);
+    uint32_t kept = 0u;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        slot += w < wave ? red[0][w] : 0u;
+        kept += red[0][w];
+    }
+    uint2 *dst = L.cand + ((size_t)rr * L.P + c) * (size_t)L.stride;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (take & (1u << e)) {
+            if (slot < (uint32_t)L.stride)
+                dst[slot] = make_uint2(key[e], (uint32_t)(p0[e >> 2] + (e & 3)));
+            ++slot;
+        }
+    // (more than the slots hold cannot happen; were it to, the partition
+    // reports that it dropped every key, and the exact selection runs)
+    if (tid == 0)
+        L.meta[(size_t)rr * L.P + c] =
+            kept > (uint32_t)L.stride
+                ? make_uint2(0u, 0xffffffffu)
+                : make_uint2(kept,
+                             kept < nvalid ? (uint32_t)min(theta, (uint64_t)0xffffffffu) : 0u);
+}
+
+// Sum, smallest and largest of the threads' values (uniform results).
+__device__ __forceinline__ void block_sum_min_max(uint32_t &s, uint32_t &mn, uint32_t &mx,
+                                                  uint32_t (&red)[3][kTkWaves]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        s += (uint32_t)__shfl_xor((int)s, off, 64);
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    }
+    if (lane == 0) {
+        red[0][wave] = s;
+        red[1][wave] = mn;
+        red[2][wave] = mx;
+    }
+    __syncthreads();
+    s = 0u;
+    mn = 0xffffffffu;
+    mx = 0u;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) {
+        s += red[0][w];
+        mn = min(mn, red[1][w]);
+        mx = max(mx, red[2][w]);
+    }
+    __syncthreads();
+}
+
+struct PartSmem {
+    SelectSmem sel;
+    uint32_t red[3][kTkWaves];
+    uint32_t cnt[kPartMaxP];  // kept keys of each partition
+    uint32_t nties;
+    uint2 ties[kPartTies];
+    uint32_t bits[kWideMaxS / 32];
+};
+// the exact per-row selection, when the kept keys do not decide, reuses it
+union PartResolveSmem {
+    PartSmem p;
+    RowSmemT<kTkThreads, 16384> row;
+};
+
+// grid: x = row in chunk, y = batch (workgroup id b * rows + r: the XCD that
+// ran the row's partitions)
+__global__ __launch_bounds__(kTkThreads) void topk_part_resolve_kernel(
+    const float *__restrict__ scores, size_t batch_stride, const int32_t *__restrict__ q_pos,
+    int T, int S, int row0, int rows, int k, int cur, int ostride, int32_t *__restrict__ idx,
+    PartLayout L) {
+    __shared__ PartResolveSmem smu;
+    PartSmem &sm = smu.p;
+    const int r = blockIdx.x, b = blockIdx.y;
+    const int i = row0 + r;
+    const int t = query_pos(q_pos, b, i, T, S) - cur;
+    const int n = t < 0 ? 0 : t + 1;
+    int32_t *out = idx + ((size_t)b * T + i) * ostride;
+    const int tid = threadIdx.x;
+    if (n <= k) {
+        for (int p = tid; p < k; p += kTkThreads) out[p] = p < n ? p : -1;
+        return;
+    }
+    const size_t rr = (size_t)b * rows + r;
+    const int P = L.P, stride = L.stride;
+    const int nslots = P * stride;
+    const u32x4 *cp = reinterpret_cast<const u32x4 *>(L.cand + rr * (size_t)nslots);
+
+    // ---- every load up front: the partitions' counts and thresholds, and
+    // all their slots (two per 16-byte piece; slots past a count are ignored)
+    const uint2 mt = tid < P ? L.meta[rr * P + tid] : make_uint2(0u, 0u);
+    u32x4 cv[kPartPieces];
+#pragma unroll
+    for (int u = 0; u < kPartPieces; ++u) {
+        const int pc = tid + u * kTkThreads;
+        cv[u] = 2 * pc < nslots ? cp[pc] : u32x4{0u, 0u, 0u, 0u};
+    }
+    // while they are in flight: clear the bitmap, the histogram, the group
+    const int nw = (n + 31) / 32;
+    for (int w = tid; w < nw; w += kTkThreads) sm.bits[w] = 0u;
+    for (int j = tid; j < kTkBins; j += kTkThreads) sm.sel.hist[j] = 0u;
+    if (tid == 0) sm.nties = 0u;
+    if (tid < P) sm.cnt[tid] = mt.x;
+    uint32_t unused_s = 0u, unused_mn = 0xffffffffu, theta = mt.y;
+    block_sum_min_max(unused_s, unused_mn, theta, sm.red);  // also publishes the above
+
+    // ---- the kept keys at or above theta
+    uint32_t vmask = 0u, nkeys = 0u, lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int u = 0; u < kPartPieces; ++u)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int q = 2 * (tid + u * kTkThreads) + e;
+            if (q < nslots) {
+                const int c = q / stride;
+                const uint32_t key = cv[u][2 * e], p = cv[u][2 * e + 1];
+                if ((uint32_t)(q - c * stride) < sm.cnt[c] && p < (uint32_t)n && key >= theta) {
+                    vmask |= 1u << (2 * u + e);
+                    ++nkeys;
+                    lo = min(lo, key);
+                    hi = max(hi, key);
+                }
+            }
+        }
+    block_sum_min_max(nkeys, lo, hi, sm.red);
+    if (nkeys < (uint32_t)k) {  // uniform: a dropped key may belong to the top k
+        select_row<kTkThreads, 16384>(scores + (size_t)b * batch_stride + (size_t)r * S, n, k,
+                                      out, nullptr, 0, smu.row);
+        return;
+    }
+    auto each = [&](auto f) {
+#pragma unroll
+        for (int u = 0; u < kPartPieces; ++u)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                if (vmask & (1u << (2 * u + e))) f(cv[u][2 * e], cv[u][2 * e + 1]);
+    };
+    auto set_bit = [&](uint32_t p) { atomicOr(&sm.bits[p >> 5], 1u << (p & 31)); };
+
+    // ---- one histogram pass over [lo, hi]: bin d holds the k-th largest
+    int shift = 0;
+    while (((hi - lo) >> shift) >= (uint32_t)kTkBins) ++shift;
+    each([&](uint32_t key, uint32_t) { atomicAdd(&sm.sel.hist[(key - lo) >> shift], 1u); });
+    __syncthreads();
+    {
+        constexpr int kPer = kTkBins / kTkThreads;
+        uint32_t hb[kPer], c = 0u;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            hb[j] = sm.sel.hist[tid * kPer + j];
+            c += hb[j];
+        }
+        uint32_t tot;
+        const uint32_t pre = block_excl_scan<kTkWaves>(c, sm.sel.scan, tot);
+        uint32_t run = tot - pre - c;  // keys in the bins of later threads
+#pragma unroll
+        for (int j = kPer - 1; j >= 0; --j) {
+            const uint32_t before = run;
+            run += hb[j];
+            if (before < (uint32_t)k && run >= (uint32_t)k) {
+                sm.sel.found_bin = (uint32_t)(tid * kPer + j);
+                sm.sel.found_above = before;
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t d = sm.sel.found_bin;
+    const uint32_t need = (uint32_t)k - sm.sel.found_above;  // keys to take from bin d
+
+    // ---- the bins above d are taken; bin d's keys are gathered and ranked
+    // (larger key first, then lower position)
+    each([&](uint32_t key, uint32_t p) {
+        const uint32_t bin = (key - lo) >> shift;
+        if (bin > d) {
+            set_bit(p);
+        } else if (bin == d) {
+            const uint32_t s = atomicAdd(&sm.nties, 1u);
+            if (s < (uint32_t)kPartTies) sm.ties[s] = make_uint2(key, p);
+        }
+    });
+    __syncthreads();
+    const uint32_t m = sm.nties;
+    if (m <= (uint32_t)kPartTies) {
+        for (uint32_t a = tid; a < m; a += kTkThreads) {
+            const uint2 ca = sm.ties[a];
+            uint32_t ahead = 0u;
+            for (uint32_t g = 0; g < m; ++g) {
+                const uint2 cg = sm.ties[g];
+                ahead += (cg.x > ca.x || (cg.x == ca.x && cg.y < ca.y)) ? 1u : 0u;
+            }
+            if (ahead < need) set_bit(ca.y);
+        }
+    } else {  // a crowded bin: exact threshold among its keys, then ties by position
+        const uint32_t blo = lo + (d << shift);
+        const uint32_t bhi = hi - blo > (1u << shift) - 1u ? blo + ((1u << shift) - 1u) : hi;
+        auto eachd = [&](auto f) {
+            each([&](uint32_t key, uint32_t) {
+                if (((key - lo) >> shift) == d) f(key);
+            });
+        };
+        uint32_t tau, need_tau;
+        block_select_in(eachd, blo, bhi, need, sm.sel, tau, need_tau);
+        uint32_t nt = 0u, unused_mn2 = 0xffffffffu, unused_mx2 = 0u;
+        each([&](uint32_t key, uint32_t) { nt += key == tau ? 1u : 0u; });
+        block_sum_min_max(nt, unused_mn2, unused_mx2, sm.red);
+        uint32_t pos_cut = 0xffffffffu;  // ties at positions <= pos_cut are taken
+        if (need_tau < nt) {
+            auto each2 = [&](auto f) {
+                each([&](uint32_t key, uint32_t p) { f(key == tau ? ~p : 0u); });
+            };
+            uint32_t lo2, hi2, tau2, need2;
+            block_key_range(each2, sm.sel, lo2, hi2);
+            block_select_in(each2, lo2, hi2, need_tau, sm.sel, tau2, need2);
+            pos_cut = ~tau2;
+        }
+        each([&](uint32_t key, uint32_t p) {
+            if (((key - lo) >> shift) == d && (key > tau || (key == tau && p <= pos_cut)))
+                set_bit(p);
+        });
+    }
+    __syncthreads();
+
+    // ---- ordered compaction: contiguous words per thread, prefix of popcounts
+    const int per = (nw + kTkThreads - 1) / kTkThreads;
+    const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
+    uint32_t cntw = 0u;
+    for (int w = w0; w < w1; ++w) cntw += (uint32_t)__popc(sm.bits[w]);
+    uint32_t total;
+    uint32_t slot = block_excl_scan<kTkWaves>(cntw, sm.sel.scan, total);
+    for (int w = w0; w < w1; ++w) {
+        uint32_t x = sm.bits[w];
+        while (x) {
+            const int bit = __builtin_ctz(x);
+            x &= x - 1u;
+            out[slot++] = w * 32 + bit;
+        }
+    }
+}
+
 // The current-token variant: the selection kernels ran with budget k-1 over
 // the positions before t, writing slots 0..k-2 of each k-wide row (ascending,
 // -1 after the n_sel = min(k-1, t) selected).  Position t is the largest of
@@ -1013,6 +1445,38 @@ bool use_wide(int B, int rows, int S) {
     return S >= kWideMinS && S <= kWideMaxS && (long long)B * rows <= kWideMaxRows;
 }
 
+// Partition plan of a wide launch with budget k (P = 0 in the result: the
+// path does not apply): P partitions of 2048 positions a row.  A partition
+// keeps at most cap keys, about k / P of which belong to the top k of a
+// random row: cap leaves six standard deviations and a margin above that,
+// and at least 40 so that a window of consecutive top positions (one
+// 32-position tile per partition) fits; the kept keys of a row must fit the
+// resolve's registers (kPartMax).  The layout sits at the head of the wide
+// path's workspace, which is larger.
+PartLayout part_plan(void *ws, int nrows, int S, int k) {
+    PartLayout L{};
+    const int P = ceil_div(S, kPartKeys);
+    if (k < 1 || P > kPartMaxP) return L;
+    const double mu = (double)k / P;
+    int cap = (int)std::ceil(mu + 6.0 * std::sqrt(mu) + 8.0);
+    cap = (std::max(cap, 40) + 7) & ~7;
+    const int stride = cap;  // even
+    if ((long long)P * cap > kPartMax || cap >= kPartKeys) return L;
+    const size_t meta_bytes = ((size_t)nrows * P * sizeof(uint2) + 15) & ~(size_t)15;
+    if (15 + meta_bytes + (size_t)nrows * P * stride * sizeof(uint2) >
+        (size_t)nrows * wide_row_bytes(S) + 64)
+        return L;  // not reached for S >= kWideMinS; the layout must fit the workspace
+    // both arrays 16-byte aligned (the resolve reads the slots as 16-byte
+    // pieces); the workspace's 64 spare bytes cover the padding
+    const uintptr_t m = ((uintptr_t)ws + 15) & ~(uintptr_t)15;
+    L.meta = reinterpret_cast<uint2 *>(m);
+    L.cand = reinterpret_cast<uint2 *>(m + meta_bytes);
+    L.P = P;
+    L.stride = stride;
+    L.cap = cap;
+    return L;
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int B, int T, int S, int) {
@@ -1024,8 +1488,9 @@ size_t topk_workspace_bytes(int B, int T, int S, int) {
 
 // Counters of the wide path that must be zero when its first kernel starts
 // (the histograms and per-row words at the head of the workspace).
-size_t topk_clear_words(int B, int rows, int S) {
-    if (!use_wide(B, rows, S)) return 0;
+size_t topk_clear_words(int B, int rows, int S, int k, bool include_current) {
+    const int kk = k - (include_current ? 1 : 0);
+    if (!use_wide(B, rows, S) || kk < 1 || part_plan(nullptr, B * rows, S, kk).P > 0) return 0;
     return (size_t)B * rows * (2 * kDigits + kMetaWords);
 }
 
@@ -1045,7 +1510,16 @@ hipError_t launch_topk(const float *scores, size_t batch_stride, const int32_t *
     const int words = (S + 31) / 32;
     if (bits && !(topk_writes_bitmap(B, rows, S, k, include_current) && row_hi))
         return hipErrorInvalidValue;
-    if (kk >= 1 && use_wide(B, rows, S) && workspace) {
+    const PartLayout PL =
+        kk >= 1 && use_wide(B, rows, S) && workspace ? part_plan(workspace, B * rows, S, kk)
+                                                     : PartLayout{};
+    if (PL.P > 0) {
+        const int nwg = 8 * ceil_div(B * rows, 8) * PL.P;
+        hipLaunchKernelGGL(topk_part_kernel, dim3(nwg), dim3(256), 0, stream, scores,
+                           batch_stride, q_pos, B, T, S, row0, rows, kk, cur, PL);
+        hipLaunchKernelGGL(topk_part_resolve_kernel, dim3(rows, B), dim3(kTkThreads), 0, stream,
+                           scores, batch_stride, q_pos, T, S, row0, rows, kk, cur, k, idx, PL);
+    } else if (kk >= 1 && use_wide(B, rows, S) && workspace) {
         const WideLayout L = wide_layout(workspace, B * rows, S);
         const int nrows = B * rows;
         if (!workspace_cleared)

@@ -592,3 +592,48 @@ def test_topk_wide_path_edges(case):
         pos = torch.tensor([[10], [2047], [2048], [2049]], dtype=torch.int32)
     idx = dsa.dsa_topk(sc.to(DEV), k, q_pos=pos.to(DEV))
     assert_selection_equal(idx, oracle.topk(sc, k, q_pos=pos), case)
+
+
+@pytest.mark.parametrize("case", ["random", "window", "one_partition", "ties_small",
+                                  "ties_1100", "levels3", "short_rows", "odd_S", "big_k"])
+def test_topk_partition_path(case):
+    """Few wide rows: every workgroup keeps the keys of its partition (64
+    tiles of 32 positions, dealt round-robin) at or above a threshold, and the row's
+    top k is selected among the kept keys when no partition can have dropped
+    one of them, else by the exact per-row passes.  Cases: a window of top
+    scores (one tile per partition: decided by the kept keys), every tile of
+    one partition on top (it must drop some: the exact passes), a few and
+    more than a thousand copies of the k-th largest score (ranked pairwise,
+    or by a second search on the positions), heavy ties, rows barely longer
+    than k, rows that are not 16-byte aligned, and a budget too large for the
+    partitions (the split-row path)."""
+    B, S, k = 3, 131072, 2048
+    if case == "odd_S":
+        S = 40001
+    if case == "big_k":
+        S, k = 40000, 8192
+    levels = 3 if case == "levels3" else None
+    sc = synth.random_scores((B, 1, S), seed=sum(map(ord, case)) + 5, levels=levels)
+    pos = torch.tensor([[S - 1], [S - 2], [S // 2 + 3]], dtype=torch.int32)
+    P = -(-S // 2048)
+    if case == "window":
+        sc[0, 0, 50000:52048] += 10.0
+        sc[1, 0, 50013:52061] += 10.0
+        sc[2, 0, 1000:3048] += 10.0
+    if case == "one_partition":
+        for bb in range(B):
+            for u in range(64):
+                t0 = 32 * (7 + P * u)
+                sc[bb, 0, t0:t0 + 32] += 10.0
+    if case in ("ties_small", "ties_1100"):
+        copies = 9 if case == "ties_small" else 1100
+        g = np.random.default_rng(3)
+        for bb in range(B):
+            n = int(pos[bb, 0]) + 1
+            kth = torch.sort(sc[bb, 0, :n], descending=True).values[k - 1]
+            where = torch.from_numpy(g.choice(n, copies, replace=False))
+            sc[bb, 0, where] = kth
+    if case == "short_rows":
+        pos = torch.tensor([[2048], [2100], [20000]], dtype=torch.int32)
+    idx = dsa.dsa_topk(sc.to(DEV), k, q_pos=pos.to(DEV))
+    assert_selection_equal(idx, oracle.topk(sc, k, q_pos=pos), case)
