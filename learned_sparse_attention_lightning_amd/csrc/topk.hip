@@ -1020,6 +1020,7 @@ struct PartLayout {
     int P;        // partitions a row; 0: the partition path does not apply
     int stride;   // slots a partition (even, >= cap)
     int cap;      // keys a partition keeps at most
+    uint32_t magic;  // ceil(2^32 / stride): slot / stride = umulhi(slot, magic) for a row's slots
 };
 
 // Over a 256-bin histogram hw of fewer than 4096 keys (every lane of the
@@ -1192,22 +1193,37 @@ __global__ __launch_bounds__(256) void topk_part_kernel(
                              kept < nvalid ? (uint32_t)min(theta, (uint64_t)0xffffffffu) : 0u);
 }
 
-// Sum, smallest and largest of the threads' values (uniform results).
+// Sum, smallest or largest of v over the 64 lanes of a wave, uniform; every
+// lane must be active.  DPP within each row of 16 lanes (quad permutations,
+// then the half-row and row mirrors), then the four rows' results.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xb1, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4e, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, false));
+    return op(op((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                 (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+              op((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                 (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
+// Sum, smallest and largest of the threads' values (uniform results; every
+// thread active).  One LDS-only barrier: `red` may be written again only
+// after a later barrier (callers alternate two buffers), and global loads in
+// flight are not waited for.
 __device__ __forceinline__ void block_sum_min_max(uint32_t &s, uint32_t &mn, uint32_t &mx,
                                                   uint32_t (&red)[3][kTkWaves]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        s += (uint32_t)__shfl_xor((int)s, off, 64);
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-    }
+    s = wave_reduce(s, [](uint32_t a, uint32_t b) { return a + b; });
+    mn = wave_reduce(mn, [](uint32_t a, uint32_t b) { return min(a, b); });
+    mx = wave_reduce(mx, [](uint32_t a, uint32_t b) { return max(a, b); });
     if (lane == 0) {
         red[0][wave] = s;
         red[1][wave] = mn;
         red[2][wave] = mx;
     }
-    __syncthreads();
+    lds_barrier();
     s = 0u;
     mn = 0xffffffffu;
     mx = 0u;
@@ -1217,12 +1233,40 @@ __device__ __forceinline__ void block_sum_min_max(uint32_t &s, uint32_t &mn, uin
         mn = min(mn, red[1][w]);
         mx = max(mx, red[2][w]);
     }
-    __syncthreads();
+}
+
+// Exclusive prefix sum over the workgroup in thread order of values below
+// 2^Bits, and the total: one ballot per bit within a wave, the waves'
+// totals through LDS (one LDS-only barrier; `wsum` reused only after a
+// later barrier).
+template <int Bits>
+__device__ __forceinline__ uint32_t block_excl_scan_small(uint32_t v, uint32_t *wsum,
+                                                          uint32_t &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t below = 0u, wtot = 0u;
+#pragma unroll
+    for (int bit = 0; bit < Bits; ++bit) {
+        const uint64_t m = __ballot((v >> bit) & 1u);
+        below += lanes_below(m) << bit;
+        wtot += (uint32_t)__popcll(m) << bit;
+    }
+    if (lane == 0) wsum[wave] = wtot;
+    lds_barrier();
+    uint32_t before = 0u, sum = 0u;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) {
+        const uint32_t c = wsum[w];
+        before += w < wave ? c : 0u;
+        sum += c;
+    }
+    total = sum;
+    return before + below;
 }
 
 struct PartSmem {
     SelectSmem sel;
-    uint32_t red[3][kTkWaves];
+    uint32_t red[2][3][kTkWaves];
+    uint32_t wsum[2][kTkWaves];
     uint32_t cnt[kPartMaxP];  // kept keys of each partition
     uint32_t nties;
     uint2 ties[kPartTies];
@@ -1259,21 +1303,23 @@ __global__ __launch_bounds__(kTkThreads) void topk_part_resolve_kernel(
 
     // ---- every load up front: the partitions' counts and thresholds, and
     // all their slots (two per 16-byte piece; slots past a count are ignored)
-    const uint2 mt = tid < P ? L.meta[rr * P + tid] : make_uint2(0u, 0u);
+    // (unconditional, clamped into the row's slots, so that the waits count
+    // each load: the counts first, the slots after; pieces past the slots
+    // are never used)
+    uint2 mt = L.meta[rr * P + min(tid, P - 1)];
     u32x4 cv[kPartPieces];
 #pragma unroll
-    for (int u = 0; u < kPartPieces; ++u) {
-        const int pc = tid + u * kTkThreads;
-        cv[u] = 2 * pc < nslots ? cp[pc] : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int u = 0; u < kPartPieces; ++u) cv[u] = cp[min(tid + u * kTkThreads, nslots / 2 - 1)];
+    if (tid >= P) mt = make_uint2(0u, 0u);
     // while they are in flight: clear the bitmap, the histogram, the group
+    // (the barriers below are LDS-only, so the loads stay in flight)
     const int nw = (n + 31) / 32;
     for (int w = tid; w < nw; w += kTkThreads) sm.bits[w] = 0u;
     for (int j = tid; j < kTkBins; j += kTkThreads) sm.sel.hist[j] = 0u;
     if (tid == 0) sm.nties = 0u;
     if (tid < P) sm.cnt[tid] = mt.x;
     uint32_t unused_s = 0u, unused_mn = 0xffffffffu, theta = mt.y;
-    block_sum_min_max(unused_s, unused_mn, theta, sm.red);  // also publishes the above
+    block_sum_min_max(unused_s, unused_mn, theta, sm.red[0]);  // also publishes the above
 
     // ---- the kept keys at or above theta
     uint32_t vmask = 0u, nkeys = 0u, lo = 0xffffffffu, hi = 0u;
@@ -1283,7 +1329,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_part_resolve_kernel(
         for (int e = 0; e < 2; ++e) {
             const int q = 2 * (tid + u * kTkThreads) + e;
             if (q < nslots) {
-                const int c = q / stride;
+                const int c = (int)__umulhi((uint32_t)q, L.magic);  // q / stride
                 const uint32_t key = cv[u][2 * e], p = cv[u][2 * e + 1];
                 if ((uint32_t)(q - c * stride) < sm.cnt[c] && p < (uint32_t)n && key >= theta) {
                     vmask |= 1u << (2 * u + e);
@@ -1293,8 +1339,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_part_resolve_kernel(
                 }
             }
         }
-    block_sum_min_max(nkeys, lo, hi, sm.red);
+    block_sum_min_max(nkeys, lo, hi, sm.red[1]);
     if (nkeys < (uint32_t)k) {  // uniform: a dropped key may belong to the top k
+        __syncthreads();
         select_row<kTkThreads, 16384>(scores + (size_t)b * batch_stride + (size_t)r * S, n, k,
                                       out, nullptr, 0, smu.row);
         return;
@@ -1312,7 +1359,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_part_resolve_kernel(
     int shift = 0;
     while (((hi - lo) >> shift) >= (uint32_t)kTkBins) ++shift;
     each([&](uint32_t key, uint32_t) { atomicAdd(&sm.sel.hist[(key - lo) >> shift], 1u); });
-    __syncthreads();
+    lds_barrier();
     {
         constexpr int kPer = kTkBins / kTkThreads;
         uint32_t hb[kPer], c = 0u;
@@ -1321,8 +1368,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_part_resolve_kernel(
             hb[j] = sm.sel.hist[tid * kPer + j];
             c += hb[j];
         }
-        uint32_t tot;
-        const uint32_t pre = block_excl_scan<kTkWaves>(c, sm.sel.scan, tot);
+        uint32_t tot;  // the kept keys: fewer than 2^14
+        const uint32_t pre = block_excl_scan_small<14>(c, sm.wsum[0], tot);
         uint32_t run = tot - pre - c;  // keys in the bins of later threads
 #pragma unroll
         for (int j = kPer - 1; j >= 0; --j) {
@@ -1334,7 +1381,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_part_resolve_kernel(
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     const uint32_t d = sm.sel.found_bin;
     const uint32_t need = (uint32_t)k - sm.sel.found_above;  // keys to take from bin d
 
@@ -1349,7 +1396,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_part_resolve_kernel(
             if (s < (uint32_t)kPartTies) sm.ties[s] = make_uint2(key, p);
         }
     });
-    __syncthreads();
+    lds_barrier();
     const uint32_t m = sm.nties;
     if (m <= (uint32_t)kPartTies) {
         for (uint32_t a = tid; a < m; a += kTkThreads) {
@@ -1373,7 +1420,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_part_resolve_kernel(
         block_select_in(eachd, blo, bhi, need, sm.sel, tau, need_tau);
         uint32_t nt = 0u, unused_mn2 = 0xffffffffu, unused_mx2 = 0u;
         each([&](uint32_t key, uint32_t) { nt += key == tau ? 1u : 0u; });
-        block_sum_min_max(nt, unused_mn2, unused_mx2, sm.red);
+        block_sum_min_max(nt, unused_mn2, unused_mx2, sm.red[0]);
         uint32_t pos_cut = 0xffffffffu;  // ties at positions <= pos_cut are taken
         if (need_tau < nt) {
             auto each2 = [&](auto f) {
@@ -1396,8 +1443,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_part_resolve_kernel(
     const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
     uint32_t cntw = 0u;
     for (int w = w0; w < w1; ++w) cntw += (uint32_t)__popc(sm.bits[w]);
-    uint32_t total;
-    uint32_t slot = block_excl_scan<kTkWaves>(cntw, sm.sel.scan, total);
+    uint32_t total;  // per <= 8 words a thread: at most 256
+    uint32_t slot = block_excl_scan_small<9>(cntw, sm.wsum[1], total);
     for (int w = w0; w < w1; ++w) {
         uint32_t x = sm.bits[w];
         while (x) {
@@ -1474,6 +1521,7 @@ PartLayout part_plan(void *ws, int nrows, int S, int k) {
     L.P = P;
     L.stride = stride;
     L.cap = cap;
+    L.magic = (uint32_t)(((1ull << 32) + stride - 1) / stride);
     return L;
 }
 
