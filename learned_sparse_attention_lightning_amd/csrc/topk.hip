@@ -1063,6 +1063,21 @@ __device__ __forceinline__ void part_first_bin(const uint32_t *hw, int lane, uin
     room -= (uint32_t)__builtin_amdgcn_readlane((int)at_count, src);
 }
 
+// Sum, smallest or largest of v over the 64 lanes of a wave, uniform; every
+// lane must be active.  DPP within each row of 16 lanes (quad permutations,
+// then the half-row and row mirrors), then the four rows' results.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xb1, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4e, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, false));
+    return op(op((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                 (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+              op((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                 (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
 // grid: 1-D, 8 * ceil(B * rows / 8) * P workgroups, one a partition.
 // Workgroup id mod 8 (its XCD) takes the rows rr = b * rows + r with rr mod 8
 // equal to it, the XCD of the row's resolve workgroup.
@@ -1108,13 +1123,10 @@ __global__ __launch_bounds__(256) void topk_part_kernel(
             hi = max(hi, key[e]);
         }
     }
-    uint32_t nvalid = (uint32_t)__popc(valid);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
-        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
-        nvalid += (uint32_t)__shfl_xor((int)nvalid, off, 64);
-    }
+    lo = wave_reduce(lo, [](uint32_t a, uint32_t b) { return min(a, b); });
+    hi = wave_reduce(hi, [](uint32_t a, uint32_t b) { return max(a, b); });
+    uint32_t nvalid =
+        wave_reduce((uint32_t)__popc(valid), [](uint32_t a, uint32_t b) { return a + b; });
     if (lane == 0) {
         red[0][wave] = lo;
         red[1][wave] = hi;
@@ -1191,21 +1203,6 @@ __global__ __launch_bounds__(256) void topk_part_kernel(
                 ? make_uint2(0u, 0xffffffffu)
                 : make_uint2(kept,
                              kept < nvalid ? (uint32_t)min(theta, (uint64_t)0xffffffffu) : 0u);
-}
-
-// Sum, smallest or largest of v over the 64 lanes of a wave, uniform; every
-// lane must be active.  DPP within each row of 16 lanes (quad permutations,
-// then the half-row and row mirrors), then the four rows' results.
-template <typename Op>
-__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
-    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xb1, 0xf, 0xf, false));
-    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4e, 0xf, 0xf, false));
-    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, false));
-    v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, false));
-    return op(op((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
-                 (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
-              op((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
-                 (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 
 // Sum, smallest and largest of the threads' values (uniform results; every
