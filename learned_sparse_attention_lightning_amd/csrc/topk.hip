@@ -106,7 +106,7 @@ struct SelectSmemT {
     uint32_t hist[kTkBins];
     uint32_t red_lo[NT / 64], red_hi[NT / 64];
     uint32_t scan[NT / 64];
-    uint32_t found_bin, found_above;
+    uint32_t found_bin, found_above, gcount;
 };
 using SelectSmem = SelectSmemT<kTkThreads>;
 
@@ -144,11 +144,21 @@ __device__ void block_key_range(Each each, SelectSmemT<NT> &sm, uint32_t &lo_out
     hi_out = hi;
 }
 
+// Keys left in range below which a histogram pass gives way to ranking them
+// pairwise.
+constexpr uint32_t kRankMax = 256;
+
 // Key value tau of the need-th largest of the keys visited by `each` (every
 // key of the set, over the workgroup), all of which lie in [lo, hi], and how
 // many keys equal to tau belong to the top `need` (need_out).  1 <= need <=
 // number of keys.  Called by all kTkThreads threads; the result is uniform.
-template <typename Each, int NT>
+// Histogram passes narrow [lo, hi] to the bin holding the need-th largest;
+// with Rank, once that bin holds at most kRankMax keys of several values
+// they are gathered and each counts the keys above it and at it: the value
+// with fewer than need above and at least need at or above is tau.  (Rank is
+// taken by the per-row workgroups of rows up to 4096 keys, where it saves a
+// pass or two; in the larger workgroups its registers cost occupancy.)
+template <bool Rank = false, typename Each, int NT>
 __device__ void block_select_in(Each each, uint32_t lo, uint32_t hi, uint32_t need,
                                 SelectSmemT<NT> &sm, uint32_t &tau_out, uint32_t &need_out) {
     const int tid = threadIdx.x;
@@ -188,11 +198,41 @@ __device__ void block_select_in(Each each, uint32_t lo, uint32_t hi, uint32_t ne
         __syncthreads();
         const uint32_t bin = sm.found_bin;
         need -= sm.found_above;
+        const uint32_t m = sm.hist[bin];  // keys in the narrowed range
         const uint32_t new_lo = lo + (bin << shift);
         const uint32_t width_m1 = (1u << shift) - 1u;
         hi = (hi - new_lo > width_m1) ? new_lo + width_m1 : hi;
         lo = new_lo;
         __syncthreads();
+        if (Rank && lo != hi && m <= kRankMax) {  // uniform
+            if (tid == 0) sm.gcount = 0u;
+            __syncthreads();
+            each([&](uint32_t u) {
+                if (u >= lo && u <= hi) {
+                    const uint32_t sl = atomicAdd(&sm.gcount, 1u);
+                    if (sl < kRankMax) sm.hist[sl] = u;
+                }
+            });
+            __syncthreads();
+            for (uint32_t a = tid; a < m; a += NT) {
+                const uint32_t ka = sm.hist[a];
+                uint32_t gt = 0u, ge = 0u;
+                for (uint32_t g = 0; g < m; ++g) {
+                    const uint32_t kg = sm.hist[g];
+                    gt += kg > ka ? 1u : 0u;
+                    ge += kg >= ka ? 1u : 0u;
+                }
+                if (gt < need && need <= ge) {  // every key equal to tau writes the same
+                    sm.found_bin = ka;
+                    sm.found_above = gt;
+                }
+            }
+            __syncthreads();
+            tau_out = sm.found_bin;
+            need_out = need - sm.found_above;
+            __syncthreads();
+            return;
+        }
     }
     tau_out = lo;
     need_out = need;
@@ -502,7 +542,7 @@ __device__ void select_row(const float *__restrict__ row, int n, int k, int32_t 
     if (!cached) block_key_range(each, sm.sel, lo, hi);
 
     uint32_t tau, need;
-    block_select_in(each, lo, hi, (uint32_t)k, sm.sel, tau, need);
+    block_select_in<(CACHE <= 4096)>(each, lo, hi, (uint32_t)k, sm.sel, tau, need);
 
     // ordered selection: all keys > tau, plus the first `need` keys == tau
     const int seg = ceil_div(ceil_div(n, (NT / 64)), 64) * 64;  // positions per wave
