@@ -698,6 +698,15 @@ hipError_t launch_indexer(const void *q_idx, const void *k_idx, int idx_dtype, c
             while (kchunk < keys_hi) kchunk <<= 1;
             while (kchunk > 4096 && nrb * ((keys_avg + kchunk - 1) / kchunk) < kPfMinWgs)
                 kchunk >>= 1;
+            if (!write_masked) {
+                // the same count of key ranges, made equal (whole tiles): with
+                // power-of-two ranges a row block's last range was short, the
+                // CUs that drew those finished early and others ran one more
+                // full range, so a launch took as long as if the rows reached
+                // the next multiple of the range
+                const long long n0 = (keys_hi + kchunk - 1) / kchunk;
+                kchunk = (int)(((keys_hi + n0 - 1) / n0 + kPfKeys - 1) / kPfKeys * kPfKeys);
+            }
             const int nkc = write_masked ? ceil_div(S, kchunk)
                                          : (int)((keys_hi + kchunk - 1) / kchunk);
             const long long wgs = nrb * nkc;
