@@ -564,17 +564,21 @@ def test_forward_short_last_chunk():
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("path", ["partitions", "slices"])
 @pytest.mark.parametrize("case", ["levels3", "all_equal", "k1", "kS", "short_rows", "neg",
                                   "planted_ties", "wide_tie_group"])
-def test_topk_wide_path_edges(case):
-    """Few wide rows take the split-row path: ties, degenerate budgets,
-    rows shorter than the budget and negative scores.  planted_ties puts a
-    handful of copies of the k-th largest value across the row (a small tie
-    group straddling the threshold, ranked by position); wide_tie_group puts
-    thousands (the group exceeds the ranking buffer and takes the general
-    threshold search)."""
-    B, S = 4, 40000
-    k = {"k1": 1, "kS": S}.get(case, 2048)
+def test_topk_wide_path_edges(case, path):
+    """Few wide rows: ties, degenerate budgets, rows shorter than the budget
+    and negative scores, on both wide paths -- the partition path (k = 2048
+    of 40000) and the split-row path (k = 8192 of 131072: more kept keys
+    than the partitions' resolve holds).  planted_ties puts a handful of
+    copies of the k-th largest value across the row (a small tie group
+    straddling the threshold, ranked by position); wide_tie_group puts
+    thousands (the split-row path's group then exceeds its ranking buffer and
+    takes the general threshold search; the partition path keeps them and
+    ranks them by a second search, or runs the exact selection)."""
+    B, S, kb = (4, 40000, 2048) if path == "partitions" else (4, 131072, 8192)
+    k = {"k1": 1, "kS": S}.get(case, kb)
     levels = {"levels3": 3, "all_equal": 1}.get(case)
     sc = synth.random_scores((B, 1, S), seed=sum(map(ord, case)), levels=levels)
     if case == "neg":
@@ -589,9 +593,9 @@ def test_topk_wide_path_edges(case):
             sc[bb, 0, where] = kth
     pos = torch.tensor([[S - 1], [S - 1], [20000], [S - 7]], dtype=torch.int32)
     if case == "short_rows":
-        pos = torch.tensor([[10], [2047], [2048], [2049]], dtype=torch.int32)
+        pos = torch.tensor([[10], [kb - 1], [kb], [kb + 1]], dtype=torch.int32)
     idx = dsa.dsa_topk(sc.to(DEV), k, q_pos=pos.to(DEV))
-    assert_selection_equal(idx, oracle.topk(sc, k, q_pos=pos), case)
+    assert_selection_equal(idx, oracle.topk(sc, k, q_pos=pos), f"{case} {path}")
 
 
 @pytest.mark.parametrize("case", ["random", "window", "one_partition", "ties_small",
@@ -605,8 +609,8 @@ def test_topk_partition_path(case):
     one partition on top (it must drop some: the exact passes), a few and
     more than a thousand copies of the k-th largest score (ranked pairwise,
     or by a second search on the positions), heavy ties, rows barely longer
-    than k, rows that are not 16-byte aligned, and a budget too large for the
-    partitions (the split-row path)."""
+    than k, rows that are not 16-byte aligned, and a large budget (k = 8192 of
+    40000: 20 partitions keeping up to 544 keys each)."""
     B, S, k = 3, 131072, 2048
     if case == "odd_S":
         S = 40001
