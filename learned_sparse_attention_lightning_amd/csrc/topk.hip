@@ -239,7 +239,7 @@ __device__ void block_select_in(Each each, uint32_t lo, uint32_t hi, uint32_t ne
 }
 
 // block_select_in over keys key_at(0..n-1), range found first.
-template <typename KeyAt, int NT>
+template <bool Rank = false, typename KeyAt, int NT>
 __device__ void block_select(KeyAt key_at, int n, uint32_t need, SelectSmemT<NT> &sm,
                              uint32_t &tau_out, uint32_t &need_out) {
     auto each = [&](auto f) {
@@ -247,7 +247,7 @@ __device__ void block_select(KeyAt key_at, int n, uint32_t need, SelectSmemT<NT>
     };
     uint32_t lo, hi;
     block_key_range(each, sm, lo, hi);
-    block_select_in(each, lo, hi, need, sm, tau_out, need_out);
+    block_select_in<Rank>(each, lo, hi, need, sm, tau_out, need_out);
 }
 
 // ------------------------------------------------------- per-row kernel ----
@@ -271,6 +271,9 @@ constexpr int kSampleRun = 32;
 template <int NT, int CACHE>
 __device__ bool sampled_select(const float *__restrict__ row, int n, int k,
                                int32_t *__restrict__ out, RowSmemT<NT, CACHE> &sm) {
+    // the two threshold searches rank their last bin in the 512-thread tier,
+    // where that fits the registers (elsewhere it spills)
+    constexpr bool kSampledRank = NT == 512;
     constexpr int W = NT / 64;
     constexpr int kCap = CACHE / 2 / W;        // candidates per wave
     constexpr int kMaxRuns = CACHE / 2 / kSampleRun;
@@ -309,7 +312,8 @@ __device__ bool sampled_select(const float *__restrict__ row, int n, int k,
     const uint32_t need_s =
         (uint32_t)min((long long)ns, (long long)k * ns * 5 / (4LL * n) + 32);
     uint32_t tau_s, unused;
-    block_select([&](int j) -> uint32_t { return ck[j]; }, ns, need_s, sm.sel, tau_s, unused);
+    block_select<kSampledRank>([&](int j) -> uint32_t { return ck[j]; }, ns, need_s, sm.sel, tau_s,
+                               unused);
     __syncthreads();  // every thread is done with the samples
     // 2. one pass over the row: each wave keeps its segment's keys >= tau_s,
     // in position order.  Segments are whole multiples of 256 positions, so
@@ -409,7 +413,7 @@ __device__ bool sampled_select(const float *__restrict__ row, int n, int k,
     };
     uint32_t lo, hi, tau, need;
     block_key_range(each, sm.sel, lo, hi);
-    block_select_in(each, lo, hi, (uint32_t)k, sm.sel, tau, need);
+    block_select_in<kSampledRank>(each, lo, hi, (uint32_t)k, sm.sel, tau, need);
     // 4. in position order (wave regions in order, each in order): all keys
     // > tau and the first `need` keys == tau
     const uint32_t mine = cw[wave];
