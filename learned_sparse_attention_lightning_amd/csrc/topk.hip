@@ -1057,6 +1057,7 @@ constexpr int kPartMax = 12288;                        // kept keys a row's reso
 constexpr int kPartPieces = kPartMax / 2 / kTkThreads;  // 16-byte pieces per resolve thread
 constexpr int kPartMaxP = kWideMaxS / kPartKeys;       // 128
 constexpr int kPartTies = 1024;                        // keys equal to tau ranked pairwise
+constexpr uint32_t kPartRefineMin = 32;                // crossing bins below this are not refined
 
 struct PartLayout {
     uint2 *meta;  // [rows][P] (kept count, threshold; 0 when nothing was dropped)
@@ -1192,8 +1193,10 @@ __global__ __launch_bounds__(256) void topk_part_kernel(
         uint32_t room = (uint32_t)L.cap, first;
         part_first_bin(hist, lane, room, first);
         theta = (uint64_t)lo + ((uint64_t)first << shift);
-        if (first >= 1 && shift > 0) {  // uniform: refine inside bin first - 1
-            // (it holds a key; the bins above it hold cap - room keys)
+        // refine inside bin first - 1 (it holds a key; the bins above it hold
+        // cap - room keys) unless it holds few: then keeping only the bins
+        // above it loses little (a row of random scores: never refined)
+        if (first >= 1 && shift > 0 && hist[first - 1] > kPartRefineMin) {  // uniform
             const uint32_t b1 = first - 1;
             const uint32_t base = lo + (b1 << shift);
             const int s2 = shift > 8 ? shift - 8 : 0;
