@@ -63,7 +63,10 @@ __global__ __launch_bounds__(256) void attention_gather_kernel(
 
     for (int c0 = 0; c0 < k; c0 += 64) {
         const int j = c0 + lane;
-        const int s = j < k ? sel[j] : -1;
+        // entries past the cache (outside the contract) count as unused, as in
+        // the selection bitmap of the MHA kernel
+        const int sj = j < k ? sel[j] : -1;
+        const int s = sj < S ? sj : -1;
         float logit = -INFINITY;
         if (s >= 0) {
             const size_t koff = form == DSA_MHA ? (((size_t)b * S + s) * H + h) * dqk

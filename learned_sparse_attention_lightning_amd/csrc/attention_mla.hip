@@ -153,6 +153,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
     const int ntiles = split_tiles(len);
     const int32_t *sel_row = idx + ((size_t)b * T + i) * k + e_begin;
     const uint8_t *lat_b = reinterpret_cast<const uint8_t *>(lat) + (size_t)b * S * kLatRowBytes;
+    const int32_t s_last = S - 1;  // gathers stay inside the sequence's rows
     const size_t rowq = (size_t)b * T + i;
     const size_t prow = (size_t)qidx;  // row of this launch's split partials
     // selected row of entry e of the split (-1: masked or past the split)
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             const int32_t s = sm.sel[sel_slot(t)][l32];
 #pragma unroll
             for (int j = 0; j < kRopeSteps; ++j)
-                rp[j] = *reinterpret_cast<const bf16x8 *>(lat_b + rope_offset(s, half, j));
+                rp[j] = *reinterpret_cast<const bf16x8 *>(lat_b + rope_offset(s, s_last, half, j));
         };
         // this wave's half of S^T(t): K fragments from the LDS ring (and, for
         // kh = 1, the rope registers)
@@ -202,7 +203,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
         // the sum with the partner's half is -inf too.  Whole tiles are the
         // rule; the branch is uniform.
         auto mask_tile = [&](int t, f32x16 &acc) {
-            const uint32_t vmask = (uint32_t)__ballot(sm.sel[sel_slot(t)][l32] >= 0);
+            // an entry counts when it is a cached position: -1 (unused) and
+            // entries past the cache (outside the contract) are masked
+            const uint32_t vmask =
+                (uint32_t)__ballot((uint32_t)sm.sel[sel_slot(t)][l32] < (uint32_t)S);
             if (vmask != 0xffffffffu) {
                 const uint32_t mh = vmask >> (4 * half);
 #pragma unroll
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
 #pragma unroll
             for (int m = 0; m < kStageRows; ++m) {
                 const int32_t s = __builtin_amdgcn_readfirstlane(rowv[m]);
-                st[m] = *reinterpret_cast<const u32x4 *>(lat_b + gather_offset(s, lane));
+                st[m] = *reinterpret_cast<const u32x4 *>(lat_b + gather_offset(s, s_last, lane));
             }
         };
         auto stage_store = [&](int t, const u32x4 (&st)[kStageRows]) {
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_attention_kernel(
             for (int m = 0; m < kStageRows; ++m) {
                 const int32_t s =
                     __builtin_amdgcn_readfirstlane(sel_of(t * kKt + kStageRows * d + m));
-                st[m] = *reinterpret_cast<const u32x4 *>(lat_b + gather_offset(s, lane));
+                st[m] = *reinterpret_cast<const u32x4 *>(lat_b + gather_offset(s, s_last, lane));
             }
         };
         u32x4 stg[2][kStageRows];

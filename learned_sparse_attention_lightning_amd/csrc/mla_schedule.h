@@ -151,17 +151,20 @@ __host__ __device__ inline int split_tiles(int len) {
 // element offsets into q, out, the split partials and lse) ----
 
 // Row s of the latent table: masked entries (s < 0) read row 0 (their
-// probability is forced to 0).
-__host__ __device__ inline uint64_t latent_row_offset(int32_t s) {
-    return (uint64_t)(uint32_t)(s > 0 ? s : 0) * (uint64_t)kLatRowBytes;
+// probability is forced to 0).  Entries past the cache (s > last = S - 1) are
+// outside the selection's contract; their loads are kept inside the
+// sequence's rows (row `last`), so a bad selection cannot read past the table.
+__host__ __device__ inline uint64_t latent_row_offset(int32_t s, int32_t last) {
+    const int32_t r = s > 0 ? (s < last ? s : last) : 0;
+    return (uint64_t)(uint32_t)r * (uint64_t)kLatRowBytes;
 }
 // 16-byte piece `lane` (0..63) of a row's value dims, gathered by a PV wave.
-__host__ __device__ inline uint64_t gather_offset(int32_t s, int lane) {
-    return latent_row_offset(s) + 16ull * (uint64_t)lane;
+__host__ __device__ inline uint64_t gather_offset(int32_t s, int32_t last, int lane) {
+    return latent_row_offset(s, last) + 16ull * (uint64_t)lane;
 }
 // Rope piece j (0..3) of lane half `half` (kh = 1 S waves).
-__host__ __device__ inline uint64_t rope_offset(int32_t s, int half, int j) {
-    return latent_row_offset(s) + (uint64_t)kVRowBytes + 16ull * (uint64_t)half +
+__host__ __device__ inline uint64_t rope_offset(int32_t s, int32_t last, int half, int j) {
+    return latent_row_offset(s, last) + (uint64_t)kVRowBytes + 16ull * (uint64_t)half +
            32ull * (uint64_t)j;
 }
 // First element of the 8 query dims of k-step ks for (head tile ht, lane

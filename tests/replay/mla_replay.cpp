@@ -58,7 +58,7 @@ struct Launch {
     bool causal_tail;
     int out_bytes;        // 2 (bf16) or 4 (fp32)
     std::vector<int> qpos;  // [B*T] or empty (t = S - T + i)
-    std::string sel;        // "causal" | "max" | "holes"
+    std::string sel;        // "causal" | "max" | "holes" | "wild"
 };
 
 int row_pos(const Launch &L, int b, int i) {
@@ -76,6 +76,11 @@ std::vector<int32_t> make_selection(const Launch &L, uint64_t seed) {
             const int t = row_pos(L, b, i);
             if (L.sel == "max") {
                 for (int e = 0; e < L.k; ++e) row[e] = L.S - 1;
+            } else if (L.sel == "wild") {
+                // outside the contract: entries at and far past the cache's end
+                for (int e = 0; e < L.k; ++e)
+                    row[e] = (e % 3 == 0) ? L.S + (int32_t)(rng() % 1000000u)
+                                          : (e % 3 == 1) ? INT32_MAX - (int32_t)(rng() % 7u) : L.S;
             } else if (L.sel == "holes") {
                 for (int e = 0; e < L.k; ++e)
                     row[e] = (rng() % 5 == 0) ? -1 : (int32_t)(rng() % (uint64_t)L.S);
@@ -221,14 +226,14 @@ void replay_workgroup(Ctx &C, int id) {
         return -1;
     };
     auto gather = [&](int32_t s) {  // one wave load of a row's value dims, lanes 0..63
-        in_bounds("latent gather", lat_b + (long long)gather_offset(s, 0),
-                  lat_b + (long long)gather_offset(s, 63) + 16, C.buf.lat_bytes);
+        in_bounds("latent gather", lat_b + (long long)gather_offset(s, L.S - 1, 0),
+                  lat_b + (long long)gather_offset(s, L.S - 1, 63) + 16, C.buf.lat_bytes);
     };
     auto rope = [&](int32_t s) {
         for (int half = 0; half < 2; ++half)
             for (int j = 0; j < kRopeSteps; ++j)
-                in_bounds("rope load", lat_b + (long long)rope_offset(s, half, j),
-                          lat_b + (long long)rope_offset(s, half, j) + 16, C.buf.lat_bytes);
+                in_bounds("rope load", lat_b + (long long)rope_offset(s, L.S - 1, half, j),
+                          lat_b + (long long)rope_offset(s, L.S - 1, half, j) + 16, C.buf.lat_bytes);
     };
 
     // ---- the 8 waves, phase by phase (a phase ends at a workgroup barrier)
@@ -694,6 +699,8 @@ int main(int argc, char **argv) {
         // the 128K decode step: 8 sequences x 131072, one query row each
         mk("128K decode (forward: causal tail)", 8, 1, 131072, 128, 2048, 0, 1, true, 2, "causal"),
         mk("128K decode, every entry = S-1", 8, 1, 131072, 128, 2048, 0, 1, false, 2, "max"),
+        mk("128K decode, entries past the cache (outside the contract)", 8, 1, 131072, 128, 2048,
+           0, 1, false, 2, "wild"),
         mk("128K decode, holes and -1 anywhere", 8, 1, 131072, 128, 2048, 0, 1, false, 2,
            "holes"),
         mk("128K decode, positions t < k (empty splits)", 8, 1, 131072, 128, 2048, 0, 1, true, 2,

@@ -224,3 +224,38 @@ def test_forward_include_current_c4_full():
     err = max_abs_err(out, ref)
     _say(f"c4 with the current token: max-abs err {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("case", ["mla-decode-h128", "mla-prefill-h128", "mla-decode-h16",
+                                  "mha-prefill-h16"])
+def test_attention_entries_past_cache_count_as_unused(case):
+    """Selection entries at or past the cache's end (s >= S) are outside the
+    selection's contract; every attention kernel counts them as unused slots,
+    like -1, and reads nothing past the sequence's rows: outputs equal the
+    oracle's on the selection with those entries set to -1."""
+    form, kind, h = case.split("-")
+    heads = int(h[1:])
+    if form == "mla":
+        base = configs.get("c4" if kind == "decode" else "c2")
+    else:
+        base = configs.get("c1")
+    T = 1 if kind == "decode" else 300
+    w = base.with_(name=f"wild-{case}", B=4 if kind == "decode" else 1, T=T, S=3000,
+                   num_heads=heads)
+    x = synth.make_inputs(w, device=DEV, seed=31)
+    sc = dsa.dsa_indexer_scores(x["q_idx"], x["k_idx"], x["w"])
+    idx = dsa.dsa_topk(sc, w.index_topk).cpu()
+    rng = np.random.default_rng(37)
+    wild = torch.from_numpy(rng.random(idx.shape) < 0.2) & (idx >= 0)
+    vals = torch.tensor([w.S, w.S + 1, w.S + 4097, 2**31 - 1], dtype=torch.int32)
+    pick = torch.from_numpy(rng.integers(0, len(vals), idx.shape))
+    idx_wild = torch.where(wild, vals[pick], idx)
+    idx_ref = torch.where(wild, torch.full_like(idx, -1), idx)
+    _say(f"{case}: {int(wild.sum())} entries past the cache of {idx.numel()}")
+    desc = dsa.desc_for(w)
+    out = dsa.dsa_sparse_attention(desc, x["q"], x["kv"], x.get("v"), idx_wild.to(DEV))
+    torch.cuda.synchronize()
+    rows = list(range(T)) if T <= 8 else [0, 1, 2, 150, T - 2, T - 1]
+    ref = oracle.sparse_attention(form, x["q"][:, rows], x["kv"], x.get("v"),
+                                  idx_ref[:, rows], w.scale, d_v=w.d_v)
+    assert max_abs_err(out[:, rows], ref) <= TOL["bf16"]

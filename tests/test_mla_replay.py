@@ -6,7 +6,8 @@ tile schedule, workgroup mapping, split plan and global addresses from
 (csrc/mla_schedule.h), and checks every LDS ring access against the barrier
 schedule and every global address against its buffer.  The launches include
 the 128K-context decode (8 x 131072, 128 heads, k = 2048) with valid, extreme
-(every entry S-1), holed, short (t < k) and past-the-cache selections, and a
+(every entry S-1), holed, short (t < k), past-the-cache positions and
+out-of-contract entries (>= S) selections, and a
 model of the kernel as committed at 07:13 on the day a GPU fault was reported
 at that shape.
 
@@ -74,11 +75,14 @@ MUTANTS = [
      "constexpr int sel_slot(int tile) { return tile % kSelRing; }",
      "constexpr int sel_slot(int tile) { return tile % (kSelRing / 2); }"),
     ("masked entries gather row -1",
-     "return (uint64_t)(uint32_t)(s > 0 ? s : 0) * (uint64_t)kLatRowBytes;",
-     "return (uint64_t)(uint32_t)s * (uint64_t)kLatRowBytes;"),
+     "const int32_t r = s > 0 ? (s < last ? s : last) : 0;",
+     "const int32_t r = s < last ? s : last;"),
+    ("entries past the cache not clamped",
+     "const int32_t r = s > 0 ? (s < last ? s : last) : 0;",
+     "const int32_t r = s > 0 ? s : 0;"),
     ("rope pieces one piece too far",
-     "return latent_row_offset(s) + (uint64_t)kVRowBytes + 16ull * (uint64_t)half +",
-     "return latent_row_offset(s) + (uint64_t)kVRowBytes + 16ull + 16ull * (uint64_t)half +"),
+     "return latent_row_offset(s, last) + (uint64_t)kVRowBytes + 16ull * (uint64_t)half +",
+     "return latent_row_offset(s, last) + (uint64_t)kVRowBytes + 16ull + 16ull * (uint64_t)half +"),
     ("partials without the dim offset",
      "return (prow * splits * H + head) * kDv + d + (size_t)split * part_split_stride(H);",
      "return (prow * splits * H + head) * kDv + (size_t)split * part_split_stride(H);"),
