@@ -170,6 +170,8 @@ dsa_status_t dsa_topk_ex(const float *scores, const int32_t *q_pos, int B, int T
  * 4.1):
  *   out[b,i,h,:] = sum_{s in S} softmax_s( scale * q[b,i,h,:] . key(s,h) ) * value(s,h)
  * where S = the entries of idx[b,i,:] that are >= 0 (distinct, each < S).
+ * Entries >= S are outside this contract; they count as unused slots (like
+ * -1) and no kernel reads a row past the sequence's S rows for them.
  *   MHA: kv = K [B,S,H,d_qk], v = V [B,S,H,d_v]; key(s,h) = K[b,s,h],
  *        value(s,h) = V[b,s,h].
  *   MLA: kv = latent [B,S,d_qk], v = NULL; key(s,h) = latent[b,s,:] (all
